@@ -1,0 +1,120 @@
+"""CPU oracle for single-precision GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never imports, links or
+calls it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``sgemm_oracle.c`` (plain C, fp64 accumulation, one
+rounding to float).  This module builds that file with gcc and marshals numpy
+arrays into it.  The operation is C = alpha * (A * B) + beta * C on row-major
+matrices, as defined in "a CUDA matmul" (plasmient.com labs) section 00 and
+"The GEMM Scrapbook" introduction; see the C file's header for the readings
+taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sgemm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile sgemm_oracle.c into liboracle.so next to it (gcc, no GPU code).
+
+    -ffp-contract=off keeps the epilogue as separate multiply and add; the
+    k-loop products are exact in double, so contraction there would not change
+    any result either.
+    """
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+           "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_sgemm.restype = ctypes.c_int
+        lib.oracle_sgemm.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def sgemm_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nthreads=None) -> int:
+    """Direct call on flat float32 numpy buffers (C is updated in place)."""
+    lib = _load()
+
+    def ptr(x):
+        if x is None:
+            return None
+        assert x.dtype == np.float32 and x.flags.c_contiguous
+        return x.ctypes.data
+
+    return lib.oracle_sgemm(int(M), int(N), int(K), float(alpha), ptr(A), int(lda),
+                            ptr(B), int(ldb), float(beta), ptr(C), int(ldc),
+                            int(nthreads or default_threads()))
+
+
+def _ld(x: np.ndarray) -> int:
+    """Leading dimension (in elements) of a row-major 2-D float32 view."""
+    assert x.dtype == np.float32 and x.ndim == 2
+    assert x.shape[1] <= 1 or x.strides[1] == 4, "rows must be contiguous"
+    ld = x.strides[0] // 4
+    if x.shape[0] <= 1 or x.shape[1] == 0:
+        ld = max(ld, x.shape[1], 1)
+    return ld
+
+
+def _base(x: np.ndarray):
+    return x.ctypes.data if x.size else None
+
+
+def sgemm(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None,
+          alpha: float = 1.0, beta: float = 0.0, nthreads: int | None = None) -> np.ndarray:
+    """C = alpha * A @ B + beta * C on 2-D float32 arrays (row-major views with
+    unit column stride; padded rows are allowed).  C is updated in place when
+    given; otherwise a new (M, N) array is returned (beta must then be 0)."""
+    lib = _load()
+    M, K = A.shape
+    K2, N = B.shape
+    assert K == K2, "inner dimensions differ"
+    if C is None:
+        assert beta == 0.0
+        C = np.empty((M, N), dtype=np.float32)
+    assert C.shape == (M, N)
+    st = lib.oracle_sgemm(M, N, K, float(alpha), _base(A), _ld(A), _base(B), _ld(B),
+                          float(beta), _base(C), _ld(C),
+                          int(nthreads or default_threads()))
+    if st != 0:
+        raise RuntimeError(f"oracle_sgemm returned {st}")
+    return C
+
+
+def version() -> int:
+    return _load().oracle_version()

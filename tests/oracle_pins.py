@@ -1,0 +1,225 @@
+"""Pins for the CPU oracle: checks that tie it to the mathematics, not to itself.
+
+Each pin calls an oracle entry point through ``call(M, N, K, alpha, A, lda,
+B, ldb, beta, C, ldc) -> status`` on flat float32 buffers, so the same pins run
+against the real oracle and against deliberately broken copies of it (see
+test_oracle.py).  The pins are:
+
+  brute_force   exact rational arithmetic (fractions.Fraction) on every shape
+                with M, N, K in 1..4, random fp32 entries and random alpha/beta:
+                the oracle must equal the correctly rounded fp32 value of the
+                exact result, up to the fp64 summation error bound.
+  identity      A = I gives C = B, B = I gives C = A, exactly.
+  ones          all-ones A and B give C = K exactly.
+  permutation   B a permutation matrix gives an exact column shuffle of A.
+  one_hot       a single 1 in A and in B gives a single 1 in C at (i, j).
+  beta0_nan     beta = 0 never reads C: NaN-filled C gives a finite result.
+  alpha0_nan    alpha = 0 never reads A or B: C = beta * C exactly.
+  ld_padding    NaN in the row padding of A and B does not leak; C's padding
+                is left untouched.
+
+The definition pinned: C = alpha * (A * B) + beta * C, each cell a dot product
+of a row of A and a column of B ("a CUDA matmul" section 00; "The GEMM
+Scrapbook" introduction; "The 1% kernel" section 1).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+F32 = np.float32
+
+
+def rn32(x: Fraction) -> float:
+    """Correctly rounded (nearest, ties to even) float32 value of a rational."""
+    if x == 0:
+        return 0.0
+    f = np.float32(float(x))
+    best, best_key = None, None
+    for c in (np.nextafter(f, F32(-np.inf)), f, np.nextafter(f, F32(np.inf))):
+        key = (abs(Fraction(float(c)) - x), int(np.float32(c).view(np.uint32)) & 1)
+        if best_key is None or key < best_key:
+            best, best_key = float(c), key
+    return best
+
+
+def exact_cell(A, B, C0, i, j, alpha, beta):
+    """(exact value, magnitude bound) of alpha * sum_k A[i,k] B[k,j] + beta * C0[i,j]."""
+    K = A.shape[1]
+    terms = [Fraction(float(A[i, k])) * Fraction(float(B[k, j])) for k in range(K)]
+    a = Fraction(float(alpha))
+    b = Fraction(float(beta))
+    if alpha == 0 or K == 0:
+        val = Fraction(0) if beta == 0 else b * Fraction(float(C0[i, j]))
+        return val, abs(val)
+    val = a * sum(terms, Fraction(0))
+    mag = abs(a) * sum((abs(t) for t in terms), Fraction(0))
+    if beta != 0:
+        bc = b * Fraction(float(C0[i, j]))
+        val += bc
+        mag += abs(bc)
+    return val, mag
+
+
+def within_fp64_rounding(r: float, exact: Fraction, mag: Fraction, K: int) -> bool:
+    """r must lie between RN32(exact - d) and RN32(exact + d), where d bounds the
+    error of summing K exact products and the epilogue in fp64."""
+    d = Fraction(K + 4, 2 ** 52) * mag
+    return rn32(exact - d) <= r <= rn32(exact + d)
+
+
+def run(call, A, B, C0, alpha, beta, lda=None, ldb=None, ldc=None):
+    """Call the oracle on dense copies; returns (status, C)."""
+    M, K = A.shape
+    N = B.shape[1]
+    A_ = np.ascontiguousarray(A, dtype=F32).reshape(-1)
+    B_ = np.ascontiguousarray(B, dtype=F32).reshape(-1)
+    C = (np.ascontiguousarray(C0, dtype=F32).copy() if C0 is not None
+         else np.full((M, N), np.nan, dtype=F32))
+    st = call(M, N, K, alpha, A_, lda or max(K, 1), B_, ldb or max(N, 1), beta,
+              C.reshape(-1), ldc or max(N, 1))
+    return st, C
+
+
+def pin_brute_force(call, rng, dims=range(1, 5)) -> list[str]:
+    fails = []
+    for M in dims:
+        for N in dims:
+            for K in dims:
+                A = rng.uniform(-2, 2, (M, K)).astype(F32)
+                B = rng.uniform(-2, 2, (K, N)).astype(F32)
+                C0 = rng.uniform(-2, 2, (M, N)).astype(F32)
+                for alpha, beta in ((1.0, 0.0), (float(F32(rng.uniform(-3, 3))),
+                                                 float(F32(rng.uniform(-3, 3))))):
+                    st, C = run(call, A, B, C0 if beta != 0 else None, alpha, beta)
+                    if st != 0:
+                        fails.append(f"brute_force status {st} at {(M, N, K)}")
+                        continue
+                    for i in range(M):
+                        for j in range(N):
+                            ex, mag = exact_cell(A, B, C0, i, j, alpha, beta)
+                            if not within_fp64_rounding(float(C[i, j]), ex, mag, K):
+                                fails.append(f"brute_force {(M, N, K)} cell {(i, j)}: "
+                                             f"{C[i, j]!r} vs exact {float(ex)!r}")
+                                break
+    return fails
+
+
+def pin_closed_forms(call, rng) -> list[str]:
+    fails = []
+    # identity on both sides, ragged shapes
+    for (M, K) in ((5, 5), (17, 17), (33, 33)):
+        I = np.eye(K, dtype=F32)
+        for N in (1, 7, 40):
+            B = rng.uniform(-1, 1, (K, N)).astype(F32)
+            st, C = run(call, I, B, None, 1.0, 0.0)
+            if st or not np.array_equal(C, B):
+                fails.append(f"identity-left {(M, N, K)}")
+            A = rng.uniform(-1, 1, (N, K)).astype(F32)
+            st, C = run(call, A, I, None, 1.0, 0.0)
+            if st or not np.array_equal(C, A):
+                fails.append(f"identity-right {(N, K)}")
+    # all ones: C = K
+    for (M, N, K) in ((3, 5, 7), (16, 9, 100), (1, 1, 1000)):
+        st, C = run(call, np.ones((M, K), F32), np.ones((K, N), F32), None, 1.0, 0.0)
+        if st or not np.all(C == F32(K)):
+            fails.append(f"ones {(M, N, K)}")
+    # permutation: B = P with P[perm[j], j] = 1, so C[:, j] = A[:, perm[j]]
+    for (M, K) in ((6, 11), (13, 29)):
+        perm = rng.permutation(K)
+        P = np.zeros((K, K), F32)
+        P[perm, np.arange(K)] = 1.0
+        A = rng.uniform(-1, 1, (M, K)).astype(F32)
+        st, C = run(call, A, P, None, 1.0, 0.0)
+        if st or not np.array_equal(C, A[:, perm]):
+            fails.append(f"permutation {(M, K)}")
+    # one-hot: A = e_i e_k^T, B = e_k e_j^T -> single 1 at (i, j)
+    M, N, K = 7, 9, 5
+    for (i, j, k) in ((0, 0, 0), (6, 8, 4), (3, 1, 2)):
+        A = np.zeros((M, K), F32); A[i, k] = 1
+        B = np.zeros((K, N), F32); B[k, j] = 1
+        st, C = run(call, A, B, None, 1.0, 0.0)
+        E = np.zeros((M, N), F32); E[i, j] = 1
+        if st or not np.array_equal(C, E):
+            fails.append(f"one_hot {(i, j, k)}")
+    return fails
+
+
+def pin_alpha_beta(call, rng) -> list[str]:
+    fails = []
+    M, N, K = 9, 11, 13
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    # beta == 0: C must not be read
+    st, C = run(call, A, B, np.full((M, N), np.nan, F32), 1.5, 0.0)
+    if st or not np.all(np.isfinite(C)):
+        fails.append("beta0_nan")
+    # alpha == 0: A and B must not be read; C = beta * C exactly (beta = 0.5)
+    C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+    st, C = run(call, np.full((M, K), np.nan, F32), np.full((K, N), np.nan, F32),
+                C0, 0.0, 0.5)
+    if st or not np.array_equal(C, C0 * F32(0.5)):
+        fails.append("alpha0_nan")
+    # alpha == 0, beta == 0: zero fill without reading anything
+    st, C = run(call, np.full((M, K), np.nan, F32), np.full((K, N), np.nan, F32),
+                np.full((M, N), np.nan, F32), 0.0, 0.0)
+    if st or not np.all(C == 0):
+        fails.append("alpha0_beta0")
+    # integer-valued alpha/beta case: exact
+    Ai = rng.integers(-4, 5, (M, K)).astype(F32)
+    Bi = rng.integers(-4, 5, (K, N)).astype(F32)
+    Ci = rng.integers(-4, 5, (M, N)).astype(F32)
+    st, C = run(call, Ai, Bi, Ci, 0.5, -1.25)
+    want = (0.5 * (Ai.astype(np.int64) @ Bi.astype(np.int64)) - 1.25 * Ci).astype(F32)
+    if st or not np.array_equal(C, want):
+        fails.append("alpha_beta_integer")
+    return fails
+
+
+def pin_ld_padding(call, rng) -> list[str]:
+    fails = []
+    M, N, K = 7, 10, 6
+    pa, pb, pc = 3, 5, 2
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+    As = np.full((M, K + pa), np.nan, F32); As[:, :K] = A
+    Bs = np.full((K, N + pb), np.nan, F32); Bs[:, :N] = B
+    Cs = np.full((M, N + pc), 777.0, F32); Cs[:, :N] = C0
+    st = call(M, N, K, 1.0, As.reshape(-1), K + pa, Bs.reshape(-1), N + pb, 1.0,
+              Cs.reshape(-1), N + pc)
+    _, Ctight = run(call, A, B, C0, 1.0, 1.0)
+    if st or not np.array_equal(Cs[:, :N], Ctight):
+        fails.append("ld_padding values")
+    if not np.all(Cs[:, N:] == 777.0):
+        fails.append("ld_padding C pad written")
+    return fails
+
+
+def all_pins(call, seed=1234, square_only=False) -> list[str]:
+    """Every pin; square_only restricts brute force to M = N = K (used for
+    broken copies whose indexing is only memory-safe on square shapes)."""
+    rng = np.random.default_rng(seed)
+    fails = []
+    if square_only:
+        return _square_brute(call, rng)
+    fails += pin_brute_force(call, rng)
+    fails += pin_closed_forms(call, rng)
+    fails += pin_alpha_beta(call, rng)
+    fails += pin_ld_padding(call, rng)
+    return fails
+
+
+def _square_brute(call, rng) -> list[str]:
+    fails = []
+    for n in range(2, 6):
+        A = rng.uniform(-2, 2, (n, n)).astype(F32)
+        B = rng.uniform(-2, 2, (n, n)).astype(F32)
+        st, C = run(call, A, B, None, 1.0, 0.0)
+        for i in range(n):
+            for j in range(n):
+                ex, mag = exact_cell(A, B, None, i, j, 1.0, 0.0)
+                if st or not within_fp64_rounding(float(C[i, j]), ex, mag, n):
+                    fails.append(f"square brute {n} {(i, j)}")
+    return fails

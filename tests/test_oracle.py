@@ -1,0 +1,181 @@
+"""The CPU oracle against what the mathematics fixes (runs without a GPU).
+
+Beyond the pins in oracle_pins.py this file checks the oracle against test-only
+library routines (numpy int64 and float64 matrix products), checks thread-count
+invariance and argument validation, and compiles deliberately broken copies of
+the oracle to show that each plausible mistake fails at least one pin.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle_pins import all_pins, run
+
+F32 = np.float32
+HERE = os.path.dirname(os.path.abspath(__file__))
+ORACLE_SRC = os.path.join(os.path.dirname(HERE), "oracle", "sgemm_oracle.c")
+
+
+def _caller(lib, nthreads=1):
+    fn = lib.oracle_sgemm
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+
+    def call(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+        p = lambda x: x.ctypes.data if (x is not None and x.size) else None
+        return fn(M, N, K, alpha, p(A), lda, p(B), ldb, beta, p(C), ldc, nthreads)
+    return call
+
+
+@pytest.fixture(scope="module")
+def call(oracle_mod):
+    return _caller(ctypes.CDLL(oracle_mod._LIB), nthreads=3)
+
+
+def test_all_pins_pass(call):
+    assert all_pins(call) == []
+
+
+def test_integer_exact_matches_int64_library(oracle_mod):
+    rng = np.random.default_rng(7)
+    M, N, K = 67, 45, 301
+    A = rng.integers(-4, 5, (M, K))
+    B = rng.integers(-4, 5, (K, N))
+    C = oracle_mod.sgemm(A.astype(F32), B.astype(F32))
+    assert np.array_equal(C, (A @ B).astype(F32))
+
+
+def test_matches_float64_library_within_one_ulp(oracle_mod):
+    rng = np.random.default_rng(8)
+    n = 256
+    A = rng.uniform(-1, 1, (n, n)).astype(F32)
+    B = rng.uniform(-1, 1, (n, n)).astype(F32)
+    C = oracle_mod.sgemm(A, B)
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(F32))
+    assert np.all(np.abs(C.astype(np.float64) - ref) <= ulp)
+
+
+def test_large_k_sampled_rows_float64(oracle_mod):
+    """Rows sampled from a 4096-deep product agree with the float64 library."""
+    rng = np.random.default_rng(9)
+    M, N, K = 8, 512, 4096
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    C = oracle_mod.sgemm(A, B)
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    assert np.all(np.abs(C - ref) <= np.spacing(np.abs(ref).astype(F32)))
+
+
+def test_thread_count_does_not_change_bits(oracle_mod):
+    rng = np.random.default_rng(10)
+    A = rng.uniform(-1, 1, (97, 130)).astype(F32)
+    B = rng.uniform(-1, 1, (130, 61)).astype(F32)
+    C1 = oracle_mod.sgemm(A, B, nthreads=1)
+    C7 = oracle_mod.sgemm(A, B, nthreads=7)
+    assert np.array_equal(C1, C7)
+
+
+def test_scaling_by_two_is_exact(oracle_mod):
+    rng = np.random.default_rng(11)
+    A = rng.uniform(-1, 1, (40, 50)).astype(F32)
+    B = rng.uniform(-1, 1, (50, 30)).astype(F32)
+    assert np.array_equal(oracle_mod.sgemm(A * F32(2), B), oracle_mod.sgemm(A, B) * F32(2))
+
+
+def test_fp32_probe_is_exact(oracle_mod):
+    """17-significant-bit A times {-1,0,1} B over K=256: every partial sum is a
+    multiple of 2^-16 below 2^8 in magnitude, hence exact in fp32 and fp64."""
+    import workloads
+    A, B, _ = workloads.inputs("probe256")
+    C = oracle_mod.sgemm(A, B)
+    exact = (np.rint(A.astype(np.float64) * 2 ** 16).astype(np.int64)
+             @ B.astype(np.int64)).astype(np.float64) * 2.0 ** -16
+    assert np.array_equal(C.astype(np.float64), exact)
+
+
+def test_quick_returns(call):
+    # M == 0 / N == 0 touch nothing, even with null pointers
+    assert call(0, 5, 5, 1.0, None, 5, None, 5, 0.0, None, 5) == 0
+    assert call(5, 0, 5, 1.0, None, 5, None, 1, 0.0, None, 1) == 0
+    # K == 0: C = beta * C
+    C = np.arange(6, dtype=F32)
+    assert call(2, 3, 0, 1.0, None, 1, None, 3, 2.0, C, 3) == 0
+    assert np.array_equal(C, np.arange(6, dtype=F32) * 2)
+    # alpha == 0, beta == 1: unchanged, NaN included
+    C = np.array([1.0, np.nan, 3.0, 4.0], F32)
+    A = np.full(4, np.nan, F32)
+    assert call(2, 2, 2, 0.0, A, 2, A, 2, 1.0, C, 2) == 0
+    assert np.isnan(C[1]) and C[0] == 1 and C[3] == 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 1, 1, 1, 1, 1), -1),
+    ((1, -1, 1, 1, 1, 1), -2),
+    ((1, 1, -1, 1, 1, 1), -3),
+    ((2, 3, 4, 3, 3, 3), -6),   # lda < K
+    ((2, 3, 4, 4, 2, 3), -8),   # ldb < N
+    ((2, 3, 4, 4, 3, 2), -11),  # ldc < N
+])
+def test_argument_validation(call, args, code):
+    M, N, K, lda, ldb, ldc = args
+    buf = np.zeros(64, F32)
+    assert call(M, N, K, 1.0, buf, lda, buf, ldb, 0.0, buf, ldc) == code
+
+
+def test_null_operands_rejected(call):
+    buf = np.zeros(16, F32)
+    assert call(2, 2, 2, 1.0, None, 2, buf, 2, 0.0, buf, 2) == -5
+    assert call(2, 2, 2, 1.0, buf, 2, None, 2, 0.0, buf, 2) == -7
+    assert call(2, 2, 2, 1.0, buf, 2, buf, 2, 0.0, None, 2) == -10
+
+
+# --- deliberately broken copies of the oracle must fail the pins -----------
+MUTANTS = {
+    # a dropped term: the first k is skipped
+    "dropped_term": ("for (int k = 0; k < K; ++k)", "for (int k = 1; k < K; ++k)", False),
+    # a wrong sign in the accumulation
+    "wrong_sign": ("acc[j] += a * (double)brow[j];", "acc[j] -= a * (double)brow[j];", False),
+    # a wrong index: A walked backwards along k
+    "wrong_index": ("const double a = (double)arow[k];",
+                    "const double a = (double)arow[K - 1 - k];", False),
+    # a transposed operand: A(k, i) instead of A(i, k) (memory-safe on squares)
+    "transposed_a": ("const double a = (double)arow[k];",
+                     "const double a = (double)b->A[(long long)k * b->lda + i];", True),
+    # alpha dropped
+    "no_alpha": ("double out = b->alpha * acc[j];", "double out = acc[j];", False),
+    # beta == 0 still reads C
+    "beta0_reads_c": ("if (b->beta != 0.0)\n", "if (1)\n", False),
+    # alpha == 0 path ignores beta
+    "alpha0_ignores_beta": ("(float)(b->beta * (double)crow[j]);", "crow[j];", False),
+    # epilogue sign error on beta
+    "beta_sign": ("out += b->beta * (double)crow[j];", "out -= b->beta * (double)crow[j];",
+                  False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new, square_only = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new, 1)
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(mutated)
+    subprocess.run(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-pthread",
+                    str(c), "-o", str(so)], check=True)
+    call = _caller(ctypes.CDLL(str(so)))
+    fails = all_pins(call, square_only=square_only)
+    if square_only:
+        # the square subset must catch it; the full suite is not memory-safe here
+        assert fails, f"mutant {name} passed every square pin"
+    else:
+        assert fails, f"mutant {name} passed every pin"
