@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""SGEMM benchmark on one MI355X: GFLOP/s and fraction of the fp32 peak.
+
+    python bench.py [--steps K] [--warmup W]            # headline line (4096^3)
+    python bench.py --workload mlp_up                   # another named workload
+    python bench.py --sweep gpurun_out/sweep.json        # every workload, table
+    python bench.py --copy-bytes 1073741824              # plain copy (counter calibration)
+
+A step is one C = alpha*(A*B) + beta*C call on the resident, seeded synthetic
+inputs of the workload (workloads.py).  GFLOP/s counts 2*M*N*K per call, the
+convention of the pages' ladder table ("The GEMM Scrapbook"), and divides by
+wall-clock time over the timed steps; the kernel's own average duration comes
+from HIP events recorded on the stream the kernel is launched on.  The CPU
+oracle is timed on a bounded sample of the same workload as a reported
+baseline (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM GFLOP/s at 4096³ fp32 and % of MI355X fp32 peak (1 GPU)"
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and packed vector)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    1: ["mfma_gemm.hip", "gemm_internal.hpp"],
+    2: ["valu_gemm.hip", "gemm_internal.hpp"],
+    3: ["skinny_gemm.hip", "gemm_internal.hpp"],
+}
+
+
+def kernel_source_hash(variant: int) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(variant, []):
+        with open(os.path.join(ROOT, "fp32_sgemm_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square4096")
+    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 MFMA, 2 VALU, 3 skinny")
+    ap.add_argument("--tile", type=int, default=-1)
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--sweep", metavar="JSON_OUT", default=None)
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, A, B, C0, target_s: float) -> dict:
+    """Time the CPU oracle on a bounded band of rows of the same workload."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.default_threads()
+    rows = 1 if w.M < 1 else min(w.M, 8)
+    while True:
+        a = np.ascontiguousarray(A[:rows])
+        c = None if C0 is None else np.ascontiguousarray(C0[:rows])
+        t0 = time.perf_counter()
+        oracle.sgemm(a, B, c, w.alpha, w.beta if c is not None else 0.0, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= 0.6 * target_s or rows >= w.M:
+            break
+        rows = min(w.M, max(rows + 1, int(rows * target_s / max(dt, 1e-3))))
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"rows 0..{rows - 1} of {w.name} ({rows} x {w.N} x {w.K}, "
+                      f"{flops / 1e9:.2f} GFLOP), fp64-accumulating C oracle on {threads} threads"}
+
+
+def make_call(sg, w, dA, dB, dC, args):
+    kw = {}
+    if args.variant or args.tile >= 0 or args.group_m:
+        kw = dict(variant=args.variant, tile=args.tile, group_m=args.group_m)
+    return lambda: sg.gemm(dA, dB, dC, w.alpha, w.beta, **kw)
+
+
+def time_calls(torch, call, steps, warmup, flush=None):
+    """(wall seconds for `steps` calls, per-call event durations in ms)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    if flush is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record()
+            call()
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        wall = 0.0
+        for i in range(steps):
+            flush()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            starts[i].record()
+            call()
+            ends[i].record()
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, durs
+
+
+def traffic_for(variant_used: int, kernel: str):
+    """Measured HBM bytes per launch, if recorded for this exact kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(kernel)
+    if not entry or entry.get("source_hash") != kernel_source_hash(variant_used):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def headline(args):
+    import torch
+    import fp32_sgemm_02_amd as sg
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    A, B, C0 = workloads.inputs(w)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty((w.M, w.N), device=dev)
+    call = make_call(sg, w, dA, dB, dC, args)
+    chosen = sg.select(w.M, w.N, w.K, dA.data_ptr(), w.K, dB.data_ptr(), w.N, dC.data_ptr(), w.N)
+    variant = args.variant or chosen.variant
+    tile = args.tile if args.tile >= 0 else chosen.tile
+    if args.variant and args.tile < 0:
+        tile = -1
+    wall, durs = time_calls(torch, call, args.steps, args.warmup)
+    torch.cuda.synchronize()
+
+    flops = w.flops
+    value = flops * args.steps / wall / 1e9
+    kern_s = statistics.mean(durs) / 1e3
+    desc = sg.tile_info(variant, tile) if tile >= 0 else {}
+    kernel = f"v{variant}_t{tile}"
+    bound = w.bound
+    if bound == "hbm":
+        achieved = w.min_bytes / kern_s / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = flops / kern_s / 1e12
+        peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
+    traffic = traffic_for(variant, kernel)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "pct_of_peak": round(100 * value / (PEAK_FP32_TFLOPS * 1e3), 2),
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
+                   "beta": w.beta, "dist": w.dist, "seed": w.seed, "variant": variant,
+                   "tile": tile, "tile_desc": desc},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": kernel, "kernel_ms_mean": round(kern_s * 1e3, 4),
+                     "kernel_ms_min": round(min(durs), 4),
+                     "kernel_ms_median": round(statistics.median(durs), 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, C0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def sweep(args):
+    import numpy as np
+    import torch
+    import fp32_sgemm_02_amd as sg
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    scratch = torch.empty(512 * 1024 * 1024 // 4, device=dev)   # larger than the 256 MB MALL
+    flush = lambda: scratch.fill_(1.0)
+    rows = []
+    names = [n for n in workloads.WORKLOADS if n != "probe256"]
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        A, B, C0 = workloads.inputs(w)
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty((w.M, w.N), device=dev)
+        variants = [0] + ([2] if name == "square4096" else [])
+        for v in variants:
+            a = argparse.Namespace(variant=v, tile=-1, group_m=0)
+            call = make_call(sg, w, dA, dB, dC, a)
+            hbm = w.bound == "hbm"
+            wall, durs = time_calls(torch, call, 10 if hbm else 20, 3, flush if hbm else None)
+            med = statistics.median(durs) / 1e3
+            cfg = sg.select(w.M, w.N, w.K)
+            row = {"workload": name, "M": w.M, "N": w.N, "K": w.K,
+                   "variant": v or cfg.variant, "tile": cfg.tile if v == 0 else -1,
+                   "kernel_ms_median": round(med * 1e3, 4),
+                   "gflops": round(w.flops / med / 1e9, 1),
+                   "gbs": round(w.min_bytes / med / 1e9, 1), "bound": w.bound}
+            if hbm:
+                row["pct_roofline"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
+            else:
+                row["pct_roofline"] = round(100 * row["gflops"] / (PEAK_FP32_TFLOPS * 1e3), 2)
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    with open(args.sweep, "w") as fh:
+        json.dump(rows, fh, indent=1)
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+
+    torch.cuda.set_device(0)
+    n = args.copy_bytes // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    wall, durs = time_calls(torch, lambda: dst.copy_(src), args.steps, args.warmup)
+    ms = statistics.mean(durs)
+    print(json.dumps({"copy_bytes": n * 4, "read_bytes": n * 4, "write_bytes": n * 4,
+                      "kernel_ms_mean": round(ms, 4),
+                      "gbs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_bytes:
+        copy_calibration(args)
+    elif args.sweep:
+        sweep(args)
+    else:
+        headline(args)
+
+
+if __name__ == "__main__":
+    main()

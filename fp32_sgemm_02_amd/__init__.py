@@ -1,0 +1,177 @@
+"""fp32_sgemm_02_amd -- single-precision GEMM for AMD Instinct MI355X (gfx950).
+
+C = alpha * (A * B) + beta * C on row-major fp32 matrices, computed by the
+hand-written HIP kernels of ``libfp32sgemm.so`` (C ABI: include/fp32_sgemm.h).
+This module only marshals arguments: every step of the product runs in the
+library's GPU kernels.  PyTorch supplies device memory and streams.
+
+The operation is the SGEMM of "a CUDA matmul" (plasmient.com labs) section 00
+and "The GEMM Scrapbook" introduction: A is M x K, B is K x N, C is M x N, and
+every cell of C is the dot product of a row of A and a column of B.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "sgemm", "sgemm_ex", "gemm", "select", "tile_count", "tile_info", "status_string",
+    "version", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
+    "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp32sgemm.so")
+
+VARIANT_AUTO, VARIANT_MFMA, VARIANT_VALU, VARIANT_SKINNY = 0, 1, 2, 3
+FLAG_SCALAR_IO = 0x1
+
+
+class SgemmConfig(ctypes.Structure):
+    """Mirror of ``sgemm_config``."""
+    _fields_ = [("variant", ctypes.c_int), ("tile", ctypes.c_int),
+                ("flags", ctypes.c_int), ("group_m", ctypes.c_int)]
+
+
+class TileDesc(ctypes.Structure):
+    """Mirror of ``sgemm_tile_desc``."""
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("bm", "bn", "bk", "wm", "wn", "tm", "tn", "threads", "lds_bytes")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"sgemm status {status}: {status_string(status)}")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m fp32_sgemm_02_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.sgemm.restype = i
+    lib.sgemm.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_ex.restype = i
+    lib.sgemm_ex.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p, ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_select.restype = i
+    lib.sgemm_select.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_tile_count.restype = i
+    lib.sgemm_tile_count.argtypes = [i]
+    lib.sgemm_tile_info.restype = i
+    lib.sgemm_tile_info.argtypes = [i, i, ctypes.POINTER(TileDesc)]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_status_string.argtypes = [i]
+    lib.sgemm_version.restype = i
+    lib.sgemm_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    """Raw C-ABI call: A, B, C are device addresses (int) or None; returns the status."""
+    return _load().sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None,
+             cfg: SgemmConfig | None = None) -> int:
+    """Raw C-ABI call with an explicit configuration (None = automatic)."""
+    return _load().sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                            ctypes.byref(cfg) if cfg is not None else None)
+
+
+def select(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None) -> SgemmConfig:
+    """The configuration sgemm() picks for this shape (and these addresses)."""
+    out = SgemmConfig()
+    st = _load().sgemm_select(M, N, K, A, lda or max(K, 1), B, ldb or max(N, 1), C,
+                              ldc or max(N, 1), ctypes.byref(out))
+    if st != 0:
+        raise SgemmError(st)
+    return out
+
+
+def tile_count(variant: int) -> int:
+    return _load().sgemm_tile_count(variant)
+
+
+def tile_info(variant: int, tile: int) -> dict:
+    d = TileDesc()
+    st = _load().sgemm_tile_info(variant, tile, ctypes.byref(d))
+    if st != 0:
+        raise SgemmError(st)
+    return d.as_dict()
+
+
+def status_string(status: int) -> str:
+    return _load().sgemm_status_string(status).decode()
+
+
+def version() -> int:
+    return _load().sgemm_version()
+
+
+def _ld(t) -> int:
+    """Leading dimension of a 2-D row-major tensor view, in elements."""
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride(1) == 1)")
+    ld = t.stride(0)
+    if rows <= 1 or cols == 0:
+        ld = max(ld, cols, 1)
+    return ld
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, variant: int = VARIANT_AUTO,
+         tile: int = -1, flags: int = 0, group_m: int = 0, stream=None):
+    """C = alpha * A @ B + beta * C for 2-D float32 CUDA tensors (row-major
+    views with unit column stride; padded rows are used through their leading
+    dimension).  C is updated in place when given; otherwise a new tensor is
+    returned (beta must then be 0).  Runs asynchronously on ``stream``
+    (default: the current stream of A's device)."""
+    import torch
+
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    for name, t in (("A", A), ("B", B)):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if B.device != A.device:
+        raise ValueError("A and B must be on the same device")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        if C.dtype != torch.float32 or C.device != A.device or tuple(C.shape) != (M, N):
+            raise ValueError(f"C must be float32 ({M}, {N}) on {A.device}")
+    with torch.cuda.device(A.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        ptr = lambda t: t.data_ptr() if t.numel() else None
+        args = (M, N, K, float(alpha), ptr(A), _ld(A), ptr(B), _ld(B), float(beta), ptr(C),
+                _ld(C), s)
+        if variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0:
+            st = sgemm(*args)
+        else:
+            st = sgemm_ex(*args, cfg=SgemmConfig(variant, tile, flags, group_m))
+    if st != 0:
+        raise SgemmError(st)
+    return C

@@ -1,0 +1,259 @@
+// skinny_gemm.hip -- SGEMM shapes with few rows (M <= 16) or few columns
+// (N <= 16) of C.  They do O(1) flops per byte of the large operand, far below
+// the ridge point of the roofline ("The GEMM Scrapbook", roofline paragraph:
+// peak flops over memory bandwidth), so they are bound by HBM and the kernels
+// are built to stream the large operand exactly once with wide, coalesced
+// loads, with K split over the waves of a workgroup and a fixed-order LDS
+// reduction (no atomics, so results are bitwise repeatable).
+//
+// Few rows (kind 0): C (M x N) = A (M x K) * B (K x N), B streamed.  The M <= 16
+// rows of A are the A operand of v_mfma_f32_16x16x4_f32 (rows >= M read as
+// zero); each workgroup owns a strip of 16*VW columns.  Lane l (i = l % 16,
+// g = l / 16) in MFMA step s of a 16-wide k-chunk supplies k = 4g + s, and VW
+// consecutive B values of row k (columns VW*i + c, c < VW, feed MFMA column
+// block c), so a row of the strip is one contiguous 64*VW-byte run per 16
+// lanes.  The result register r of block c is C[4g + r][VW*i + c].
+//
+// Few columns (kind 1): each wave owns one row of A and walks it with 16-byte
+// loads (neighbouring lanes on neighbouring addresses: "a CUDA matmul"
+// section 04), multiplying by the N <= NB columns of B (small, cache
+// resident), then reduces its 64 lanes.
+#include "gemm_internal.hpp"
+
+namespace sg {
+namespace {
+
+// ---------------------------------------------------------------- kind 0 ----
+template <int VW, int W>
+struct RowsShape {
+    static constexpr int NT = 64 * W;
+    static constexpr int STRIP = 16 * VW;
+    static constexpr int RED = W * VW * 64 * 4;      // floats of the reduction buffer
+    static constexpr int LDS_BYTES = RED * 4;
+};
+
+template <int VW, bool VEC>
+__device__ __forceinline__ void load_brow(const Problem &p, int k, int gn, float (&v)[VW]) {
+#pragma unroll
+    for (int c = 0; c < VW; ++c) v[c] = 0.f;
+    if (k >= p.K) return;
+    const float *src = p.B + (long long)k * p.ldb + gn;
+    if (VEC && gn + VW - 1 < p.N) {
+        if constexpr (VW == 4) {
+            const floatx4 t = *reinterpret_cast<const floatx4 *>(src);
+            v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+            return;
+        } else if constexpr (VW == 2) {
+            typedef float floatx2 __attribute__((ext_vector_type(2)));
+            const floatx2 t = *reinterpret_cast<const floatx2 *>(src);
+            v[0] = t[0]; v[1] = t[1];
+            return;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < VW; ++c)
+        if (gn + c < p.N) v[c] = src[c];
+}
+
+template <int VW, int W, int U, bool VEC>
+__global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p) {
+    using S = RowsShape<VW, W>;
+    __shared__ __attribute__((aligned(16))) float red[S::RED];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * S::STRIP;
+    const int gn = n0 + VW * i;
+    const bool row_ok = i < p.M;
+    const float *arow = p.A + (long long)(row_ok ? i : 0) * p.lda;
+
+    floatx4 acc[VW];
+#pragma unroll
+    for (int c = 0; c < VW; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int chunks = (p.K + 15) / 16;
+    // wave w takes chunks w, w + W, w + 2W, ...; U chunks per round so that
+    // 4*U loads of B are in flight per lane.
+    for (int j0 = wave; j0 < chunks; j0 += U * W) {
+        float bv[U][4][VW];
+        floatx4 av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (j0 + u * W) * 16 + 4 * g;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) load_brow<VW, VEC>(p, k0 + s, gn, bv[u][s]);
+            floatx4 a = {0.f, 0.f, 0.f, 0.f};
+            if (row_ok) {
+                if (VEC && k0 + 3 < p.K) {
+                    a = *reinterpret_cast<const floatx4 *>(arow + k0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (k0 + e < p.K) a[e] = arow[k0 + e];
+                }
+            }
+            av[u] = a;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int c = 0; c < VW; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][s], bv[u][s][c], acc[c],
+                                                                  0, 0, 0);
+    }
+
+    // fixed-order reduction over the W waves
+#pragma unroll
+    for (int c = 0; c < VW; ++c)
+        *reinterpret_cast<floatx4 *>(red + ((wave * VW + c) * 64 + lane) * 4) = acc[c];
+    __syncthreads();
+    const bool read_c = (p.beta != 0.f);
+    for (int e = tid; e < VW * 64 * 4; e += S::NT) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += red[w * VW * 64 * 4 + e];
+        const int r = e & 3, l = (e >> 2) & 63, c = e >> 8;
+        const int row = 4 * (l >> 4) + r;
+        const int col = n0 + VW * (l & 15) + c;
+        if (row < p.M && col < p.N) {
+            float *dst = p.C + (long long)row * p.ldc + col;
+            float out = p.alpha * sum;
+            if (read_c) out = fmaf(p.beta, *dst, out);
+            *dst = out;
+        }
+    }
+}
+
+template <int VW, int W, int U, bool VEC>
+hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
+    const int strips = (p.N + 16 * VW - 1) / (16 * VW);
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VEC>), dim3(strips), dim3(64 * W), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- kind 1 ----
+template <int NB, int W, int U, bool VEC>
+__global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * W + wave;
+    if (row >= p.M) return;                       // whole wave leaves together; no barrier below
+    const float *arow = p.A + (long long)row * p.lda;
+    float acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = 0.f;
+
+    for (int k0 = 4 * lane; k0 < p.K; k0 += 256 * U) {
+        floatx4 av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + 256 * u;
+            floatx4 a = {0.f, 0.f, 0.f, 0.f};
+            if (VEC && k + 3 < p.K) {
+                a = *reinterpret_cast<const floatx4 *>(arow + k);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (k + e < p.K) a[e] = arow[k + e];
+            }
+            av[u] = a;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = k0 + 256 * u + e;
+                if (k >= p.K) continue;
+                const float *brow = p.B + (long long)k * p.ldb;
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    if (j < p.N) acc[j] = fmaf(av[u][e], brow[j], acc[j]);
+            }
+    }
+    // butterfly reduction over the 64 lanes (fixed order)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        float v = acc[j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        acc[j] = v;
+    }
+    const bool read_c = (p.beta != 0.f);
+    float *crow = p.C + (long long)row * p.ldc;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        if (lane == j && j < p.N) {
+            float out = p.alpha * acc[j];
+            if (read_c) out = fmaf(p.beta, crow[j], out);
+            crow[j] = out;
+        }
+    }
+}
+
+template <int NB, int W, int U, bool VEC>
+hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
+    const int blocks = (p.M + W - 1) / W;
+    hipLaunchKernelGGL((cols_kernel<NB, W, U, VEC>), dim3(blocks), dim3(64 * W), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int VW, int W, int U>
+constexpr TileEntry rows_entry() {
+    using S = RowsShape<VW, W>;
+    return TileEntry{{16, 16 * VW, 16 * W, 16, 16 * VW, 0, 0, S::NT, S::LDS_BYTES},
+                     &launch_rows<VW, W, U, true>, &launch_rows<VW, W, U, false>};
+}
+
+template <int NB, int W, int U>
+constexpr TileEntry cols_entry() {
+    return TileEntry{{W, NB, 256 * U, 1, NB, 0, 0, 64 * W, 0},
+                     &launch_cols<NB, W, U, true>, &launch_cols<NB, W, U, false>};
+}
+
+constexpr int kRowsEntries = 4;   // entries [0, 4) are kind 0
+
+}  // namespace
+
+const TileEntry *skinny_tiles(int *count) {
+    static const TileEntry tiles[] = {
+        rows_entry<1, 8, 4>(),    // 0: 16-column strips
+        rows_entry<2, 8, 4>(),    // 1: 32-column strips
+        rows_entry<4, 8, 2>(),    // 2: 64-column strips
+        rows_entry<2, 16, 2>(),   // 3: 32-column strips, 16 waves
+        cols_entry<1, 4, 4>(),    // 4
+        cols_entry<2, 4, 4>(),    // 5
+        cols_entry<4, 4, 4>(),    // 6
+        cols_entry<8, 4, 2>(),    // 7
+        cols_entry<16, 4, 2>(),   // 8
+    };
+    *count = sizeof(tiles) / sizeof(tiles[0]);
+    return tiles;
+}
+
+int skinny_kind(int tile) { return tile < kRowsEntries ? 0 : 1; }
+
+bool skinny_fits(int tile, int M, int N) {
+    int count = 0;
+    const TileEntry *tiles = skinny_tiles(&count);
+    if (tile < 0 || tile >= count) return false;
+    return skinny_kind(tile) == 0 ? M <= 16 : N <= tiles[tile].desc.bn;
+}
+
+int skinny_pick(int M, int N, int K) {
+    (void)K;
+    if (M <= 16) {
+        // enough strips to cover the CUs with the widest strip that allows it
+        if ((N + 63) / 64 >= 256) return 2;
+        if ((N + 31) / 32 >= 128) return 1;
+        return 0;
+    }
+    if (N <= 16) {
+        int count = 0;
+        const TileEntry *tiles = skinny_tiles(&count);
+        for (int t = kRowsEntries; t < count; ++t)
+            if (N <= tiles[t].desc.bn) return t;
+    }
+    return -1;
+}
+
+}  // namespace sg

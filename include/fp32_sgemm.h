@@ -1,0 +1,145 @@
+/*
+ * fp32_sgemm.h -- C ABI of the MI355X (gfx950) single-precision GEMM library.
+ *
+ * Operation (the one every entry point computes):
+ *     C = alpha * (A * B) + beta * C
+ * with A of size M x K, B of size K x N and C of size M x N, all fp32; every
+ * cell of C is the dot product of one row of A and one column of B.
+ *   -- "a CUDA matmul" (plasmient.com labs), section 00 "Start here": the
+ *      SGEMM definition and its alpha/beta form; section 02: the kernel
+ *      signature (M, N, K, alpha, A, B, beta, C) this ABI extends.
+ *   -- "The GEMM Scrapbook" (iamartyaa.github.io), introduction: A is M x K,
+ *      B is K x N, C is M x N, each cell a row-by-column dot product.
+ *   -- "The 1% kernel" (notes.ybc.sh, GPU level 1), section 4: row-major
+ *      flat storage, element (r, c) at offset r * width + c.
+ *
+ * Layout: row-major with leading dimensions (counted in floats):
+ *     A(i,k) = A[i*lda + k],  B(k,j) = B[k*ldb + j],  C(i,j) = C[i*ldc + j]
+ * Requirements: lda >= max(1,K), ldb >= max(1,N), ldc >= max(1,N).  Floats of
+ * a row beyond its logical width (the padding) are never read, and never
+ * written in C.
+ *
+ * Memory and ownership: A, B and C are DEVICE pointers owned by the caller.
+ * The library keeps no pointer after a call returns and allocates no device
+ * memory.  Work is enqueued on `stream` (NULL = the null stream) and the call
+ * returns without synchronising: the caller keeps A, B and C alive and
+ * unmodified until that stream's work has completed.  C must not overlap A
+ * or B (A and B may alias each other).  Calls are thread-safe.
+ *
+ * Special cases (the pages are silent; these follow the reference BLAS):
+ *   - M == 0 or N == 0: nothing is done.
+ *   - alpha == 0 or K == 0: C = beta * C; A and B are not read.  With
+ *     beta == 1 as well, nothing is done.
+ *   - beta == 0: C is written without being read, so NaN/Inf already in C
+ *     never reaches the result.
+ *
+ * Status codes returned by every compute entry point:
+ *     0                 success (work enqueued)
+ *     -i (1..12)        the i-th argument is invalid (1-based, in the order
+ *                       of sgemm's parameter list): a negative dimension, a
+ *                       leading dimension that is too small, a null pointer
+ *                       for an operand that will be read or written, or a
+ *                       pointer that is not 4-byte aligned
+ *     -13               sgemm_ex: the configuration is invalid or does not
+ *                       apply to this shape (see sgemm_config)
+ *     > 0               a hipError_t reported by the kernel launch
+ * No C++ exception crosses this interface.
+ *
+ * Numerics: products are accumulated in fp32 (fp32 MFMA or fp32 FMA); the
+ * order of the K-sum is implementation-defined but fixed for a given shape and
+ * configuration, so repeated calls give bitwise-identical results.  No input
+ * is rounded to a narrower format.
+ */
+#ifndef FP32_SGEMM_H
+#define FP32_SGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+/* Kernel families selectable through sgemm_config.variant. */
+enum sgemm_variant {
+    SGEMM_VARIANT_AUTO = 0,    /* choose by shape (what sgemm() does) */
+    SGEMM_VARIANT_MFMA = 1,    /* fp32 matrix-core (v_mfma_f32_*_f32) tiles */
+    SGEMM_VARIANT_VALU = 2,    /* per-thread register micro-tiles of fp32 FMAs */
+    SGEMM_VARIANT_SKINNY = 3,  /* memory-bound shapes: M <= 16 or N <= 16 */
+    SGEMM_VARIANT_COUNT = 4
+};
+
+/* sgemm_config.flags bits */
+#define SGEMM_FLAG_SCALAR_IO 0x1   /* force 4-byte loads/stores (no 16-byte vectors) */
+
+/*
+ * Explicit configuration for sgemm_ex: which kernel family, which compiled
+ * tile configuration of that family (`tile` indexes the list reported by
+ * sgemm_tile_info; -1 = the family's choice for the shape), and flag bits.
+ * `group_m` sets the number of tile-rows per block of the tile-ordering
+ * swizzle (0 = the library's choice).
+ */
+typedef struct sgemm_config {
+    int variant;
+    int tile;
+    int flags;
+    int group_m;
+} sgemm_config;
+
+/* Description of one compiled tile configuration. */
+typedef struct sgemm_tile_desc {
+    int bm, bn, bk;   /* workgroup tile of C (bm x bn) and K step (bk) */
+    int wm, wn;       /* per-wave tile of C */
+    int tm, tn;       /* per-lane micro-tile (VALU family; 0 for MFMA) */
+    int threads;      /* workgroup size */
+    int lds_bytes;    /* LDS per workgroup */
+} sgemm_tile_desc;
+
+/*
+ * sgemm: C = alpha * (A * B) + beta * C, kernel family and tile chosen from
+ * the shape.  Arguments, in order: M, N, K (dimensions, >= 0); alpha; A
+ * (device, M x K, leading dimension lda); B (device, K x N, ldb); beta; C
+ * (device, M x N, ldc, read when beta != 0 and written); stream.
+ * Returns a status code as described above.
+ */
+int sgemm(int M, int N, int K, float alpha,
+          const float *A, int lda, const float *B, int ldb,
+          float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * sgemm_ex: as sgemm, with the kernel family and tile taken from *cfg
+ * (NULL = automatic, identical to sgemm).  Returns -13 when cfg names an
+ * unknown family or tile index, or a family that does not apply to the shape
+ * (SGEMM_VARIANT_SKINNY requires M <= 16 or N <= 16).  Used by the tuner,
+ * the benchmark and the tests to reach each family directly.
+ */
+int sgemm_ex(int M, int N, int K, float alpha,
+             const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, hipStream_t stream,
+             const sgemm_config *cfg);
+
+/*
+ * sgemm_select: the configuration sgemm() would use for this shape and these
+ * pointers/leading dimensions, written to *out (variant, tile, flags,
+ * group_m).  Reads no memory behind A, B or C.  Returns 0, or -14 when out is
+ * NULL.
+ */
+int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B,
+                 int ldb, const float *C, int ldc, sgemm_config *out);
+
+/* Number of compiled tile configurations of a family (0 for unknown). */
+int sgemm_tile_count(int variant);
+
+/* Describe tile configuration `tile` of `variant`; 0 on success, -13 if none. */
+int sgemm_tile_info(int variant, int tile, sgemm_tile_desc *out);
+
+/* Static text for a status code (never NULL). */
+const char *sgemm_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP32_SGEMM_H */

@@ -1,0 +1,110 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects invalid arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp32_sgemm_02_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions() -> set[str]:
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = declared_functions()
+    assert {"sgemm", "sgemm_ex", "sgemm_status_string", "sgemm_version"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", sg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = declared - exported
+    assert not missing, f"declared but not exported: {missing}"
+    lib = ctypes.CDLL(sg.LIB_PATH)
+    for name in declared:
+        getattr(lib, name)
+
+
+def test_version_and_tables():
+    assert sg.version() == 100
+    for v in (sg.VARIANT_MFMA, sg.VARIANT_VALU, sg.VARIANT_SKINNY):
+        n = sg.tile_count(v)
+        assert n > 0
+        for t in range(n):
+            d = sg.tile_info(v, t)
+            assert d["bm"] > 0 and d["bn"] > 0 and d["threads"] % 64 == 0
+            assert d["lds_bytes"] <= 160 * 1024
+    assert sg.tile_count(0) == 0 and sg.tile_count(99) == 0
+    with pytest.raises(sg.SgemmError):
+        sg.tile_info(sg.VARIANT_MFMA, 999)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, 4, 4, 4), -1),
+    ((4, -1, 4, 4, 4, 4), -2),
+    ((4, 4, -1, 4, 4, 4), -3),
+    ((4, 4, 8, 7, 4, 4), -6),     # lda < K
+    ((4, 8, 4, 4, 7, 8), -8),     # ldb < N
+    ((4, 8, 4, 4, 8, 7), -11),    # ldc < N
+    ((4, 4, 0, 0, 4, 4), -6),     # lda < max(1, K) with K = 0
+])
+def test_invalid_arguments_rejected_before_launch(args, code):
+    M, N, K, lda, ldb, ldc = args
+    fake = 0x1000   # never dereferenced: validation fails first
+    assert sg.sgemm(M, N, K, 1.0, fake, lda, fake, ldb, 0.0, fake, ldc) == code
+    assert sg.status_string(code).startswith(f"invalid argument {-code}")
+
+
+def test_null_and_misaligned_pointers_rejected():
+    good = 0x10000
+    assert sg.sgemm(4, 4, 4, 1.0, None, 4, good, 4, 0.0, good, 4) == -5
+    assert sg.sgemm(4, 4, 4, 1.0, good, 4, None, 4, 0.0, good, 4) == -7
+    assert sg.sgemm(4, 4, 4, 1.0, good, 4, good, 4, 0.0, None, 4) == -10
+    assert sg.sgemm(4, 4, 4, 1.0, good + 2, 4, good, 4, 0.0, good, 4) == -5
+    assert sg.sgemm(4, 4, 4, 1.0, good, 4, good + 1, 4, 0.0, good, 4) == -7
+    assert sg.sgemm(4, 4, 4, 1.0, good, 4, good, 4, 0.0, good + 3, 4) == -10
+
+
+def test_empty_products_are_no_ops_without_device():
+    # M == 0 or N == 0 return before any device call, even with null pointers
+    assert sg.sgemm(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4) == 0
+    assert sg.sgemm(4, 0, 4, 1.0, None, 4, None, 1, 0.0, None, 1) == 0
+    # alpha == 0 with beta == 1 leaves C untouched: nothing is launched
+    assert sg.sgemm(4, 4, 4, 0.0, None, 4, None, 4, 1.0, 0x10000, 4) == 0
+    # K == 0 with beta == 1 likewise
+    assert sg.sgemm(4, 4, 0, 1.0, None, 1, None, 4, 1.0, 0x10000, 4) == 0
+
+
+def test_bad_configuration():
+    good = 0x10000
+    cfg = sg.SgemmConfig(99, -1, 0, 0)
+    assert sg.sgemm_ex(4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, None, cfg) == -13
+    cfg = sg.SgemmConfig(sg.VARIANT_MFMA, 999, 0, 0)
+    assert sg.sgemm_ex(64, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
+    # the skinny family does not apply to a 64 x 64 product
+    cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, -1, 0, 0)
+    assert sg.sgemm_ex(64, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
+    # a few-columns tile cannot serve a few-rows shape with many columns
+    cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, sg.tile_count(sg.VARIANT_SKINNY) - 1, 0, 0)
+    assert sg.sgemm_ex(8, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
+
+
+def test_automatic_selection():
+    assert sg.select(4096, 4096, 4096).variant == sg.VARIANT_MFMA
+    assert sg.select(1, 4096, 4096).variant == sg.VARIANT_SKINNY
+    assert sg.select(4096, 1, 4096).variant == sg.VARIANT_SKINNY
+    assert sg.select(16, 14336, 4096).variant == sg.VARIANT_SKINNY
+    assert sg.select(777, 777, 33, 0x10000, 33).flags & sg.FLAG_SCALAR_IO
+    assert sg.select(256, 256, 256, 0x10000, 256, 0x20000, 256, 0x30000, 256).flags == 0

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Every test here is marked ``gpu`` and needs an MI355X.  Shapes span several
+tiles with ragged tails; the full-size workloads are checked on sampled rows
+that the oracle computes one by one.  Floating-point inputs are held to the
+tolerance in parity.py; integer-valued inputs must match bit for bit.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+import fp32_sgemm_02_amd as sg
+import workloads
+from parity import max_err_ratio, sample_rows
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def run_gpu(A, B, C0, alpha, beta, **kw):
+    """C on the GPU through the C ABI; C0 None means a NaN-poisoned C (beta must be 0)."""
+    M, N = A.shape[0], B.shape[1]
+    C = dev(C0) if C0 is not None else torch.full((M, N), float("nan"), device=DEV)
+    sg.gemm(dev(A), dev(B), C, alpha, beta, **kw)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def check(A, B, C0, alpha, beta, C, oracle_mod, rows=None, exact=False, label=""):
+    if rows is not None:
+        ref = oracle_mod.sgemm(np.ascontiguousarray(A[rows]), B,
+                               None if C0 is None else np.ascontiguousarray(C0[rows]),
+                               alpha, beta if C0 is not None else 0.0)
+        got = C[rows]
+        c0 = None if C0 is None else C0[rows]
+    else:
+        ref = oracle_mod.sgemm(A, B, None if C0 is None else C0.copy(), alpha,
+                               beta if C0 is not None else 0.0)
+        got, c0 = C, C0
+    if exact:
+        assert np.array_equal(got, ref), f"{label}: not bit-exact " \
+            f"(max diff {np.nanmax(np.abs(got - ref))})"
+        return 0.0
+    r = max_err_ratio(got, ref, A.shape[1], alpha, beta, A, B, c0)
+    assert r <= 1.0, f"{label}: max err/tol = {r}"
+    return r
+
+
+def tiles(variant):
+    return list(range(sg.tile_count(variant)))
+
+
+def uniform(M, N, K, seed, with_c=True):
+    return workloads.draw(M, N, K, "uniform", seed, with_c)
+
+
+# ---------------------------------------------------------------- per tile --
+SMALL_SHAPES = [(300, 520, 77), (257, 129, 33), (64, 64, 16), (1000, 300, 5), (129, 1031, 200)]
+
+
+@pytest.mark.parametrize("variant,tile", [(sg.VARIANT_MFMA, t) for t in range(9)] +
+                         [(sg.VARIANT_VALU, t) for t in range(3)])
+def test_tile_parity_ragged(variant, tile, oracle_mod):
+    if tile >= sg.tile_count(variant):
+        pytest.skip("tile not compiled")
+    for i, (M, N, K) in enumerate(SMALL_SHAPES):
+        A, B, C0 = uniform(M, N, K, 100 + i)
+        C = run_gpu(A, B, C0, 0.5, -1.25, variant=variant, tile=tile)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, label=f"v{variant} t{tile} {(M, N, K)}")
+        C = run_gpu(A, B, None, 1.0, 0.0, variant=variant, tile=tile)
+        check(A, B, None, 1.0, 0.0, C, oracle_mod, label=f"v{variant} t{tile} {(M, N, K)} b0")
+
+
+@pytest.mark.parametrize("variant,tile", [(sg.VARIANT_MFMA, t) for t in range(9)] +
+                         [(sg.VARIANT_VALU, t) for t in range(3)])
+def test_tile_integer_bit_exact(variant, tile, oracle_mod):
+    if tile >= sg.tile_count(variant):
+        pytest.skip("tile not compiled")
+    A, B, C0 = workloads.draw(333, 271, 1001, "int4", 7, True)
+    C = run_gpu(A, B, C0, 0.5, -1.25, variant=variant, tile=tile)
+    check(A, B, C0, 0.5, -1.25, C, oracle_mod, exact=True, label=f"v{variant} t{tile} int")
+    # the scalar (4-byte) I/O path of the same tile
+    C = run_gpu(A, B, C0, 0.5, -1.25, variant=variant, tile=tile, flags=sg.FLAG_SCALAR_IO)
+    check(A, B, C0, 0.5, -1.25, C, oracle_mod, exact=True, label=f"v{variant} t{tile} int scalar")
+
+
+SKINNY_CASES = {
+    0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
+    1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],
+}
+
+
+@pytest.mark.parametrize("tile", range(9))
+def test_skinny_tiles(tile, oracle_mod):
+    if tile >= sg.tile_count(sg.VARIANT_SKINNY):
+        pytest.skip("tile not compiled")
+    desc = sg.tile_info(sg.VARIANT_SKINNY, tile)
+    kind = 0 if desc["wm"] == 16 else 1
+    for i, (M, N, K) in enumerate(SKINNY_CASES[kind]):
+        if kind == 1 and N > desc["bn"]:
+            continue
+        A, B, C0 = uniform(M, N, K, 200 + i)
+        kw = dict(variant=sg.VARIANT_SKINNY, tile=tile)
+        C = run_gpu(A, B, C0, 0.5, -1.25, **kw)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, label=f"skinny t{tile} {(M, N, K)}")
+        C = run_gpu(A, B, C0, 0.5, -1.25, flags=sg.FLAG_SCALAR_IO, **kw)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, label=f"skinny t{tile} {(M, N, K)} scalar")
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 300 + i, True)
+        C = run_gpu(Ai, Bi, Ci, 0.5, -1.25, **kw)
+        check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=f"skinny t{tile} int")
+
+
+# ------------------------------------------------------------ tiny shapes --
+def test_tiny_shapes_brute_force(oracle_mod):
+    """Every (M, N, K) from a set of tiny sizes, through automatic dispatch,
+    bit-exact on integer inputs."""
+    sizes = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 33]
+    for M, N, K in itertools.product(sizes, sizes, sizes):
+        A, B, C0 = workloads.draw(M, N, K, "int4", M * 10007 + N * 101 + K, True)
+        C = run_gpu(A, B, C0, 0.5, -1.25)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, exact=True, label=f"tiny {(M, N, K)}")
+
+
+# ------------------------------------------------------- full-size shapes --
+FULL = [n for n in workloads.WORKLOADS if n != "probe256"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size(name, oracle_mod):
+    """Each named workload at its full size, automatic dispatch (the launch
+    configuration the benchmark times), sampled rows against the oracle."""
+    w = workloads.WORKLOADS[name]
+    A, B, C0 = workloads.inputs(w)
+    C = run_gpu(A, B, C0, w.alpha, w.beta)
+    exact = w.dist == "int4"
+    flops_per_row = 2 * w.N * w.K
+    rows = None if w.M * flops_per_row <= 4e9 else sample_rows(w.M, max(8, int(2e9 // flops_per_row)))
+    r = check(A, B, C0, w.alpha, w.beta, C, oracle_mod, rows=rows, exact=exact, label=name)
+    print(f"{name}: max err/tol = {r:.3g} on {'all' if rows is None else len(rows)} rows")
+    assert np.all(np.isfinite(C))
+
+
+def test_valu_family_full_size(oracle_mod):
+    w = workloads.WORKLOADS["square4096"]
+    A, B, _ = workloads.inputs(w)
+    C = run_gpu(A, B, None, 1.0, 0.0, variant=sg.VARIANT_VALU)
+    check(A, B, None, 1.0, 0.0, C, oracle_mod, rows=sample_rows(w.M, 48), label="valu 4096")
+
+
+def test_integer_full_size_every_mfma_tile(oracle_mod):
+    A, B, C0 = workloads.inputs("int4096_blas")
+    rows = sample_rows(4096, 24)
+    for tile in tiles(sg.VARIANT_MFMA):
+        C = run_gpu(A, B, C0, 0.5, -1.25, variant=sg.VARIANT_MFMA, tile=tile)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, rows=rows, exact=True, label=f"tile {tile}")
+
+
+# ------------------------------------------------------------ edge cases --
+def test_fp32_probe_bit_exact(oracle_mod):
+    """17-significant-bit inputs: exact in fp32, wrong under any narrower input format."""
+    A, B, _ = workloads.inputs("probe256")
+    for variant in (sg.VARIANT_AUTO, sg.VARIANT_MFMA, sg.VARIANT_VALU):
+        C = run_gpu(A, B, None, 1.0, 0.0, variant=variant)
+        check(A, B, None, 1.0, 0.0, C, oracle_mod, exact=True, label=f"probe v{variant}")
+
+
+def test_beta_zero_never_reads_c(oracle_mod):
+    for (M, N, K) in ((300, 500, 70), (1, 300, 50), (300, 1, 50)):
+        A, B, _ = uniform(M, N, K, 11, False)
+        C = run_gpu(A, B, None, 1.0, 0.0)        # C starts as NaN
+        assert np.all(np.isfinite(C))
+        check(A, B, None, 1.0, 0.0, C, oracle_mod, label=f"beta0 {(M, N, K)}")
+
+
+def test_alpha_zero_never_reads_a_b():
+    M, N, K = 100, 70, 30
+    A = np.full((M, K), np.nan, F32)
+    B = np.full((K, N), np.nan, F32)
+    C0 = np.random.default_rng(1).uniform(-1, 1, (M, N)).astype(F32)
+    C = run_gpu(A, B, C0, 0.0, 0.5)
+    assert np.array_equal(C, C0 * F32(0.5))
+    C = run_gpu(A, B, C0, 0.0, 0.0)
+    assert np.all(C == 0)
+    C = run_gpu(A, B, C0, 0.0, 1.0)
+    assert np.array_equal(C, C0)
+
+
+def test_k_zero_and_empty():
+    C0 = np.arange(12, dtype=F32).reshape(3, 4)
+    C = dev(C0)
+    sg.gemm(torch.empty((3, 0), device=DEV), torch.empty((0, 4), device=DEV), C, 1.0, 2.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), C0 * 2)
+    out = sg.gemm(torch.empty((0, 5), device=DEV), torch.ones((5, 4), device=DEV))
+    assert out.shape == (0, 4)
+
+
+def test_leading_dimension_padding(oracle_mod):
+    """NaN in the row padding of A and B never reaches C; C's padding is untouched."""
+    rng = np.random.default_rng(5)
+    for (M, N, K) in ((300, 257, 129), (5, 1000, 300), (1000, 3, 300), (64, 64, 64)):
+        for pa, pb, pc in ((4, 4, 4), (3, 5, 1)):
+            A = rng.uniform(-1, 1, (M, K)).astype(F32)
+            B = rng.uniform(-1, 1, (K, N)).astype(F32)
+            C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+            As = torch.full((M, K + pa), float("nan"), device=DEV)
+            Bs = torch.full((K, N + pb), float("nan"), device=DEV)
+            Cs = torch.full((M, N + pc), 777.0, device=DEV)
+            As[:, :K] = dev(A)
+            Bs[:, :N] = dev(B)
+            Cs[:, :N] = dev(C0)
+            sg.gemm(As[:, :K], Bs[:, :N], Cs[:, :N], 1.0, 1.0)
+            torch.cuda.synchronize()
+            Ch = Cs.cpu().numpy()
+            assert np.all(Ch[:, N:] == 777.0), "C padding written"
+            check(A, B, C0, 1.0, 1.0, Ch[:, :N].copy(), oracle_mod,
+                  label=f"ld {(M, N, K)} pad {(pa, pb, pc)}")
+
+
+def test_unaligned_pointers_use_scalar_io(oracle_mod):
+    """Operands starting 4 bytes past a 16-byte boundary are valid (4-byte aligned)."""
+    rng = np.random.default_rng(6)
+    M, N, K = 333, 290, 157
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+    a = torch.zeros(M * K + 1, device=DEV); a[1:] = dev(A).reshape(-1)
+    b = torch.zeros(K * N + 1, device=DEV); b[1:] = dev(B).reshape(-1)
+    c = torch.zeros(M * N + 1, device=DEV); c[1:] = dev(C0).reshape(-1)
+    cfg = sg.select(M, N, K, a[1:].data_ptr(), K, b[1:].data_ptr(), N, c[1:].data_ptr(), N)
+    assert cfg.flags & sg.FLAG_SCALAR_IO
+    sg.gemm(a[1:].view(M, K), b[1:].view(K, N), c[1:].view(M, N), 0.5, -1.25)
+    torch.cuda.synchronize()
+    check(A, B, C0, 0.5, -1.25, c[1:].view(M, N).cpu().numpy(), oracle_mod, label="unaligned")
+
+
+def test_closed_forms_ragged():
+    """Identity, permutation and all-ones products are exact at ragged shapes."""
+    rng = np.random.default_rng(8)
+    for K in (33, 300, 1031):
+        I = np.eye(K, dtype=F32)
+        for N in (1, 17, 257):
+            Bm = rng.uniform(-1, 1, (K, N)).astype(F32)
+            assert np.array_equal(run_gpu(I, Bm, None, 1.0, 0.0), Bm)
+        for M in (1, 19, 500):
+            Am = rng.uniform(-1, 1, (M, K)).astype(F32)
+            assert np.array_equal(run_gpu(Am, I, None, 1.0, 0.0), Am)
+            perm = rng.permutation(K)
+            P = np.zeros((K, K), F32)
+            P[perm, np.arange(K)] = 1
+            assert np.array_equal(run_gpu(Am, P, None, 1.0, 0.0), Am[:, perm])
+    for (M, N, K) in ((129, 65, 4096), (1, 300, 4096), (300, 1, 4096), (4097, 1000, 3001)):
+        C = run_gpu(np.ones((M, K), F32), np.ones((K, N), F32), None, 1.0, 0.0)
+        assert np.all(C == K)
+
+
+def test_deterministic_and_scaling():
+    A, B, _ = uniform(1000, 1000, 1000, 12, False)
+    for variant in (sg.VARIANT_MFMA, sg.VARIANT_VALU):
+        C1 = run_gpu(A, B, None, 1.0, 0.0, variant=variant)
+        C2 = run_gpu(A, B, None, 1.0, 0.0, variant=variant)
+        assert np.array_equal(C1, C2)
+        C3 = run_gpu(A * F32(2), B, None, 1.0, 0.0, variant=variant)
+        assert np.array_equal(C3, C1 * F32(2))
+    for (M, N, K) in ((1, 4096, 4096), (4096, 1, 4096), (16, 14336, 512)):
+        A, B, _ = uniform(M, N, K, 13, False)
+        assert np.array_equal(run_gpu(A, B, None, 1.0, 0.0), run_gpu(A, B, None, 1.0, 0.0))
