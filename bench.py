@@ -46,6 +46,15 @@ def kernel_source_hash(variant: int) -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_name(variant: int, desc: dict) -> str:
+    """A name for the compiled kernel that does not depend on table order."""
+    fam = {1: "mfma", 2: "valu", 3: "skinny"}.get(variant, f"v{variant}")
+    if not desc:
+        return fam
+    return (f"{fam}_{desc['bm']}x{desc['bn']}x{desc['bk']}_w{desc['wm']}x{desc['wn']}"
+            f"_s{desc.get('stages', 0)}_t{desc['threads']}")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +69,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--sweep", metavar="JSON_OUT", default=None)
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--probes", action="store_true",
+                    help="measure the MFMA-f32 and VALU-FMA ceilings with register-only loops")
     return ap.parse_args()
 
 
@@ -161,7 +172,7 @@ def headline(args):
     value = flops * args.steps / wall / 1e9
     kern_s = statistics.mean(durs) / 1e3
     desc = sg.tile_info(variant, tile) if tile >= 0 else {}
-    kernel = f"v{variant}_t{tile}"
+    kernel = kernel_name(variant, desc)
     bound = w.bound
     if bound == "hbm":
         achieved = w.min_bytes / kern_s / 1e9
@@ -255,13 +266,46 @@ def copy_calibration(args):
                       "gbs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
+def probes(args):
+    """Register-only MFMA and FMA loops: the rates the chip sustains on this machine."""
+    import ctypes
+
+    import torch
+
+    torch.cuda.set_device(0)
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp32_sgemm_02_amd", "libfp32probes.so"))
+    for fn in ("probe_mfma_flops", "probe_valu_flops"):
+        getattr(lib, fn).restype = ctypes.c_double
+        getattr(lib, fn).argtypes = [ctypes.c_int, ctypes.c_int]
+    for fn in ("probe_mfma_f32", "probe_valu_f32"):
+        getattr(lib, fn).restype = ctypes.c_int
+        getattr(lib, fn).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 256 * 8
+    out = torch.empty(blocks * 256, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for name, iters, peak in (("mfma_f32", 2000, PEAK_FP32_TFLOPS),
+                              ("valu_fma_f32", 20000, PEAK_FP32_TFLOPS / 2)):
+        launch = getattr(lib, f"probe_{name.split('_')[0]}_f32")
+        flops = getattr(lib, f"probe_{name.split('_')[0]}_flops")(blocks, iters)
+        call = lambda: launch(blocks, iters, out.data_ptr(), stream)
+        _, durs = time_calls(torch, call, 10, 3)
+        med = statistics.median(durs) / 1e3
+        tf = flops / med / 1e12
+        print(json.dumps({"probe": name, "tflops": round(tf, 2), "peak_tflops": peak,
+                          "frac": round(tf / peak, 4), "kernel_ms_median": round(med * 1e3, 4),
+                          "implied_clock_ghz": round(tf * 1e12 / (256 * (256 if name.startswith("mfma") else 128)) / 1e9, 3)}),
+              flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.copy_bytes:
+    if args.probes:
+        probes(args)
+    elif args.copy_bytes:
         copy_calibration(args)
     elif args.sweep:
         sweep(args)

@@ -36,7 +36,7 @@ class SgemmConfig(ctypes.Structure):
 class TileDesc(ctypes.Structure):
     """Mirror of ``sgemm_tile_desc``."""
     _fields_ = [(n, ctypes.c_int) for n in
-                ("bm", "bn", "bk", "wm", "wn", "tm", "tn", "threads", "lds_bytes")]
+                ("bm", "bn", "bk", "wm", "wn", "tm", "tn", "threads", "lds_bytes", "stages")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -26,6 +26,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scale.hip", "mfma_gemm.hip", "valu_gemm.hip", "skinny_gemm.hip"]
+PROBE_SOURCES = ["peak_probes.hip"]
+PROBE_LIB = os.path.join(HERE, "libfp32probes.so")
 
 COMMON_FLAGS = [
     "-x", "hip", "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
@@ -48,18 +50,20 @@ def _compile(src: str, resources: bool) -> tuple[str, str]:
 def build(resources: bool = False, jobs: int | None = None) -> str:
     """Compile every source and link libfp32sgemm.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2) - 1), 8)
+    allsrc = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(allsrc), max(1, (os.cpu_count() or 2) - 1), 8)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, resources), SOURCES))
-    objs = [o for o, _ in results]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        results = dict(zip(allsrc, ex.map(lambda s: _compile(s, resources), allsrc)))
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        objs = [results[s][0] for s in srcs]
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
     if resources:
-        for (_, log) in results:
+        for (_, log) in results.values():
             for line in summarize_resources(log):
                 print(line)
     return LIB

@@ -16,7 +16,7 @@
 namespace sg {
 namespace {
 
-constexpr int kVersion = 100;   // 0.1.0
+constexpr int kVersion = 200;   // 0.2.0
 constexpr int kBadConfig = -13;
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -49,7 +49,7 @@ Tuned auto_select(int M, int N, int K) {
     if (lookup_tuned(M, N, K, t)) return t;
     int count = 0;
     const TileEntry *tiles = mfma_tiles(&count);
-    const int order[] = {1, 6, 3, 8, 7};
+    const int order[] = {2, 5, 7};
     for (int idx : order)
         if (idx < count && tiles_for(tiles[idx], M, N) >= 200)
             return Tuned{SGEMM_VARIANT_MFMA, idx, 0};

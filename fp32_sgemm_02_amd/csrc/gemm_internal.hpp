@@ -54,6 +54,31 @@ hipError_t launch_scale(int M, int N, float beta, float *C, long long ldc,
 
 // ---- device helpers shared by the families ---------------------------------
 
+// Ends one software-pipeline step.  The accumulators pass through an empty
+// asm statement, so the arithmetic of this step must be complete at this
+// point; the memory clobber keeps the LDS reads issued for the next step from
+// moving above it.  Without this the compiler sinks all the (side-effect
+// free) arithmetic of a loop body below its loads and then needs registers
+// for every step's operands at once.  The asm emits no instruction.
+template <int N>
+__device__ __forceinline__ void pipeline_fence(float (&acc)[N]) {
+    static_assert(N % 4 == 0, "accumulators in groups of four");
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+        asm volatile("" : "+v"(acc[i]), "+v"(acc[i + 1]), "+v"(acc[i + 2]), "+v"(acc[i + 3]));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Step boundary for the matrix-core kernels: memory ordering only.  The MFMA
+// builtins are not moved across it by the compiler, so tying the
+// accumulators (which would pin all of them to fixed registers at every step)
+// is unnecessary there.
+__device__ __forceinline__ void pipeline_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
 // XCD w % 8), and each XCD has its own L2.  Renumber so that XCD x receives a
 // contiguous range of logical tile ids; neighbouring tiles (which share rows

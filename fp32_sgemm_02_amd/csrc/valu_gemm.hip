@@ -16,8 +16,10 @@
 //     lanes that read LDS together cover 128 contiguous bytes and hit distinct
 //     banks;
 //   * two LDS buffers: the next K-slice is fetched from global memory while
-//     the current one is consumed (Scrapbook warptiling chapter, double
-//     buffering), one barrier per slice.
+//     the current one is consumed and written to the other buffer half-way
+//     through the slice (Scrapbook warptiling chapter, double buffering), one
+//     barrier per slice; the next k's slivers are read from LDS while the
+//     current k's 64 FMAs run.
 // The code is built with packed fp32 instructions disabled, so each FMA is a
 // plain v_fma_f32; the family's ceiling is half the chip's packed fp32 rate.
 #include "gemm_internal.hpp"
@@ -44,27 +46,66 @@ struct ValuShape {
     static_assert(BM % (16 * (NT / 64)) == 0, "A rows split evenly over waves");
 };
 
+// Guarded loads read a clamped (always valid) address and select zero outside
+// the matrix, so edge tiles do not diverge; only a 16-byte chunk straddling
+// K (or N) is read element by element.
 template <bool GUARD, bool VEC>
 __device__ __forceinline__ floatx4 vload_a(const Problem &p, int gm, int gk) {
+    if (!GUARD) {
+        const float *src = p.A + (long long)gm * p.lda + gk;
+        if (VEC) return *reinterpret_cast<const floatx4 *>(src);
+        return floatx4{src[0], src[1], src[2], src[3]};
+    }
+    const bool row_ok = gm < p.M;
+    const float *row = p.A + (row_ok ? (long long)gm * p.lda : 0);
     floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (GUARD && gm >= p.M) return v;
-    const float *src = p.A + (long long)gm * p.lda + gk;
-    if (VEC && (!GUARD || gk + 3 < p.K)) return *reinterpret_cast<const floatx4 *>(src);
+    if (VEC) {
+        const bool whole = row_ok && gk + 3 < p.K;
+        const floatx4 x = *reinterpret_cast<const floatx4 *>(row + (whole ? gk : 0));
+        if (whole) v = x;
+        else if (row_ok && gk < p.K) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (!GUARD || gk + e < p.K) v[e] = src[e];
+            for (int e = 0; e < 3; ++e)
+                if (gk + e < p.K) v[e] = row[gk + e];
+        }
+        return v;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool ok = row_ok && gk + e < p.K;
+        const float x = row[ok ? gk + e : 0];
+        v[e] = ok ? x : 0.f;
+    }
     return v;
 }
 
 template <bool GUARD, bool VEC>
 __device__ __forceinline__ floatx4 vload_b(const Problem &p, int gk, int gn) {
+    if (!GUARD) {
+        const float *src = p.B + (long long)gk * p.ldb + gn;
+        if (VEC) return *reinterpret_cast<const floatx4 *>(src);
+        return floatx4{src[0], src[1], src[2], src[3]};
+    }
+    const bool row_ok = gk < p.K;
+    const float *row = p.B + (row_ok ? (long long)gk * p.ldb : 0);
     floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (GUARD && gk >= p.K) return v;
-    const float *src = p.B + (long long)gk * p.ldb + gn;
-    if (VEC && (!GUARD || gn + 3 < p.N)) return *reinterpret_cast<const floatx4 *>(src);
+    if (VEC) {
+        const bool whole = row_ok && gn + 3 < p.N;
+        const floatx4 x = *reinterpret_cast<const floatx4 *>(row + (whole ? gn : 0));
+        if (whole) v = x;
+        else if (row_ok && gn < p.N) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (!GUARD || gn + e < p.N) v[e] = src[e];
+            for (int e = 0; e < 3; ++e)
+                if (gn + e < p.N) v[e] = row[gn + e];
+        }
+        return v;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool ok = row_ok && gn + e < p.N;
+        const float x = row[ok ? gn + e : 0];
+        v[e] = ok ? x : 0.f;
+    }
     return v;
 }
 
@@ -135,11 +176,10 @@ valu_sgemm_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     const int m0 = tm * BM, n0 = tn * BN;
     const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
-    float acc[8][8];
+    float acc_flat[64];
+    float(&acc)[8][8] = *reinterpret_cast<float(*)[8][8]>(acc_flat);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int i = 0; i < 64; ++i) acc_flat[i] = 0.f;
 
     floatx4 ra[S::A_VEC], rb[S::B_VEC];
     const int nk = (p.K + BK - 1) / BK;
@@ -151,33 +191,51 @@ valu_sgemm_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
             vfetch<BM, BN, BK, true, VEC>(p, m0, n0, k0, tid, ra, rb);
     };
 
-    // lane's A rows: wr*64 + 4*ty + {0..3} and +32; B columns: wc*64 + 4*tx + {0..3} and +32
     const int a_off = wr * 64 + 4 * ty;
     const int b_off = wc * 64 + 4 * tx;
+
+    // the lane's slivers for one k: A rows a_off + {0..3}, +32; B columns b_off + {0..3}, +32
+    struct Sliver {
+        floatx4 a0, a1, b0, b1;
+    };
+    auto read_sliver = [&](const float *stage, int k, Sliver &v) {
+        const float *As = stage + k * S::AS + a_off;
+        const float *Bs = stage + S::A_STAGE + k * S::BS + b_off;
+        v.a0 = *reinterpret_cast<const floatx4 *>(As);
+        v.a1 = *reinterpret_cast<const floatx4 *>(As + 32);
+        v.b0 = *reinterpret_cast<const floatx4 *>(Bs);
+        v.b1 = *reinterpret_cast<const floatx4 *>(Bs + 32);
+    };
 
     fetch(0);
     vstore_lds<BM, BN, BK>(smem, tid, ra, rb);
     __syncthreads();
+    Sliver cur, nxt;
+    read_sliver(smem, 0, cur);
     for (int t = 0; t < nk; ++t) {
         const bool more = (t + 1 < nk);
         if (more) fetch(t + 1);
-        const float *As = smem + (t & 1) * S::STAGE;
-        const float *Bs = As + S::A_STAGE;
+        const float *stage = smem + (t & 1) * S::STAGE;
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
-            const floatx4 a0 = *reinterpret_cast<const floatx4 *>(As + k * S::AS + a_off);
-            const floatx4 a1 = *reinterpret_cast<const floatx4 *>(As + k * S::AS + a_off + 32);
-            const floatx4 b0 = *reinterpret_cast<const floatx4 *>(Bs + k * S::BS + b_off);
-            const floatx4 b1 = *reinterpret_cast<const floatx4 *>(Bs + k * S::BS + b_off + 32);
-            const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            if (k + 1 < BK) read_sliver(stage, k + 1, nxt);
+            const float a[8] = {cur.a0[0], cur.a0[1], cur.a0[2], cur.a0[3],
+                                cur.a1[0], cur.a1[1], cur.a1[2], cur.a1[3]};
+            const float b[8] = {cur.b0[0], cur.b0[1], cur.b0[2], cur.b0[3],
+                                cur.b1[0], cur.b1[1], cur.b1[2], cur.b1[3]};
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+            // the other buffer was last read in stage t - 1, before the
+            // barrier that closed it: the next stage can be written now
+            if (k == BK / 2 && more)
+                vstore_lds<BM, BN, BK>(smem + ((t + 1) & 1) * S::STAGE, tid, ra, rb);
+            pipeline_fence(acc_flat);
+            if (k + 1 < BK) cur = nxt;
         }
-        if (more) vstore_lds<BM, BN, BK>(smem + ((t + 1) & 1) * S::STAGE, tid, ra, rb);
         __syncthreads();
+        if (more) read_sliver(smem + ((t + 1) & 1) * S::STAGE, 0, cur);
     }
 
     // epilogue: alpha/beta; beta == 0 never reads C
@@ -230,7 +288,7 @@ hipError_t launch_valu(const Problem &p, int group_m, hipStream_t stream) {
 template <int BM, int BN, int BK>
 constexpr TileEntry valu_entry() {
     using S = ValuShape<BM, BN, BK>;
-    return TileEntry{{BM, BN, BK, 64, 64, 8, 8, S::NT, S::LDS_BYTES},
+    return TileEntry{{BM, BN, BK, 64, 64, 8, 8, S::NT, S::LDS_BYTES, 2},
                      &launch_valu<BM, BN, BK, true>, &launch_valu<BM, BN, BK, false>};
 }
 

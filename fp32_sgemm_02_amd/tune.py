@@ -1,0 +1,162 @@
+"""Offline tuner: the fastest compiled configuration per problem shape.
+
+    python -m fp32_sgemm_02_amd.tune --workloads square4096,mlp_up --out tune.json
+    python -m fp32_sgemm_02_amd.tune --shapes 4097x1000x3001 --write-table
+
+For every shape it times each applicable (kernel family, tile, group_m)
+candidate on the GPU with HIP events (median of `--reps` calls after
+`--warmup`), keeps the fastest, and optionally rewrites csrc/tuned_table.inc
+with one exact-shape row per tuned shape (rebuild the library afterwards).
+Autotuning tile sizes per GPU is the rung "The GEMM Scrapbook" fine print
+credits with most of the gap before warptiling; here the candidates are the
+compiled template instances of include/fp32_sgemm.h's families.
+
+Correctness of every compiled configuration is established by the GPU parity
+tests against the CPU oracle; as a guard against a mis-tuned table the tuner
+also requires each candidate's output to agree with the automatic
+configuration's output on the same inputs (same tolerance rule as the
+tests) before it may win.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+TABLE = os.path.join(HERE, "csrc", "tuned_table.inc")
+
+GROUPS = (1, 2, 4, 8, 16)
+
+
+def parse_shape(text: str):
+    m, n, k = (int(x) for x in text.lower().split("x"))
+    return m, n, k
+
+
+def candidates(sg, M, N, K, sweep_groups: bool):
+    out = []
+    for tile in range(sg.tile_count(sg.VARIANT_MFMA)):
+        groups = GROUPS if sweep_groups else (0,)
+        for g in groups:
+            out.append((sg.VARIANT_MFMA, tile, g))
+    if M <= 16 or N <= 16:
+        for tile in range(sg.tile_count(sg.VARIANT_SKINNY)):
+            out.append((sg.VARIANT_SKINNY, tile, 0))
+    return out
+
+
+def agree(torch, C, ref, K, amax, bmax) -> bool:
+    tol = 2e-5 * K * amax * bmax
+    return bool(torch.isfinite(C).all()) and float((C - ref).abs().max()) <= tol
+
+
+def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0):
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    A = torch.rand((M, K), device=dev, generator=gen) * 2 - 1
+    B = torch.rand((K, N), device=dev, generator=gen) * 2 - 1
+    C = torch.empty((M, N), device=dev)
+    ref = torch.empty((M, N), device=dev)
+    sg.gemm(A, B, ref)
+    torch.cuda.synchronize()
+    results = []
+    for variant, tile, group in candidates(sg, M, N, K, sweep_groups):
+        try:
+            call = lambda: sg.gemm(A, B, C, variant=variant, tile=tile, group_m=group)
+            C.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+        except sg.SgemmError:
+            continue                      # configuration does not apply to this shape
+        if not agree(torch, C, ref, K, 1.0, 1.0):
+            print(f"  rejected v{variant} t{tile} g{group}: output differs", flush=True)
+            continue
+        for _ in range(warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for s, e in ev:
+            s.record()
+            call()
+            e.record()
+        torch.cuda.synchronize()
+        ms = statistics.median(s.elapsed_time(e) for s, e in ev)
+        gf = 2.0 * M * N * K / (ms / 1e3) / 1e9
+        results.append({"variant": variant, "tile": tile, "group_m": group, "ms": round(ms, 5),
+                        "gflops": round(gf, 1), "desc": sg.tile_info(variant, tile)})
+        print(f"  v{variant} t{tile} g{group}: {ms:.4f} ms  {gf:,.0f} GFLOP/s", flush=True)
+    results.sort(key=lambda r: r["ms"])
+    return results
+
+
+def write_table(best: dict, path: str = TABLE):
+    rows = []
+    for (M, N, K), r in sorted(best.items()):
+        rows.append(f"    {{{M}, {N}, {K}, {{{r['variant']}, {r['tile']}, {r['group_m']}}}}},"
+                    f"   // {r['gflops']:,.0f} GFLOP/s")
+    text = f"""// tuned_table.inc -- measured best configurations per shape (written by
+// fp32_sgemm_02_amd/tune.py; edit by re-running it).  Each row: the exact
+// (M, N, K) it was tuned on, then variant, tile, group_m.  Shapes not listed
+// fall back to the tile-count rule in auto_select().
+static const struct {{ int M, N, K; Tuned t; }} kTuned[] = {{
+    {{0, 0, 0, {{0, 0, 0}}}},   // sentinel (never matches: M == 0 returns early)
+{chr(10).join(rows)}
+}};
+
+static bool lookup_tuned(int M, int N, int K, Tuned &out) {{
+    for (const auto &e : kTuned)
+        if (e.M == M && e.N == N && e.K == K) {{ out = e.t; return true; }}
+    return false;
+}}
+"""
+    with open(path, "w") as fh:
+        fh.write(text)
+
+
+def main():
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import fp32_sgemm_02_amd as sg
+    import workloads
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workloads", default="")
+    ap.add_argument("--shapes", default="")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--groups", action="store_true", help="also sweep group_m")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--write-table", action="store_true")
+    args = ap.parse_args()
+
+    shapes = []
+    for name in filter(None, args.workloads.split(",")):
+        w = workloads.WORKLOADS[name]
+        shapes.append((w.M, w.N, w.K))
+    shapes += [parse_shape(s) for s in filter(None, args.shapes.split(","))]
+    torch.cuda.set_device(0)
+    report, best = {}, {}
+    for (M, N, K) in shapes:
+        print(f"shape {M}x{N}x{K}", flush=True)
+        res = tune_shape(sg, torch, M, N, K, args.warmup, args.reps, args.groups)
+        report[f"{M}x{N}x{K}"] = res
+        if res:
+            best[(M, N, K)] = res[0]
+            print(f"  best: v{res[0]['variant']} t{res[0]['tile']} g{res[0]['group_m']} "
+                  f"{res[0]['gflops']:,.0f} GFLOP/s", flush=True)
+        torch.cuda.empty_cache()
+    if args.out:
+        with open(args.out, "w") as fh:
+            json.dump(report, fh, indent=1)
+    if args.write_table:
+        write_table(best)
+
+
+if __name__ == "__main__":
+    main()

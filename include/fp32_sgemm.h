@@ -92,6 +92,7 @@ typedef struct sgemm_tile_desc {
     int tm, tn;       /* per-lane micro-tile (VALU family; 0 for MFMA) */
     int threads;      /* workgroup size */
     int lds_bytes;    /* LDS per workgroup */
+    int stages;       /* LDS buffers in the K pipeline (0: no LDS staging) */
 } sgemm_tile_desc;
 
 /*

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tables():
-    assert sg.version() == 100
+    assert sg.version() == 200
     for v in (sg.VARIANT_MFMA, sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         n = sg.tile_count(v)
         assert n > 0
