@@ -18,8 +18,9 @@
 //     chapter), which it computes as a sum of outer products over k
 //     (Scrapbook 2D-tiling chapter) -- here each 16 x 16 x 4 block of that sum
 //     is one MFMA instruction instead of 1024 scalar FMAs;
-//   * LDS rows of A are padded so that the 16-byte fragment reads of a wave
-//     hit distinct banks (Scrapbook warptiling chapter, bank conflicts).
+//   * LDS rows of A are padded (B rows are not) so that the 16-byte fragment
+//     reads of a wave hit distinct banks (Scrapbook warptiling chapter, bank
+//     conflicts); the strides are the ones measured conflict-free on gfx950.
 //
 // Lane layout of v_mfma_f32_16x16x4_f32 (wave64, lane l, i = l % 16, g = l / 16):
 //   A operand: A[i][g], B operand: B[g][i], result register r: D[4g + r][i].
@@ -48,8 +49,12 @@ struct MfmaShape {
     static constexpr int RB = WM / 16;          // 16-row MFMA blocks per wave
     static constexpr int CG = WN / 64;          // 64-column groups per wave
     static constexpr int KC = BK / 16;          // 16-wide k-chunks per stage
-    static constexpr int AS = BK + 4;           // LDS row stride of the A tile (floats)
-    static constexpr int BS = BN + 4;           // LDS row stride of the B tile (floats)
+    // LDS row strides (floats), chosen for conflict-free 16-byte fragment
+    // reads on gfx950 (measured with SQ_LDS_BANK_CONFLICT): A rows padded by 8
+    // floats (16 rows x 4 chunks read together), B rows unpadded (the four
+    // row groups of a B read then sit a multiple of 256 bytes apart).
+    static constexpr int AS = BK + 8;
+    static constexpr int BS = BN;
     static constexpr int A_STAGE = BM * AS;
     static constexpr int B_STAGE = BK * BS;
     static constexpr int STAGE = A_STAGE + B_STAGE;
@@ -135,7 +140,7 @@ __device__ __forceinline__ floatx4 load_b(const Problem &p, int gk, int gn) {
 template <class S, bool GUARD, bool VEC>
 __device__ __forceinline__ void global_to_regs(const Problem &p, int m0, int n0, int k0, int tid,
                                                floatx4 (&ra)[S::A_VEC], floatx4 (&rb)[S::B_VEC]) {
-    constexpr int BK = S::KC * 16, BN = S::BS - 4;
+    constexpr int BK = S::KC * 16, BN = S::BS;
 #pragma unroll
     for (int v = 0; v < S::A_VEC; ++v) {
         const int c = tid + v * S::NT;
@@ -153,7 +158,7 @@ __device__ __forceinline__ void global_to_regs(const Problem &p, int m0, int n0,
 template <class S>
 __device__ __forceinline__ void regs_to_lds(float *stage, int tid, const floatx4 (&ra)[S::A_VEC],
                                             const floatx4 (&rb)[S::B_VEC]) {
-    constexpr int BK = S::KC * 16, BN = S::BS - 4;
+    constexpr int BK = S::KC * 16, BN = S::BS;
     float *As = stage;
     float *Bs = stage + S::A_STAGE;
 #pragma unroll
