@@ -4,6 +4,8 @@
     python bench.py [--steps K] [--warmup W]            # headline line (4096^3)
     python bench.py --workload mlp_up                   # another named workload
     python bench.py --sweep gpurun_out/sweep.json        # every workload, table
+                                                        # (memory-bound shapes rotate over
+                                                        # operand copies > the 256 MB MALL)
     python bench.py --copy-bytes 1073741824              # plain copy (counter calibration)
 
 A step is one C = alpha*(A*B) + beta*C call on the resident, seeded synthetic
@@ -97,42 +99,60 @@ def cpu_baseline(w, A, B, C0, target_s: float) -> dict:
                       f"{flops / 1e9:.2f} GFLOP), fp64-accumulating C oracle on {threads} threads"}
 
 
-def make_call(sg, w, dA, dB, dC, args):
-    kw = {}
-    if args.variant or args.tile >= 0 or args.group_m:
-        kw = dict(variant=args.variant, tile=args.tile, group_m=args.group_m)
-    return lambda: sg.gemm(dA, dB, dC, w.alpha, w.beta, **kw)
-
-
-def time_calls(torch, call, steps, warmup, flush=None):
-    """(wall seconds for `steps` calls, per-call event durations in ms)."""
+def time_calls(torch, call, steps, warmup):
+    """(wall seconds for `steps` back-to-back calls, per-call event durations in
+    ms).  The events are recorded on torch's current stream, the stream the
+    library launches on."""
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    if flush is None:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            starts[i].record()
-            call()
-            ends[i].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        wall = 0.0
-        for i in range(steps):
-            flush()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            starts[i].record()
-            call()
-            ends[i].record()
-            torch.cuda.synchronize()
-            wall += time.perf_counter() - t0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        call()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return wall, durs
+
+
+MALL_BYTES = 256 * 1024 * 1024     # MI355X Infinity Cache
+
+
+def operand_sets(torch, w, A, B, C0, dev, rotate: bool):
+    """Device copies (A, B, C) of a workload's operands.  With `rotate`, enough
+    copies that consecutive calls never find their operands in the 256 MB
+    Infinity Cache (each call's inputs were last touched more than 256 MB of
+    traffic earlier), so memory-bound shapes are timed against HBM."""
+    per_set = 4 * (w.M * w.K + w.K * w.N + w.M * w.N)
+    n = 1 if not rotate else max(2, -(-2 * MALL_BYTES // per_set) + 1)
+    sets = []
+    for _ in range(n):
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+        dC = (torch.from_numpy(C0).to(dev) if C0 is not None
+              else torch.empty((w.M, w.N), device=dev))
+        sets.append((dA, dB, dC))
+    return sets
+
+
+def time_rotating(torch, call_i, steps, warmup):
+    """Per-call event durations (ms) of call_i(0), call_i(1), ... back to back."""
+    for i in range(warmup):
+        call_i(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (s, e) in enumerate(ev):
+        s.record()
+        call_i(warmup + i)
+        e.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
 
 
 def traffic_for(variant_used: int, kernel: str):
@@ -156,10 +176,19 @@ def headline(args):
     A, B, C0 = workloads.inputs(w)
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    dA = torch.from_numpy(A).to(dev)
-    dB = torch.from_numpy(B).to(dev)
-    dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty((w.M, w.N), device=dev)
-    call = make_call(sg, w, dA, dB, dC, args)
+    # memory-bound workloads rotate over operand copies larger than the MALL
+    sets = operand_sets(torch, w, A, B, C0, dev, rotate=(w.bound == "hbm"))
+    dA, dB, dC = sets[0]
+    kw = {}
+    if args.variant or args.tile >= 0 or args.group_m:
+        kw = dict(variant=args.variant, tile=args.tile, group_m=args.group_m)
+    counter = [0]
+
+    def call():
+        a, b, c = sets[counter[0] % len(sets)]
+        counter[0] += 1
+        sg.gemm(a, b, c, w.alpha, w.beta, **kw)
+
     chosen = sg.select(w.M, w.N, w.K, dA.data_ptr(), w.K, dB.data_ptr(), w.N, dC.data_ptr(), w.N)
     variant = args.variant or chosen.variant
     tile = args.tile if args.tile >= 0 else chosen.tile
@@ -217,35 +246,33 @@ def sweep(args):
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
-    scratch = torch.empty(512 * 1024 * 1024 // 4, device=dev)   # larger than the 256 MB MALL
-    flush = lambda: scratch.fill_(1.0)
     rows = []
     names = [n for n in workloads.WORKLOADS if n != "probe256"]
     for name in names:
         w = workloads.WORKLOADS[name]
         A, B, C0 = workloads.inputs(w)
-        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
-        dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty((w.M, w.N), device=dev)
+        hbm = w.bound == "hbm"
+        sets = operand_sets(torch, w, A, B, C0, dev, rotate=hbm)
         variants = [0] + ([2] if name == "square4096" else [])
         for v in variants:
-            a = argparse.Namespace(variant=v, tile=-1, group_m=0)
-            call = make_call(sg, w, dA, dB, dC, a)
-            hbm = w.bound == "hbm"
-            wall, durs = time_calls(torch, call, 10 if hbm else 20, 3, flush if hbm else None)
+            kw = dict(variant=v) if v else {}
+            call_i = lambda i, kw=kw: sg.gemm(*sets[i % len(sets)], w.alpha, w.beta, **kw)
+            durs = time_rotating(torch, call_i, 30 if hbm else 20, 5)
             med = statistics.median(durs) / 1e3
             cfg = sg.select(w.M, w.N, w.K)
             row = {"workload": name, "M": w.M, "N": w.N, "K": w.K,
                    "variant": v or cfg.variant, "tile": cfg.tile if v == 0 else -1,
                    "kernel_ms_median": round(med * 1e3, 4),
                    "gflops": round(w.flops / med / 1e9, 1),
-                   "gbs": round(w.min_bytes / med / 1e9, 1), "bound": w.bound}
+                   "gbs": round(w.min_bytes / med / 1e9, 1), "bound": w.bound,
+                   "operand_copies": len(sets)}
             if hbm:
                 row["pct_roofline"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
             else:
                 row["pct_roofline"] = round(100 * row["gflops"] / (PEAK_FP32_TFLOPS * 1e3), 2)
             rows.append(row)
             print(json.dumps(row), flush=True)
-        del dA, dB, dC
+        del sets
         torch.cuda.empty_cache()
     with open(args.sweep, "w") as fh:
         json.dump(rows, fh, indent=1)

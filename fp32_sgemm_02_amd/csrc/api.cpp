@@ -40,13 +40,13 @@ long long tiles_for(const TileEntry &t, int M, int N) {
     return (long long)((M + t.desc.bm - 1) / t.desc.bm) * ((N + t.desc.bn - 1) / t.desc.bn);
 }
 
-// Automatic choice: the skinny family for memory-bound shapes, otherwise the
-// tuned MFMA configuration for the shape (tuned_table.inc), else the largest
-// tile that still yields about one workgroup per CU.
+// Automatic choice: the measured best configuration for this exact shape
+// (tuned_table.inc), else the skinny family for memory-bound shapes, else the
+// largest MFMA tile that still yields about one workgroup per CU.
 Tuned auto_select(int M, int N, int K) {
-    if (skinny_pick(M, N, K) >= 0) return Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
     Tuned t;
     if (lookup_tuned(M, N, K, t)) return t;
+    if (skinny_pick(M, N, K) >= 0) return Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
     int count = 0;
     const TileEntry *tiles = mfma_tiles(&count);
     const int order[] = {2, 5, 7};
@@ -152,7 +152,7 @@ int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B, i
     if (!out) return -14;
     const sg::Tuned t = sg::auto_select(M, N, K);
     out->variant = t.variant;
-    out->tile = t.variant == SGEMM_VARIANT_SKINNY ? sg::skinny_pick(M, N, K) : t.tile;
+    out->tile = (t.variant == SGEMM_VARIANT_SKINNY && t.tile < 0) ? sg::skinny_pick(M, N, K) : t.tile;
     out->group_m = t.group_m;
     out->flags = sg::vector_io_ok(A, lda, B, ldb, C, ldc) ? 0 : SGEMM_FLAG_SCALAR_IO;
     return 0;

@@ -55,13 +55,61 @@ __device__ __forceinline__ void load_brow(const Problem &p, int k, int gn, float
         if (gn + c < p.N) v[c] = src[c];
 }
 
+// One round of a wave's loads: U 16-wide k-chunks (chunk indices j, j + W,
+// ..., j + (U-1)W), for each 4 B rows of VW values and a 4-value A sliver.
+template <int VW, int U>
+struct RowsRound {
+    float b[U][4][VW];
+    floatx4 a[U];
+};
+
 template <int VW, int W, int U, bool VEC>
-__global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p) {
+__device__ __forceinline__ void rows_load(const Problem &p, int j, int g, int gn, bool row_ok,
+                                          const float *arow, RowsRound<VW, U> &r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k0 = (j + u * W) * 16 + 4 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) load_brow<VW, VEC>(p, k0 + s, gn, r.b[u][s]);
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) {
+            if (VEC && k0 + 3 < p.K) {
+                a = *reinterpret_cast<const floatx4 *>(arow + k0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (k0 + e < p.K) a[e] = arow[k0 + e];
+            }
+        }
+        r.a[u] = a;
+    }
+}
+
+template <int VW, int U>
+__device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&acc)[VW]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < VW; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.a[u][s], r.b[u][s][c], acc[c], 0, 0,
+                                                              0);
+}
+
+// The strip's B columns are streamed once.  Each wave walks its chunks in
+// rounds of U with two register sets: the loads of round r + 1 are issued
+// before the MFMAs of round r, so a round's memory latency overlaps the
+// previous round's arithmetic (loads past K read as zero, so the extra round
+// at the end touches no memory).
+template <int VW, int W, int U, bool VEC>
+__global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) {
     using S = RowsShape<VW, W>;
     __shared__ __attribute__((aligned(16))) float red[S::RED];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * S::STRIP;
+    // neighbouring strips share cache lines of B: keep them on one XCD's L2
+    const int n0 = xcd_remap(blockIdx.x, strips) * S::STRIP;
     const int gn = n0 + VW * i;
     const bool row_ok = i < p.M;
     const float *arow = p.A + (long long)(row_ok ? i : 0) * p.lda;
@@ -71,36 +119,16 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p) {
     for (int c = 0; c < VW; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const int chunks = (p.K + 15) / 16;
-    // wave w takes chunks w, w + W, w + 2W, ...; U chunks per round so that
-    // 4*U loads of B are in flight per lane.
-    for (int j0 = wave; j0 < chunks; j0 += U * W) {
-        float bv[U][4][VW];
-        floatx4 av[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k0 = (j0 + u * W) * 16 + 4 * g;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) load_brow<VW, VEC>(p, k0 + s, gn, bv[u][s]);
-            floatx4 a = {0.f, 0.f, 0.f, 0.f};
-            if (row_ok) {
-                if (VEC && k0 + 3 < p.K) {
-                    a = *reinterpret_cast<const floatx4 *>(arow + k0);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (k0 + e < p.K) a[e] = arow[k0 + e];
-                }
-            }
-            av[u] = a;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int c = 0; c < VW; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][s], bv[u][s][c], acc[c],
-                                                                  0, 0, 0);
+    RowsRound<VW, U> r0, r1;
+    rows_load<VW, W, U, VEC>(p, wave, g, gn, row_ok, arow, r0);
+    for (int j = wave; j < chunks; j += 2 * U * W) {
+        rows_load<VW, W, U, VEC>(p, j + U * W, g, gn, row_ok, arow, r1);
+        pipeline_fence();
+        rows_mfma<VW, U>(r0, acc);
+        if (j + U * W >= chunks) break;
+        rows_load<VW, W, U, VEC>(p, j + 2 * U * W, g, gn, row_ok, arow, r0);
+        pipeline_fence();
+        rows_mfma<VW, U>(r1, acc);
     }
 
     // fixed-order reduction over the W waves
@@ -128,12 +156,70 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p) {
 template <int VW, int W, int U, bool VEC>
 hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
     const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VEC>), dim3(strips), dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VEC>), dim3(strips), dim3(64 * W), 0, stream, p,
+                       strips);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- kind 1 ----
-template <int NB, int W, int U, bool VEC>
+// One round of a lane's loads: U 4-float chunks of its row of A (k = 4*lane +
+// 256u + 0..3) and the matching 4 x NB values of B.
+template <int NB, int U>
+struct ColsRound {
+    floatx4 a[U];
+    float b[U][4][NB];
+};
+
+// BT: B is a tight K x NB block (ldb == N == NB), so the 4*NB values of four
+// consecutive k are contiguous and are read as NB 16-byte loads.
+template <int NB, int U, bool VEC, bool BT>
+__device__ __forceinline__ void cols_load(const Problem &p, const float *arow, int kbase,
+                                          ColsRound<NB, U> &r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = kbase + 256 * u;
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+        if (VEC && k + 3 < p.K) {
+            a = *reinterpret_cast<const floatx4 *>(arow + k);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k + e < p.K) a[e] = arow[k + e];
+        }
+        r.a[u] = a;
+        if (BT && k + 3 < p.K) {
+            const floatx4 *src = reinterpret_cast<const floatx4 *>(p.B + (long long)k * NB);
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const floatx4 v = src[q];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) r.b[u][(4 * q + x) / NB][(4 * q + x) % NB] = v[x];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *brow = p.B + (long long)(k + e) * p.ldb;
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    r.b[u][e][j] = (k + e < p.K && j < p.N) ? brow[j] : 0.f;
+            }
+        }
+    }
+}
+
+template <int NB, int U>
+__device__ __forceinline__ void cols_fma(const ColsRound<NB, U> &r, float (&acc)[NB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[j] = fmaf(r.a[u][e], r.b[u][e][j], acc[j]);
+}
+
+// One wave per row of A; rounds of U chunks double-buffered as in the
+// few-rows kernel (loads past K read as zero and touch no memory).
+template <int NB, int W, int U, bool VEC, bool BT>
 __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * W + wave;
@@ -143,32 +229,17 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[j] = 0.f;
 
-    for (int k0 = 4 * lane; k0 < p.K; k0 += 256 * U) {
-        floatx4 av[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = k0 + 256 * u;
-            floatx4 a = {0.f, 0.f, 0.f, 0.f};
-            if (VEC && k + 3 < p.K) {
-                a = *reinterpret_cast<const floatx4 *>(arow + k);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (k + e < p.K) a[e] = arow[k + e];
-            }
-            av[u] = a;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = k0 + 256 * u + e;
-                if (k >= p.K) continue;
-                const float *brow = p.B + (long long)k * p.ldb;
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    if (j < p.N) acc[j] = fmaf(av[u][e], brow[j], acc[j]);
-            }
+    ColsRound<NB, U> r0, r1;
+    cols_load<NB, U, VEC, BT>(p, arow, 4 * lane, r0);
+    // kw: the wave's base column of A for the round in r0 (uniform over lanes)
+    for (int kw = 0; kw < p.K; kw += 2 * 256 * U) {
+        cols_load<NB, U, VEC, BT>(p, arow, 4 * lane + kw + 256 * U, r1);
+        pipeline_fence();
+        cols_fma<NB, U>(r0, acc);
+        if (kw + 256 * U >= p.K) break;
+        cols_load<NB, U, VEC, BT>(p, arow, 4 * lane + kw + 2 * 256 * U, r0);
+        pipeline_fence();
+        cols_fma<NB, U>(r1, acc);
     }
     // butterfly reduction over the 64 lanes (fixed order)
 #pragma unroll
@@ -193,7 +264,12 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
 template <int NB, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
     const int blocks = (p.M + W - 1) / W;
-    hipLaunchKernelGGL((cols_kernel<NB, W, U, VEC>), dim3(blocks), dim3(64 * W), 0, stream, p);
+    if (VEC && p.N == NB && p.ldb == NB)
+        hipLaunchKernelGGL((cols_kernel<NB, W, U, VEC, VEC>), dim3(blocks), dim3(64 * W), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((cols_kernel<NB, W, U, VEC, false>), dim3(blocks), dim3(64 * W), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
@@ -216,10 +292,10 @@ constexpr int kRowsEntries = 4;   // entries [0, 4) are kind 0
 
 const TileEntry *skinny_tiles(int *count) {
     static const TileEntry tiles[] = {
-        rows_entry<1, 8, 4>(),    // 0: 16-column strips
-        rows_entry<2, 8, 4>(),    // 1: 32-column strips
-        rows_entry<4, 8, 2>(),    // 2: 64-column strips
-        rows_entry<2, 16, 2>(),   // 3: 32-column strips, 16 waves
+        rows_entry<1, 16, 4>(),   // 0: 16-column strips
+        rows_entry<2, 16, 2>(),   // 1: 32-column strips
+        rows_entry<4, 16, 1>(),   // 2: 64-column strips
+        rows_entry<2, 8, 4>(),    // 3: 32-column strips, 8 waves
         cols_entry<1, 4, 4>(),    // 4
         cols_entry<2, 4, 4>(),    // 5
         cols_entry<4, 4, 4>(),    // 6
@@ -242,9 +318,9 @@ bool skinny_fits(int tile, int M, int N) {
 int skinny_pick(int M, int N, int K) {
     (void)K;
     if (M <= 16) {
-        // enough strips to cover the CUs with the widest strip that allows it
+        // the widest strip that still gives every CU a workgroup, else 16 columns
         if ((N + 63) / 64 >= 256) return 2;
-        if ((N + 31) / 32 >= 128) return 1;
+        if ((N + 31) / 32 >= 256) return 1;
         return 0;
     }
     if (N <= 16) {

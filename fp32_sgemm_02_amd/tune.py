@@ -54,12 +54,18 @@ def agree(torch, C, ref, K, amax, bmax) -> bool:
     return bool(torch.isfinite(C).all()) and float((C - ref).abs().max()) <= tol
 
 
-def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0):
+def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=False):
+    """Time every candidate on (M, N, K).  With `rotate`, consecutive timed
+    calls use different copies of A and B whose total exceeds the 256 MB
+    Infinity Cache, so memory-bound shapes read their operands from HBM."""
     dev = "cuda:0"
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
-    A = torch.rand((M, K), device=dev, generator=gen) * 2 - 1
-    B = torch.rand((K, N), device=dev, generator=gen) * 2 - 1
+    per_set = 4 * (M * K + K * N)
+    copies = max(2, -(-2 * 256 * 1024 * 1024 // per_set) + 1) if rotate else 1
+    As = [torch.rand((M, K), device=dev, generator=gen) * 2 - 1 for _ in range(copies)]
+    Bs = [torch.rand((K, N), device=dev, generator=gen) * 2 - 1 for _ in range(copies)]
+    A, B = As[0], Bs[0]
     C = torch.empty((M, N), device=dev)
     ref = torch.empty((M, N), device=dev)
     sg.gemm(A, B, ref)
@@ -76,13 +82,15 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0):
         if not agree(torch, C, ref, K, 1.0, 1.0):
             print(f"  rejected v{variant} t{tile} g{group}: output differs", flush=True)
             continue
-        for _ in range(warmup):
-            call()
+        call_i = lambda i: sg.gemm(As[i % copies], Bs[i % copies], C, variant=variant, tile=tile,
+                                   group_m=group)
+        for i in range(warmup):
+            call_i(i)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
-        for s, e in ev:
+        for i, (s, e) in enumerate(ev):
             s.record()
-            call()
+            call_i(warmup + i)
             e.record()
         torch.cuda.synchronize()
         ms = statistics.median(s.elapsed_time(e) for s, e in ev)
@@ -131,6 +139,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--groups", action="store_true", help="also sweep group_m")
+    ap.add_argument("--rotate", action="store_true",
+                    help="rotate over operand copies larger than the 256 MB Infinity Cache "
+                         "(memory-bound shapes)")
     ap.add_argument("--out", default=None)
     ap.add_argument("--write-table", action="store_true")
     args = ap.parse_args()
@@ -144,7 +155,8 @@ def main():
     report, best = {}, {}
     for (M, N, K) in shapes:
         print(f"shape {M}x{N}x{K}", flush=True)
-        res = tune_shape(sg, torch, M, N, K, args.warmup, args.reps, args.groups)
+        res = tune_shape(sg, torch, M, N, K, args.warmup, args.reps, args.groups,
+                         rotate=args.rotate)
         report[f"{M}x{N}x{K}"] = res
         if res:
             best[(M, N, K)] = res[0]
