@@ -33,16 +33,19 @@ METRIC = "SGEMM GFLOP/s at 4096³ fp32 and % of MI355X fp32 peak (1 GPU)"
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and packed vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TILE_WHOLE = 0x1   # sgemm_tile_desc.flags bit of the direct-load MFMA tiles
 KERNEL_SOURCES = {
     1: ["mfma_gemm.hip", "gemm_internal.hpp"],
+    "direct": ["mfma_direct.hip", "gemm_internal.hpp"],
     2: ["valu_gemm.hip", "gemm_internal.hpp"],
     3: ["skinny_gemm.hip", "gemm_internal.hpp"],
 }
 
 
-def kernel_source_hash(variant: int) -> str:
+def kernel_source_hash(variant: int, desc: dict | None = None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(variant, []):
+    key = "direct" if variant == 1 and desc and desc.get("flags", 0) & TILE_WHOLE else variant
+    for f in KERNEL_SOURCES.get(key, []):
         with open(os.path.join(ROOT, "fp32_sgemm_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -53,6 +56,8 @@ def kernel_name(variant: int, desc: dict) -> str:
     fam = {1: "mfma", 2: "valu", 3: "skinny"}.get(variant, f"v{variant}")
     if not desc:
         return fam
+    if variant == 1 and desc.get("flags", 0) & TILE_WHOLE:
+        fam = "mfma_direct"
     return (f"{fam}_{desc['bm']}x{desc['bn']}x{desc['bk']}_w{desc['wm']}x{desc['wn']}"
             f"_s{desc.get('stages', 0)}_t{desc['threads']}")
 
@@ -155,14 +160,14 @@ def time_rotating(torch, call_i, steps, warmup):
     return [s.elapsed_time(e) for s, e in ev]
 
 
-def traffic_for(variant_used: int, kernel: str):
+def traffic_for(variant_used: int, kernel: str, desc: dict | None = None):
     """Measured HBM bytes per launch, if recorded for this exact kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     entry = rec.get(kernel)
-    if not entry or entry.get("source_hash") != kernel_source_hash(variant_used):
+    if not entry or entry.get("source_hash") != kernel_source_hash(variant_used, desc):
         return None
     return entry.get("bytes_per_launch")
 
@@ -209,7 +214,7 @@ def headline(args):
     else:
         achieved = flops / kern_s / 1e12
         peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
-    traffic = traffic_for(variant, kernel)
+    traffic = traffic_for(variant, kernel, desc)
     out = {
         "metric": METRIC,
         "value": round(value, 1),

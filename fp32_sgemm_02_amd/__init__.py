@@ -18,6 +18,7 @@ __all__ = [
     "sgemm", "sgemm_ex", "gemm", "select", "tile_count", "tile_info", "status_string",
     "version", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO",
+    "TILE_WHOLE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libfp32sgemm.so")
 
 VARIANT_AUTO, VARIANT_MFMA, VARIANT_VALU, VARIANT_SKINNY = 0, 1, 2, 3
 FLAG_SCALAR_IO = 0x1
+TILE_WHOLE = 0x1
 
 
 class SgemmConfig(ctypes.Structure):
@@ -36,7 +38,7 @@ class SgemmConfig(ctypes.Structure):
 class TileDesc(ctypes.Structure):
     """Mirror of ``sgemm_tile_desc``."""
     _fields_ = [(n, ctypes.c_int) for n in
-                ("bm", "bn", "bk", "wm", "wn", "tm", "tn", "threads", "lds_bytes", "stages")]
+                ("bm", "bn", "bk", "wm", "wn", "tm", "tn", "threads", "lds_bytes", "stages", "flags")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

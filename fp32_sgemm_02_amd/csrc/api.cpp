@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <vector>
 
 #include "gemm_internal.hpp"
 
@@ -40,25 +41,32 @@ long long tiles_for(const TileEntry &t, int M, int N) {
     return (long long)((M + t.desc.bm - 1) / t.desc.bm) * ((N + t.desc.bn - 1) / t.desc.bn);
 }
 
-// Automatic choice: the measured best configuration for this exact shape
-// (tuned_table.inc), else the skinny family for memory-bound shapes, else the
-// largest MFMA tile that still yields about one workgroup per CU.
-Tuned auto_select(int M, int N, int K) {
-    Tuned t;
-    if (lookup_tuned(M, N, K, t)) return t;
-    if (skinny_pick(M, N, K) >= 0) return Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
-    int count = 0;
-    const TileEntry *tiles = mfma_tiles(&count);
-    const int order[] = {2, 5, 7};
-    for (int idx : order)
-        if (idx < count && tiles_for(tiles[idx], M, N) >= 200)
-            return Tuned{SGEMM_VARIANT_MFMA, idx, 0};
-    return Tuned{SGEMM_VARIANT_MFMA, 7, 0};
+// The MFMA family: the general tiles followed by the whole-tile (direct-load)
+// tiles, in one table.
+const TileEntry *mfma_family(int *count) {
+    static const std::vector<TileEntry> all = [] {
+        std::vector<TileEntry> v;
+        int n = 0;
+        const TileEntry *t = mfma_tiles(&n);
+        v.insert(v.end(), t, t + n);
+        t = mfma_direct_tiles(&n);
+        v.insert(v.end(), t, t + n);
+        return v;
+    }();
+    *count = (int)all.size();
+    return all.data();
+}
+
+// Whether tile t can run this problem (whole-tile tiles need 16-byte I/O and
+// whole tiles).
+bool tile_applies(const TileEntry &t, const Problem &p, bool vec) {
+    if (!(t.desc.flags & SGEMM_TILE_WHOLE)) return true;
+    return vec && direct_applies(p, t.desc.bm, t.desc.bn, t.desc.bk);
 }
 
 const TileEntry *family(int variant, int *count) {
     switch (variant) {
-    case SGEMM_VARIANT_MFMA: return mfma_tiles(count);
+    case SGEMM_VARIANT_MFMA: return mfma_family(count);
     case SGEMM_VARIANT_VALU: return valu_tiles(count);
     case SGEMM_VARIANT_SKINNY: return skinny_tiles(count);
     default: *count = 0; return nullptr;
@@ -83,6 +91,83 @@ int validate(int M, int N, int K, float alpha, const float *A, int lda, const fl
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
+// The general MFMA tile for a shape (never a whole-tile one): the largest tile
+// that still yields about one workgroup per CU.
+int general_mfma_tile(int M, int N) {
+    int count = 0;
+    const TileEntry *tiles = mfma_tiles(&count);
+    const int order[] = {2, 5, 7};
+    for (int idx : order)
+        if (idx < count && tiles_for(tiles[idx], M, N) >= 200) return idx;
+    return 7;
+}
+
+// The MFMA tile for a shape that is not in the tuned table: the first
+// whole-tile (direct-load) configuration that applies and still yields about
+// one workgroup per CU, else the general rule.
+int default_mfma_tile(const Problem &p, bool vec) {
+    int count = 0;
+    const TileEntry *tiles = mfma_family(&count);
+    for (int i = 0; i < count; ++i)
+        if ((tiles[i].desc.flags & SGEMM_TILE_WHOLE) && tile_applies(tiles[i], p, vec) &&
+            tiles_for(tiles[i], p.M, p.N) >= 200)
+            return i;
+    return general_mfma_tile(p.M, p.N);
+}
+
+// Automatic choice: the measured best configuration for this exact shape
+// (tuned_table.inc), else the skinny family for memory-bound shapes, else the
+// default MFMA rule.  A tuned whole-tile choice is checked against the actual
+// operands in resolve().
+Tuned auto_select(const Problem &p, bool vec) {
+    Tuned t;
+    if (lookup_tuned(p.M, p.N, p.K, t)) return t;
+    if (skinny_pick(p.M, p.N, p.K) >= 0) return Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
+    return Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, vec), 0};
+}
+
+// The configuration a call runs with: explicit (sgemm_ex) or automatic, with
+// a whole-tile choice replaced by the general rule where the operands do not
+// allow it.  Returns 0 or kBadConfig.
+struct Choice {
+    int variant, tile, group_m;
+    bool vec;
+};
+
+int resolve(const Problem &p, const sgemm_config *cfg, Choice &out) {
+    const int flags = cfg ? cfg->flags : 0;
+    const bool vec = !(flags & SGEMM_FLAG_SCALAR_IO) &&
+                     vector_io_ok(p.A, (int)p.lda, p.B, (int)p.ldb, p.C, (int)p.ldc);
+    int variant = cfg ? cfg->variant : SGEMM_VARIANT_AUTO;
+    int tile = cfg ? cfg->tile : -1;
+    int group_m = cfg ? cfg->group_m : 0;
+    if (variant < 0 || variant >= SGEMM_VARIANT_COUNT) return kBadConfig;
+    const bool explicit_tile = (variant != SGEMM_VARIANT_AUTO) && tile >= 0;
+    if (variant == SGEMM_VARIANT_AUTO) {
+        const Tuned a = auto_select(p, vec);
+        variant = a.variant;
+        tile = a.tile;
+        if (group_m <= 0) group_m = a.group_m;
+    }
+    int count = 0;
+    const TileEntry *tiles = family(variant, &count);
+    if (!tiles) return kBadConfig;
+    if (variant == SGEMM_VARIANT_SKINNY) {
+        if (tile < 0) tile = skinny_pick(p.M, p.N, p.K);
+        if (!skinny_fits(tile, p.M, p.N)) return kBadConfig;   // shape is not skinny
+    } else if (tile < 0) {
+        tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, vec) : 0;
+    }
+    if (tile >= count) return kBadConfig;
+    if (!tile_applies(tiles[tile], p, vec)) {
+        if (explicit_tile) return kBadConfig;
+        tile = general_mfma_tile(p.M, p.N);   // automatic whole-tile choice that cannot run here
+    }
+    if (!(vec ? tiles[tile].vec : tiles[tile].scalar)) return kBadConfig;
+    out = Choice{variant, tile, group_m, vec};
+    return 0;
+}
+
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
         float beta, float *C, int ldc, hipStream_t stream, const sgemm_config *cfg) {
     const int v = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
@@ -94,42 +179,18 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
         return to_status(launch_scale(M, N, beta, C, ldc, stream));
     }
 
-    Tuned choice{SGEMM_VARIANT_AUTO, -1, 0};
-    int flags = 0;
-    if (cfg) {
-        choice = Tuned{cfg->variant, cfg->tile, cfg->group_m};
-        flags = cfg->flags;
-        if (choice.variant < 0 || choice.variant >= SGEMM_VARIANT_COUNT) return kBadConfig;
-    }
-    if (choice.variant == SGEMM_VARIANT_AUTO) {
-        const Tuned a = auto_select(M, N, K);
-        choice.variant = a.variant;
-        if (choice.tile < 0) choice.tile = a.tile;
-        if (choice.group_m <= 0) choice.group_m = a.group_m;
-    }
-
+    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    Choice ch;
+    const int st = resolve(p, cfg, ch);
+    if (st != 0) return st;
     int count = 0;
-    const TileEntry *tiles = family(choice.variant, &count);
-    if (!tiles) return kBadConfig;
-    if (choice.variant == SGEMM_VARIANT_SKINNY) {
-        if (choice.tile < 0) choice.tile = skinny_pick(M, N, K);
-        if (!skinny_fits(choice.tile, M, N)) return kBadConfig;   // shape is not skinny
-    } else if (choice.tile < 0) {
-        choice.tile = 0;
-        if (choice.variant == SGEMM_VARIANT_MFMA) choice.tile = auto_select(M, N, K).tile;
-        if (choice.tile < 0) choice.tile = 0;
-    }
-    if (choice.tile >= count) return kBadConfig;
-
-    Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
-    const TileEntry &t = tiles[choice.tile];
-    const bool vec = !(flags & SGEMM_FLAG_SCALAR_IO) && vector_io_ok(A, lda, B, ldb, C, ldc);
+    const TileEntry &t = family(ch.variant, &count)[ch.tile];
     static const bool log = std::getenv("FP32_SGEMM_LOG") != nullptr;
     if (log)
         std::fprintf(stderr, "sgemm M=%d N=%d K=%d variant=%d tile=%d (%dx%dx%d) group_m=%d %s\n",
-                     M, N, K, choice.variant, choice.tile, t.desc.bm, t.desc.bn, t.desc.bk,
-                     choice.group_m, vec ? "vec16" : "scalar");
-    return to_status((vec ? t.vec : t.scalar)(p, choice.group_m, stream));
+                     M, N, K, ch.variant, ch.tile, t.desc.bm, t.desc.bn, t.desc.bk, ch.group_m,
+                     ch.vec ? "vec16" : "scalar");
+    return to_status((ch.vec ? t.vec : t.scalar)(p, ch.group_m, stream));
 }
 
 }  // namespace
@@ -150,11 +211,17 @@ int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const fl
 int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                  const float *C, int ldc, sgemm_config *out) {
     if (!out) return -14;
-    const sg::Tuned t = sg::auto_select(M, N, K);
-    out->variant = t.variant;
-    out->tile = (t.variant == SGEMM_VARIANT_SKINNY && t.tile < 0) ? sg::skinny_pick(M, N, K) : t.tile;
-    out->group_m = t.group_m;
-    out->flags = sg::vector_io_ok(A, lda, B, ldb, C, ldc) ? 0 : SGEMM_FLAG_SCALAR_IO;
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    const sg::Problem p{M, N, K, 1.f, 0.f, A, lda, B, ldb, const_cast<float *>(C), ldc};
+    sg::Choice ch;
+    const int st = sg::resolve(p, nullptr, ch);
+    if (st != 0) return st;
+    out->variant = ch.variant;
+    out->tile = ch.tile;
+    out->group_m = ch.group_m;
+    out->flags = ch.vec ? 0 : SGEMM_FLAG_SCALAR_IO;
     return 0;
 }
 

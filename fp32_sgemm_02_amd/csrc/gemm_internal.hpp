@@ -39,6 +39,8 @@ struct TileEntry {
 // Kernel families (each defined in its own .hip file): the compiled tile
 // configurations, as a table owned by the family (host functions only).
 const TileEntry *mfma_tiles(int *count);
+const TileEntry *mfma_direct_tiles(int *count);   // SGEMM_TILE_WHOLE tiles
+bool direct_applies(const Problem &p, int bm, int bn, int bk);
 const TileEntry *valu_tiles(int *count);
 const TileEntry *skinny_tiles(int *count);
 

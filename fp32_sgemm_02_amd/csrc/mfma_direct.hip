@@ -1,0 +1,343 @@
+// mfma_direct.hip -- fp32 SGEMM on the matrix cores with global -> LDS
+// direct loads, for problems made of whole tiles.
+//
+// Same operation and the same tiling hierarchy as mfma_gemm.hip (workgroup
+// tiles of C, K-slices staged in LDS and reused, wave tiles computed as sums
+// of 16x16x4 outer-product blocks -- "The GEMM Scrapbook", shared-memory,
+// 2D-tiling and warptiling chapters; "a CUDA matmul" section 05), with three
+// changes to how a K-slice reaches LDS:
+//   * it is copied by buffer_load_dwordx4 ... lds: the memory pipeline writes
+//     each lane's 16 bytes straight into LDS, so the slice occupies no
+//     registers and costs no LDS-write instructions (on gfx950 a burst of
+//     ds_write_b128 per stage stalled the single wave of each SIMD for
+//     ~1,100 cycles);
+//   * the LDS image is unpadded: lane l of a load lands at byte 16*l of its
+//     1 KB block.  Bank conflicts on the A-fragment reads are avoided by an
+//     XOR swizzle instead of padding: the 16-byte chunk c of A-tile row r is
+//     stored in slot c ^ ((r >> 1) & (BK/4 - 1)), a pattern measured
+//     conflict-free for the 16-row x 4-chunk reads of a wave ("The GEMM
+//     Scrapbook", warptiling chapter: arrange accesses so the lanes hit
+//     distinct banks);
+//   * the barrier that publishes stage t+1 sits in the middle of stage t, so
+//     the first fragments of stage t+1 are read while stage t's last MFMAs
+//     run, and the direct loads into the buffer freed by that barrier start
+//     right after it.
+// Used only when A, B, C are 16-byte aligned with leading dimensions that are
+// multiples of 4 and M, N, K are multiples of BM, BN, BK: no guards.
+//
+// Register budget: a wave tile of 128x64 (or 64x128) keeps 128 accumulators
+// per lane, which the compiler holds in place; with 128x128 wave tiles (256
+// accumulators) it shuffled accumulators between register files on every
+// K-step.  So the 256x256 tiles run 8 waves, two per SIMD, and the second
+// wave of a SIMD covers the LDS latency of the first.
+//
+// Pipeline per workgroup (NBUF LDS buffers, stage t in buffer t % NBUF):
+//   prologue   issue stages 0 .. NBUF-1; wait for stage 0; barrier; read
+//              stage 0's fragments
+//   stage t    steps 0-1: MFMAs of stage t
+//              wait until this wave's loads of stage t+1 have landed; barrier
+//              (stage t+1 is then complete for every wave, and every wave has
+//              finished reading stage t from LDS)
+//              steps 2-3: MFMAs of stage t; issue the loads of stage t+NBUF
+//              into buffer t % NBUF; read stage t+1's fragments, either
+//              between the two steps (PREFETCH, two fragment sets) or after
+//              them (one set)
+// A load issued in stage t is waited for in the middle of stage t+NBUF-1:
+// NBUF = 2 leaves it 4 MFMA steps to land, NBUF = 3 leaves 8.
+#include <type_traits>
+
+#include "gemm_internal.hpp"
+
+namespace sg {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+}  // namespace
+
+bool direct_applies(const Problem &p, int bm, int bn, int bk);
+
+namespace {
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF>
+struct DirectShape {
+    static constexpr int WAVES_M = BM / WM;
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NT = NW * 64;
+    static constexpr int RB = WM / 16;
+    static constexpr int CG = WN / 64;
+    static constexpr int CPR_A = BK / 4;                // 16-byte chunks per A-tile row
+    static constexpr int CPR_B = BN / 4;                // ... per B-tile row
+    static constexpr int A_STAGE = BM * BK;             // floats
+    static constexpr int B_STAGE = BK * BN;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int LDS_BYTES = NBUF * STAGE * 4;
+    static constexpr int LA = A_STAGE / 4 / 64 / NW;    // direct loads per wave per stage (A)
+    static constexpr int LB = B_STAGE / 4 / 64 / NW;    // ... (B)
+    static constexpr int L = LA + LB;
+    static_assert(BK == 16, "one 16-wide k-chunk per stage");
+    static_assert(WM % 16 == 0 && WN % 64 == 0, "wave tile: 16-row x 64-column units");
+    static_assert(LA * 64 * NW * 4 == A_STAGE && LB * 64 * NW * 4 == B_STAGE,
+                  "stage loads divide evenly into 1 KB blocks per wave");
+    static_assert(NBUF >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring of 2+ stages");
+    static_assert(L * (NBUF - 1) <= 63, "outstanding loads fit the vmcnt counter");
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct loads of one stage.  For A-tile block j of this wave (rows
+// 16 * (wave * LA + j) .. +15 for BK = 16), lane l loads row r = l / 4 of the
+// block, logical chunk (l % 4) ^ swz(r), so that slot l % 4 of the row holds
+// it.  B-tile block j is row (wave * LB + j) of the slice (BN = 256) or part
+// of one (smaller BN): lane l loads its 16-byte chunk in row order.
+template <class S>
+struct DirectLanes {
+    int a_off[S::LA];   // byte offsets within the A panel (row-major, lda)
+    int b_off[S::LB];   // byte offsets within the B slice (row-major, ldb)
+};
+
+template <class S>
+__device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int wave, int lane) {
+    DirectLanes<S> d;
+#pragma unroll
+    for (int j = 0; j < S::LA; ++j) {
+        const int c = (wave * S::LA + j) * 64 + lane;       // chunk index in the A tile
+        const int r = c / S::CPR_A, slot = c % S::CPR_A;
+        const int chunk = slot ^ ((r >> 1) & (S::CPR_A - 1));
+        d.a_off[j] = (r * (int)p.lda + 4 * chunk) * 4;
+    }
+#pragma unroll
+    for (int j = 0; j < S::LB; ++j) {
+        const int c = (wave * S::LB + j) * 64 + lane;
+        const int r = c / S::CPR_B, q = c % S::CPR_B;
+        d.b_off[j] = (r * (int)p.ldb + 4 * q) * 4;
+    }
+    return d;
+}
+
+// Loads [lo, hi) of stage t (index < LA: A blocks, else B blocks).
+template <class S>
+__device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, int t, float *buf,
+                                            int wave, const DirectLanes<S> &d, int lo, int hi) {
+    constexpr int BK = 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.A + (long long)m0 * p.lda + (long long)t * BK), (short)0,
+        (int)((S::RB * 16 * S::WAVES_M) * p.lda * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.B + (long long)t * BK * p.ldb + n0), (short)0, (int)(BK * p.ldb * 4),
+        0x00020000);
+#pragma unroll
+    for (int q = 0; q < S::L; ++q) {
+        if (q < lo || q >= hi) continue;
+        if (q < S::LA) {
+            lds_void *dst = (lds_void *)(buf + (wave * S::LA + q) * 256);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, d.a_off[q], 0, 0, 0);
+        } else {
+            const int j = q - S::LA;
+            lds_void *dst = (lds_void *)(buf + S::A_STAGE + (wave * S::LB + j) * 256);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, d.b_off[j], 0, 0, 0);
+        }
+    }
+}
+
+template <class S>
+struct DFrag {
+    floatx4 a[S::RB];       // A(row 16rb + i, k = 4g + 0..3)
+    floatx4 b[4][S::CG];    // per MFMA step s: B(k = 4g + s, columns 64cg + 4i + 0..3)
+};
+
+// Fragment reads of one stage buffer; `part` 0..3 reads a quarter of the A
+// fragments and the B fragments of step `part`.
+template <class S>
+__device__ __forceinline__ void read_frag_part(const float *buf, int part, int lane, int wr, int wc,
+                                               DFrag<S> &f) {
+    constexpr int BK = 16;
+    const int i = lane & 15, g = lane >> 4;
+    const int slot = g ^ ((i >> 1) & 3);
+    const float *As = buf + (wr * S::RB * 16 + i) * BK + 4 * slot;
+    const float *Bs = buf + S::A_STAGE + (4 * g + part) * (S::CPR_B * 4) + wc * S::CG * 64 + 4 * i;
+    constexpr int AP = (S::RB + 3) / 4;
+#pragma unroll
+    for (int q = 0; q < AP; ++q) {
+        const int rb = part * AP + q;
+        if (rb < S::RB) f.a[rb] = *reinterpret_cast<const floatx4 *>(As + rb * 16 * BK);
+    }
+#pragma unroll
+    for (int cg = 0; cg < S::CG; ++cg)
+        f.b[part][cg] = *reinterpret_cast<const floatx4 *>(Bs + cg * 64);
+}
+
+template <class S>
+__device__ __forceinline__ void direct_mfma_step(const DFrag<S> &f, int s,
+                                                 floatx4 (&acc)[S::RB][S::CG * 4]) {
+#pragma unroll
+    for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+        for (int cg = 0; cg < S::CG; ++cg)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[rb][cg * 4 + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    f.a[rb][s], f.b[s][cg][c], acc[rb][cg * 4 + c], 0, 0, 0);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool PREFETCH>
+__global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF>::NT), 1)
+mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
+    __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / S::WAVES_N, wc = wave % S::WAVES_N;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = p.K / BK;
+    const DirectLanes<S> d = direct_lanes<S>(p, wave, lane);
+
+    floatx4 acc[S::RB][S::CG * 4];
+#pragma unroll
+    for (int a = 0; a < S::RB; ++a)
+#pragma unroll
+        for (int b = 0; b < S::CG * 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: stages 0 .. NBUF-1 in flight; stage 0 complete and published
+#pragma unroll
+    for (int t = 0; t < NBUF; ++t)
+        if (t < nk) issue_stage<S>(p, m0, n0, t, smem + t * S::STAGE, wave, d, 0, S::L);
+    if (nk >= NBUF)
+        wait_vmcnt<(NBUF - 1) * S::L>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+
+    // Stage t's fragments are in f[t % 2]; the loop body covers two stages so
+    // the two fragment sets swap roles without a register copy.
+    DFrag<S> f0, f1;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) read_frag_part<S>(smem, s, lane, wr, wc, f0);
+
+    auto stage = [&](int t, const DFrag<S> &cur, DFrag<S> &nxt) {
+        // steps 0 and 1 of stage t
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            direct_mfma_step<S>(cur, s, acc);
+            pipeline_fence();
+        }
+        // stage t+1 complete (loads issued so far: stages 0 .. min(nk, t+NBUF)-1;
+        // those after t+1 may stay in flight)
+        const bool more = (t + 1 < nk);
+        if (more) {
+            if (t + NBUF <= nk)
+                wait_vmcnt<(NBUF - 2) * S::L>();
+            else
+                wait_vmcnt<0>();
+        }
+        __syncthreads();
+        const int tf = t + NBUF;
+        const float *nbuf = smem + ((t + 1) % NBUF) * S::STAGE;
+        float *fbuf = smem + (t % NBUF) * S::STAGE;
+        // steps 2 and 3 of stage t, with stage t+1's fragments (PREFETCH) and
+        // the loads of stage t+NBUF (into the buffer stage t no longer needs)
+        // between them
+#pragma unroll
+        for (int s = 2; s < 4; ++s) {
+            if (PREFETCH && more) {
+                read_frag_part<S>(nbuf, 2 * (s - 2), lane, wr, wc, nxt);
+                read_frag_part<S>(nbuf, 2 * (s - 2) + 1, lane, wr, wc, nxt);
+            }
+            if (tf < nk)
+                issue_stage<S>(p, m0, n0, tf, fbuf, wave, d, s == 2 ? 0 : S::L / 2,
+                               s == 2 ? S::L / 2 : S::L);
+            direct_mfma_step<S>(cur, s, acc);
+            pipeline_fence();
+        }
+        if (!PREFETCH && more) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) read_frag_part<S>(nbuf, s, lane, wr, wc, nxt);
+        }
+    };
+    if (PREFETCH) {
+        int t = 0;
+        for (; t + 1 < nk; t += 2) {
+            stage(t, f0, f1);
+            stage(t + 1, f1, f0);
+        }
+        if (t < nk) stage(t, f0, f1);
+    } else {
+        for (int t = 0; t < nk; ++t) stage(t, f0, f0);
+    }
+
+    // epilogue: alpha/beta (beta == 0 never reads C), 16-byte stores
+    const int i = lane & 15, g = lane >> 4;
+    const bool read_c = (p.beta != 0.f);
+    const int row0 = m0 + wr * WM, col0 = n0 + wc * WN;
+#pragma unroll
+    for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float *crow = p.C + (long long)(row0 + rb * 16 + 4 * g + r) * p.ldc;
+#pragma unroll
+            for (int cg = 0; cg < S::CG; ++cg) {
+                floatx4 *dst = reinterpret_cast<floatx4 *>(crow + col0 + cg * 64 + 4 * i);
+                floatx4 v;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[c] = p.alpha * acc[rb][cg * 4 + c][r];
+                if (read_c) {
+                    const floatx4 old = *dst;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[c] = fmaf(p.beta, old[c], v[c]);
+                }
+                *dst = v;
+            }
+        }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool PREFETCH>
+hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
+    // whole tiles only, and buffer offsets within 31 bits; the dispatcher
+    // checks direct_applies() before choosing the tile
+    if (!direct_applies(p, BM, BN, BK)) return hipErrorInvalidValue;
+    const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+    const long long tiles = (long long)tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (group_m <= 0) group_m = 4;
+    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, PREFETCH>), dim3((unsigned)tiles),
+                       dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool PREFETCH = true>
+constexpr TileEntry direct_entry() {
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
+    return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF, SGEMM_TILE_WHOLE},
+                     &launch_direct<BM, BN, BK, WM, WN, NBUF, PREFETCH>, nullptr};
+}
+
+}  // namespace
+
+bool direct_applies(const Problem &p, int bm, int bn, int bk) {
+    return p.M % bm == 0 && p.N % bn == 0 && p.K % bk == 0 && p.K >= bk &&
+           (long long)bm * p.lda * 4 < (1LL << 31) && (long long)bk * p.ldb * 4 < (1LL << 31);
+}
+
+const TileEntry *mfma_direct_tiles(int *count) {
+    static const TileEntry tiles[] = {
+        direct_entry<256, 256, 16, 128, 64, 2, false>(),
+        direct_entry<256, 256, 16, 64, 128, 2, false>(),
+        direct_entry<256, 256, 16, 128, 64, 3, false>(),
+        direct_entry<256, 128, 16, 64, 64, 2, false>(),
+        direct_entry<128, 128, 16, 32, 64, 2, false>(),
+        direct_entry<128, 128, 16, 64, 64, 3, true>(),
+    };
+    *count = sizeof(tiles) / sizeof(tiles[0]);
+    return tiles;
+}
+
+}  // namespace sg

@@ -387,7 +387,7 @@ hipError_t launch_mfma(const Problem &p, int group_m, hipStream_t stream) {
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int OCC>
 constexpr TileEntry mfma_entry() {
     using S = MfmaShape<BM, BN, BK, WM, WN, NBUF, OCC>;
-    return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF},
+    return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF, 0},
                      &launch_mfma<BM, BN, BK, WM, WN, NBUF, OCC, true>,
                      &launch_mfma<BM, BN, BK, WM, WN, NBUF, OCC, false>};
 }

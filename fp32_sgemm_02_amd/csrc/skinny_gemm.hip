@@ -276,13 +276,13 @@ hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
 template <int VW, int W, int U>
 constexpr TileEntry rows_entry() {
     using S = RowsShape<VW, W>;
-    return TileEntry{{16, 16 * VW, 16 * W, 16, 16 * VW, 0, 0, S::NT, S::LDS_BYTES, 0},
+    return TileEntry{{16, 16 * VW, 16 * W, 16, 16 * VW, 0, 0, S::NT, S::LDS_BYTES, 0, 0},
                      &launch_rows<VW, W, U, true>, &launch_rows<VW, W, U, false>};
 }
 
 template <int NB, int W, int U>
 constexpr TileEntry cols_entry() {
-    return TileEntry{{W, NB, 256 * U, 1, NB, 0, 0, 64 * W, 0, 0},
+    return TileEntry{{W, NB, 256 * U, 1, NB, 0, 0, 64 * W, 0, 0, 0},
                      &launch_cols<NB, W, U, true>, &launch_cols<NB, W, U, false>};
 }
 

@@ -288,7 +288,7 @@ hipError_t launch_valu(const Problem &p, int group_m, hipStream_t stream) {
 template <int BM, int BN, int BK>
 constexpr TileEntry valu_entry() {
     using S = ValuShape<BM, BN, BK>;
-    return TileEntry{{BM, BN, BK, 64, 64, 8, 8, S::NT, S::LDS_BYTES, 2},
+    return TileEntry{{BM, BN, BK, 64, 64, 8, 8, S::NT, S::LDS_BYTES, 2, 0},
                      &launch_valu<BM, BN, BK, true>, &launch_valu<BM, BN, BK, false>};
 }
 

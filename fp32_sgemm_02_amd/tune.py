@@ -102,7 +102,27 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
     return results
 
 
-def write_table(best: dict, path: str = TABLE):
+def read_table(path: str = TABLE) -> dict:
+    """The rows of an existing table, {(M, N, K): {variant, tile, group_m, gflops}}."""
+    import re
+
+    rows = {}
+    if not os.path.exists(path):
+        return rows
+    pat = re.compile(r"\{(\d+), (\d+), (\d+), \{(\d+), (\d+), (\d+)\}\},\s*// ([\d,.]+) GFLOP/s")
+    for line in open(path):
+        m = pat.search(line)
+        if m and int(m.group(1)) > 0:
+            M, N, K, v, t, g = (int(m.group(i)) for i in range(1, 7))
+            rows[(M, N, K)] = {"variant": v, "tile": t, "group_m": g,
+                               "gflops": float(m.group(7).replace(",", ""))}
+    return rows
+
+
+def write_table(best: dict, path: str = TABLE, merge: bool = True):
+    """Rewrite the table with `best`; rows for other shapes are kept when `merge`."""
+    if merge:
+        best = {**read_table(path), **best}
     rows = []
     for (M, N, K), r in sorted(best.items()):
         rows.append(f"    {{{M}, {N}, {K}, {{{r['variant']}, {r['tile']}, {r['group_m']}}}}},"
@@ -144,7 +164,16 @@ def main():
                          "(memory-bound shapes)")
     ap.add_argument("--out", default=None)
     ap.add_argument("--write-table", action="store_true")
+    ap.add_argument("--from-json", default=None,
+                    help="write the table from a saved --out report instead of timing")
     args = ap.parse_args()
+    if args.from_json:
+        report = json.load(open(args.from_json))
+        best = {parse_shape(k): v[0] for k, v in report.items() if v}
+        write_table(best)
+        for k, r in sorted(best.items()):
+            print(k, r["variant"], r["tile"], r["group_m"], r["gflops"])
+        return
 
     shapes = []
     for name in filter(None, args.workloads.split(",")):

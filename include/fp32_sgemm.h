@@ -93,7 +93,15 @@ typedef struct sgemm_tile_desc {
     int threads;      /* workgroup size */
     int lds_bytes;    /* LDS per workgroup */
     int stages;       /* LDS buffers in the K pipeline (0: no LDS staging) */
+    int flags;        /* SGEMM_TILE_* bits */
 } sgemm_tile_desc;
+
+/* sgemm_tile_desc.flags: the tile only serves problems made of whole tiles
+ * (M, N, K multiples of bm, bn, bk) with A, B, C 16-byte aligned, leading
+ * dimensions that are multiples of 4, and bm * lda and bk * ldb below 2^29
+ * elements (31-bit byte offsets within one tile's panel).  Asked for explicitly
+ * elsewhere, sgemm_ex returns -13; automatic dispatch never picks it there. */
+#define SGEMM_TILE_WHOLE 0x1
 
 /*
  * sgemm: C = alpha * (A * B) + beta * C, kernel family and tile chosen from
@@ -121,8 +129,8 @@ int sgemm_ex(int M, int N, int K, float alpha,
 /*
  * sgemm_select: the configuration sgemm() would use for this shape and these
  * pointers/leading dimensions, written to *out (variant, tile, flags,
- * group_m).  Reads no memory behind A, B or C.  Returns 0, or -14 when out is
- * NULL.
+ * group_m).  Reads no memory behind A, B or C.  Returns 0; -1, -2 or -3 for a
+ * negative M, N or K; -14 when out is NULL.
  */
 int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B,
                  int ldb, const float *C, int ldc, sgemm_config *out);

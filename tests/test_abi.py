@@ -101,6 +101,47 @@ def test_bad_configuration():
     assert sg.sgemm_ex(8, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
 
 
+def whole_tiles():
+    return [t for t in range(sg.tile_count(sg.VARIANT_MFMA))
+            if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_WHOLE]
+
+
+def test_whole_tiles_rejected_where_they_cannot_run():
+    """Whole-tile (direct-load) configurations refuse, before any launch,
+    shapes that are not made of whole tiles, unaligned operands and scalar I/O."""
+    assert whole_tiles(), "no whole-tile MFMA configuration compiled"
+    good = 0x10000
+    for t in whole_tiles():
+        d = sg.tile_info(sg.VARIANT_MFMA, t)
+        bm, bn, bk = d["bm"], d["bn"], d["bk"]
+        for (M, N, K) in ((bm + 1, bn, 4 * bk), (bm, bn + 4, 4 * bk), (bm, bn, 4 * bk + 4),
+                          (2 * bm - 16, bn, bk), (bm, bn, bk // 2)):
+            cfg = sg.SgemmConfig(sg.VARIANT_MFMA, t, 0, 0)
+            assert sg.sgemm_ex(M, N, K, 1.0, good, K, good, N, 0.0, good, N, None, cfg) == -13
+        M, N, K = 2 * bm, bn, 4 * bk
+        cfg = sg.SgemmConfig(sg.VARIANT_MFMA, t, sg.FLAG_SCALAR_IO, 0)
+        assert sg.sgemm_ex(M, N, K, 1.0, good, K, good, N, 0.0, good, N, None, cfg) == -13
+        cfg = sg.SgemmConfig(sg.VARIANT_MFMA, t, 0, 0)
+        assert sg.sgemm_ex(M, N, K, 1.0, good + 4, K, good, N, 0.0, good, N, None, cfg) == -13
+        assert sg.sgemm_ex(M, N, K, 1.0, good, K + 2, good, N, 0.0, good, N, None, cfg) == -13
+
+
+def test_automatic_selection_never_picks_an_inapplicable_whole_tile():
+    for (M, N, K) in ((4096, 4096, 4096), (8192, 8192, 8192), (8192, 14336, 4096)):
+        for a in (0x10000, 0x10004):
+            cfg = sg.select(M, N, K, a, K, 0x20000, N, 0x30000, N)
+            d = sg.tile_info(cfg.variant, cfg.tile)
+            if d["flags"] & sg.TILE_WHOLE:
+                assert a % 16 == 0 and M % d["bm"] == 0 and N % d["bn"] == 0
+        cfg = sg.select(M + 1, N, K, 0x10000, K, 0x20000, N, 0x30000, N)
+        assert not sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_WHOLE
+    # an untuned shape made of whole tiles gets a whole tile, an untuned ragged one does not
+    cfg = sg.select(6144, 6144, 6144, 0x10000, 6144, 0x20000, 6144, 0x30000, 6144)
+    assert sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_WHOLE
+    cfg = sg.select(6143, 6144, 6144, 0x10000, 6144, 0x20000, 6144, 0x30000, 6144)
+    assert not sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_WHOLE
+
+
 def test_automatic_selection():
     assert sg.select(4096, 4096, 4096).variant == sg.VARIANT_MFMA
     assert sg.select(1, 4096, 4096).variant == sg.VARIANT_SKINNY

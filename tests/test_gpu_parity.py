@@ -101,6 +101,54 @@ def test_tile_integer_bit_exact(variant, tile, oracle_mod):
     check(A, B, C0, 0.5, -1.25, C, oracle_mod, exact=True, label=f"v{variant} t{tile} int scalar")
 
 
+# ------------------------------------------------------ whole-tile MFMA --
+def whole_tiles():
+    return [t for t in tiles(sg.VARIANT_MFMA)
+            if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_WHOLE]
+
+
+@pytest.mark.parametrize("slot", range(12))
+def test_whole_tile_parity(slot, oracle_mod):
+    """Direct-load tiles on shapes made of whole tiles: 1, 2, 3, 5 and 17
+    K-steps (fewer than the LDS ring, odd and even counts, many), alpha/beta,
+    beta = 0 over a NaN C, integer inputs bit-exact, and padded rows."""
+    wt = whole_tiles()
+    if slot >= len(wt):
+        pytest.skip("no such whole-tile configuration")
+    tile = wt[slot]
+    d = sg.tile_info(sg.VARIANT_MFMA, tile)
+    bm, bn, bk = d["bm"], d["bn"], d["bk"]
+    kw = dict(variant=sg.VARIANT_MFMA, tile=tile)
+    for i, (mt, nt, kt) in enumerate(((1, 1, 1), (2, 1, 2), (1, 3, 3), (2, 2, 5), (3, 2, 17))):
+        M, N, K = mt * bm, nt * bn, kt * bk
+        lab = f"whole t{tile} {(M, N, K)}"
+        A, B, C0 = uniform(M, N, K, 400 + i)
+        C = run_gpu(A, B, C0, 0.5, -1.25, **kw)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, label=lab)
+        C = run_gpu(A, B, None, 1.0, 0.0, **kw)
+        check(A, B, None, 1.0, 0.0, C, oracle_mod, label=lab + " b0")
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 500 + i, True)
+        C = run_gpu(Ai, Bi, Ci, 0.5, -1.25, **kw)
+        check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=lab + " int")
+    # rows padded by multiples of 4 floats keep every row 16-byte aligned
+    M, N, K = 2 * bm, bn, 4 * bk
+    rng = np.random.default_rng(tile)
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+    As = torch.full((M, K + 4), float("nan"), device=DEV)
+    Bs = torch.full((K, N + 8), float("nan"), device=DEV)
+    Cs = torch.full((M, N + 4), 777.0, device=DEV)
+    As[:, :K] = dev(A)
+    Bs[:, :N] = dev(B)
+    Cs[:, :N] = dev(C0)
+    sg.gemm(As[:, :K], Bs[:, :N], Cs[:, :N], 0.5, -1.25, **kw)
+    torch.cuda.synchronize()
+    Ch = Cs.cpu().numpy()
+    assert np.all(Ch[:, N:] == 777.0), "C padding written"
+    check(A, B, C0, 0.5, -1.25, Ch[:, :N].copy(), oracle_mod, label=f"whole t{tile} padded")
+
+
 SKINNY_CASES = {
     0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
     1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],
