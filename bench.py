@@ -105,24 +105,24 @@ def cpu_baseline(w, A, B, C0, target_s: float) -> dict:
 
 
 def time_calls(torch, call, steps, warmup):
-    """(wall seconds for `steps` back-to-back calls, per-call event durations in
-    ms).  The events are recorded on torch's current stream, the stream the
-    library launches on."""
+    """(wall seconds for `steps` back-to-back calls, mean device time per call
+    in ms).  One pair of HIP events brackets the whole timed region on torch's
+    current stream, the stream the library launches on, so the mean is the
+    average launch duration (plus whatever gaps the host leaves between
+    launches) without per-call events between the kernels."""
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         call()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, durs
+    return wall, start.elapsed_time(end) / steps
 
 
 MALL_BYTES = 256 * 1024 * 1024     # MI355X Infinity Cache
@@ -199,12 +199,12 @@ def headline(args):
     tile = args.tile if args.tile >= 0 else chosen.tile
     if args.variant and args.tile < 0:
         tile = -1
-    wall, durs = time_calls(torch, call, args.steps, args.warmup)
+    wall, kern_ms = time_calls(torch, call, args.steps, args.warmup)
     torch.cuda.synchronize()
 
     flops = w.flops
     value = flops * args.steps / wall / 1e9
-    kern_s = statistics.mean(durs) / 1e3
+    kern_s = kern_ms / 1e3
     desc = sg.tile_info(variant, tile) if tile >= 0 else {}
     kernel = kernel_name(variant, desc)
     bound = w.bound
@@ -234,9 +234,7 @@ def headline(args):
                    "tile": tile, "tile_desc": desc},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel, "kernel_ms_mean": round(kern_s * 1e3, 4),
-                     "kernel_ms_min": round(min(durs), 4),
-                     "kernel_ms_median": round(statistics.median(durs), 4)},
+                     "kernel": kernel, "kernel_ms_mean": round(kern_s * 1e3, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, C0, args.cpu_seconds)
@@ -244,9 +242,14 @@ def headline(args):
 
 
 def sweep(args):
+    """Every named workload through automatic dispatch.  `kernel_ms_median` is
+    the device time per call from HIP-graph replay (calls back to back with no
+    host launch gaps); `eager_call_ms_median` brackets single eager calls with
+    events and includes the host launch path, which dominates small shapes."""
     import numpy as np
     import torch
     import fp32_sgemm_02_amd as sg
+    from fp32_sgemm_02_amd.tune import time_graph
     import workloads
 
     torch.cuda.set_device(0)
@@ -262,12 +265,14 @@ def sweep(args):
         for v in variants:
             kw = dict(variant=v) if v else {}
             call_i = lambda i, kw=kw: sg.gemm(*sets[i % len(sets)], w.alpha, w.beta, **kw)
-            durs = time_rotating(torch, call_i, 30 if hbm else 20, 5)
-            med = statistics.median(durs) / 1e3
+            eager = statistics.median(time_rotating(torch, call_i, 30 if hbm else 20, 5)) / 1e3
+            calls = max(len(sets), 20 if w.flops < 1e11 else 5)
+            med = statistics.median(time_graph(torch, call_i, calls)) / 1e3
             cfg = sg.select(w.M, w.N, w.K)
             row = {"workload": name, "M": w.M, "N": w.N, "K": w.K,
                    "variant": v or cfg.variant, "tile": cfg.tile if v == 0 else -1,
                    "kernel_ms_median": round(med * 1e3, 4),
+                   "eager_call_ms_median": round(eager * 1e3, 4),
                    "gflops": round(w.flops / med / 1e9, 1),
                    "gbs": round(w.min_bytes / med / 1e9, 1), "bound": w.bound,
                    "operand_copies": len(sets)}
@@ -291,8 +296,7 @@ def copy_calibration(args):
     n = args.copy_bytes // 4
     src = torch.ones(n, device="cuda:0")
     dst = torch.empty_like(src)
-    wall, durs = time_calls(torch, lambda: dst.copy_(src), args.steps, args.warmup)
-    ms = statistics.mean(durs)
+    wall, ms = time_calls(torch, lambda: dst.copy_(src), args.steps, args.warmup)
     print(json.dumps({"copy_bytes": n * 4, "read_bytes": n * 4, "write_bytes": n * 4,
                       "kernel_ms_mean": round(ms, 4),
                       "gbs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
@@ -320,11 +324,11 @@ def probes(args):
         launch = getattr(lib, f"probe_{name.split('_')[0]}_f32")
         flops = getattr(lib, f"probe_{name.split('_')[0]}_flops")(blocks, iters)
         call = lambda: launch(blocks, iters, out.data_ptr(), stream)
-        _, durs = time_calls(torch, call, 10, 3)
-        med = statistics.median(durs) / 1e3
+        _, ms = time_calls(torch, call, 10, 3)
+        med = ms / 1e3
         tf = flops / med / 1e12
         print(json.dumps({"probe": name, "tflops": round(tf, 2), "peak_tflops": peak,
-                          "frac": round(tf / peak, 4), "kernel_ms_median": round(med * 1e3, 4),
+                          "frac": round(tf / peak, 4), "kernel_ms_mean": round(med * 1e3, 4),
                           "implied_clock_ghz": round(tf * 1e12 / (256 * (256 if name.startswith("mfma") else 128)) / 1e9, 3)}),
               flush=True)
 
@@ -332,7 +336,7 @@ def probes(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.probes:

@@ -158,7 +158,10 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out) {
     } else if (tile < 0) {
         tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, vec) : 0;
     }
-    if (tile >= count) return kBadConfig;
+    if (tile >= count) {
+        if (explicit_tile || variant != SGEMM_VARIANT_MFMA) return kBadConfig;
+        tile = general_mfma_tile(p.M, p.N);   // a tuned row naming a tile that is not compiled
+    }
     if (!tile_applies(tiles[tile], p, vec)) {
         if (explicit_tile) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // automatic whole-tile choice that cannot run here

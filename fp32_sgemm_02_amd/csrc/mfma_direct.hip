@@ -18,10 +18,9 @@
 //     conflict-free for the 16-row x 4-chunk reads of a wave ("The GEMM
 //     Scrapbook", warptiling chapter: arrange accesses so the lanes hit
 //     distinct banks);
-//   * the barrier that publishes stage t+1 sits in the middle of stage t, so
-//     the first fragments of stage t+1 are read while stage t's last MFMAs
-//     run, and the direct loads into the buffer freed by that barrier start
-//     right after it.
+//   * the barrier that publishes stage t+1 sits in the middle of stage t,
+//     and every LDS read and load issue of a stage is spread between its
+//     MFMAs (rolling fragments, below) instead of queueing at its end.
 // Used only when A, B, C are 16-byte aligned with leading dimensions that are
 // multiples of 4 and M, N, K are multiples of BM, BN, BK: no guards.
 //
@@ -31,19 +30,21 @@
 // K-step.  So the 256x256 tiles run 8 waves, two per SIMD, and the second
 // wave of a SIMD covers the LDS latency of the first.
 //
-// Pipeline per workgroup (NBUF LDS buffers, stage t in buffer t % NBUF):
-//   prologue   issue stages 0 .. NBUF-1; wait for stage 0; barrier; read
-//              stage 0's fragments
-//   stage t    steps 0-1: MFMAs of stage t
-//              wait until this wave's loads of stage t+1 have landed; barrier
-//              (stage t+1 is then complete for every wave, and every wave has
-//              finished reading stage t from LDS)
-//              steps 2-3: MFMAs of stage t; issue the loads of stage t+NBUF
-//              into buffer t % NBUF; read stage t+1's fragments, either
-//              between the two steps (PREFETCH, two fragment sets) or after
-//              them (one set)
-// A load issued in stage t is waited for in the middle of stage t+NBUF-1:
-// NBUF = 2 leaves it 4 MFMA steps to land, NBUF = 3 leaves 8.
+// Rolling fragments.  The MFMAs of a stage run row block by row block (all
+// four k-steps of 16-row block rb, then rb+1), so A fragment a[rb] is dead as
+// soon as its block is done and its registers take the next stage's a[rb];
+// only the B fragments need a second set.  With RB row blocks per wave and
+// H = RB/2, per workgroup (NBUF LDS buffers, stage t in buffer t % NBUF):
+//   prologue     issue stages 0 .. NBUF-1; wait for stage 0; barrier; read
+//                a[0 .. H-1] and B of stage 0
+//   stage t      blocks 0 .. H-1: before block rb, read a[H + rb] of stage t
+//                wait until this wave's loads of stage t+1 have landed;
+//                barrier (stage t+1 is then complete for every wave, and no
+//                wave reads stage t's buffer any more)
+//                blocks H .. RB-1: before block rb, read the next stage's
+//                a[rb - H] and a share of its B fragments, and issue a share
+//                of the loads of stage t+NBUF into buffer t % NBUF
+// A load issued in stage t is waited for in the middle of stage t+NBUF-1.
 #include <type_traits>
 
 #include "gemm_internal.hpp"
@@ -75,7 +76,8 @@ struct DirectShape {
     static constexpr int LA = A_STAGE / 4 / 64 / NW;    // direct loads per wave per stage (A)
     static constexpr int LB = B_STAGE / 4 / 64 / NW;    // ... (B)
     static constexpr int L = LA + LB;
-    static_assert(BK == 16, "one 16-wide k-chunk per stage");
+    static constexpr int KC = BK / 16;                  // 16-wide k-chunks per stage
+    static_assert(BK == 16 || BK == 32, "one or two 16-wide k-chunks per stage");
     static_assert(WM % 16 == 0 && WN % 64 == 0, "wave tile: 16-row x 64-column units");
     static_assert(LA * 64 * NW * 4 == A_STAGE && LB * 64 * NW * 4 == B_STAGE,
                   "stage loads divide evenly into 1 KB blocks per wave");
@@ -91,11 +93,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Direct loads of one stage.  For A-tile block j of this wave (rows
-// 16 * (wave * LA + j) .. +15 for BK = 16), lane l loads row r = l / 4 of the
-// block, logical chunk (l % 4) ^ swz(r), so that slot l % 4 of the row holds
-// it.  B-tile block j is row (wave * LB + j) of the slice (BN = 256) or part
-// of one (smaller BN): lane l loads its 16-byte chunk in row order.
+// Direct loads of one stage.  The A tile is BM rows of CPR_A 16-byte chunks;
+// A-tile block j of this wave covers chunks 64 * (wave * LA + j) .. +63 in
+// row-major order, and the lane that fills slot `slot` of row r loads
+// logical chunk slot ^ swz(r), swz(r) = (r >> 1) & (CPR_A - 1).  B-tile
+// block j covers the next 64 chunks of the row-major BK x BN slice, each lane
+// loading its own chunk.
 template <class S>
 struct DirectLanes {
     int a_off[S::LA];   // byte offsets within the A panel (row-major, lda)
@@ -125,7 +128,7 @@ __device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int wav
 template <class S>
 __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, int t, float *buf,
                                             int wave, const DirectLanes<S> &d, int lo, int hi) {
-    constexpr int BK = 16;
+    constexpr int BK = S::KC * 16;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.A + (long long)m0 * p.lda + (long long)t * BK), (short)0,
         (int)((S::RB * 16 * S::WAVES_M) * p.lda * 4), 0x00020000);
@@ -146,50 +149,48 @@ __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, in
     }
 }
 
+// Fragment reads of k-chunk kc of a stage.  For lane (i, g):
+// a = A(row 16rb + i, k = 16kc + 4g + 0..3) (logical chunk 4kc + g of the
+// row, stored in slot (4kc + g) ^ swz); b[s][cg] = B(k = 16kc + 4g + s,
+// columns 64cg + 4i + 0..3), the B operand of MFMA step s.
 template <class S>
-struct DFrag {
-    floatx4 a[S::RB];       // A(row 16rb + i, k = 4g + 0..3)
-    floatx4 b[4][S::CG];    // per MFMA step s: B(k = 4g + s, columns 64cg + 4i + 0..3)
-};
-
-// Fragment reads of one stage buffer; `part` 0..3 reads a quarter of the A
-// fragments and the B fragments of step `part`.
-template <class S>
-__device__ __forceinline__ void read_frag_part(const float *buf, int part, int lane, int wr, int wc,
-                                               DFrag<S> &f) {
-    constexpr int BK = 16;
+__device__ __forceinline__ void read_a(const float *buf, int kc, int rb, int lane, int wr,
+                                       floatx4 &a) {
     const int i = lane & 15, g = lane >> 4;
-    const int slot = g ^ ((i >> 1) & 3);
-    const float *As = buf + (wr * S::RB * 16 + i) * BK + 4 * slot;
-    const float *Bs = buf + S::A_STAGE + (4 * g + part) * (S::CPR_B * 4) + wc * S::CG * 64 + 4 * i;
-    constexpr int AP = (S::RB + 3) / 4;
-#pragma unroll
-    for (int q = 0; q < AP; ++q) {
-        const int rb = part * AP + q;
-        if (rb < S::RB) f.a[rb] = *reinterpret_cast<const floatx4 *>(As + rb * 16 * BK);
-    }
-#pragma unroll
-    for (int cg = 0; cg < S::CG; ++cg)
-        f.b[part][cg] = *reinterpret_cast<const floatx4 *>(Bs + cg * 64);
+    const int slot = (4 * kc + g) ^ ((i >> 1) & (S::CPR_A - 1));
+    a = *reinterpret_cast<const floatx4 *>(buf + (wr * S::RB * 16 + rb * 16 + i) * (S::CPR_A * 4) +
+                                           4 * slot);
 }
 
 template <class S>
-__device__ __forceinline__ void direct_mfma_step(const DFrag<S> &f, int s,
-                                                 floatx4 (&acc)[S::RB][S::CG * 4]) {
+__device__ __forceinline__ void read_b(const float *buf, int kc, int s, int lane, int wc,
+                                       floatx4 (&b)[4][S::CG]) {
+    const int i = lane & 15, g = lane >> 4;
+    const float *Bs = buf + S::A_STAGE + (16 * kc + 4 * g + s) * (S::CPR_B * 4) +
+                      wc * S::CG * 64 + 4 * i;
 #pragma unroll
-    for (int rb = 0; rb < S::RB; ++rb)
+    for (int cg = 0; cg < S::CG; ++cg) b[s][cg] = *reinterpret_cast<const floatx4 *>(Bs + cg * 64);
+}
+
+template <class S>
+__device__ __forceinline__ void roll_block(const floatx4 &a, const floatx4 (&b)[4][S::CG],
+                                           floatx4 (&acc)[S::CG * 4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int cg = 0; cg < S::CG; ++cg)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                acc[rb][cg * 4 + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    f.a[rb][s], f.b[s][cg][c], acc[rb][cg * 4 + c], 0, 0, 0);
+                acc[cg * 4 + c] =
+                    __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s][cg][c], acc[cg * 4 + c], 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool PREFETCH>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF>
 __global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF>::NT), 1)
 mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
+    constexpr int RB = S::RB, H = RB / 2;
+    static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,9 +201,9 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     const int nk = p.K / BK;
     const DirectLanes<S> d = direct_lanes<S>(p, wave, lane);
 
-    floatx4 acc[S::RB][S::CG * 4];
+    floatx4 acc[RB][S::CG * 4];
 #pragma unroll
-    for (int a = 0; a < S::RB; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
         for (int b = 0; b < S::CG * 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -216,61 +217,70 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
         wait_vmcnt<0>();
     __syncthreads();
 
-    // Stage t's fragments are in f[t % 2]; the loop body covers two stages so
-    // the two fragment sets swap roles without a register copy.
-    DFrag<S> f0, f1;
+    floatx4 a[RB];
+    floatx4 b0[4][S::CG], b1[4][S::CG];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) read_frag_part<S>(smem, s, lane, wr, wc, f0);
+    for (int rb = 0; rb < H; ++rb) read_a<S>(smem, 0, rb, lane, wr, a[rb]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) read_b<S>(smem, 0, s, lane, wc, b0);
 
-    auto stage = [&](int t, const DFrag<S> &cur, DFrag<S> &nxt) {
-        // steps 0 and 1 of stage t
+    // One k-chunk: the MFMAs of chunk kc of stage t with B fragments bc, and
+    // the fragments of the following chunk (of this stage, or chunk 0 of the
+    // next) read into a[] and bn.  The last chunk of a stage holds the barrier
+    // and issues the loads of stage t+NBUF.
+    auto chunk = [&](int t, int kc, const floatx4 (&bc)[4][S::CG], floatx4 (&bn)[4][S::CG]) {
+        const float *cbuf = smem + (t % NBUF) * S::STAGE;
+        const bool last = (kc == S::KC - 1);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            direct_mfma_step<S>(cur, s, acc);
+        for (int rb = 0; rb < H; ++rb) {
+            read_a<S>(cbuf, kc, rb + H, lane, wr, a[rb + H]);
+            roll_block<S>(a[rb], bc, acc[rb]);
             pipeline_fence();
         }
-        // stage t+1 complete (loads issued so far: stages 0 .. min(nk, t+NBUF)-1;
-        // those after t+1 may stay in flight)
-        const bool more = (t + 1 < nk);
-        if (more) {
-            if (t + NBUF <= nk)
-                wait_vmcnt<(NBUF - 2) * S::L>();
-            else
-                wait_vmcnt<0>();
-        }
-        __syncthreads();
-        const int tf = t + NBUF;
-        const float *nbuf = smem + ((t + 1) % NBUF) * S::STAGE;
-        float *fbuf = smem + (t % NBUF) * S::STAGE;
-        // steps 2 and 3 of stage t, with stage t+1's fragments (PREFETCH) and
-        // the loads of stage t+NBUF (into the buffer stage t no longer needs)
-        // between them
-#pragma unroll
-        for (int s = 2; s < 4; ++s) {
-            if (PREFETCH && more) {
-                read_frag_part<S>(nbuf, 2 * (s - 2), lane, wr, wc, nxt);
-                read_frag_part<S>(nbuf, 2 * (s - 2) + 1, lane, wr, wc, nxt);
+        const bool more = !last || (t + 1 < nk);     // a following chunk exists
+        const float *nbuf = cbuf;
+        int nkc = kc + 1;
+        if (last) {
+            if (more) {
+                if (t + NBUF <= nk)
+                    wait_vmcnt<(NBUF - 2) * S::L>();
+                else
+                    wait_vmcnt<0>();
             }
-            if (tf < nk)
-                issue_stage<S>(p, m0, n0, tf, fbuf, wave, d, s == 2 ? 0 : S::L / 2,
-                               s == 2 ? S::L / 2 : S::L);
-            direct_mfma_step<S>(cur, s, acc);
-            pipeline_fence();
+            __syncthreads();
+            nbuf = smem + ((t + 1) % NBUF) * S::STAGE;
+            nkc = 0;
         }
-        if (!PREFETCH && more) {
+        const int tf = t + NBUF;
+        float *fbuf = smem + (t % NBUF) * S::STAGE;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) read_frag_part<S>(nbuf, s, lane, wr, wc, nxt);
+        for (int j = 0; j < H; ++j) {
+            if (more) {
+                read_a<S>(nbuf, nkc, j, lane, wr, a[j]);
+#pragma unroll
+                for (int s = (4 * j) / H; s < (4 * (j + 1)) / H; ++s)
+                    read_b<S>(nbuf, nkc, s, lane, wc, bn);
+            }
+            if (last && tf < nk)
+                issue_stage<S>(p, m0, n0, tf, fbuf, wave, d, (S::L * j) / H, (S::L * (j + 1)) / H);
+            roll_block<S>(a[H + j], bc, acc[H + j]);
+            pipeline_fence();
         }
     };
-    if (PREFETCH) {
+    if (S::KC == 2) {
+        // an even number of chunks per stage: the B sets are back in place
+        for (int t = 0; t < nk; ++t) {
+            chunk(t, 0, b0, b1);
+            chunk(t, 1, b1, b0);
+        }
+    } else {
+        // one chunk per stage: two stages per iteration swap the B sets back
         int t = 0;
         for (; t + 1 < nk; t += 2) {
-            stage(t, f0, f1);
-            stage(t + 1, f1, f0);
+            chunk(t, 0, b0, b1);
+            chunk(t + 1, 0, b1, b0);
         }
-        if (t < nk) stage(t, f0, f1);
-    } else {
-        for (int t = 0; t < nk; ++t) stage(t, f0, f0);
+        if (t < nk) chunk(t, 0, b0, b1);
     }
 
     // epilogue: alpha/beta (beta == 0 never reads C), 16-byte stores
@@ -278,7 +288,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     const bool read_c = (p.beta != 0.f);
     const int row0 = m0 + wr * WM, col0 = n0 + wc * WN;
 #pragma unroll
-    for (int rb = 0; rb < S::RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float *crow = p.C + (long long)(row0 + rb * 16 + 4 * g + r) * p.ldc;
@@ -298,26 +308,24 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool PREFETCH>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF>
 hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
     using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
-    // whole tiles only, and buffer offsets within 31 bits; the dispatcher
-    // checks direct_applies() before choosing the tile
     if (!direct_applies(p, BM, BN, BK)) return hipErrorInvalidValue;
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
-    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, PREFETCH>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF>), dim3((unsigned)tiles),
                        dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool PREFETCH = true>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF>
 constexpr TileEntry direct_entry() {
     using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
     return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF, SGEMM_TILE_WHOLE},
-                     &launch_direct<BM, BN, BK, WM, WN, NBUF, PREFETCH>, nullptr};
+                     &launch_direct<BM, BN, BK, WM, WN, NBUF>, nullptr};
 }
 
 }  // namespace
@@ -329,12 +337,14 @@ bool direct_applies(const Problem &p, int bm, int bn, int bk) {
 
 const TileEntry *mfma_direct_tiles(int *count) {
     static const TileEntry tiles[] = {
-        direct_entry<256, 256, 16, 128, 64, 2, false>(),
-        direct_entry<256, 256, 16, 64, 128, 2, false>(),
-        direct_entry<256, 256, 16, 128, 64, 3, false>(),
-        direct_entry<256, 128, 16, 64, 64, 2, false>(),
-        direct_entry<128, 128, 16, 32, 64, 2, false>(),
-        direct_entry<128, 128, 16, 64, 64, 3, true>(),
+        direct_entry<256, 256, 16, 64, 128, 2>(),
+        direct_entry<256, 256, 16, 128, 64, 2>(),
+        direct_entry<256, 128, 16, 64, 64, 2>(),
+        direct_entry<128, 128, 16, 32, 64, 2>(),
+        direct_entry<128, 128, 16, 64, 64, 2>(),
+        direct_entry<256, 256, 32, 64, 128, 2>(),
+        direct_entry<256, 256, 32, 128, 64, 2>(),
+        direct_entry<128, 128, 32, 32, 64, 2>(),
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;

@@ -54,7 +54,39 @@ def agree(torch, C, ref, K, amax, bmax) -> bool:
     return bool(torch.isfinite(C).all()) and float((C - ref).abs().max()) <= tol
 
 
-def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=False):
+def time_graph(torch, call_i, calls: int, replays: int = 5):
+    """Device time per call (ms) with no host gaps: `calls` consecutive calls
+    call_i(0), call_i(1), ... captured in one HIP graph on a side stream, the
+    graph replayed `replays` times; returns one per-call time per replay.
+    The library's launches go to torch's current stream, which inside the
+    capture is the capture stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(calls, 3)):
+            call_i(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            call_i(i)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(replays):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / calls)
+    del g
+    return out
+
+
+def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=False,
+               graph=False):
     """Time every candidate on (M, N, K).  With `rotate`, consecutive timed
     calls use different copies of A and B whose total exceeds the 256 MB
     Infinity Cache, so memory-bound shapes read their operands from HBM."""
@@ -84,16 +116,19 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
             continue
         call_i = lambda i: sg.gemm(As[i % copies], Bs[i % copies], C, variant=variant, tile=tile,
                                    group_m=group)
-        for i in range(warmup):
-            call_i(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for i, (s, e) in enumerate(ev):
-            s.record()
-            call_i(warmup + i)
-            e.record()
-        torch.cuda.synchronize()
-        ms = statistics.median(s.elapsed_time(e) for s, e in ev)
+        if graph:
+            ms = statistics.median(time_graph(torch, call_i, max(reps, copies)))
+        else:
+            for i in range(warmup):
+                call_i(i)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for i, (s, e) in enumerate(ev):
+                s.record()
+                call_i(warmup + i)
+                e.record()
+            torch.cuda.synchronize()
+            ms = statistics.median(s.elapsed_time(e) for s, e in ev)
         gf = 2.0 * M * N * K / (ms / 1e3) / 1e9
         results.append({"variant": variant, "tile": tile, "group_m": group, "ms": round(ms, 5),
                         "gflops": round(gf, 1), "desc": sg.tile_info(variant, tile)})
@@ -162,6 +197,9 @@ def main():
     ap.add_argument("--rotate", action="store_true",
                     help="rotate over operand copies larger than the 256 MB Infinity Cache "
                          "(memory-bound shapes)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time calls replayed from a HIP graph (no host launch gaps; for "
+                         "shapes whose kernels are shorter than the host launch path)")
     ap.add_argument("--out", default=None)
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--from-json", default=None,
@@ -185,7 +223,7 @@ def main():
     for (M, N, K) in shapes:
         print(f"shape {M}x{N}x{K}", flush=True)
         res = tune_shape(sg, torch, M, N, K, args.warmup, args.reps, args.groups,
-                         rotate=args.rotate)
+                         rotate=args.rotate, graph=args.graph)
         report[f"{M}x{N}x{K}"] = res
         if res:
             best[(M, N, K)] = res[0]

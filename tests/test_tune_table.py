@@ -20,7 +20,15 @@ def test_table_round_trip_and_merge(tmp_path):
     assert "lookup_tuned" in text and "sentinel" in text
 
 
-def test_shipped_table_parses():
+def test_shipped_table_parses_and_names_compiled_tiles():
+    import fp32_sgemm_02_amd as sg
+
     rows = tune.read_table()
     assert (4096, 4096, 4096) in rows
-    assert all(r["variant"] in (1, 2, 3) for r in rows.values())
+    for shape, r in rows.items():
+        assert r["variant"] in (1, 2, 3), shape
+        assert 0 <= r["tile"] < sg.tile_count(r["variant"]), f"{shape}: tile {r['tile']} not compiled"
+        # the tuned row is what automatic dispatch picks for aligned operands
+        M, N, K = shape
+        cfg = sg.select(M, N, K, 0x10000, K, 0x20000, N, 0x30000, N)
+        assert (cfg.variant, cfg.tile) == (r["variant"], r["tile"]), shape
