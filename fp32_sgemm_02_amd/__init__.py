@@ -16,9 +16,9 @@ import os
 
 __all__ = [
     "sgemm", "sgemm_ex", "gemm", "select", "tile_count", "tile_info", "status_string",
-    "version", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
-    "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO",
-    "TILE_WHOLE",
+    "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
+    "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
+    "TILE_WHOLE", "TILE_DIRECT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +26,9 @@ LIB_PATH = os.path.join(_HERE, "libfp32sgemm.so")
 
 VARIANT_AUTO, VARIANT_MFMA, VARIANT_VALU, VARIANT_SKINNY = 0, 1, 2, 3
 FLAG_SCALAR_IO = 0x1
+FLAG_UNTUNED = 0x2
 TILE_WHOLE = 0x1
+TILE_DIRECT = 0x2
 
 
 class SgemmConfig(ctypes.Structure):
@@ -69,6 +71,9 @@ def _load():
     lib.sgemm_ex.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p, ctypes.POINTER(SgemmConfig)]
     lib.sgemm_select.restype = i
     lib.sgemm_select.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_plan.restype = i
+    lib.sgemm_plan.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig),
+                               ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.sgemm_tile_count.restype = i
     lib.sgemm_tile_count.argtypes = [i]
     lib.sgemm_tile_info.restype = i
@@ -101,6 +106,19 @@ def select(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None) -> Sge
     if st != 0:
         raise SgemmError(st)
     return out
+
+
+def plan(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None):
+    """(main-part configuration, edge rows, edge columns) of sgemm()'s
+    automatic plan for this shape (and these addresses)."""
+    out = SgemmConfig()
+    rows, cols = ctypes.c_int(0), ctypes.c_int(0)
+    st = _load().sgemm_plan(M, N, K, A, lda or max(K, 1), B, ldb or max(N, 1), C,
+                            ldc or max(N, 1), ctypes.byref(out), ctypes.byref(rows),
+                            ctypes.byref(cols))
+    if st != 0:
+        raise SgemmError(st)
+    return out, rows.value, cols.value
 
 
 def tile_count(variant: int) -> int:

@@ -57,11 +57,15 @@ const TileEntry *mfma_family(int *count) {
     return all.data();
 }
 
-// Whether tile t can run this problem (whole-tile tiles need 16-byte I/O and
-// whole tiles).
-bool tile_applies(const TileEntry &t, const Problem &p, bool vec) {
-    if (!(t.desc.flags & SGEMM_TILE_WHOLE)) return true;
-    return vec && direct_applies(p, t.desc.bm, t.desc.bn, t.desc.bk);
+// Whether tile t can run this problem: whole-tile tiles need whole tiles and
+// 16-byte I/O for every operand (io_ok), direct-load tiles need their 31-bit
+// panel offsets to fit.
+bool tile_applies(const TileEntry &t, const Problem &p, bool io_ok) {
+    if (t.desc.flags & SGEMM_TILE_WHOLE)
+        return io_ok && direct_applies(p, t.desc.bm, t.desc.bn, t.desc.bk, false);
+    if (t.desc.flags & SGEMM_TILE_DIRECT)
+        return direct_applies(p, t.desc.bm, t.desc.bn, t.desc.bk, true);
+    return true;
 }
 
 const TileEntry *family(int variant, int *count) {
@@ -91,8 +95,9 @@ int validate(int M, int N, int K, float alpha, const float *A, int lda, const fl
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
-// The general MFMA tile for a shape (never a whole-tile one): the largest tile
-// that still yields about one workgroup per CU.
+// The general MFMA tile for a shape: the largest tile that still yields
+// about one workgroup per CU.  The fallback when a chosen direct-load tile
+// cannot run (it always can).
 int general_mfma_tile(int M, int N) {
     int count = 0;
     const TileEntry *tiles = mfma_tiles(&count);
@@ -102,53 +107,111 @@ int general_mfma_tile(int M, int N) {
     return 7;
 }
 
-// The MFMA tile for a shape that is not in the tuned table: the first
-// whole-tile (direct-load) configuration that applies and still yields about
-// one workgroup per CU, else the general rule.
-int default_mfma_tile(const Problem &p, bool vec) {
+constexpr int kCUs = 256;
+
+// Estimated time of tile t on an M x N output: rounds of workgroups over the
+// 256 CUs, each round costing one tile's work at the tile's measured
+// efficiency.  Rounding up to whole rounds is what makes a 4097-row product
+// with 256-row tiles cost as much as a 4352-row one.
+double tile_cost(const TileEntry &t, int M, int N) {
+    const long long rounds = (tiles_for(t, M, N) + kCUs - 1) / kCUs;
+    return (double)rounds * t.desc.bm * t.desc.bn / (t.eff_pct > 0 ? t.eff_pct : 50);
+}
+
+// Edge strips.  When a tile leaves at most 16 rows (or columns) past its last
+// whole tile row (column) and those cost a whole extra round of workgroups,
+// the strip can go to the skinny family instead (few rows: the MFMA strip
+// kernel; few columns: the row-streaming kernel).  Returns the rows / columns
+// split off (0: none).
+struct Strips {
+    int rows, cols;
+};
+
+Strips edge_strips(const Problem &p, const TileEntry &t) {
+    Strips s{0, 0};
+    const int bm = t.desc.bm, bn = t.desc.bn;
+    const int mr = p.M % bm, nr = p.N % bn;
+    const long long tn = (p.N + bn - 1) / bn, tm = (p.M + bm - 1) / bm;
+    auto rounds = [](long long tiles) { return (tiles + kCUs - 1) / kCUs; };
+    if (mr > 0 && mr <= 16 && p.M > bm && rounds(tm * tn) > rounds((tm - 1) * tn)) s.rows = mr;
+    const long long tm2 = (p.M - s.rows + bm - 1) / bm;
+    if (nr > 0 && nr <= 16 && p.N > bn && rounds(tm2 * tn) > rounds(tm2 * (tn - 1))) s.cols = nr;
+    return s;
+}
+
+Problem main_part(const Problem &p, Strips s) {
+    Problem m = p;
+    m.M -= s.rows;
+    m.N -= s.cols;
+    return m;
+}
+
+// The MFMA tile for a shape that is not in the tuned table: the applicable
+// tile of least estimated time (ties: the earlier, i.e. general, tile),
+// counting for each tile the option of handing its edge strips to the skinny
+// family (`strips`, when not null, receives the chosen tile's strips; a strip
+// is charged 5 % of the main part, far below the round it saves).
+int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
     int count = 0;
     const TileEntry *tiles = mfma_family(&count);
-    for (int i = 0; i < count; ++i)
-        if ((tiles[i].desc.flags & SGEMM_TILE_WHOLE) && tile_applies(tiles[i], p, vec) &&
-            tiles_for(tiles[i], p.M, p.N) >= 200)
-            return i;
-    return general_mfma_tile(p.M, p.N);
+    int best = general_mfma_tile(p.M, p.N);
+    double best_cost = tile_cost(tiles[best], p.M, p.N);
+    Strips best_strips{0, 0};
+    for (int i = 0; i < count; ++i) {
+        const Strips sp = strips ? edge_strips(p, tiles[i]) : Strips{0, 0};
+        const Problem m = main_part(p, sp);
+        if (!tile_applies(tiles[i], m, io_ok)) continue;
+        double c = tile_cost(tiles[i], m.M, m.N);
+        if (sp.rows || sp.cols) c *= 1.05;
+        if (c < best_cost) {
+            best = i;
+            best_cost = c;
+            best_strips = sp;
+        }
+    }
+    if (strips) *strips = best_strips;
+    return best;
 }
 
-// Automatic choice: the measured best configuration for this exact shape
-// (tuned_table.inc), else the skinny family for memory-bound shapes, else the
-// default MFMA rule.  A tuned whole-tile choice is checked against the actual
-// operands in resolve().
-Tuned auto_select(const Problem &p, bool vec) {
-    Tuned t;
-    if (lookup_tuned(p.M, p.N, p.K, t)) return t;
-    if (skinny_pick(p.M, p.N, p.K) >= 0) return Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
-    return Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, vec), 0};
-}
+// Automatic choice (in resolve): the measured best configuration for this
+// exact shape (tuned_table.inc), else the skinny family for memory-bound
+// shapes, else the MFMA tile of least estimated time, possibly with edge
+// strips split off.  A choice that cannot run on the actual operands falls
+// back to the general rule.
 
 // The configuration a call runs with: explicit (sgemm_ex) or automatic, with
-// a whole-tile choice replaced by the general rule where the operands do not
-// allow it.  Returns 0 or kBadConfig.
+// an automatic choice that cannot run on these operands replaced by the
+// general rule.  `vec` selects the tile's 16-byte-capable launcher (general
+// tiles: every operand allows 16-byte I/O; direct-load tiles decide per
+// operand themselves) unless 4-byte I/O is asked for.  Returns 0 or kBadConfig.
 struct Choice {
     int variant, tile, group_m;
     bool vec;
 };
 
-int resolve(const Problem &p, const sgemm_config *cfg, Choice &out) {
+int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *strips = nullptr) {
     const int flags = cfg ? cfg->flags : 0;
-    const bool vec = !(flags & SGEMM_FLAG_SCALAR_IO) &&
-                     vector_io_ok(p.A, (int)p.lda, p.B, (int)p.ldb, p.C, (int)p.ldc);
+    const bool want_vec = !(flags & SGEMM_FLAG_SCALAR_IO);
+    const bool io_ok = want_vec && vector_io_ok(p.A, (int)p.lda, p.B, (int)p.ldb, p.C, (int)p.ldc);
     int variant = cfg ? cfg->variant : SGEMM_VARIANT_AUTO;
     int tile = cfg ? cfg->tile : -1;
     int group_m = cfg ? cfg->group_m : 0;
     if (variant < 0 || variant >= SGEMM_VARIANT_COUNT) return kBadConfig;
     const bool explicit_tile = (variant != SGEMM_VARIANT_AUTO) && tile >= 0;
+    if (strips) *strips = Strips{0, 0};
     if (variant == SGEMM_VARIANT_AUTO) {
-        const Tuned a = auto_select(p, vec);
+        Tuned a;
+        if ((flags & SGEMM_FLAG_UNTUNED) || !lookup_tuned(p.M, p.N, p.K, a)) {
+            if (skinny_pick(p.M, p.N, p.K) >= 0)
+                a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
+            else
+                a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok, strips), 0};
+        }
         variant = a.variant;
         tile = a.tile;
         if (group_m <= 0) group_m = a.group_m;
     }
+    const Problem pm = strips ? main_part(p, *strips) : p;
     int count = 0;
     const TileEntry *tiles = family(variant, &count);
     if (!tiles) return kBadConfig;
@@ -156,19 +219,33 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out) {
         if (tile < 0) tile = skinny_pick(p.M, p.N, p.K);
         if (!skinny_fits(tile, p.M, p.N)) return kBadConfig;   // shape is not skinny
     } else if (tile < 0) {
-        tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, vec) : 0;
+        tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, io_ok) : 0;
     }
     if (tile >= count) {
         if (explicit_tile || variant != SGEMM_VARIANT_MFMA) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // a tuned row naming a tile that is not compiled
     }
-    if (!tile_applies(tiles[tile], p, vec)) {
+    if (!tile_applies(tiles[tile], pm, io_ok)) {
         if (explicit_tile) return kBadConfig;
-        tile = general_mfma_tile(p.M, p.N);   // automatic whole-tile choice that cannot run here
+        tile = general_mfma_tile(p.M, p.N);   // automatic choice that cannot run here
+        if (strips) *strips = Strips{0, 0};
     }
+    const bool vec = (tiles[tile].desc.flags & SGEMM_TILE_DIRECT) ? want_vec : io_ok;
     if (!(vec ? tiles[tile].vec : tiles[tile].scalar)) return kBadConfig;
     out = Choice{variant, tile, group_m, vec};
     return 0;
+}
+
+
+int launch(const Problem &p, const Choice &ch, hipStream_t stream) {
+    int count = 0;
+    const TileEntry &t = family(ch.variant, &count)[ch.tile];
+    static const bool log = std::getenv("FP32_SGEMM_LOG") != nullptr;
+    if (log)
+        std::fprintf(stderr, "sgemm M=%d N=%d K=%d variant=%d tile=%d (%dx%dx%d) group_m=%d %s\n",
+                     p.M, p.N, p.K, ch.variant, ch.tile, t.desc.bm, t.desc.bn, t.desc.bk,
+                     ch.group_m, ch.vec ? "vec16" : "scalar");
+    return to_status((ch.vec ? t.vec : t.scalar)(p, ch.group_m, stream));
 }
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -184,16 +261,25 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 
     const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
     Choice ch;
-    const int st = resolve(p, cfg, ch);
+    Strips sp;
+    int st = resolve(p, cfg, ch, &sp);
     if (st != 0) return st;
-    int count = 0;
-    const TileEntry &t = family(ch.variant, &count)[ch.tile];
-    static const bool log = std::getenv("FP32_SGEMM_LOG") != nullptr;
-    if (log)
-        std::fprintf(stderr, "sgemm M=%d N=%d K=%d variant=%d tile=%d (%dx%dx%d) group_m=%d %s\n",
-                     M, N, K, ch.variant, ch.tile, t.desc.bm, t.desc.bn, t.desc.bk, ch.group_m,
-                     ch.vec ? "vec16" : "scalar");
-    return to_status((ch.vec ? t.vec : t.scalar)(p, ch.group_m, stream));
+    if (!sp.rows && !sp.cols) return launch(p, ch, stream);
+    // main part, then the column strip beside it, then the row strip below
+    const int m1 = M - sp.rows, n1 = N - sp.cols;
+    st = launch(main_part(p, sp), ch, stream);
+    if (st == 0 && sp.cols) {
+        const Problem cols{m1, sp.cols, K, alpha, beta, A, lda, B + n1, ldb, C + n1, ldc};
+        st = resolve(cols, nullptr, ch);
+        if (st == 0) st = launch(cols, ch, stream);
+    }
+    if (st == 0 && sp.rows) {
+        const Problem rows{sp.rows, N, K, alpha, beta, A + (long long)m1 * lda, lda, B, ldb,
+                           C + (long long)m1 * ldc, ldc};
+        st = resolve(rows, nullptr, ch);
+        if (st == 0) st = launch(rows, ch, stream);
+    }
+    return st;
 }
 
 }  // namespace
@@ -211,21 +297,29 @@ int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const fl
     return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, cfg);
 }
 
-int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                 const float *C, int ldc, sgemm_config *out) {
+int sgemm_plan(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+               const float *C, int ldc, sgemm_config *out, int *edge_rows, int *edge_cols) {
     if (!out) return -14;
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
     const sg::Problem p{M, N, K, 1.f, 0.f, A, lda, B, ldb, const_cast<float *>(C), ldc};
     sg::Choice ch;
-    const int st = sg::resolve(p, nullptr, ch);
+    sg::Strips sp{0, 0};
+    const int st = sg::resolve(p, nullptr, ch, &sp);
     if (st != 0) return st;
     out->variant = ch.variant;
     out->tile = ch.tile;
     out->group_m = ch.group_m;
     out->flags = ch.vec ? 0 : SGEMM_FLAG_SCALAR_IO;
+    if (edge_rows) *edge_rows = sp.rows;
+    if (edge_cols) *edge_cols = sp.cols;
     return 0;
+}
+
+int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                 const float *C, int ldc, sgemm_config *out) {
+    return sgemm_plan(M, N, K, A, lda, B, ldb, C, ldc, out, nullptr, nullptr);
 }
 
 int sgemm_tile_count(int variant) {

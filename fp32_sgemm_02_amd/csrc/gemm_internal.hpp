@@ -34,13 +34,14 @@ struct TileEntry {
     sgemm_tile_desc desc;
     LaunchFn vec;
     LaunchFn scalar;
+    int eff_pct = 0;   // measured fraction of the fp32 peak at 4096^3 (dispatch cost model)
 };
 
 // Kernel families (each defined in its own .hip file): the compiled tile
 // configurations, as a table owned by the family (host functions only).
 const TileEntry *mfma_tiles(int *count);
 const TileEntry *mfma_direct_tiles(int *count);   // SGEMM_TILE_WHOLE tiles
-bool direct_applies(const Problem &p, int bm, int bn, int bk);
+bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 const TileEntry *valu_tiles(int *count);
 const TileEntry *skinny_tiles(int *count);
 

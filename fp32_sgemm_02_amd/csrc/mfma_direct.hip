@@ -45,6 +45,7 @@
 //                a[rb - H] and a share of its B fragments, and issue a share
 //                of the loads of stage t+NBUF into buffer t % NBUF
 // A load issued in stage t is waited for in the middle of stage t+NBUF-1.
+#include <cstdint>
 #include <type_traits>
 
 #include "gemm_internal.hpp"
@@ -55,11 +56,13 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 }  // namespace
 
-bool direct_applies(const Problem &p, int bm, int bn, int bk);
+bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 
 namespace {
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF>
+// AV, BV: floats per direct load of A and B (4: buffer_load_dwordx4, needs
+// 16-byte aligned rows; 1: buffer_load_dword, any 4-byte aligned layout).
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4>
 struct DirectShape {
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
@@ -73,14 +76,16 @@ struct DirectShape {
     static constexpr int B_STAGE = BK * BN;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int LDS_BYTES = NBUF * STAGE * 4;
-    static constexpr int LA = A_STAGE / 4 / 64 / NW;    // direct loads per wave per stage (A)
-    static constexpr int LB = B_STAGE / 4 / 64 / NW;    // ... (B)
+    static constexpr int LA = A_STAGE / AV / 64 / NW;   // direct loads per wave per stage (A)
+    static constexpr int LB = B_STAGE / BV / 64 / NW;   // ... (B)
+    static constexpr int AVEC = AV, BVEC = BV;
     static constexpr int L = LA + LB;
     static constexpr int KC = BK / 16;                  // 16-wide k-chunks per stage
     static_assert(BK == 16 || BK == 32, "one or two 16-wide k-chunks per stage");
     static_assert(WM % 16 == 0 && WN % 64 == 0, "wave tile: 16-row x 64-column units");
-    static_assert(LA * 64 * NW * 4 == A_STAGE && LB * 64 * NW * 4 == B_STAGE,
-                  "stage loads divide evenly into 1 KB blocks per wave");
+    static_assert((AV == 4 || AV == 1) && (BV == 4 || BV == 1), "dword or dwordx4 loads");
+    static_assert(LA * 64 * NW * AV == A_STAGE && LB * 64 * NW * BV == B_STAGE,
+                  "stage loads divide evenly over the waves");
     static_assert(NBUF >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring of 2+ stages");
     static_assert(L * (NBUF - 1) <= 63, "outstanding loads fit the vmcnt counter");
 };
@@ -93,39 +98,52 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Direct loads of one stage.  The A tile is BM rows of CPR_A 16-byte chunks;
-// A-tile block j of this wave covers chunks 64 * (wave * LA + j) .. +63 in
-// row-major order, and the lane that fills slot `slot` of row r loads
-// logical chunk slot ^ swz(r), swz(r) = (r >> 1) & (CPR_A - 1).  B-tile
-// block j covers the next 64 chunks of the row-major BK x BN slice, each lane
-// loading its own chunk.
+// Direct loads of one stage.  The A tile is BM rows of CPR_A 16-byte chunks
+// stored row-major; the chunk in slot `slot` of row r holds logical chunk
+// slot ^ swz(r), swz(r) = (r >> 1) & (CPR_A - 1).  Load j of a wave fills the
+// next 64 * AV floats of the tile image (lane l writes floats AV*l .. +AV-1 of
+// them), so each lane loads whatever global element(s) belong there.  The B
+// slice (BK x BN, row-major, unswizzled) is filled the same way.
+//
+// With edges (GUARD), a lane whose element lies outside the matrix gets an
+// offset past the buffer's range: the hardware then writes zeros into LDS
+// without touching memory.  Rows past M and columns past N are fixed per
+// lane; the k bound is applied on the last stage only.
+constexpr int kOutOfRange = (int)0x80000000u;
+
 template <class S>
 struct DirectLanes {
     int a_off[S::LA];   // byte offsets within the A panel (row-major, lda)
     int b_off[S::LB];   // byte offsets within the B slice (row-major, ldb)
+    int a_k[S::LA];     // k within the stage of each A load (its first element)
+    int b_k[S::LB];     // k within the stage of each B load
 };
 
-template <class S>
-__device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int wave, int lane) {
+template <class S, bool GUARD>
+__device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int m0, int n0, int wave,
+                                                       int lane) {
+    constexpr int BK = S::KC * 16;
     DirectLanes<S> d;
 #pragma unroll
     for (int j = 0; j < S::LA; ++j) {
-        const int c = (wave * S::LA + j) * 64 + lane;       // chunk index in the A tile
-        const int r = c / S::CPR_A, slot = c % S::CPR_A;
-        const int chunk = slot ^ ((r >> 1) & (S::CPR_A - 1));
-        d.a_off[j] = (r * (int)p.lda + 4 * chunk) * 4;
+        const int w = (wave * S::LA + j) * 64 * S::AVEC + S::AVEC * lane;   // float in the tile
+        const int r = w / BK, kk = w % BK;
+        const int k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
+        d.a_k[j] = k;
+        d.a_off[j] = (GUARD && m0 + r >= p.M) ? kOutOfRange : (r * (int)p.lda + k) * 4;
     }
 #pragma unroll
     for (int j = 0; j < S::LB; ++j) {
-        const int c = (wave * S::LB + j) * 64 + lane;
-        const int r = c / S::CPR_B, q = c % S::CPR_B;
-        d.b_off[j] = (r * (int)p.ldb + 4 * q) * 4;
+        const int w = (wave * S::LB + j) * 64 * S::BVEC + S::BVEC * lane;
+        const int r = w / (S::CPR_B * 4), n = w % (S::CPR_B * 4);
+        d.b_k[j] = r;
+        d.b_off[j] = (GUARD && n0 + n >= p.N) ? kOutOfRange : (r * (int)p.ldb + n) * 4;
     }
     return d;
 }
 
-// Loads [lo, hi) of stage t (index < LA: A blocks, else B blocks).
-template <class S>
+// Loads [lo, hi) of stage t (index < LA: A loads, else B loads).
+template <class S, bool GUARD>
 __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, int t, float *buf,
                                             int wave, const DirectLanes<S> &d, int lo, int hi) {
     constexpr int BK = S::KC * 16;
@@ -135,16 +153,20 @@ __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, in
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.B + (long long)t * BK * p.ldb + n0), (short)0, (int)(BK * p.ldb * 4),
         0x00020000);
+    const int krem = p.K - t * BK;   // k below this stays inside the matrix
+    const bool tail = GUARD && krem < BK;
 #pragma unroll
     for (int q = 0; q < S::L; ++q) {
         if (q < lo || q >= hi) continue;
         if (q < S::LA) {
-            lds_void *dst = (lds_void *)(buf + (wave * S::LA + q) * 256);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, d.a_off[q], 0, 0, 0);
+            lds_void *dst = (lds_void *)(buf + (wave * S::LA + q) * 64 * S::AVEC);
+            const int off = (tail && d.a_k[q] >= krem) ? kOutOfRange : d.a_off[q];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 4 * S::AVEC, off, 0, 0, 0);
         } else {
             const int j = q - S::LA;
-            lds_void *dst = (lds_void *)(buf + S::A_STAGE + (wave * S::LB + j) * 256);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, d.b_off[j], 0, 0, 0);
+            lds_void *dst = (lds_void *)(buf + S::A_STAGE + (wave * S::LB + j) * 64 * S::BVEC);
+            const int off = (tail && d.b_k[j] >= krem) ? kOutOfRange : d.b_off[j];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 4 * S::BVEC, off, 0, 0, 0);
         }
     }
 }
@@ -185,10 +207,13 @@ __device__ __forceinline__ void roll_block(const floatx4 &a, const floatx4 (&b)[
                     __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s][cg][c], acc[cg * 4 + c], 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF>
+// GUARD: the problem has edges (M, N or K not tile multiples, or C not fit
+// for 16-byte stores): zero-filled loads outside the matrix and guarded
+// stores.  cvec: C rows allow 16-byte stores (used with GUARD only).
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV, int BV, bool GUARD>
 __global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF>::NT), 1)
-mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
+mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV>;
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
@@ -198,8 +223,8 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     int tm, tn;
     tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = p.K / BK;
-    const DirectLanes<S> d = direct_lanes<S>(p, wave, lane);
+    const int nk = (p.K + BK - 1) / BK;
+    const DirectLanes<S> d = direct_lanes<S, GUARD>(p, m0, n0, wave, lane);
 
     floatx4 acc[RB][S::CG * 4];
 #pragma unroll
@@ -210,7 +235,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     // prologue: stages 0 .. NBUF-1 in flight; stage 0 complete and published
 #pragma unroll
     for (int t = 0; t < NBUF; ++t)
-        if (t < nk) issue_stage<S>(p, m0, n0, t, smem + t * S::STAGE, wave, d, 0, S::L);
+        if (t < nk) issue_stage<S, GUARD>(p, m0, n0, t, smem + t * S::STAGE, wave, d, 0, S::L);
     if (nk >= NBUF)
         wait_vmcnt<(NBUF - 1) * S::L>();
     else
@@ -262,7 +287,8 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
                     read_b<S>(nbuf, nkc, s, lane, wc, bn);
             }
             if (last && tf < nk)
-                issue_stage<S>(p, m0, n0, tf, fbuf, wave, d, (S::L * j) / H, (S::L * (j + 1)) / H);
+                issue_stage<S, GUARD>(p, m0, n0, tf, fbuf, wave, d, (S::L * j) / H,
+                                      (S::L * (j + 1)) / H);
             roll_block<S>(a[H + j], bc, acc[H + j]);
             pipeline_fence();
         }
@@ -283,7 +309,8 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
         if (t < nk) chunk(t, 0, b0, b1);
     }
 
-    // epilogue: alpha/beta (beta == 0 never reads C), 16-byte stores
+    // epilogue: alpha/beta (beta == 0 never reads C); 16-byte stores, and
+    // with edges only rows < M and columns < N are touched
     const int i = lane & 15, g = lane >> 4;
     const bool read_c = (p.beta != 0.f);
     const int row0 = m0 + wr * WM, col0 = n0 + wc * WN;
@@ -291,60 +318,105 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float *crow = p.C + (long long)(row0 + rb * 16 + 4 * g + r) * p.ldc;
+            const int gm = row0 + rb * 16 + 4 * g + r;
+            if (GUARD && gm >= p.M) continue;
+            float *crow = p.C + (long long)gm * p.ldc;
 #pragma unroll
             for (int cg = 0; cg < S::CG; ++cg) {
-                floatx4 *dst = reinterpret_cast<floatx4 *>(crow + col0 + cg * 64 + 4 * i);
+                const int gn = col0 + cg * 64 + 4 * i;
                 floatx4 v;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) v[c] = p.alpha * acc[rb][cg * 4 + c][r];
-                if (read_c) {
-                    const floatx4 old = *dst;
+                if (!GUARD || (cvec && gn + 3 < p.N)) {
+                    floatx4 *dst = reinterpret_cast<floatx4 *>(crow + gn);
+                    if (read_c) {
+                        const floatx4 old = *dst;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) v[c] = fmaf(p.beta, old[c], v[c]);
+                        for (int c = 0; c < 4; ++c) v[c] = fmaf(p.beta, old[c], v[c]);
+                    }
+                    *dst = v;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (gn + c >= p.N) continue;
+                        float out = v[c];
+                        if (read_c) out = fmaf(p.beta, crow[gn + c], out);
+                        crow[gn + c] = out;
+                    }
                 }
-                *dst = v;
             }
         }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF>
-hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
-    if (!direct_applies(p, BM, BN, BK)) return hipErrorInvalidValue;
-    const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV, int BV, bool GUARD>
+hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stream) {
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV>;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
-    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF>), dim3((unsigned)tiles),
-                       dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, AV, BV, GUARD>),
+                       dim3((unsigned)tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m,
+                       (int)cvec);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF>
-constexpr TileEntry direct_entry() {
+// Picks the kernel instance for the operands: the whole-tile instance when
+// the problem is made of whole tiles with 16-byte rows everywhere, else (for
+// tiles compiled with EDGES) a guarded instance with dwordx4 loads for each
+// operand whose rows allow them (16-byte aligned rows, and K or N a multiple
+// of 4 so that a 16-byte chunk is entirely inside or outside the matrix).
+// VEC = false (4-byte I/O asked for) uses dword loads and scalar stores.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES, bool VEC>
+hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
+    if (!direct_applies(p, BM, BN, BK, EDGES)) return hipErrorInvalidValue;
+    const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
+    const bool av = VEC && aligned16(p.A) && p.lda % 4 == 0 && p.K % 4 == 0;
+    const bool bv = VEC && aligned16(p.B) && p.ldb % 4 == 0 && p.N % 4 == 0;
+    const bool cv = VEC && aligned16(p.C) && p.ldc % 4 == 0;
+    if (whole && av && bv && cv)
+        return launch_one<BM, BN, BK, WM, WN, NBUF, 4, 4, false>(p, group_m, true, stream);
+    if constexpr (EDGES) {
+        if (av && bv) return launch_one<BM, BN, BK, WM, WN, NBUF, 4, 4, true>(p, group_m, cv, stream);
+        if (av) return launch_one<BM, BN, BK, WM, WN, NBUF, 4, 1, true>(p, group_m, cv, stream);
+        if (bv) return launch_one<BM, BN, BK, WM, WN, NBUF, 1, 4, true>(p, group_m, cv, stream);
+        return launch_one<BM, BN, BK, WM, WN, NBUF, 1, 1, true>(p, group_m, cv, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES>
+constexpr TileEntry direct_entry(int eff_pct) {
     using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
-    return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF, SGEMM_TILE_WHOLE},
-                     &launch_direct<BM, BN, BK, WM, WN, NBUF>, nullptr};
+    return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF,
+                      SGEMM_TILE_DIRECT | (EDGES ? 0 : SGEMM_TILE_WHOLE)},
+                     &launch_direct<BM, BN, BK, WM, WN, NBUF, EDGES, true>,
+                     EDGES ? &launch_direct<BM, BN, BK, WM, WN, NBUF, EDGES, false> : nullptr,
+                     eff_pct};
 }
 
 }  // namespace
 
-bool direct_applies(const Problem &p, int bm, int bn, int bk) {
-    return p.M % bm == 0 && p.N % bn == 0 && p.K % bk == 0 && p.K >= bk &&
-           (long long)bm * p.lda * 4 < (1LL << 31) && (long long)bk * p.ldb * 4 < (1LL << 31);
+bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges) {
+    const bool offsets_fit =
+        (long long)bm * p.lda * 4 < (1LL << 31) && (long long)bk * p.ldb * 4 < (1LL << 31);
+    if (edges) return offsets_fit;
+    return offsets_fit && p.M % bm == 0 && p.N % bn == 0 && p.K % bk == 0 && p.K >= bk;
 }
 
 const TileEntry *mfma_direct_tiles(int *count) {
     static const TileEntry tiles[] = {
-        direct_entry<256, 256, 16, 64, 128, 2>(),
-        direct_entry<256, 256, 16, 128, 64, 2>(),
-        direct_entry<256, 128, 16, 64, 64, 2>(),
-        direct_entry<128, 128, 16, 32, 64, 2>(),
-        direct_entry<128, 128, 16, 64, 64, 2>(),
-        direct_entry<256, 256, 32, 64, 128, 2>(),
-        direct_entry<256, 256, 32, 128, 64, 2>(),
-        direct_entry<128, 128, 32, 32, 64, 2>(),
+        // argument: % of the fp32 peak measured at 4096^3
+        direct_entry<256, 256, 16, 64, 128, 2, false>(93),
+        direct_entry<256, 256, 16, 128, 64, 2, true>(92),
+        direct_entry<256, 128, 16, 64, 64, 2, true>(91),
+        direct_entry<128, 128, 16, 32, 64, 2, true>(92),
+        direct_entry<128, 128, 16, 64, 64, 2, true>(90),
+        direct_entry<256, 256, 32, 64, 128, 2, false>(93),
+        direct_entry<256, 256, 32, 128, 64, 2, false>(93),
+        direct_entry<128, 128, 32, 32, 64, 2, false>(91),
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;

@@ -385,11 +385,11 @@ hipError_t launch_mfma(const Problem &p, int group_m, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int OCC>
-constexpr TileEntry mfma_entry() {
+constexpr TileEntry mfma_entry(int eff_pct) {
     using S = MfmaShape<BM, BN, BK, WM, WN, NBUF, OCC>;
     return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF, 0},
                      &launch_mfma<BM, BN, BK, WM, WN, NBUF, OCC, true>,
-                     &launch_mfma<BM, BN, BK, WM, WN, NBUF, OCC, false>};
+                     &launch_mfma<BM, BN, BK, WM, WN, NBUF, OCC, false>, eff_pct};
 }
 
 }  // namespace
@@ -397,14 +397,15 @@ constexpr TileEntry mfma_entry() {
 // Compiled tile configurations (index = sgemm_config.tile for the MFMA family).
 const TileEntry *mfma_tiles(int *count) {
     static const TileEntry tiles[] = {
-        mfma_entry<256, 256, 16, 128, 128, 3, 1>(),   // 0: 4 waves, 256 accumulators per lane
-        mfma_entry<256, 256, 16, 128, 128, 2, 1>(),   // 1
-        mfma_entry<256, 256, 32, 128, 128, 2, 1>(),   // 2
-        mfma_entry<256, 128, 16, 128, 64, 3, 1>(),    // 3: 4 waves, 128 accumulators per lane
-        mfma_entry<128, 128, 16, 64, 64, 3, 2>(),     // 4: 2 waves per SIMD
-        mfma_entry<128, 128, 32, 64, 64, 2, 2>(),     // 5
-        mfma_entry<128, 64, 32, 64, 64, 2, 2>(),      // 6
-        mfma_entry<64, 64, 32, 32, 64, 2, 2>(),       // 7: small problems
+        // argument: % of the fp32 peak measured at 4096^3
+        mfma_entry<256, 256, 16, 128, 128, 3, 1>(80),   // 0: 4 waves, 256 accumulators per lane
+        mfma_entry<256, 256, 16, 128, 128, 2, 1>(83),   // 1
+        mfma_entry<256, 256, 32, 128, 128, 2, 1>(84),   // 2
+        mfma_entry<256, 128, 16, 128, 64, 3, 1>(75),    // 3: 4 waves, 128 accumulators per lane
+        mfma_entry<128, 128, 16, 64, 64, 3, 2>(81),     // 4: 2 waves per SIMD
+        mfma_entry<128, 128, 32, 64, 64, 2, 2>(82),     // 5
+        mfma_entry<128, 64, 32, 64, 64, 2, 2>(75),      // 6
+        mfma_entry<64, 64, 32, 32, 64, 2, 2>(75),       // 7: small problems
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;

@@ -38,14 +38,17 @@ def parse_shape(text: str):
 
 
 def candidates(sg, M, N, K, sweep_groups: bool):
-    out = []
+    """(variant, tile, group_m, flags) to time.  The first is the automatic
+    plan without the tuned table (the cost model, edge strips included); when
+    it wins, the shape needs no table row."""
+    out = [(sg.VARIANT_AUTO, -1, 0, sg.FLAG_UNTUNED)]
     for tile in range(sg.tile_count(sg.VARIANT_MFMA)):
         groups = GROUPS if sweep_groups else (0,)
         for g in groups:
-            out.append((sg.VARIANT_MFMA, tile, g))
+            out.append((sg.VARIANT_MFMA, tile, g, 0))
     if M <= 16 or N <= 16:
         for tile in range(sg.tile_count(sg.VARIANT_SKINNY)):
-            out.append((sg.VARIANT_SKINNY, tile, 0))
+            out.append((sg.VARIANT_SKINNY, tile, 0, 0))
     return out
 
 
@@ -103,9 +106,9 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
     sg.gemm(A, B, ref)
     torch.cuda.synchronize()
     results = []
-    for variant, tile, group in candidates(sg, M, N, K, sweep_groups):
+    for variant, tile, group, flags in candidates(sg, M, N, K, sweep_groups):
         try:
-            call = lambda: sg.gemm(A, B, C, variant=variant, tile=tile, group_m=group)
+            call = lambda: sg.gemm(A, B, C, variant=variant, tile=tile, group_m=group, flags=flags)
             C.fill_(float("nan"))
             call()
             torch.cuda.synchronize()
@@ -115,7 +118,7 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
             print(f"  rejected v{variant} t{tile} g{group}: output differs", flush=True)
             continue
         call_i = lambda i: sg.gemm(As[i % copies], Bs[i % copies], C, variant=variant, tile=tile,
-                                   group_m=group)
+                                   group_m=group, flags=flags)
         if graph:
             ms = statistics.median(time_graph(torch, call_i, max(reps, copies)))
         else:
@@ -130,9 +133,15 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
             torch.cuda.synchronize()
             ms = statistics.median(s.elapsed_time(e) for s, e in ev)
         gf = 2.0 * M * N * K / (ms / 1e3) / 1e9
-        results.append({"variant": variant, "tile": tile, "group_m": group, "ms": round(ms, 5),
-                        "gflops": round(gf, 1), "desc": sg.tile_info(variant, tile)})
-        print(f"  v{variant} t{tile} g{group}: {ms:.4f} ms  {gf:,.0f} GFLOP/s", flush=True)
+        if variant == sg.VARIANT_AUTO:
+            main, rows, cols = sg.plan(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)
+            desc = {"model": True, "variant": main.variant, "tile": main.tile,
+                    "edge_rows": rows, "edge_cols": cols}
+        else:
+            desc = sg.tile_info(variant, tile)
+        results.append({"variant": variant, "tile": tile, "group_m": group, "flags": flags,
+                        "ms": round(ms, 5), "gflops": round(gf, 1), "desc": desc})
+        print(f"  v{variant} t{tile} g{group} f{flags}: {ms:.4f} ms  {gf:,.0f} GFLOP/s", flush=True)
     results.sort(key=lambda r: r["ms"])
     return results
 
@@ -155,9 +164,12 @@ def read_table(path: str = TABLE) -> dict:
 
 
 def write_table(best: dict, path: str = TABLE, merge: bool = True):
-    """Rewrite the table with `best`; rows for other shapes are kept when `merge`."""
+    """Rewrite the table with `best`; rows for other shapes are kept when `merge`.
+    A shape whose best candidate is the untuned automatic plan (variant 0)
+    gets no row, and loses any row it had."""
     if merge:
         best = {**read_table(path), **best}
+    best = {k: v for k, v in best.items() if v["variant"] != 0}
     rows = []
     for (M, N, K), r in sorted(best.items()):
         rows.append(f"    {{{M}, {N}, {K}, {{{r['variant']}, {r['tile']}, {r['group_m']}}}}},"

@@ -70,6 +70,7 @@ enum sgemm_variant {
 
 /* sgemm_config.flags bits */
 #define SGEMM_FLAG_SCALAR_IO 0x1   /* force 4-byte loads/stores (no 16-byte vectors) */
+#define SGEMM_FLAG_UNTUNED 0x2     /* automatic choice: skip the tuned table, use the cost model */
 
 /*
  * Explicit configuration for sgemm_ex: which kernel family, which compiled
@@ -102,6 +103,10 @@ typedef struct sgemm_tile_desc {
  * elements (31-bit byte offsets within one tile's panel).  Asked for explicitly
  * elsewhere, sgemm_ex returns -13; automatic dispatch never picks it there. */
 #define SGEMM_TILE_WHOLE 0x1
+/* sgemm_tile_desc.flags: the tile's loads go straight from memory to LDS
+ * through 32-bit buffer offsets, so it needs bm * lda and bk * ldb below 2^29
+ * elements; sgemm_ex returns -13 otherwise. */
+#define SGEMM_TILE_DIRECT 0x2
 
 /*
  * sgemm: C = alpha * (A * B) + beta * C, kernel family and tile chosen from
@@ -129,11 +134,23 @@ int sgemm_ex(int M, int N, int K, float alpha,
 /*
  * sgemm_select: the configuration sgemm() would use for this shape and these
  * pointers/leading dimensions, written to *out (variant, tile, flags,
- * group_m).  Reads no memory behind A, B or C.  Returns 0; -1, -2 or -3 for a
- * negative M, N or K; -14 when out is NULL.
+ * group_m).  When sgemm() also hands edge strips to the skinny family (see
+ * sgemm_plan), *out describes the main part.  Reads no memory behind A, B or
+ * C.  Returns 0; -1, -2 or -3 for a negative M, N or K; -14 when out is NULL.
  */
 int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B,
                  int ldb, const float *C, int ldc, sgemm_config *out);
+
+/*
+ * sgemm_plan: sgemm_select plus the edge strips of the automatic plan.  When
+ * the chosen MFMA tile would leave at most 16 rows (columns) in an extra,
+ * mostly idle round of workgroups, sgemm() computes the last *edge_rows rows
+ * (last *edge_cols columns) of C with the skinny family in a second (third)
+ * launch on the same stream and the rest with the tile in *out.  edge_rows
+ * and edge_cols may be NULL.  Same return values as sgemm_select.
+ */
+int sgemm_plan(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+               const float *C, int ldc, sgemm_config *out, int *edge_rows, int *edge_cols);
 
 /* Number of compiled tile configurations of a family (0 for unknown). */
 int sgemm_tile_count(int variant);

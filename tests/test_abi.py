@@ -133,13 +133,43 @@ def test_automatic_selection_never_picks_an_inapplicable_whole_tile():
             d = sg.tile_info(cfg.variant, cfg.tile)
             if d["flags"] & sg.TILE_WHOLE:
                 assert a % 16 == 0 and M % d["bm"] == 0 and N % d["bn"] == 0
-        cfg = sg.select(M + 1, N, K, 0x10000, K, 0x20000, N, 0x30000, N)
-        assert not sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_WHOLE
-    # an untuned shape made of whole tiles gets a whole tile, an untuned ragged one does not
+        # one row more: a whole tile only for the main part, with the row split off
+        cfg, rows, cols = sg.plan(M + 1, N, K, 0x10000, K, 0x20000, N, 0x30000, N)
+        d = sg.tile_info(cfg.variant, cfg.tile)
+        if d["flags"] & sg.TILE_WHOLE:
+            assert rows == 1 and (M + 1 - rows) % d["bm"] == 0 and (N - cols) % d["bn"] == 0
+    # untuned large shapes, whole or ragged, get a direct-load tile; a ragged
+    # one never a whole-tile one
     cfg = sg.select(6144, 6144, 6144, 0x10000, 6144, 0x20000, 6144, 0x30000, 6144)
-    assert sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_WHOLE
-    cfg = sg.select(6143, 6144, 6144, 0x10000, 6144, 0x20000, 6144, 0x30000, 6144)
-    assert not sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_WHOLE
+    assert sg.tile_info(cfg.variant, cfg.tile)["flags"] & sg.TILE_DIRECT
+    cfg = sg.select(6143, 6144, 6143, 0x10000, 6143, 0x20000, 6144, 0x30000, 6144)
+    d = sg.tile_info(cfg.variant, cfg.tile)
+    assert d["flags"] & sg.TILE_DIRECT and not d["flags"] & sg.TILE_WHOLE
+
+
+def test_edge_strip_plan():
+    """The automatic plan hands at most 16 edge rows / columns to the skinny
+    family, only when they would cost an extra round of workgroups, and the
+    main part then divides into the chosen tile's rows / columns."""
+    a, b, c = 0x10000, 0x20000, 0x30000
+    cfg, rows, cols = sg.plan(4097, 1000, 3001, a, 3001, b, 1000, c, 1000)
+    assert (rows, cols) == (1, 0)
+    d = sg.tile_info(cfg.variant, cfg.tile)
+    assert cfg.variant == sg.VARIANT_MFMA and 4096 % d["bm"] == 0
+    assert d["flags"] & sg.TILE_DIRECT
+    for (M, N, K) in ((4096, 4096, 4096), (300, 257, 129), (1000, 1000, 1000), (4200, 4100, 512),
+                      (2049, 2048, 2048), (2048, 2051, 700), (8193, 8200, 100), (20, 5000, 64)):
+        cfg, rows, cols = sg.plan(M, N, K, a, K, b, N, c, N)
+        d = sg.tile_info(cfg.variant, cfg.tile)
+        assert 0 <= rows <= 16 and 0 <= cols <= 16
+        if rows:
+            assert (M - rows) % d["bm"] == 0 and M - rows >= d["bm"]
+        if cols:
+            assert (N - cols) % d["bn"] == 0 and N - cols >= d["bn"]
+        if (M, N, K) == (4096, 4096, 4096):
+            assert (rows, cols) == (0, 0)
+        if cfg.variant == sg.VARIANT_SKINNY:
+            assert (rows, cols) == (0, 0)
 
 
 def test_automatic_selection():

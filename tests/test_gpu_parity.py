@@ -149,6 +149,79 @@ def test_whole_tile_parity(slot, oracle_mod):
     check(A, B, C0, 0.5, -1.25, Ch[:, :N].copy(), oracle_mod, label=f"whole t{tile} padded")
 
 
+# ---------------------------------------------- direct-load tiles, edges --
+def direct_edge_tiles():
+    out = []
+    for t in tiles(sg.VARIANT_MFMA):
+        f = sg.tile_info(sg.VARIANT_MFMA, t)["flags"]
+        if f & sg.TILE_DIRECT and not f & sg.TILE_WHOLE:
+            out.append(t)
+    return out
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_direct_tile_edges(slot, oracle_mod):
+    """Direct-load tiles on ragged shapes: M, N, K not tile multiples, K under
+    one stage, odd K and N (4-byte loads of A and B), alpha/beta, beta = 0 over
+    a NaN C, integer inputs bit-exact, the 4-byte I/O flag, and padded rows
+    of odd length (unaligned rows for every operand)."""
+    et = direct_edge_tiles()
+    if slot >= len(et):
+        pytest.skip("no such direct-load tile with edges")
+    tile = et[slot]
+    d = sg.tile_info(sg.VARIANT_MFMA, tile)
+    bm, bn, bk = d["bm"], d["bn"], d["bk"]
+    kw = dict(variant=sg.VARIANT_MFMA, tile=tile)
+    shapes = [(bm + 1, bn + 3, 17), (2 * bm - 5, bn - 4, 3 * bk + 5), (37, 45, 5),
+              (bm, bn, bk), (3 * bm + 16, 2 * bn + 4, 64), (300, 520, 77), (1, 1, 1)]
+    for i, (M, N, K) in enumerate(shapes):
+        lab = f"direct t{tile} {(M, N, K)}"
+        A, B, C0 = uniform(M, N, K, 700 + i)
+        C = run_gpu(A, B, C0, 0.5, -1.25, **kw)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, label=lab)
+        C = run_gpu(A, B, None, 1.0, 0.0, **kw)
+        check(A, B, None, 1.0, 0.0, C, oracle_mod, label=lab + " b0")
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 800 + i, True)
+        C = run_gpu(Ai, Bi, Ci, 0.5, -1.25, **kw)
+        check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=lab + " int")
+        C = run_gpu(Ai, Bi, Ci, 0.5, -1.25, flags=sg.FLAG_SCALAR_IO, **kw)
+        check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=lab + " int scalar")
+    rng = np.random.default_rng(tile)
+    for (M, N, K), (pa, pb, pc) in (((bm + 7, bn + 9, 40), (3, 5, 1)),
+                                    ((2 * bm, bn, 2 * bk), (4, 4, 4))):
+        A = rng.uniform(-1, 1, (M, K)).astype(F32)
+        B = rng.uniform(-1, 1, (K, N)).astype(F32)
+        C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+        As = torch.full((M, K + pa), float("nan"), device=DEV)
+        Bs = torch.full((K, N + pb), float("nan"), device=DEV)
+        Cs = torch.full((M, N + pc), 777.0, device=DEV)
+        As[:, :K] = dev(A)
+        Bs[:, :N] = dev(B)
+        Cs[:, :N] = dev(C0)
+        sg.gemm(As[:, :K], Bs[:, :N], Cs[:, :N], 0.5, -1.25, **kw)
+        torch.cuda.synchronize()
+        Ch = Cs.cpu().numpy()
+        assert np.all(Ch[:, N:] == 777.0), "C padding written"
+        check(A, B, C0, 0.5, -1.25, Ch[:, :N].copy(), oracle_mod,
+              label=f"direct t{tile} padded {(pa, pb, pc)}")
+
+
+@pytest.mark.parametrize("shape", [(2049, 2048, 64), (2048, 2051, 70), (4112, 1000, 48),
+                                   (4097, 1000, 301)])
+def test_automatic_plan_with_edge_strips(shape, oracle_mod):
+    """Automatic dispatch that hands edge rows / columns to the skinny family:
+    every row of C against the oracle, integer inputs bit-exact."""
+    M, N, K = shape
+    A, B, C0 = workloads.draw(M, N, K, "int4", 950, True)
+    dA, dB, dC = dev(A), dev(B), dev(C0)
+    cfg, rows, cols = sg.plan(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+    assert rows or cols, "shape no longer exercises an edge strip"
+    sg.gemm(dA, dB, dC, 0.5, -1.25)
+    torch.cuda.synchronize()
+    check(A, B, C0, 0.5, -1.25, dC.cpu().numpy(), oracle_mod, exact=True,
+          label=f"plan {shape} strips {(rows, cols)}")
+
+
 SKINNY_CASES = {
     0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
     1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],

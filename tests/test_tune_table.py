@@ -18,6 +18,11 @@ def test_table_round_trip_and_merge(tmp_path):
     assert got[(1, 4096, 4096)] == first[(1, 4096, 4096)]
     text = open(path).read()
     assert "lookup_tuned" in text and "sentinel" in text
+    # the untuned automatic plan winning removes the shape's row
+    tune.write_table({(1, 4096, 4096): {"variant": 0, "tile": -1, "group_m": 0, "gflops": 1.0}},
+                     path)
+    assert (1, 4096, 4096) not in tune.read_table(path)
+    assert (4096, 4096, 4096) in tune.read_table(path)
 
 
 def test_shipped_table_parses_and_names_compiled_tiles():
