@@ -12,9 +12,11 @@ A step is one C = alpha*(A*B) + beta*C call on the resident, seeded synthetic
 inputs of the workload (workloads.py).  GFLOP/s counts 2*M*N*K per call, the
 convention of the pages' ladder table ("The GEMM Scrapbook"), and divides by
 wall-clock time over the timed steps; the kernel's own average duration comes
-from HIP events recorded on the stream the kernel is launched on.  The CPU
-oracle is timed on a bounded sample of the same workload as a reported
-baseline (rank 0, N = 1 only).
+from HIP events recorded on the stream the kernel is launched on, and is also
+set against the rate of a register-only MFMA loop measured in the same run.
+The CPU oracle is timed on a bounded sample of the same workload as a
+reported baseline (rank 0, N = 1 only); the rows it computes also check the
+GPU's output of one more call on the original C.
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ METRIC = "SGEMM GFLOP/s at 4096³ fp32 and % of MI355X fp32 peak (1 GPU)"
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and packed vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-TILE_WHOLE = 0x1   # sgemm_tile_desc.flags bit of the direct-load MFMA tiles
+TILE_DIRECT = 0x2  # sgemm_tile_desc.flags bit of the direct-load MFMA tiles
 KERNEL_SOURCES = {
     1: ["mfma_gemm.hip", "gemm_internal.hpp"],
     "direct": ["mfma_direct.hip", "gemm_internal.hpp"],
@@ -44,7 +46,7 @@ KERNEL_SOURCES = {
 
 def kernel_source_hash(variant: int, desc: dict | None = None) -> str:
     h = hashlib.sha256()
-    key = "direct" if variant == 1 and desc and desc.get("flags", 0) & TILE_WHOLE else variant
+    key = "direct" if variant == 1 and desc and desc.get("flags", 0) & TILE_DIRECT else variant
     for f in KERNEL_SOURCES.get(key, []):
         with open(os.path.join(ROOT, "fp32_sgemm_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -56,7 +58,7 @@ def kernel_name(variant: int, desc: dict) -> str:
     fam = {1: "mfma", 2: "valu", 3: "skinny"}.get(variant, f"v{variant}")
     if not desc:
         return fam
-    if variant == 1 and desc.get("flags", 0) & TILE_WHOLE:
+    if variant == 1 and desc.get("flags", 0) & TILE_DIRECT:
         fam = "mfma_direct"
     return (f"{fam}_{desc['bm']}x{desc['bn']}x{desc['bk']}_w{desc['wm']}x{desc['wn']}"
             f"_s{desc.get('stages', 0)}_t{desc['threads']}")
@@ -81,8 +83,9 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, A, B, C0, target_s: float) -> dict:
-    """Time the CPU oracle on a bounded band of rows of the same workload."""
+def cpu_baseline(w, A, B, C0, target_s: float):
+    """Time the CPU oracle on a bounded band of rows of the same workload.
+    Returns (the baseline record, the oracle's rows 0..R-1 of C)."""
     import numpy as np
     import oracle
 
@@ -92,16 +95,32 @@ def cpu_baseline(w, A, B, C0, target_s: float) -> dict:
         a = np.ascontiguousarray(A[:rows])
         c = None if C0 is None else np.ascontiguousarray(C0[:rows])
         t0 = time.perf_counter()
-        oracle.sgemm(a, B, c, w.alpha, w.beta if c is not None else 0.0, nthreads=threads)
+        ref = oracle.sgemm(a, B, c, w.alpha, w.beta if c is not None else 0.0, nthreads=threads)
         dt = time.perf_counter() - t0
         if dt >= 0.6 * target_s or rows >= w.M:
             break
         rows = min(w.M, max(rows + 1, int(rows * target_s / max(dt, 1e-3))))
     flops = 2.0 * rows * w.N * w.K
-    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"rows 0..{rows - 1} of {w.name} ({rows} x {w.N} x {w.K}, "
-                      f"{flops / 1e9:.2f} GFLOP), fp64-accumulating C oracle on {threads} threads"}
+    out = {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(dt, 3),
+           "sample": f"rows 0..{rows - 1} of {w.name} ({rows} x {w.N} x {w.K}, "
+                     f"{flops / 1e9:.2f} GFLOP), fp64-accumulating C oracle on {threads} threads"}
+    return out, ref
+
+
+def cpu_baseline_one_core(target: str = "square256") -> dict:
+    """The oracle on one core for a small workload, as a per-core reference."""
+    import oracle
+    import workloads
+
+    w = workloads.WORKLOADS[target]
+    A, B, C0 = workloads.inputs(w)
+    t0 = time.perf_counter()
+    oracle.sgemm(A, B, None if C0 is None else C0.copy(), w.alpha,
+                 w.beta if C0 is not None else 0.0, nthreads=1)
+    dt = time.perf_counter() - t0
+    return {"workload": w.name, "value": round(w.flops / dt / 1e9, 3), "unit": "GFLOP/s",
+            "cores": 1, "seconds": round(dt, 4)}
 
 
 def time_calls(torch, call, steps, warmup):
@@ -173,6 +192,7 @@ def traffic_for(variant_used: int, kernel: str, desc: dict | None = None):
 
 
 def headline(args):
+    import numpy as np
     import torch
     import fp32_sgemm_02_amd as sg
     import workloads
@@ -236,8 +256,23 @@ def headline(args):
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": kernel, "kernel_ms_mean": round(kern_s * 1e3, 4)},
     }
+    probe = measure_probe(torch, "mfma_f32")
+    if bound != "hbm":
+        out["roofline"]["probe_tflops"] = probe["tflops"]
+        out["roofline"]["frac_of_probe"] = round(achieved / probe["tflops"], 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B, C0, args.cpu_seconds)
+        base, ref = cpu_baseline(w, A, B, C0, args.cpu_seconds)
+        # the GPU's rows of one more call on the original C, against the oracle's
+        dCv = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty((w.M, w.N), device=dev)
+        sg.gemm(dA, dB, dCv, w.alpha, w.beta, **kw)
+        got = dCv[:ref.shape[0]].cpu().numpy()
+        tol = (2e-5 * w.K * abs(w.alpha) * float(np.abs(A).max()) * float(np.abs(B).max())
+               + (1e-6 * abs(w.beta) * np.abs(C0[:ref.shape[0]]) if C0 is not None else 0.0))
+        err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        base["checked_rows"] = int(ref.shape[0])
+        base["max_err_over_tol"] = float(np.max(err / tol)) if err.size else 0.0
+        base["one_core"] = cpu_baseline_one_core()
+        out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
 
 
@@ -302,35 +337,40 @@ def copy_calibration(args):
                       "gbs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
-def probes(args):
-    """Register-only MFMA and FMA loops: the rates the chip sustains on this box."""
+def measure_probe(torch, name: str, steps: int = 10, warmup: int = 3) -> dict:
+    """A register-only loop of fp32 MFMAs ("mfma_f32") or plain FMAs
+    ("valu_fma_f32") on every SIMD: the rate this machine sustains."""
     import ctypes
 
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp32_sgemm_02_amd", "libfp32probes.so"))
+    kind = name.split("_")[0]
+    getattr(lib, f"probe_{kind}_flops").restype = ctypes.c_double
+    getattr(lib, f"probe_{kind}_flops").argtypes = [ctypes.c_int, ctypes.c_int]
+    getattr(lib, f"probe_{kind}_f32").restype = ctypes.c_int
+    getattr(lib, f"probe_{kind}_f32").argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+    blocks = 256 * 8
+    iters = 2000 if kind == "mfma" else 20000
+    peak = PEAK_FP32_TFLOPS if kind == "mfma" else PEAK_FP32_TFLOPS / 2
+    out = torch.empty(blocks * 256, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    flops = getattr(lib, f"probe_{kind}_flops")(blocks, iters)
+    launch = getattr(lib, f"probe_{kind}_f32")
+    _, ms = time_calls(torch, lambda: launch(blocks, iters, out.data_ptr(), stream), steps, warmup)
+    tf = flops / (ms / 1e3) / 1e12
+    per_cu_clk = 256 if kind == "mfma" else 128
+    return {"probe": name, "tflops": round(tf, 2), "peak_tflops": peak,
+            "frac": round(tf / peak, 4), "kernel_ms_mean": round(ms, 4),
+            "implied_clock_ghz": round(tf * 1e12 / (256 * per_cu_clk) / 1e9, 3)}
+
+
+def probes(args):
+    """Register-only MFMA and FMA loops: the rates the chip sustains on this box."""
     import torch
 
     torch.cuda.set_device(0)
-    lib = ctypes.CDLL(os.path.join(ROOT, "fp32_sgemm_02_amd", "libfp32probes.so"))
-    for fn in ("probe_mfma_flops", "probe_valu_flops"):
-        getattr(lib, fn).restype = ctypes.c_double
-        getattr(lib, fn).argtypes = [ctypes.c_int, ctypes.c_int]
-    for fn in ("probe_mfma_f32", "probe_valu_f32"):
-        getattr(lib, fn).restype = ctypes.c_int
-        getattr(lib, fn).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    blocks = 256 * 8
-    out = torch.empty(blocks * 256, device="cuda:0")
-    stream = torch.cuda.current_stream().cuda_stream
-    for name, iters, peak in (("mfma_f32", 2000, PEAK_FP32_TFLOPS),
-                              ("valu_fma_f32", 20000, PEAK_FP32_TFLOPS / 2)):
-        launch = getattr(lib, f"probe_{name.split('_')[0]}_f32")
-        flops = getattr(lib, f"probe_{name.split('_')[0]}_flops")(blocks, iters)
-        call = lambda: launch(blocks, iters, out.data_ptr(), stream)
-        _, ms = time_calls(torch, call, 10, 3)
-        med = ms / 1e3
-        tf = flops / med / 1e12
-        print(json.dumps({"probe": name, "tflops": round(tf, 2), "peak_tflops": peak,
-                          "frac": round(tf / peak, 4), "kernel_ms_mean": round(med * 1e3, 4),
-                          "implied_clock_ghz": round(tf * 1e12 / (256 * (256 if name.startswith("mfma") else 128)) / 1e9, 3)}),
-              flush=True)
+    for name in ("mfma_f32", "valu_fma_f32"):
+        print(json.dumps(measure_probe(torch, name)), flush=True)
 
 
 def main():

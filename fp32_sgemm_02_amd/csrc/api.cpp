@@ -230,7 +230,10 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
         tile = general_mfma_tile(p.M, p.N);   // automatic choice that cannot run here
         if (strips) *strips = Strips{0, 0};
     }
-    const bool vec = (tiles[tile].desc.flags & SGEMM_TILE_DIRECT) ? want_vec : io_ok;
+    // direct-load and skinny tiles pick 16-byte paths per operand themselves
+    const bool per_operand =
+        (tiles[tile].desc.flags & SGEMM_TILE_DIRECT) || variant == SGEMM_VARIANT_SKINNY;
+    const bool vec = per_operand ? want_vec : io_ok;
     if (!(vec ? tiles[tile].vec : tiles[tile].scalar)) return kBadConfig;
     out = Choice{variant, tile, group_m, vec};
     return 0;

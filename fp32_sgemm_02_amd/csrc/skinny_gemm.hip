@@ -18,6 +18,8 @@
 // loads (neighbouring lanes on neighbouring addresses: "a CUDA matmul"
 // section 04), multiplying by the N <= NB columns of B (small, cache
 // resident), then reduces its 64 lanes.
+#include <cstdint>
+
 #include "gemm_internal.hpp"
 
 namespace sg {
@@ -63,17 +65,18 @@ struct RowsRound {
     floatx4 a[U];
 };
 
-template <int VW, int W, int U, bool VEC>
+// VA: rows of A allow 16-byte loads; VB: rows of B allow VW-float loads.
+template <int VW, int W, int U, bool VA, bool VB>
 __device__ __forceinline__ void rows_load(const Problem &p, int j, int g, int gn, bool row_ok,
                                           const float *arow, RowsRound<VW, U> &r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int k0 = (j + u * W) * 16 + 4 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) load_brow<VW, VEC>(p, k0 + s, gn, r.b[u][s]);
+        for (int s = 0; s < 4; ++s) load_brow<VW, VB>(p, k0 + s, gn, r.b[u][s]);
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
         if (row_ok) {
-            if (VEC && k0 + 3 < p.K) {
+            if (VA && k0 + 3 < p.K) {
                 a = *reinterpret_cast<const floatx4 *>(arow + k0);
             } else {
 #pragma unroll
@@ -102,7 +105,7 @@ __device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&a
 // before the MFMAs of round r, so a round's memory latency overlaps the
 // previous round's arithmetic (loads past K read as zero, so the extra round
 // at the end touches no memory).
-template <int VW, int W, int U, bool VEC>
+template <int VW, int W, int U, bool VA, bool VB>
 __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) {
     using S = RowsShape<VW, W>;
     __shared__ __attribute__((aligned(16))) float red[S::RED];
@@ -120,13 +123,13 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
 
     const int chunks = (p.K + 15) / 16;
     RowsRound<VW, U> r0, r1;
-    rows_load<VW, W, U, VEC>(p, wave, g, gn, row_ok, arow, r0);
+    rows_load<VW, W, U, VA, VB>(p, wave, g, gn, row_ok, arow, r0);
     for (int j = wave; j < chunks; j += 2 * U * W) {
-        rows_load<VW, W, U, VEC>(p, j + U * W, g, gn, row_ok, arow, r1);
+        rows_load<VW, W, U, VA, VB>(p, j + U * W, g, gn, row_ok, arow, r1);
         pipeline_fence();
         rows_mfma<VW, U>(r0, acc);
         if (j + U * W >= chunks) break;
-        rows_load<VW, W, U, VEC>(p, j + 2 * U * W, g, gn, row_ok, arow, r0);
+        rows_load<VW, W, U, VA, VB>(p, j + 2 * U * W, g, gn, row_ok, arow, r0);
         pipeline_fence();
         rows_mfma<VW, U>(r1, acc);
     }
@@ -153,12 +156,28 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     }
 }
 
-template <int VW, int W, int U, bool VEC>
-hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
+bool aligned_to(const void *ptr, unsigned bytes) {
+    return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1)) == 0;
+}
+
+template <int VW, int W, int U, bool VA, bool VB>
+hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VEC>), dim3(strips), dim3(64 * W), 0, stream, p,
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB>), dim3(strips), dim3(64 * W), 0, stream, p,
                        strips);
     return hipGetLastError();
+}
+
+// VEC: wide loads wherever an operand's rows allow them (decided per operand);
+// otherwise 4-byte loads throughout.
+template <int VW, int W, int U, bool VEC>
+hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
+    const bool va = VEC && aligned_to(p.A, 16) && p.lda % 4 == 0;
+    const bool vb = VEC && aligned_to(p.B, 4 * VW) && p.ldb % VW == 0;
+    if (va && vb) return launch_rows_as<VW, W, U, true, true>(p, stream);
+    if (va) return launch_rows_as<VW, W, U, true, false>(p, stream);
+    if (vb) return launch_rows_as<VW, W, U, false, true>(p, stream);
+    return launch_rows_as<VW, W, U, false, false>(p, stream);
 }
 
 // ---------------------------------------------------------------- kind 1 ----
@@ -261,16 +280,23 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
     }
 }
 
+template <int NB, int W, int U, bool VA, bool BT>
+hipError_t launch_cols_as(const Problem &p, hipStream_t stream) {
+    const int blocks = (p.M + W - 1) / W;
+    hipLaunchKernelGGL((cols_kernel<NB, W, U, VA, BT>), dim3(blocks), dim3(64 * W), 0, stream, p);
+    return hipGetLastError();
+}
+
+// VEC: 16-byte loads of A where its rows allow them, and B read as one tight
+// K x NB block where it is one (decided per operand); otherwise 4-byte loads.
 template <int NB, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
-    const int blocks = (p.M + W - 1) / W;
-    if (VEC && p.N == NB && p.ldb == NB)
-        hipLaunchKernelGGL((cols_kernel<NB, W, U, VEC, VEC>), dim3(blocks), dim3(64 * W), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((cols_kernel<NB, W, U, VEC, false>), dim3(blocks), dim3(64 * W), 0,
-                           stream, p);
-    return hipGetLastError();
+    const bool va = VEC && aligned_to(p.A, 16) && p.lda % 4 == 0;
+    const bool bt = VEC && aligned_to(p.B, 16) && p.N == NB && p.ldb == NB;
+    if (va && bt) return launch_cols_as<NB, W, U, true, true>(p, stream);
+    if (va) return launch_cols_as<NB, W, U, true, false>(p, stream);
+    if (bt) return launch_cols_as<NB, W, U, false, true>(p, stream);
+    return launch_cols_as<NB, W, U, false, false>(p, stream);
 }
 
 template <int VW, int W, int U>
