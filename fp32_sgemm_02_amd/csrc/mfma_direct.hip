@@ -62,11 +62,17 @@ namespace {
 
 // AV, BV: floats per direct load of A and B (4: buffer_load_dwordx4, needs
 // 16-byte aligned rows; 1: buffer_load_dword, any 4-byte aligned layout).
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4>
+// KG: k-groups.  With KG > 1 the waves form KG groups that each own the same
+// BM x BN tile of C and take turns over the 16-wide k-chunks of a stage
+// (group g: chunks g*KC/KG ..); their partial sums meet in LDS at the end.
+// It multiplies the waves working on one tile, for problems whose tiles are
+// too few or too small to keep every SIMD busy.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4, int KG = 1>
 struct DirectShape {
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
-    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int WAVES_MN = WAVES_M * WAVES_N;  // waves of one k-group
+    static constexpr int NW = WAVES_MN * KG;
     static constexpr int NT = NW * 64;
     static constexpr int RB = WM / 16;
     static constexpr int CG = WN / 64;
@@ -81,7 +87,11 @@ struct DirectShape {
     static constexpr int AVEC = AV, BVEC = BV;
     static constexpr int L = LA + LB;
     static constexpr int KC = BK / 16;                  // 16-wide k-chunks per stage
+    static constexpr int KCW = KC / KG;                 // ... per wave
+    static constexpr int RED_FLOATS = (KG - 1) * WAVES_MN * (WM / 16) * (WN / 64) * 16 * 64;
     static_assert(BK == 16 || BK == 32, "one or two 16-wide k-chunks per stage");
+    static_assert(KG >= 1 && KC % KG == 0, "k-groups split the chunks of a stage evenly");
+    static_assert(RED_FLOATS <= NBUF * STAGE, "k-group partial sums fit the LDS ring");
     static_assert(WM % 16 == 0 && WN % 64 == 0, "wave tile: 16-row x 64-column units");
     static_assert((AV == 4 || AV == 1) && (BV == 4 || BV == 1), "dword or dwordx4 loads");
     static_assert(LA * 64 * NW * AV == A_STAGE && LB * 64 * NW * BV == B_STAGE,
@@ -210,16 +220,18 @@ __device__ __forceinline__ void roll_block(const floatx4 &a, const floatx4 (&b)[
 // GUARD: the problem has edges (M, N or K not tile multiples, or C not fit
 // for 16-byte stores): zero-filled loads outside the matrix and guarded
 // stores.  cvec: C rows allow 16-byte stores (used with GUARD only).
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV, int BV, bool GUARD>
-__global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF>::NT), 1)
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, int AV, int BV, bool GUARD>
+__global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>::NT), 1)
 mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG>;
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / S::WAVES_N, wc = wave % S::WAVES_N;
+    const int kg = wave / S::WAVES_MN, wv = wave % S::WAVES_MN;   // k-group, wave within it
+    const int wr = wv / S::WAVES_N, wc = wv % S::WAVES_N;
+    const int kc0 = kg * S::KCW;                                 // this wave's first chunk
     int tm, tn;
     tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -245,17 +257,18 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     floatx4 a[RB];
     floatx4 b0[4][S::CG], b1[4][S::CG];
 #pragma unroll
-    for (int rb = 0; rb < H; ++rb) read_a<S>(smem, 0, rb, lane, wr, a[rb]);
+    for (int rb = 0; rb < H; ++rb) read_a<S>(smem, kc0, rb, lane, wr, a[rb]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) read_b<S>(smem, 0, s, lane, wc, b0);
+    for (int s = 0; s < 4; ++s) read_b<S>(smem, kc0, s, lane, wc, b0);
 
-    // One k-chunk: the MFMAs of chunk kc of stage t with B fragments bc, and
-    // the fragments of the following chunk (of this stage, or chunk 0 of the
-    // next) read into a[] and bn.  The last chunk of a stage holds the barrier
-    // and issues the loads of stage t+NBUF.
-    auto chunk = [&](int t, int kc, const floatx4 (&bc)[4][S::CG], floatx4 (&bn)[4][S::CG]) {
+    // One k-chunk: the MFMAs of this wave's chunk kc0 + kc of stage t with B
+    // fragments bc, and the fragments of its following chunk (of this stage,
+    // or its first chunk of the next) read into a[] and bn.  A wave's last
+    // chunk of a stage holds the barrier and issues the loads of stage t+NBUF.
+    auto chunk = [&](int t, int kcw, const floatx4 (&bc)[4][S::CG], floatx4 (&bn)[4][S::CG]) {
         const float *cbuf = smem + (t % NBUF) * S::STAGE;
-        const bool last = (kc == S::KC - 1);
+        const bool last = (kcw == S::KCW - 1);
+        const int kc = kc0 + kcw;
 #pragma unroll
         for (int rb = 0; rb < H; ++rb) {
             read_a<S>(cbuf, kc, rb + H, lane, wr, a[rb + H]);
@@ -274,7 +287,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
             }
             __syncthreads();
             nbuf = smem + ((t + 1) % NBUF) * S::STAGE;
-            nkc = 0;
+            nkc = kc0;
         }
         const int tf = t + NBUF;
         float *fbuf = smem + (t % NBUF) * S::STAGE;
@@ -293,20 +306,51 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
             pipeline_fence();
         }
     };
-    if (S::KC == 2) {
-        // an even number of chunks per stage: the B sets are back in place
+    if (S::KCW == 2) {
+        // an even number of chunks per stage and wave: the B sets are back in place
         for (int t = 0; t < nk; ++t) {
             chunk(t, 0, b0, b1);
             chunk(t, 1, b1, b0);
         }
     } else {
-        // one chunk per stage: two stages per iteration swap the B sets back
+        // one chunk per stage and wave: two stages per iteration swap the B sets back
         int t = 0;
         for (; t + 1 < nk; t += 2) {
             chunk(t, 0, b0, b1);
             chunk(t + 1, 0, b1, b0);
         }
         if (t < nk) chunk(t, 0, b0, b1);
+    }
+
+    // k-groups: groups 1.. leave their partial sums in LDS (the ring is free
+    // once every wave has left the loop); group 0 adds them in group order
+    // and writes C
+    if constexpr (KG > 1) {
+        constexpr int PER_WAVE = RB * S::CG * 4;          // floatx4 per lane
+        __syncthreads();
+        if (kg > 0) {
+            floatx4 *dst = reinterpret_cast<floatx4 *>(smem) +
+                           ((kg - 1) * S::WAVES_MN + wv) * PER_WAVE * 64 + lane;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < S::CG * 4; ++j) dst[(rb * S::CG * 4 + j) * 64] = acc[rb][j];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int g = 1; g < KG; ++g) {
+            const floatx4 *src = reinterpret_cast<const floatx4 *>(smem) +
+                                 ((g - 1) * S::WAVES_MN + wv) * PER_WAVE * 64 + lane;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < S::CG * 4; ++j) {
+                    const floatx4 v = src[(rb * S::CG * 4 + j) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[rb][j][e] += v[e];
+                }
+        }
     }
 
     // epilogue: alpha/beta (beta == 0 never reads C); 16-byte stores, and
@@ -350,14 +394,14 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV, int BV, bool GUARD>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, int AV, int BV, bool GUARD>
 hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stream) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG>;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
-    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, AV, BV, GUARD>),
+    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, AV, BV, GUARD>),
                        dim3((unsigned)tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m,
                        (int)cvec);
     return hipGetLastError();
@@ -369,7 +413,7 @@ hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stre
 // operand whose rows allow them (16-byte aligned rows, and K or N a multiple
 // of 4 so that a 16-byte chunk is entirely inside or outside the matrix).
 // VEC = false (4-byte I/O asked for) uses dword loads and scalar stores.
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES, bool VEC>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool EDGES, bool VEC>
 hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
     if (!direct_applies(p, BM, BN, BK, EDGES)) return hipErrorInvalidValue;
     const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
@@ -377,23 +421,24 @@ hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
     const bool bv = VEC && aligned16(p.B) && p.ldb % 4 == 0 && p.N % 4 == 0;
     const bool cv = VEC && aligned16(p.C) && p.ldc % 4 == 0;
     if (whole && av && bv && cv)
-        return launch_one<BM, BN, BK, WM, WN, NBUF, 4, 4, false>(p, group_m, true, stream);
+        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 4, 4, false>(p, group_m, true, stream);
     if constexpr (EDGES) {
-        if (av && bv) return launch_one<BM, BN, BK, WM, WN, NBUF, 4, 4, true>(p, group_m, cv, stream);
-        if (av) return launch_one<BM, BN, BK, WM, WN, NBUF, 4, 1, true>(p, group_m, cv, stream);
-        if (bv) return launch_one<BM, BN, BK, WM, WN, NBUF, 1, 4, true>(p, group_m, cv, stream);
-        return launch_one<BM, BN, BK, WM, WN, NBUF, 1, 1, true>(p, group_m, cv, stream);
+        if (av && bv)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 4, 4, true>(p, group_m, cv, stream);
+        if (av) return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 4, 1, true>(p, group_m, cv, stream);
+        if (bv) return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 1, 4, true>(p, group_m, cv, stream);
+        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 1, 1, true>(p, group_m, cv, stream);
     }
     return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES, int KG = 1>
 constexpr TileEntry direct_entry(int eff_pct) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>;
     return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF,
                       SGEMM_TILE_DIRECT | (EDGES ? 0 : SGEMM_TILE_WHOLE)},
-                     &launch_direct<BM, BN, BK, WM, WN, NBUF, EDGES, true>,
-                     EDGES ? &launch_direct<BM, BN, BK, WM, WN, NBUF, EDGES, false> : nullptr,
+                     &launch_direct<BM, BN, BK, WM, WN, NBUF, KG, EDGES, true>,
+                     EDGES ? &launch_direct<BM, BN, BK, WM, WN, NBUF, KG, EDGES, false> : nullptr,
                      eff_pct};
 }
 
@@ -417,6 +462,10 @@ const TileEntry *mfma_direct_tiles(int *count) {
         direct_entry<256, 256, 32, 64, 128, 2, false>(93),
         direct_entry<256, 256, 32, 128, 64, 2, false>(93),
         direct_entry<128, 128, 32, 32, 64, 2, false>(91),
+        direct_entry<64, 64, 32, 32, 64, 2, true, 2>(90),     // 2 k-groups of 2 waves
+        direct_entry<128, 64, 32, 32, 64, 2, true, 2>(90),    // 2 k-groups of 4 waves
+        direct_entry<64, 128, 32, 32, 64, 2, true, 2>(91),    // 2 k-groups of 4 waves
+        direct_entry<128, 128, 32, 64, 64, 2, true, 2>(89),   // 2 k-groups of 4 waves
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;
