@@ -54,6 +54,8 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_sgemm_op.restype = ctypes.c_int
+        lib.oracle_sgemm_op.argtypes = [ctypes.c_int, ctypes.c_int] + lib.oracle_sgemm.argtypes
         lib.oracle_version.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -96,23 +98,26 @@ def _base(x: np.ndarray):
 
 
 def sgemm(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None,
-          alpha: float = 1.0, beta: float = 0.0, nthreads: int | None = None) -> np.ndarray:
-    """C = alpha * A @ B + beta * C on 2-D float32 arrays (row-major views with
-    unit column stride; padded rows are allowed).  C is updated in place when
-    given; otherwise a new (M, N) array is returned (beta must then be 0)."""
+          alpha: float = 1.0, beta: float = 0.0, nthreads: int | None = None,
+          trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+    """C = alpha * op(A) @ op(B) + beta * C on 2-D float32 arrays (row-major
+    views with unit column stride; padded rows are allowed).  op(X) is X, or X
+    transposed when trans_x (X is then stored transposed: A as K x M, B as
+    N x K).  C is updated in place when given; otherwise a new (M, N) array is
+    returned (beta must then be 0)."""
     lib = _load()
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
     assert K == K2, "inner dimensions differ"
     if C is None:
         assert beta == 0.0
         C = np.empty((M, N), dtype=np.float32)
     assert C.shape == (M, N)
-    st = lib.oracle_sgemm(M, N, K, float(alpha), _base(A), _ld(A), _base(B), _ld(B),
-                          float(beta), _base(C), _ld(C),
-                          int(nthreads or default_threads()))
+    st = lib.oracle_sgemm_op(int(trans_a), int(trans_b), M, N, K, float(alpha), _base(A), _ld(A),
+                             _base(B), _ld(B), float(beta), _base(C), _ld(C),
+                             int(nthreads or default_threads()))
     if st != 0:
-        raise RuntimeError(f"oracle_sgemm returned {st}")
+        raise RuntimeError(f"oracle_sgemm_op returned {st}")
     return C
 
 

@@ -18,6 +18,10 @@
  * Storage: row-major flat arrays ("The 1% kernel", section 4: element (r, c)
  * lives at offset r * width + c), generalised with leading dimensions:
  *   A(i,k) = A[i*lda + k],  B(k,j) = B[k*ldb + j],  C(i,j) = C[i*ldc + j].
+ * oracle_sgemm_op also takes either operand transposed in storage (the
+ * "GEneral" matrix-multiply of the BLAS, which the pages name but only use
+ * untransposed): op(A)(i,k) = A[k*lda + i] when trans_a, op(B)(k,j) =
+ * B[j*ldb + k] when trans_b.  The arithmetic is the same in every case.
  *
  * Arithmetic: every product of two floats is exact in double (24+24 <= 53
  * significant bits); the K products of a cell are summed in double in
@@ -39,14 +43,14 @@
 #include <stdlib.h>
 #include <stddef.h>
 
-#define ORACLE_VERSION 1
+#define ORACLE_VERSION 2
 
 typedef struct {
     int i0, i1;          /* band of rows [i0, i1) */
     int N, K;
     double alpha, beta;
-    const float *A; long long lda;
-    const float *B; long long ldb;
+    const float *A; long long a_row, a_col;   /* op(A)(i,k) = A[i*a_row + k*a_col] */
+    const float *B; long long b_row, b_col;   /* op(B)(k,j) = B[k*b_row + j*b_col] */
     float *C;       long long ldc;
     int status;
 } band_t;
@@ -67,12 +71,12 @@ static void *run_band(void *arg)
             continue;
         }
         for (int j = 0; j < N; ++j) acc[j] = 0.0;
-        const float *arow = b->A + (long long)i * b->lda;
+        const float *arow = b->A + (long long)i * b->a_row;
         for (int k = 0; k < K; ++k) {
-            const double a = (double)arow[k];
-            const float *brow = b->B + (long long)k * b->ldb;
+            const double a = (double)arow[(long long)k * b->a_col];
+            const float *brow = b->B + (long long)k * b->b_row;
             for (int j = 0; j < N; ++j)
-                acc[j] += a * (double)brow[j];
+                acc[j] += a * (double)brow[(long long)j * b->b_col];
         }
         for (int j = 0; j < N; ++j) {
             double out = b->alpha * acc[j];
@@ -89,25 +93,29 @@ static void *run_band(void *arg)
 int oracle_version(void) { return ORACLE_VERSION; }
 
 /*
+ * C = alpha * op(A) * op(B) + beta * C with op(A) M x K and op(B) K x N.
  * Returns 0 on success; -i when the i-th argument is invalid (1-based, in the
  * order of the parameter list); -100 when memory for the row accumulators or
  * threads could not be obtained.  nthreads <= 0 means one thread.
  */
-int oracle_sgemm(int M, int N, int K, float alpha,
-                 const float *A, int lda, const float *B, int ldb,
-                 float beta, float *C, int ldc, int nthreads)
+int oracle_sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                    const float *A, int lda, const float *B, int ldb,
+                    float beta, float *C, int ldc, int nthreads)
 {
-    if (M < 0) return -1;
-    if (N < 0) return -2;
-    if (K < 0) return -3;
-    if (lda < (K > 1 ? K : 1)) return -6;
-    if (ldb < (N > 1 ? N : 1)) return -8;
-    if (ldc < (N > 1 ? N : 1)) return -11;
+    if (trans_a != 0 && trans_a != 1) return -1;
+    if (trans_b != 0 && trans_b != 1) return -2;
+    if (M < 0) return -3;
+    if (N < 0) return -4;
+    if (K < 0) return -5;
+    const int a_cols = trans_a ? M : K, b_cols = trans_b ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1)) return -8;
+    if (ldb < (b_cols > 1 ? b_cols : 1)) return -10;
+    if (ldc < (N > 1 ? N : 1)) return -13;
     if (M == 0 || N == 0) return 0;
     const int reads_ab = (alpha != 0.0f && K > 0);
-    if (reads_ab && !A) return -5;
-    if (reads_ab && !B) return -7;
-    if (!C) return -10;
+    if (reads_ab && !A) return -7;
+    if (reads_ab && !B) return -9;
+    if (!C) return -12;
 
     if (nthreads < 1) nthreads = 1;
     if (nthreads > M) nthreads = M;
@@ -123,7 +131,9 @@ int oracle_sgemm(int M, int N, int K, float alpha,
         b->i1 = (int)((long long)M * (t + 1) / nthreads);
         b->N = N; b->K = K;
         b->alpha = (double)alpha; b->beta = (double)beta;
-        b->A = A; b->lda = lda; b->B = B; b->ldb = ldb; b->C = C; b->ldc = ldc;
+        b->A = A; b->a_row = trans_a ? 1 : lda; b->a_col = trans_a ? lda : 1;
+        b->B = B; b->b_row = trans_b ? 1 : ldb; b->b_col = trans_b ? ldb : 1;
+        b->C = C; b->ldc = ldc;
         b->status = -100;
     }
     int status = 0;
@@ -138,4 +148,13 @@ int oracle_sgemm(int M, int N, int K, float alpha,
         if (bands[t].status != 0) status = bands[t].status;
     free(bands); free(tids); free(started);
     return status;
+}
+
+/* The untransposed product, with the argument numbering of its own list. */
+int oracle_sgemm(int M, int N, int K, float alpha,
+                 const float *A, int lda, const float *B, int ldb,
+                 float beta, float *C, int ldc, int nthreads)
+{
+    const int st = oracle_sgemm_op(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nthreads);
+    return st < 0 && st > -100 ? st + 2 : st;   /* drop the two leading trans arguments */
 }

@@ -17,6 +17,10 @@ test_oracle.py).  The pins are:
   alpha0_nan    alpha = 0 never reads A or B: C = beta * C exactly.
   ld_padding    NaN in the row padding of A and B does not leak; C's padding
                 is left untouched.
+  transposed    (entry point with op(A), op(B)) exact rational brute force for
+                every combination of transposed storage, a permutation stored
+                transposed, padded rows of transposed operands, and the
+                argument checks of the transposed leading dimensions.
 
 The definition pinned: C = alpha * (A * B) + beta * C, each cell a dot product
 of a row of A and a column of B ("a CUDA matmul" section 00; "The GEMM
@@ -197,17 +201,93 @@ def pin_ld_padding(call, rng) -> list[str]:
     return fails
 
 
-def all_pins(call, seed=1234, square_only=False) -> list[str]:
+def run_op(call_op, ta, tb, A, B, C0, alpha, beta, lda=None, ldb=None):
+    """Call the op entry point on op(A) = A (M x K), op(B) = B (K x N) given in
+    logical form; A is stored transposed when ta (K x M), B when tb (N x K)."""
+    M, K = A.shape
+    N = B.shape[1]
+    As = np.ascontiguousarray(A.T if ta else A, dtype=F32)
+    Bs = np.ascontiguousarray(B.T if tb else B, dtype=F32)
+    C = (np.ascontiguousarray(C0, dtype=F32).copy() if C0 is not None
+         else np.full((M, N), np.nan, dtype=F32))
+    st = call_op(int(ta), int(tb), M, N, K, alpha, As.reshape(-1), lda or max(As.shape[1], 1),
+                 Bs.reshape(-1), ldb or max(Bs.shape[1], 1), beta, C.reshape(-1), max(N, 1))
+    return st, C
+
+
+def pin_transposed(call_op, rng, dims=range(1, 4), square_only=False) -> list[str]:
+    fails = []
+    combos = ((0, 0), (1, 0), (0, 1), (1, 1))
+    shapes = ([(n, n, n) for n in range(2, 5)] if square_only else
+              [(M, N, K) for M in dims for N in dims for K in dims])
+    for (M, N, K) in shapes:
+        A = rng.uniform(-2, 2, (M, K)).astype(F32)
+        B = rng.uniform(-2, 2, (K, N)).astype(F32)
+        C0 = rng.uniform(-2, 2, (M, N)).astype(F32)
+        alpha, beta = float(F32(rng.uniform(-3, 3))), float(F32(rng.uniform(-3, 3)))
+        for ta, tb in combos:
+            st, C = run_op(call_op, ta, tb, A, B, C0, alpha, beta)
+            if st != 0:
+                fails.append(f"transposed status {st} at {(ta, tb, M, N, K)}")
+                continue
+            for i in range(M):
+                for j in range(N):
+                    ex, mag = exact_cell(A, B, C0, i, j, alpha, beta)
+                    if not within_fp64_rounding(float(C[i, j]), ex, mag, K):
+                        fails.append(f"transposed {(ta, tb)} {(M, N, K)} cell {(i, j)}")
+                        break
+    if square_only:
+        return fails
+    # permutation stored transposed: op(B) = P, C = A[:, perm]
+    M, K = 5, 9
+    perm = rng.permutation(K)
+    P = np.zeros((K, K), F32)
+    P[perm, np.arange(K)] = 1.0
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    for ta in (0, 1):
+        st, C = run_op(call_op, ta, 1, A, P, None, 1.0, 0.0)
+        if st or not np.array_equal(C, A[:, perm]):
+            fails.append(f"transposed permutation ta={ta}")
+    # NaN padding of transposed storage never leaks
+    M, N, K = 6, 7, 5
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    _, Cref = run_op(call_op, 0, 0, A, B, None, 1.0, 0.0)
+    As = np.full((K, M + 3), np.nan, F32); As[:, :M] = A.T
+    Bs = np.full((N, K + 2), np.nan, F32); Bs[:, :K] = B.T
+    C = np.full((M, N), np.nan, F32)
+    st = call_op(1, 1, M, N, K, 1.0, As.reshape(-1), M + 3, Bs.reshape(-1), K + 2, 0.0,
+                 C.reshape(-1), N)
+    if st or not np.array_equal(C, Cref):
+        fails.append("transposed ld padding")
+    # leading dimensions are checked against the stored shapes
+    buf = np.zeros(64, F32)
+    if call_op(1, 0, 4, 3, 2, 1.0, buf, 3, buf, 3, 0.0, buf, 3) != -8:      # lda < M
+        fails.append("transposed lda check")
+    if call_op(0, 1, 4, 3, 5, 1.0, buf, 5, buf, 4, 0.0, buf, 3) != -10:     # ldb < K
+        fails.append("transposed ldb check")
+    if call_op(2, 0, 1, 1, 1, 1.0, buf, 1, buf, 1, 0.0, buf, 1) != -1:
+        fails.append("trans flag check")
+    return fails
+
+
+def all_pins(call, seed=1234, square_only=False, call_op=None) -> list[str]:
     """Every pin; square_only restricts brute force to M = N = K (used for
-    broken copies whose indexing is only memory-safe on square shapes)."""
+    broken copies whose indexing is only memory-safe on square shapes).
+    call_op, when given, is the entry point with transposed operands."""
     rng = np.random.default_rng(seed)
     fails = []
     if square_only:
-        return _square_brute(call, rng)
+        fails = _square_brute(call, rng)
+        if call_op is not None:
+            fails += pin_transposed(call_op, rng, square_only=True)
+        return fails
     fails += pin_brute_force(call, rng)
     fails += pin_closed_forms(call, rng)
     fails += pin_alpha_beta(call, rng)
     fails += pin_ld_padding(call, rng)
+    if call_op is not None:
+        fails += pin_transposed(call_op, rng)
     return fails
 
 

@@ -34,13 +34,47 @@ def _caller(lib, nthreads=1):
     return call
 
 
+def _op_caller(lib, nthreads=1):
+    fn = lib.oracle_sgemm_op
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+
+    def call_op(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+        p = lambda x: x.ctypes.data if (x is not None and x.size) else None
+        return fn(ta, tb, M, N, K, alpha, p(A), lda, p(B), ldb, beta, p(C), ldc, nthreads)
+    return call_op
+
+
 @pytest.fixture(scope="module")
 def call(oracle_mod):
     return _caller(ctypes.CDLL(oracle_mod._LIB), nthreads=3)
 
 
-def test_all_pins_pass(call):
-    assert all_pins(call) == []
+@pytest.fixture(scope="module")
+def call_op(oracle_mod):
+    return _op_caller(ctypes.CDLL(oracle_mod._LIB), nthreads=2)
+
+
+def test_all_pins_pass(call, call_op):
+    assert all_pins(call, call_op=call_op) == []
+
+
+def test_transposed_storage_matches_explicit_transpose(oracle_mod):
+    """op(A), op(B) read from transposed storage give the bits of the
+    untransposed product of explicit transposes (same arithmetic order)."""
+    rng = np.random.default_rng(12)
+    M, N, K = 37, 29, 301
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    B = rng.uniform(-1, 1, (K, N)).astype(F32)
+    C0 = rng.uniform(-1, 1, (M, N)).astype(F32)
+    ref = oracle_mod.sgemm(A, B, C0.copy(), 0.5, -1.25)
+    At, Bt = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    for ta, tb in ((1, 0), (0, 1), (1, 1)):
+        got = oracle_mod.sgemm(At if ta else A, Bt if tb else B, C0.copy(), 0.5, -1.25,
+                               trans_a=bool(ta), trans_b=bool(tb))
+        assert np.array_equal(got, ref), (ta, tb)
 
 
 def test_integer_exact_matches_int64_library(oracle_mod):
@@ -142,13 +176,21 @@ MUTANTS = {
     # a dropped term: the first k is skipped
     "dropped_term": ("for (int k = 0; k < K; ++k)", "for (int k = 1; k < K; ++k)", False),
     # a wrong sign in the accumulation
-    "wrong_sign": ("acc[j] += a * (double)brow[j];", "acc[j] -= a * (double)brow[j];", False),
+    "wrong_sign": ("acc[j] += a * (double)brow[(long long)j * b->b_col];",
+                   "acc[j] -= a * (double)brow[(long long)j * b->b_col];", False),
     # a wrong index: A walked backwards along k
-    "wrong_index": ("const double a = (double)arow[k];",
-                    "const double a = (double)arow[K - 1 - k];", False),
+    "wrong_index": ("const double a = (double)arow[(long long)k * b->a_col];",
+                    "const double a = (double)arow[(long long)(K - 1 - k) * b->a_col];", False),
     # a transposed operand: A(k, i) instead of A(i, k) (memory-safe on squares)
-    "transposed_a": ("const double a = (double)arow[k];",
-                     "const double a = (double)b->A[(long long)k * b->lda + i];", True),
+    "transposed_a": ("const double a = (double)arow[(long long)k * b->a_col];",
+                     "const double a = (double)b->A[(long long)k * b->a_row + "
+                     "(long long)i * b->a_col];", True),
+    # transposed storage of A ignored (memory-safe on squares)
+    "trans_a_ignored": ("b->a_row = trans_a ? 1 : lda; b->a_col = trans_a ? lda : 1;",
+                        "b->a_row = lda; b->a_col = 1;", True),
+    # transposed storage of B ignored (memory-safe on squares)
+    "trans_b_ignored": ("b->B = B; b->b_row = trans_b ? 1 : ldb; b->b_col = trans_b ? ldb : 1;",
+                        "b->B = B; b->b_row = ldb; b->b_col = 1;", True),
     # alpha dropped
     "no_alpha": ("double out = b->alpha * acc[j];", "double out = acc[j];", False),
     # beta == 0 still reads C
@@ -172,8 +214,8 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     c.write_text(mutated)
     subprocess.run(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-pthread",
                     str(c), "-o", str(so)], check=True)
-    call = _caller(ctypes.CDLL(str(so)))
-    fails = all_pins(call, square_only=square_only)
+    lib = ctypes.CDLL(str(so))
+    fails = all_pins(_caller(lib), square_only=square_only, call_op=_op_caller(lib))
     if square_only:
         # the square subset must catch it; the full suite is not memory-safe here
         assert fails, f"mutant {name} passed every square pin"
