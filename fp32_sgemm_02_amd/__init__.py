@@ -15,10 +15,10 @@ import ctypes
 import os
 
 __all__ = [
-    "sgemm", "sgemm_ex", "gemm", "select", "tile_count", "tile_info", "status_string",
+    "sgemm", "sgemm_ex", "sgemm_op", "gemm", "select", "tile_count", "tile_info", "status_string",
     "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
-    "TILE_WHOLE", "TILE_DIRECT",
+    "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +29,7 @@ FLAG_SCALAR_IO = 0x1
 FLAG_UNTUNED = 0x2
 TILE_WHOLE = 0x1
 TILE_DIRECT = 0x2
+TILE_TRANS_B = 0x4
 
 
 class SgemmConfig(ctypes.Structure):
@@ -69,6 +70,11 @@ def _load():
     lib.sgemm.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_ex.restype = i
     lib.sgemm_ex.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p, ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_op.restype = i
+    lib.sgemm_op.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_op_ex.restype = i
+    lib.sgemm_op_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p,
+                                ctypes.POINTER(SgemmConfig)]
     lib.sgemm_select.restype = i
     lib.sgemm_select.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig)]
     lib.sgemm_plan.restype = i
@@ -96,6 +102,16 @@ def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None,
     """Raw C-ABI call with an explicit configuration (None = automatic)."""
     return _load().sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
                             ctypes.byref(cfg) if cfg is not None else None)
+
+
+def sgemm_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None,
+             cfg: SgemmConfig | None = None) -> int:
+    """Raw C-ABI call of sgemm_op (cfg given: sgemm_op_ex)."""
+    if cfg is None:
+        return _load().sgemm_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                stream)
+    return _load().sgemm_op_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                               stream, ctypes.byref(cfg))
 
 
 def select(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None) -> SgemmConfig:
@@ -152,19 +168,22 @@ def _ld(t) -> int:
     return ld
 
 
-def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, variant: int = VARIANT_AUTO,
-         tile: int = -1, flags: int = 0, group_m: int = 0, stream=None):
-    """C = alpha * A @ B + beta * C for 2-D float32 CUDA tensors (row-major
-    views with unit column stride; padded rows are used through their leading
-    dimension).  C is updated in place when given; otherwise a new tensor is
-    returned (beta must then be 0).  Runs asynchronously on ``stream``
-    (default: the current stream of A's device)."""
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
+         trans_b: bool = False, variant: int = VARIANT_AUTO, tile: int = -1, flags: int = 0,
+         group_m: int = 0, stream=None):
+    """C = alpha * op(A) @ op(B) + beta * C for 2-D float32 CUDA tensors
+    (row-major views with unit column stride; padded rows are used through
+    their leading dimension).  op(X) is X, or X transposed when trans_x: A is
+    then stored K x M and B N x K (e.g. a linear layer's weight, C = X W^T
+    with B = W, trans_b=True).  C is updated in place when given; otherwise a
+    new tensor is returned (beta must then be 0).  Runs asynchronously on
+    ``stream`` (default: the current stream of A's device)."""
     import torch
 
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be 2-D")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     for name, t in (("A", A), ("B", B)):
@@ -188,10 +207,14 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, variant: int = 
         ptr = lambda t: t.data_ptr() if t.numel() else None
         args = (M, N, K, float(alpha), ptr(A), _ld(A), ptr(B), _ld(B), float(beta), ptr(C),
                 _ld(C), s)
-        if variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0:
-            st = sgemm(*args)
+        explicit = not (variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0)
+        cfg = SgemmConfig(variant, tile, flags, group_m) if explicit else None
+        if trans_a or trans_b:
+            st = sgemm_op(int(trans_a), int(trans_b), *args, cfg=cfg)
+        elif explicit:
+            st = sgemm_ex(*args, cfg=cfg)
         else:
-            st = sgemm_ex(*args, cfg=SgemmConfig(variant, tile, flags, group_m))
+            st = sgemm(*args)
     if st != 0:
         raise SgemmError(st)
     return C

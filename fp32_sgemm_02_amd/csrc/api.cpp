@@ -19,6 +19,8 @@ namespace {
 
 constexpr int kVersion = 200;   // 0.2.0
 constexpr int kBadConfig = -13;
+constexpr int kBadTransA = -21;
+constexpr int kBadTransB = -22;
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -61,6 +63,8 @@ const TileEntry *mfma_family(int *count) {
 // 16-byte I/O for every operand (io_ok), direct-load tiles need their 31-bit
 // panel offsets to fit.
 bool tile_applies(const TileEntry &t, const Problem &p, bool io_ok) {
+    if (p.trans_a) return false;                                  // no tile reads A transposed
+    if (p.trans_b && !(t.desc.flags & SGEMM_TILE_TRANS_B)) return false;
     if (t.desc.flags & SGEMM_TILE_WHOLE)
         return io_ok && direct_applies(p, t.desc.bm, t.desc.bn, t.desc.bk, false);
     if (t.desc.flags & SGEMM_TILE_DIRECT)
@@ -77,13 +81,16 @@ const TileEntry *family(int variant, int *count) {
     }
 }
 
+// Argument checks; codes follow sgemm's parameter list (a transposed operand
+// is stored K x M (A) or N x K (B), so its leading dimension covers M or K).
 int validate(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-             float *C, int ldc) {
+             float *C, int ldc, int trans_a = 0, int trans_b = 0) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
-    if (lda < (K > 1 ? K : 1)) return -6;
-    if (ldb < (N > 1 ? N : 1)) return -8;
+    const int a_cols = trans_a ? M : K, b_cols = trans_b ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1)) return -6;
+    if (ldb < (b_cols > 1 ? b_cols : 1)) return -8;
     if (ldc < (N > 1 ? N : 1)) return -11;
     if (M == 0 || N == 0) return 0;
     const bool reads_ab = (alpha != 0.f) && K > 0;
@@ -154,9 +161,11 @@ Problem main_part(const Problem &p, Strips s) {
 int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
     int count = 0;
     const TileEntry *tiles = mfma_family(&count);
-    int best = general_mfma_tile(p.M, p.N);
-    double best_cost = tile_cost(tiles[best], p.M, p.N);
+    const bool trans = p.trans_a || p.trans_b;
+    int best = trans ? -1 : general_mfma_tile(p.M, p.N);   // -1: nothing applies
+    double best_cost = trans ? 1e300 : tile_cost(tiles[best], p.M, p.N);
     Strips best_strips{0, 0};
+    if (trans) strips = nullptr;                          // the skinny family is untransposed
     for (int i = 0; i < count; ++i) {
         const Strips sp = strips ? edge_strips(p, tiles[i]) : Strips{0, 0};
         const Problem m = main_part(p, sp);
@@ -199,9 +208,14 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     if (variant < 0 || variant >= SGEMM_VARIANT_COUNT) return kBadConfig;
     const bool explicit_tile = (variant != SGEMM_VARIANT_AUTO) && tile >= 0;
     if (strips) *strips = Strips{0, 0};
+    const bool trans = p.trans_a || p.trans_b;
+    if (trans && variant != SGEMM_VARIANT_AUTO && variant != SGEMM_VARIANT_MFMA) return kBadConfig;
     if (variant == SGEMM_VARIANT_AUTO) {
         Tuned a;
-        if ((flags & SGEMM_FLAG_UNTUNED) || !lookup_tuned(p.M, p.N, p.K, a)) {
+        if (trans) {
+            a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok), 0};
+            if (a.tile < 0) return kBadConfig;
+        } else if ((flags & SGEMM_FLAG_UNTUNED) || !lookup_tuned(p.M, p.N, p.K, a)) {
             if (skinny_pick(p.M, p.N, p.K) >= 0)
                 a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
             else
@@ -221,12 +235,13 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     } else if (tile < 0) {
         tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, io_ok) : 0;
     }
+    if (tile < 0) return kBadConfig;
     if (tile >= count) {
-        if (explicit_tile || variant != SGEMM_VARIANT_MFMA) return kBadConfig;
+        if (explicit_tile || variant != SGEMM_VARIANT_MFMA || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // a tuned row naming a tile that is not compiled
     }
     if (!tile_applies(tiles[tile], pm, io_ok)) {
-        if (explicit_tile) return kBadConfig;
+        if (explicit_tile || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // automatic choice that cannot run here
         if (strips) *strips = Strips{0, 0};
     }
@@ -252,8 +267,11 @@ int launch(const Problem &p, const Choice &ch, hipStream_t stream) {
 }
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-        float beta, float *C, int ldc, hipStream_t stream, const sgemm_config *cfg) {
-    const int v = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+        float beta, float *C, int ldc, hipStream_t stream, const sgemm_config *cfg,
+        int trans_a = 0, int trans_b = 0) {
+    if (trans_a != 0 && trans_a != 1) return kBadTransA;
+    if (trans_b != 0 && trans_b != 1) return kBadTransB;
+    const int v = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc, trans_a, trans_b);
     if (v != 0) return v;
     if (M == 0 || N == 0) return 0;
 
@@ -262,7 +280,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
         return to_status(launch_scale(M, N, beta, C, ldc, stream));
     }
 
-    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, trans_a, trans_b};
     Choice ch;
     Strips sp;
     int st = resolve(p, cfg, ch, &sp);
@@ -298,6 +316,18 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, hipStream_t stream, const sgemm_config *cfg) {
     return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, cfg);
+}
+
+int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+             int lda, const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr, trans_a,
+                   trans_b);
+}
+
+int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                hipStream_t stream, const sgemm_config *cfg) {
+    return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, cfg, trans_a, trans_b);
 }
 
 int sgemm_plan(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -346,13 +376,15 @@ const char *sgemm_status_string(int status) {
     case -2: return "invalid argument 2 (N < 0)";
     case -3: return "invalid argument 3 (K < 0)";
     case -5: return "invalid argument 5 (A null or not 4-byte aligned)";
-    case -6: return "invalid argument 6 (lda < max(1, K))";
+    case -6: return "invalid argument 6 (lda too small: max(1, K), or max(1, M) with A transposed)";
     case -7: return "invalid argument 7 (B null or not 4-byte aligned)";
-    case -8: return "invalid argument 8 (ldb < max(1, N))";
+    case -8: return "invalid argument 8 (ldb too small: max(1, N), or max(1, K) with B transposed)";
     case -10: return "invalid argument 10 (C null or not 4-byte aligned)";
     case -11: return "invalid argument 11 (ldc < max(1, N))";
     case -13: return "invalid or inapplicable configuration";
     case -14: return "null output pointer";
+    case -21: return "invalid trans_a (0 or 1)";
+    case -22: return "invalid trans_b (0 or 1)";
     default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

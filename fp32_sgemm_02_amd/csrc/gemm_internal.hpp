@@ -23,6 +23,8 @@ struct Problem {
     long long ldb;
     float *C;
     long long ldc;
+    int trans_a = 0;   // A stored transposed (K x M)
+    int trans_b = 0;   // B stored transposed (N x K)
 };
 
 using LaunchFn = hipError_t (*)(const Problem &, int group_m, hipStream_t);

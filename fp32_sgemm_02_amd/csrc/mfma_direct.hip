@@ -67,7 +67,10 @@ namespace {
 // (group g: chunks g*KC/KG ..); their partial sums meet in LDS at the end.
 // It multiplies the waves working on one tile, for problems whose tiles are
 // too few or too small to keep every SIMD busy.
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4, int KG = 1>
+// TB: B is stored transposed (N x K, k contiguous, ldb >= K); its tile is then
+// held in LDS like A's (BN rows of BK floats, same swizzle).
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4, int KG = 1,
+          bool TB = false>
 struct DirectShape {
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
@@ -76,6 +79,8 @@ struct DirectShape {
     static constexpr int NT = NW * 64;
     static constexpr int RB = WM / 16;
     static constexpr int CG = WN / 64;
+    static constexpr int CB = WN / 16;                  // 16-column blocks of a wave tile
+    static constexpr bool TRANS_B = TB;
     static constexpr int CPR_A = BK / 4;                // 16-byte chunks per A-tile row
     static constexpr int CPR_B = BN / 4;                // ... per B-tile row
     static constexpr int A_STAGE = BM * BK;             // floats
@@ -145,9 +150,17 @@ __device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int m0,
 #pragma unroll
     for (int j = 0; j < S::LB; ++j) {
         const int w = (wave * S::LB + j) * 64 * S::BVEC + S::BVEC * lane;
-        const int r = w / (S::CPR_B * 4), n = w % (S::CPR_B * 4);
-        d.b_k[j] = r;
-        d.b_off[j] = (GUARD && n0 + n >= p.N) ? kOutOfRange : (r * (int)p.ldb + n) * 4;
+        if constexpr (S::TRANS_B) {
+            // BN rows (n) of BK floats, swizzled like A
+            const int r = w / BK, kk = w % BK;
+            const int k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
+            d.b_k[j] = k;
+            d.b_off[j] = (GUARD && n0 + r >= p.N) ? kOutOfRange : (r * (int)p.ldb + k) * 4;
+        } else {
+            const int r = w / (S::CPR_B * 4), n = w % (S::CPR_B * 4);
+            d.b_k[j] = r;
+            d.b_off[j] = (GUARD && n0 + n >= p.N) ? kOutOfRange : (r * (int)p.ldb + n) * 4;
+        }
     }
     return d;
 }
@@ -160,9 +173,13 @@ __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, in
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.A + (long long)m0 * p.lda + (long long)t * BK), (short)0,
         (int)((S::RB * 16 * S::WAVES_M) * p.lda * 4), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.B + (long long)t * BK * p.ldb + n0), (short)0, (int)(BK * p.ldb * 4),
-        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        S::TRANS_B ? __builtin_amdgcn_make_buffer_rsrc(
+                         (void *)(p.B + (long long)n0 * p.ldb + (long long)t * BK), (short)0,
+                         (int)((S::CB * 16 * S::WAVES_N) * p.ldb * 4), 0x00020000)
+                   : __builtin_amdgcn_make_buffer_rsrc(
+                         (void *)(p.B + (long long)t * BK * p.ldb + n0), (short)0,
+                         (int)(BK * p.ldb * 4), 0x00020000);
     const int krem = p.K - t * BK;   // k below this stays inside the matrix
     const bool tail = GUARD && krem < BK;
 #pragma unroll
@@ -183,8 +200,11 @@ __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, in
 
 // Fragment reads of k-chunk kc of a stage.  For lane (i, g):
 // a = A(row 16rb + i, k = 16kc + 4g + 0..3) (logical chunk 4kc + g of the
-// row, stored in slot (4kc + g) ^ swz); b[s][cg] = B(k = 16kc + 4g + s,
-// columns 64cg + 4i + 0..3), the B operand of MFMA step s.
+// row, stored in slot (4kc + g) ^ swz).  The B fragments of a chunk, v[]:
+//   B untransposed: v[s * CG + cg] = B(k = 16kc + 4g + s, columns
+//     64cg + 4i + 0..3), the B operand of MFMA step s for 4 column blocks;
+//   B transposed:   v[cb] = B(k = 16kc + 4g + 0..3, column 16cb + i), read
+//     like A, one 16-column block for all four steps.
 template <class S>
 __device__ __forceinline__ void read_a(const float *buf, int kc, int rb, int lane, int wr,
                                        floatx4 &a) {
@@ -195,35 +215,64 @@ __device__ __forceinline__ void read_a(const float *buf, int kc, int rb, int lan
 }
 
 template <class S>
-__device__ __forceinline__ void read_b(const float *buf, int kc, int s, int lane, int wc,
-                                       floatx4 (&b)[4][S::CG]) {
-    const int i = lane & 15, g = lane >> 4;
-    const float *Bs = buf + S::A_STAGE + (16 * kc + 4 * g + s) * (S::CPR_B * 4) +
-                      wc * S::CG * 64 + 4 * i;
-#pragma unroll
-    for (int cg = 0; cg < S::CG; ++cg) b[s][cg] = *reinterpret_cast<const floatx4 *>(Bs + cg * 64);
-}
+struct BFrag {
+    floatx4 v[4 * S::CG];
+};
 
+// Part `part` (0..3) of the B fragments of chunk kc: step `part` (B
+// untransposed) or column blocks CG*part .. CG*part + CG-1 (transposed).
 template <class S>
-__device__ __forceinline__ void roll_block(const floatx4 &a, const floatx4 (&b)[4][S::CG],
-                                           floatx4 (&acc)[S::CG * 4]) {
+__device__ __forceinline__ void read_b_part(const float *buf, int kc, int part, int lane, int wc,
+                                            BFrag<S> &b) {
+    const int i = lane & 15, g = lane >> 4;
+    if constexpr (S::TRANS_B) {
+        const int slot = (4 * kc + g) ^ ((i >> 1) & (S::CPR_A - 1));
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+        for (int q = 0; q < S::CG; ++q) {
+            const int cb = part * S::CG + q;
+            b.v[cb] = *reinterpret_cast<const floatx4 *>(
+                buf + S::A_STAGE + (wc * S::CB * 16 + cb * 16 + i) * (S::CPR_A * 4) + 4 * slot);
+        }
+    } else {
+        const float *Bs = buf + S::A_STAGE + (16 * kc + 4 * g + part) * (S::CPR_B * 4) +
+                          wc * S::CG * 64 + 4 * i;
 #pragma unroll
         for (int cg = 0; cg < S::CG; ++cg)
+            b.v[part * S::CG + cg] = *reinterpret_cast<const floatx4 *>(Bs + cg * 64);
+    }
+}
+
+// The MFMAs of one 16-row block over one k-chunk: 4 steps x the wave's
+// 16-column blocks.  acc[j] covers columns 64(j/4) + 4i + j%4 (B
+// untransposed) or 16j + i (transposed).
+template <class S>
+__device__ __forceinline__ void roll_block(const floatx4 &a, const BFrag<S> &b,
+                                           floatx4 (&acc)[S::CB]) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                acc[cg * 4 + c] =
-                    __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s][cg][c], acc[cg * 4 + c], 0, 0, 0);
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (S::TRANS_B) {
+#pragma unroll
+            for (int cb = 0; cb < S::CB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b.v[cb][s], acc[cb], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int cg = 0; cg < S::CG; ++cg)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[cg * 4 + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        a[s], b.v[s * S::CG + cg][c], acc[cg * 4 + c], 0, 0, 0);
+        }
+    }
 }
 
 // GUARD: the problem has edges (M, N or K not tile multiples, or C not fit
 // for 16-byte stores): zero-filled loads outside the matrix and guarded
 // stores.  cvec: C rows allow 16-byte stores (used with GUARD only).
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, int AV, int BV, bool GUARD>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, int AV, int BV,
+          bool GUARD>
 __global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>::NT), 1)
 mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB>;
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
@@ -238,11 +287,11 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     const int nk = (p.K + BK - 1) / BK;
     const DirectLanes<S> d = direct_lanes<S, GUARD>(p, m0, n0, wave, lane);
 
-    floatx4 acc[RB][S::CG * 4];
+    floatx4 acc[RB][S::CB];
 #pragma unroll
     for (int a = 0; a < RB; ++a)
 #pragma unroll
-        for (int b = 0; b < S::CG * 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < S::CB; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // prologue: stages 0 .. NBUF-1 in flight; stage 0 complete and published
 #pragma unroll
@@ -255,17 +304,17 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     __syncthreads();
 
     floatx4 a[RB];
-    floatx4 b0[4][S::CG], b1[4][S::CG];
+    BFrag<S> b0, b1;
 #pragma unroll
     for (int rb = 0; rb < H; ++rb) read_a<S>(smem, kc0, rb, lane, wr, a[rb]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) read_b<S>(smem, kc0, s, lane, wc, b0);
+    for (int s = 0; s < 4; ++s) read_b_part<S>(smem, kc0, s, lane, wc, b0);
 
     // One k-chunk: the MFMAs of this wave's chunk kc0 + kc of stage t with B
     // fragments bc, and the fragments of its following chunk (of this stage,
     // or its first chunk of the next) read into a[] and bn.  A wave's last
     // chunk of a stage holds the barrier and issues the loads of stage t+NBUF.
-    auto chunk = [&](int t, int kcw, const floatx4 (&bc)[4][S::CG], floatx4 (&bn)[4][S::CG]) {
+    auto chunk = [&](int t, int kcw, const BFrag<S> &bc, BFrag<S> &bn) {
         const float *cbuf = smem + (t % NBUF) * S::STAGE;
         const bool last = (kcw == S::KCW - 1);
         const int kc = kc0 + kcw;
@@ -297,7 +346,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
                 read_a<S>(nbuf, nkc, j, lane, wr, a[j]);
 #pragma unroll
                 for (int s = (4 * j) / H; s < (4 * (j + 1)) / H; ++s)
-                    read_b<S>(nbuf, nkc, s, lane, wc, bn);
+                    read_b_part<S>(nbuf, nkc, s, lane, wc, bn);
             }
             if (last && tf < nk)
                 issue_stage<S, GUARD>(p, m0, n0, tf, fbuf, wave, d, (S::L * j) / H,
@@ -326,7 +375,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     // once every wave has left the loop); group 0 adds them in group order
     // and writes C
     if constexpr (KG > 1) {
-        constexpr int PER_WAVE = RB * S::CG * 4;          // floatx4 per lane
+        constexpr int PER_WAVE = RB * S::CB;              // floatx4 per lane
         __syncthreads();
         if (kg > 0) {
             floatx4 *dst = reinterpret_cast<floatx4 *>(smem) +
@@ -334,7 +383,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int j = 0; j < S::CG * 4; ++j) dst[(rb * S::CG * 4 + j) * 64] = acc[rb][j];
+                for (int j = 0; j < S::CB; ++j) dst[(rb * S::CB + j) * 64] = acc[rb][j];
         }
         __syncthreads();
         if (kg > 0) return;
@@ -345,8 +394,8 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int j = 0; j < S::CG * 4; ++j) {
-                    const floatx4 v = src[(rb * S::CG * 4 + j) * 64];
+                for (int j = 0; j < S::CB; ++j) {
+                    const floatx4 v = src[(rb * S::CB + j) * 64];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[rb][j][e] += v[e];
                 }
@@ -365,6 +414,19 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
             const int gm = row0 + rb * 16 + 4 * g + r;
             if (GUARD && gm >= p.M) continue;
             float *crow = p.C + (long long)gm * p.ldc;
+            if constexpr (S::TRANS_B) {
+                // acc[rb][cb][r] is C(gm, col0 + 16cb + i): 16 lanes write 64
+                // contiguous bytes
+#pragma unroll
+                for (int cb = 0; cb < S::CB; ++cb) {
+                    const int gn = col0 + cb * 16 + i;
+                    if (GUARD && gn >= p.N) continue;
+                    float out = p.alpha * acc[rb][cb][r];
+                    if (read_c) out = fmaf(p.beta, crow[gn], out);
+                    crow[gn] = out;
+                }
+                continue;
+            }
 #pragma unroll
             for (int cg = 0; cg < S::CG; ++cg) {
                 const int gn = col0 + cg * 64 + 4 * i;
@@ -394,14 +456,15 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, int AV, int BV, bool GUARD>
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, int AV, int BV,
+          bool GUARD>
 hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stream) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB>;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
-    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, AV, BV, GUARD>),
+    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, AV, BV, GUARD>),
                        dim3((unsigned)tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m,
                        (int)cvec);
     return hipGetLastError();
@@ -410,33 +473,51 @@ hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stre
 // Picks the kernel instance for the operands: the whole-tile instance when
 // the problem is made of whole tiles with 16-byte rows everywhere, else (for
 // tiles compiled with EDGES) a guarded instance with dwordx4 loads for each
-// operand whose rows allow them (16-byte aligned rows, and K or N a multiple
-// of 4 so that a 16-byte chunk is entirely inside or outside the matrix).
-// VEC = false (4-byte I/O asked for) uses dword loads and scalar stores.
-template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool EDGES, bool VEC>
-hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
-    if (!direct_applies(p, BM, BN, BK, EDGES)) return hipErrorInvalidValue;
+// operand whose rows allow them (16-byte aligned rows, and the length along
+// the row -- K, or N for untransposed B -- a multiple of 4, so that a 16-byte
+// chunk is entirely inside or outside the matrix).  Transposed B is served by
+// the EDGES tiles only.  VEC = false (4-byte I/O asked for) uses dword loads
+// and scalar stores.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool EDGES, bool VEC>
+hipError_t launch_for(const Problem &p, int group_m, hipStream_t stream) {
     const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
     const bool av = VEC && aligned16(p.A) && p.lda % 4 == 0 && p.K % 4 == 0;
-    const bool bv = VEC && aligned16(p.B) && p.ldb % 4 == 0 && p.N % 4 == 0;
+    const bool bv = VEC && aligned16(p.B) && p.ldb % 4 == 0 && (TB ? p.K : p.N) % 4 == 0;
     const bool cv = VEC && aligned16(p.C) && p.ldc % 4 == 0;
-    if (whole && av && bv && cv)
-        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 4, 4, false>(p, group_m, true, stream);
+    if constexpr (!TB) {
+        if (whole && av && bv && cv)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, 4, 4, false>(p, group_m, true,
+                                                                            stream);
+    }
     if constexpr (EDGES) {
         if (av && bv)
-            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 4, 4, true>(p, group_m, cv, stream);
-        if (av) return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 4, 1, true>(p, group_m, cv, stream);
-        if (bv) return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 1, 4, true>(p, group_m, cv, stream);
-        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, 1, 1, true>(p, group_m, cv, stream);
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, 4, 4, true>(p, group_m, cv, stream);
+        if (av)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, 4, 1, true>(p, group_m, cv, stream);
+        if (bv)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, 1, 4, true>(p, group_m, cv, stream);
+        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, 1, 1, true>(p, group_m, cv, stream);
     }
     return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool EDGES, bool VEC>
+hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
+    if (p.trans_a) return hipErrorInvalidValue;
+    if (!direct_applies(p, BM, BN, BK, EDGES)) return hipErrorInvalidValue;
+    if (p.trans_b) {
+        if constexpr (EDGES)
+            return launch_for<BM, BN, BK, WM, WN, NBUF, KG, true, EDGES, VEC>(p, group_m, stream);
+        return hipErrorInvalidValue;
+    }
+    return launch_for<BM, BN, BK, WM, WN, NBUF, KG, false, EDGES, VEC>(p, group_m, stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES, int KG = 1>
 constexpr TileEntry direct_entry(int eff_pct) {
     using S = DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>;
     return TileEntry{{BM, BN, BK, WM, WN, 0, 0, S::NT, S::LDS_BYTES, NBUF,
-                      SGEMM_TILE_DIRECT | (EDGES ? 0 : SGEMM_TILE_WHOLE)},
+                      SGEMM_TILE_DIRECT | (EDGES ? SGEMM_TILE_TRANS_B : SGEMM_TILE_WHOLE)},
                      &launch_direct<BM, BN, BK, WM, WN, NBUF, KG, EDGES, true>,
                      EDGES ? &launch_direct<BM, BN, BK, WM, WN, NBUF, KG, EDGES, false> : nullptr,
                      eff_pct};
@@ -445,8 +526,9 @@ constexpr TileEntry direct_entry(int eff_pct) {
 }  // namespace
 
 bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges) {
+    const long long b_rows = p.trans_b ? bn : bk;   // rows of B a tile's panel spans
     const bool offsets_fit =
-        (long long)bm * p.lda * 4 < (1LL << 31) && (long long)bk * p.ldb * 4 < (1LL << 31);
+        (long long)bm * p.lda * 4 < (1LL << 31) && b_rows * p.ldb * 4 < (1LL << 31);
     if (edges) return offsets_fit;
     return offsets_fit && p.M % bm == 0 && p.N % bn == 0 && p.K % bk == 0 && p.K >= bk;
 }

@@ -41,7 +41,9 @@
  *                       for an operand that will be read or written, or a
  *                       pointer that is not 4-byte aligned
  *     -13               sgemm_ex: the configuration is invalid or does not
- *                       apply to this shape (see sgemm_config)
+ *                       apply to this shape (see sgemm_config); sgemm_op:
+ *                       no compiled kernel serves this transposition
+ *     -21, -22          sgemm_op: trans_a, trans_b not 0 or 1
  *     > 0               a hipError_t reported by the kernel launch
  * No C++ exception crosses this interface.
  *
@@ -107,6 +109,9 @@ typedef struct sgemm_tile_desc {
  * through 32-bit buffer offsets, so it needs bm * lda and bk * ldb below 2^29
  * elements; sgemm_ex returns -13 otherwise. */
 #define SGEMM_TILE_DIRECT 0x2
+/* sgemm_tile_desc.flags: the tile also serves B stored transposed
+ * (sgemm_op with trans_b = 1). */
+#define SGEMM_TILE_TRANS_B 0x4
 
 /*
  * sgemm: C = alpha * (A * B) + beta * C, kernel family and tile chosen from
@@ -140,6 +145,28 @@ int sgemm_ex(int M, int N, int K, float alpha,
  */
 int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B,
                  int ldb, const float *C, int ldc, sgemm_config *out);
+
+/*
+ * sgemm_op: C = alpha * op(A) * op(B) + beta * C, the general form of the
+ * BLAS (row-major, as cblas_sgemm with CblasRowMajor).  op(A) is M x K:
+ * A itself (trans_a = 0, stored M x K, lda >= max(1, K)) or A transposed
+ * (trans_a = 1, stored K x M, lda >= max(1, M)).  op(B) is K x N: B
+ * (trans_b = 0, stored K x N, ldb >= max(1, N)) or B transposed (trans_b = 1,
+ * stored N x K, ldb >= max(1, K): a weight matrix of a linear layer, C = X W^T).
+ * Status codes as sgemm's for the arguments they share (-1 M .. -11 ldc),
+ * -21 / -22 for a trans flag other than 0 or 1, and -13 when no compiled
+ * kernel serves the transposition: this version serves trans_b = 1 with the
+ * direct-load tiles flagged SGEMM_TILE_TRANS_B, and no trans_a = 1.
+ * sgemm_op(0, 0, ...) is sgemm.
+ */
+int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+             int lda, const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream);
+
+/* sgemm_op with an explicit configuration, as sgemm_ex (MFMA family only when
+ * an operand is transposed). */
+int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                hipStream_t stream, const sgemm_config *cfg);
 
 /*
  * sgemm_plan: sgemm_select plus the edge strips of the automatic plan.  When

@@ -101,6 +101,37 @@ def test_bad_configuration():
     assert sg.sgemm_ex(8, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
 
 
+def test_transposed_entry_point_validation():
+    """sgemm_op checks its trans flags and the transposed leading dimensions
+    before touching the device, and refuses what no kernel serves."""
+    good = 0x10000
+    op = sg.sgemm_op
+    assert op(2, 0, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -21
+    assert op(0, -1, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -22
+    # A stored K x M: lda must cover M
+    assert op(1, 0, 8, 4, 2, 1.0, good, 4, good, 4, 0.0, good, 4) == -6
+    # B stored N x K: ldb must cover K
+    assert op(0, 1, 4, 8, 6, 1.0, good, 6, good, 4, 0.0, good, 8) == -8
+    assert op(0, 1, -1, 8, 6, 1.0, good, 6, good, 6, 0.0, good, 8) == -1
+    # no kernel reads A transposed
+    assert op(1, 0, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64) == -13
+    # transposed B: only the MFMA family, only tiles flagged for it
+    for variant in (sg.VARIANT_VALU, sg.VARIANT_SKINNY):
+        cfg = sg.SgemmConfig(variant, -1, 0, 0)
+        assert op(0, 1, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
+    tb = [t for t in range(sg.tile_count(sg.VARIANT_MFMA))
+          if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_TRANS_B]
+    assert tb, "no tile serves transposed B"
+    for t in range(sg.tile_count(sg.VARIANT_MFMA)):
+        if t in tb:
+            continue
+        cfg = sg.SgemmConfig(sg.VARIANT_MFMA, t, 0, 0)
+        assert op(0, 1, 256, 256, 64, 1.0, good, 64, good, 64, 0.0, good, 256, None, cfg) == -13
+    # quick returns need no kernel: alpha == 0 with beta == 1, empty shapes
+    assert op(1, 1, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, good, 4) == 0
+    assert op(1, 1, 0, 4, 4, 1.0, None, 1, None, 4, 0.0, None, 4) == 0
+
+
 def whole_tiles():
     return [t for t in range(sg.tile_count(sg.VARIANT_MFMA))
             if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_WHOLE]

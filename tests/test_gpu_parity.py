@@ -222,6 +222,90 @@ def test_automatic_plan_with_edge_strips(shape, oracle_mod):
           label=f"plan {shape} strips {(rows, cols)}")
 
 
+# ------------------------------------------------------- transposed B --
+def trans_b_tiles():
+    return [t for t in tiles(sg.VARIANT_MFMA)
+            if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_TRANS_B]
+
+
+def run_gpu_tb(A, Bt, C0, alpha, beta, **kw):
+    """C = alpha * A @ Bt^T + beta * C on the GPU, B stored transposed (N x K)."""
+    M, N = A.shape[0], Bt.shape[0]
+    C = dev(C0) if C0 is not None else torch.full((M, N), float("nan"), device=DEV)
+    sg.gemm(dev(A), dev(Bt), C, alpha, beta, trans_b=True, **kw)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def check_tb(A, Bt, C0, alpha, beta, C, oracle_mod, exact=False, label=""):
+    ref = oracle_mod.sgemm(A, Bt, None if C0 is None else C0.copy(), alpha,
+                           beta if C0 is not None else 0.0, trans_b=True)
+    if exact:
+        assert np.array_equal(C, ref), f"{label}: not bit-exact"
+        return
+    r = max_err_ratio(C, ref, A.shape[1], alpha, beta, A, Bt, C0)
+    assert r <= 1.0, f"{label}: max err/tol = {r}"
+
+
+@pytest.mark.parametrize("slot", range(10))
+def test_transposed_b_tiles(slot, oracle_mod):
+    """Every tile that serves B stored transposed (N x K, a linear layer's
+    weight): ragged and whole shapes, K under one stage and odd K (4-byte
+    loads), alpha/beta, beta = 0 over NaN, integer bit-exact, 4-byte I/O."""
+    tb = trans_b_tiles()
+    if slot >= len(tb):
+        pytest.skip("no such tile")
+    tile = tb[slot]
+    d = sg.tile_info(sg.VARIANT_MFMA, tile)
+    bm, bn, bk = d["bm"], d["bn"], d["bk"]
+    kw = dict(variant=sg.VARIANT_MFMA, tile=tile)
+    for i, (M, N, K) in enumerate(((bm, bn, 4 * bk), (bm + 3, bn - 5, 3 * bk + 7), (37, 45, 5),
+                                   (2 * bm, 2 * bn + 4, 64), (1, 1, 1))):
+        lab = f"tb t{tile} {(M, N, K)}"
+        A, B, C0 = uniform(M, N, K, 1000 + i)
+        Bt = np.ascontiguousarray(B.T)
+        check_tb(A, Bt, C0, 0.5, -1.25, run_gpu_tb(A, Bt, C0, 0.5, -1.25, **kw), oracle_mod,
+                 label=lab)
+        check_tb(A, Bt, None, 1.0, 0.0, run_gpu_tb(A, Bt, None, 1.0, 0.0, **kw), oracle_mod,
+                 label=lab + " b0")
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 1100 + i, True)
+        Bit = np.ascontiguousarray(Bi.T)
+        check_tb(Ai, Bit, Ci, 0.5, -1.25, run_gpu_tb(Ai, Bit, Ci, 0.5, -1.25, **kw), oracle_mod,
+                 exact=True, label=lab + " int")
+        check_tb(Ai, Bit, Ci, 0.5, -1.25,
+                 run_gpu_tb(Ai, Bit, Ci, 0.5, -1.25, flags=sg.FLAG_SCALAR_IO, **kw), oracle_mod,
+                 exact=True, label=lab + " int scalar")
+    # padded rows of the transposed B (NaN padding must not leak)
+    M, N, K = bm + 7, bn + 9, 40
+    rng = np.random.default_rng(tile)
+    A = rng.uniform(-1, 1, (M, K)).astype(F32)
+    Bt = rng.uniform(-1, 1, (N, K)).astype(F32)
+    Bs = torch.full((N, K + 3), float("nan"), device=DEV)
+    Bs[:, :K] = dev(Bt)
+    C = torch.full((M, N), float("nan"), device=DEV)
+    sg.gemm(dev(A), Bs[:, :K], C, 1.0, 0.0, trans_b=True, **kw)
+    torch.cuda.synchronize()
+    check_tb(A, Bt, None, 1.0, 0.0, C.cpu().numpy(), oracle_mod, label=f"tb t{tile} padded")
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 4096), (8192, 14336, 4096), (4097, 1000, 3001),
+                                   (300, 257, 129)])
+def test_transposed_b_automatic(shape, oracle_mod):
+    """Automatic dispatch of C = X W^T (W stored N x K) at benchmark sizes,
+    sampled rows against the oracle; integer inputs bit-exact."""
+    M, N, K = shape
+    A, B, C0 = workloads.draw(M, N, K, "int4", 1200, True)
+    Bt = np.ascontiguousarray(B.T)
+    dA, dBt, dC = dev(A), dev(Bt), dev(C0)
+    sg.gemm(dA, dBt, dC, 0.5, -1.25, trans_b=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 24)
+    got = dC.cpu().numpy()[rows]
+    ref = oracle_mod.sgemm(np.ascontiguousarray(A[rows]), Bt, np.ascontiguousarray(C0[rows]),
+                           0.5, -1.25, trans_b=True)
+    assert np.array_equal(got, ref), f"transposed B {shape}"
+
+
 SKINNY_CASES = {
     0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
     1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],
