@@ -36,9 +36,11 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and packed vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TILE_DIRECT = 0x2  # sgemm_tile_desc.flags bit of the direct-load MFMA tiles
+TILE_TRANS_A = 0x8  # ... of those that read A stored transposed
 KERNEL_SOURCES = {
     1: ["mfma_gemm.hip", "gemm_internal.hpp"],
-    "direct": ["mfma_direct.hip", "gemm_internal.hpp"],
+    "direct": ["mfma_direct.hip", "direct_kernel.hpp", "gemm_internal.hpp"],
+    "direct_ta": ["mfma_direct_ta.hip", "direct_kernel.hpp", "gemm_internal.hpp"],
     2: ["valu_gemm.hip", "gemm_internal.hpp"],
     3: ["skinny_gemm.hip", "gemm_internal.hpp"],
 }
@@ -46,7 +48,9 @@ KERNEL_SOURCES = {
 
 def kernel_source_hash(variant: int, desc: dict | None = None) -> str:
     h = hashlib.sha256()
-    key = "direct" if variant == 1 and desc and desc.get("flags", 0) & TILE_DIRECT else variant
+    key = variant
+    if variant == 1 and desc and desc.get("flags", 0) & TILE_DIRECT:
+        key = "direct_ta" if desc["flags"] & TILE_TRANS_A else "direct"
     for f in KERNEL_SOURCES.get(key, []):
         with open(os.path.join(ROOT, "fp32_sgemm_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -59,7 +63,7 @@ def kernel_name(variant: int, desc: dict) -> str:
     if not desc:
         return fam
     if variant == 1 and desc.get("flags", 0) & TILE_DIRECT:
-        fam = "mfma_direct"
+        fam = "mfma_direct_ta" if desc["flags"] & TILE_TRANS_A else "mfma_direct"
     return (f"{fam}_{desc['bm']}x{desc['bn']}x{desc['bk']}_w{desc['wm']}x{desc['wn']}"
             f"_s{desc.get('stages', 0)}_t{desc['threads']}")
 
@@ -317,10 +321,36 @@ def sweep(args):
                 row["pct_roofline"] = round(100 * row["gflops"] / (PEAK_FP32_TFLOPS * 1e3), 2)
             rows.append(row)
             print(json.dumps(row), flush=True)
+        if name in TRANSPOSED_SWEEP:
+            rows.extend(sweep_transposed(torch, sg, time_graph, w, sets[0]))
         del sets
         torch.cuda.empty_cache()
     with open(args.sweep, "w") as fh:
         json.dump(rows, fh, indent=1)
+
+
+TRANSPOSED_SWEEP = ("square4096", "mlp_up", "mlp_down")
+
+
+def sweep_transposed(torch, sg, time_graph, w, operands):
+    """The workload with A and/or B stored transposed (sgemm_op through
+    automatic dispatch), graph-replay device time per call."""
+    A, B, C = operands
+    out = []
+    for ta, tb in ((False, True), (True, False), (True, True)):
+        As = A.t().contiguous() if ta else A
+        Bs = B.t().contiguous() if tb else B
+        call_i = lambda i: sg.gemm(As, Bs, C, w.alpha, w.beta, trans_a=ta, trans_b=tb)
+        med = statistics.median(time_graph(torch, call_i, 5)) / 1e3
+        op = ("T" if ta else "N") + ("T" if tb else "N")
+        row = {"workload": f"{w.name}_{op}", "M": w.M, "N": w.N, "K": w.K, "op": op,
+               "kernel_ms_median": round(med * 1e3, 4),
+               "gflops": round(w.flops / med / 1e9, 1), "bound": w.bound,
+               "pct_roofline": round(100 * w.flops / med / 1e9 / (PEAK_FP32_TFLOPS * 1e3), 2)}
+        print(json.dumps(row), flush=True)
+        out.append(row)
+        del As, Bs
+    return out
 
 
 def copy_calibration(args):

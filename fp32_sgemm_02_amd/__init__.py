@@ -18,7 +18,7 @@ __all__ = [
     "sgemm", "sgemm_ex", "sgemm_op", "gemm", "select", "tile_count", "tile_info", "status_string",
     "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
-    "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B",
+    "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +30,7 @@ FLAG_UNTUNED = 0x2
 TILE_WHOLE = 0x1
 TILE_DIRECT = 0x2
 TILE_TRANS_B = 0x4
+TILE_TRANS_A = 0x8
 
 
 class SgemmConfig(ctypes.Structure):

@@ -43,8 +43,8 @@ long long tiles_for(const TileEntry &t, int M, int N) {
     return (long long)((M + t.desc.bm - 1) / t.desc.bm) * ((N + t.desc.bn - 1) / t.desc.bn);
 }
 
-// The MFMA family: the general tiles followed by the whole-tile (direct-load)
-// tiles, in one table.
+// The MFMA family: the general tiles, then the direct-load tiles for
+// untransposed A, then those for transposed A, in one table.
 const TileEntry *mfma_family(int *count) {
     static const std::vector<TileEntry> all = [] {
         std::vector<TileEntry> v;
@@ -52,6 +52,8 @@ const TileEntry *mfma_family(int *count) {
         const TileEntry *t = mfma_tiles(&n);
         v.insert(v.end(), t, t + n);
         t = mfma_direct_tiles(&n);
+        v.insert(v.end(), t, t + n);
+        t = mfma_direct_ta_tiles(&n);
         v.insert(v.end(), t, t + n);
         return v;
     }();
@@ -63,7 +65,7 @@ const TileEntry *mfma_family(int *count) {
 // 16-byte I/O for every operand (io_ok), direct-load tiles need their 31-bit
 // panel offsets to fit.
 bool tile_applies(const TileEntry &t, const Problem &p, bool io_ok) {
-    if (p.trans_a) return false;                                  // no tile reads A transposed
+    if ((p.trans_a != 0) != ((t.desc.flags & SGEMM_TILE_TRANS_A) != 0)) return false;
     if (p.trans_b && !(t.desc.flags & SGEMM_TILE_TRANS_B)) return false;
     if (t.desc.flags & SGEMM_TILE_WHOLE)
         return io_ok && direct_applies(p, t.desc.bm, t.desc.bn, t.desc.bk, false);

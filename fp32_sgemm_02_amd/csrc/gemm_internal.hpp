@@ -42,7 +42,8 @@ struct TileEntry {
 // Kernel families (each defined in its own .hip file): the compiled tile
 // configurations, as a table owned by the family (host functions only).
 const TileEntry *mfma_tiles(int *count);
-const TileEntry *mfma_direct_tiles(int *count);   // SGEMM_TILE_WHOLE tiles
+const TileEntry *mfma_direct_tiles(int *count);      // direct-load tiles, A untransposed
+const TileEntry *mfma_direct_ta_tiles(int *count);   // ... A transposed
 bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 const TileEntry *valu_tiles(int *count);
 const TileEntry *skinny_tiles(int *count);

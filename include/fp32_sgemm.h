@@ -112,6 +112,9 @@ typedef struct sgemm_tile_desc {
 /* sgemm_tile_desc.flags: the tile also serves B stored transposed
  * (sgemm_op with trans_b = 1). */
 #define SGEMM_TILE_TRANS_B 0x4
+/* sgemm_tile_desc.flags: the tile serves A stored transposed (sgemm_op with
+ * trans_a = 1), and only that; such tiles need bk * lda below 2^29 elements. */
+#define SGEMM_TILE_TRANS_A 0x8
 
 /*
  * sgemm: C = alpha * (A * B) + beta * C, kernel family and tile chosen from
@@ -155,9 +158,10 @@ int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B,
  * stored N x K, ldb >= max(1, K): a weight matrix of a linear layer, C = X W^T).
  * Status codes as sgemm's for the arguments they share (-1 M .. -11 ldc),
  * -21 / -22 for a trans flag other than 0 or 1, and -13 when no compiled
- * kernel serves the transposition: this version serves trans_b = 1 with the
- * direct-load tiles flagged SGEMM_TILE_TRANS_B, and no trans_a = 1.
- * sgemm_op(0, 0, ...) is sgemm.
+ * kernel serves the transposition.  Transposed operands are served by the
+ * MFMA family's direct-load tiles: trans_a = 0 with trans_b = 1 by those
+ * flagged SGEMM_TILE_TRANS_B, trans_a = 1 (either trans_b) by those flagged
+ * SGEMM_TILE_TRANS_A.  sgemm_op(0, 0, ...) is sgemm.
  */
 int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
              int lda, const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream);

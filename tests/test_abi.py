@@ -113,8 +113,19 @@ def test_transposed_entry_point_validation():
     # B stored N x K: ldb must cover K
     assert op(0, 1, 4, 8, 6, 1.0, good, 6, good, 4, 0.0, good, 8) == -8
     assert op(0, 1, -1, 8, 6, 1.0, good, 6, good, 6, 0.0, good, 8) == -1
-    # no kernel reads A transposed
-    assert op(1, 0, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64) == -13
+    # transposed A: only the tiles flagged for it, and those serve nothing else
+    ta = [t for t in range(sg.tile_count(sg.VARIANT_MFMA))
+          if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_TRANS_A]
+    assert ta, "no tile serves transposed A"
+    for t in range(sg.tile_count(sg.VARIANT_MFMA)):
+        cfg = sg.SgemmConfig(sg.VARIANT_MFMA, t, 0, 0)
+        for trans_a in (0, 1):
+            if (t in ta) != bool(trans_a):
+                assert op(trans_a, 0, 256, 256, 64, 1.0, good, 256, good, 256, 0.0, good, 256,
+                          None, cfg) == -13, (t, trans_a)
+    for variant in (sg.VARIANT_VALU, sg.VARIANT_SKINNY):
+        cfg = sg.SgemmConfig(variant, -1, 0, 0)
+        assert op(1, 0, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
     # transposed B: only the MFMA family, only tiles flagged for it
     for variant in (sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         cfg = sg.SgemmConfig(variant, -1, 0, 0)

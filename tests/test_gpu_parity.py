@@ -151,10 +151,11 @@ def test_whole_tile_parity(slot, oracle_mod):
 
 # ---------------------------------------------- direct-load tiles, edges --
 def direct_edge_tiles():
+    """Direct-load tiles with edges that read A untransposed."""
     out = []
     for t in tiles(sg.VARIANT_MFMA):
         f = sg.tile_info(sg.VARIANT_MFMA, t)["flags"]
-        if f & sg.TILE_DIRECT and not f & sg.TILE_WHOLE:
+        if f & sg.TILE_DIRECT and not f & (sg.TILE_WHOLE | sg.TILE_TRANS_A):
             out.append(t)
     return out
 
@@ -224,8 +225,13 @@ def test_automatic_plan_with_edge_strips(shape, oracle_mod):
 
 # ------------------------------------------------------- transposed B --
 def trans_b_tiles():
-    return [t for t in tiles(sg.VARIANT_MFMA)
-            if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_TRANS_B]
+    """Tiles that serve untransposed A with B stored transposed."""
+    out = []
+    for t in tiles(sg.VARIANT_MFMA):
+        f = sg.tile_info(sg.VARIANT_MFMA, t)["flags"]
+        if f & sg.TILE_TRANS_B and not f & sg.TILE_TRANS_A:
+            out.append(t)
+    return out
 
 
 def run_gpu_tb(A, Bt, C0, alpha, beta, **kw):
@@ -306,6 +312,106 @@ def test_transposed_b_automatic(shape, oracle_mod):
     assert np.array_equal(got, ref), f"transposed B {shape}"
 
 
+# ------------------------------------------------------- transposed A --
+def trans_a_tiles():
+    return [t for t in tiles(sg.VARIANT_MFMA)
+            if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_TRANS_A]
+
+
+def run_gpu_op(As, Bs, C0, alpha, beta, trans_a, trans_b, **kw):
+    """C = alpha * op(As) @ op(Bs) + beta * C on the GPU, operands as stored
+    (A as K x M when trans_a, B as N x K when trans_b)."""
+    M = As.shape[1] if trans_a else As.shape[0]
+    N = Bs.shape[0] if trans_b else Bs.shape[1]
+    C = dev(C0) if C0 is not None else torch.full((M, N), float("nan"), device=DEV)
+    sg.gemm(dev(As), dev(Bs), C, alpha, beta, trans_a=trans_a, trans_b=trans_b, **kw)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def check_op(As, Bs, C0, alpha, beta, C, trans_a, trans_b, oracle_mod, exact=False, label=""):
+    ref = oracle_mod.sgemm(As, Bs, None if C0 is None else C0.copy(), alpha,
+                           beta if C0 is not None else 0.0, trans_a=trans_a, trans_b=trans_b)
+    if exact:
+        assert np.array_equal(C, ref), f"{label}: not bit-exact " \
+            f"(max diff {np.nanmax(np.abs(C - ref))})"
+        return
+    K = As.shape[0] if trans_a else As.shape[1]
+    r = max_err_ratio(C, ref, K, alpha, beta, As, Bs, C0)
+    assert r <= 1.0, f"{label}: max err/tol = {r}"
+
+
+def stored(A, B, trans_a, trans_b):
+    return (np.ascontiguousarray(A.T) if trans_a else A,
+            np.ascontiguousarray(B.T) if trans_b else B)
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("slot", range(8))
+def test_transposed_a_tiles(slot, trans_b, oracle_mod):
+    """Every tile that serves A stored transposed (K x M), with B either way:
+    whole and ragged shapes, M not a multiple of 4 (4-byte loads of A), K
+    under one stage and odd K, alpha/beta, beta = 0 over NaN, integer inputs
+    bit-exact, 4-byte I/O, and a NaN-padded A."""
+    ta = trans_a_tiles()
+    if slot >= len(ta):
+        pytest.skip("no such tile")
+    tile = ta[slot]
+    d = sg.tile_info(sg.VARIANT_MFMA, tile)
+    bm, bn, bk = d["bm"], d["bn"], d["bk"]
+    kw = dict(variant=sg.VARIANT_MFMA, tile=tile)
+    shapes = [(bm, bn, 4 * bk), (bm + 3, bn - 5, 3 * bk + 7), (37, 45, 5),
+              (2 * bm + 4, 2 * bn, 64), (3 * bm - 16, bn + 4, 2 * bk), (1, 1, 1)]
+    for i, (M, N, K) in enumerate(shapes):
+        lab = f"ta t{tile} tb={trans_b} {(M, N, K)}"
+        A0, B0, C0 = uniform(M, N, K, 1300 + i)
+        A, B = stored(A0, B0, True, trans_b)
+        args = (True, trans_b)
+        check_op(A, B, C0, 0.5, -1.25, run_gpu_op(A, B, C0, 0.5, -1.25, *args, **kw), *args,
+                 oracle_mod, label=lab)
+        check_op(A, B, None, 1.0, 0.0, run_gpu_op(A, B, None, 1.0, 0.0, *args, **kw), *args,
+                 oracle_mod, label=lab + " b0")
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 1400 + i, True)
+        Ai, Bi = stored(Ai, Bi, True, trans_b)
+        check_op(Ai, Bi, Ci, 0.5, -1.25, run_gpu_op(Ai, Bi, Ci, 0.5, -1.25, *args, **kw), *args,
+                 oracle_mod, exact=True, label=lab + " int")
+        check_op(Ai, Bi, Ci, 0.5, -1.25,
+                 run_gpu_op(Ai, Bi, Ci, 0.5, -1.25, *args, flags=sg.FLAG_SCALAR_IO, **kw),
+                 *args, oracle_mod, exact=True, label=lab + " int scalar")
+    # A stored K x M inside wider rows (lda = M + 3 and M + 4); NaN padding must not leak
+    rng = np.random.default_rng(tile)
+    for M, N, K, pad in ((bm + 7, bn + 9, 40, 3), (2 * bm, bn, 2 * bk, 4)):
+        At = rng.uniform(-1, 1, (K, M)).astype(F32)
+        B = rng.uniform(-1, 1, (N, K) if trans_b else (K, N)).astype(F32)
+        As = torch.full((K, M + pad), float("nan"), device=DEV)
+        As[:, :M] = dev(At)
+        C = torch.full((M, N), float("nan"), device=DEV)
+        sg.gemm(As[:, :M], dev(B), C, 1.0, 0.0, trans_a=True, trans_b=trans_b, **kw)
+        torch.cuda.synchronize()
+        check_op(At, B, None, 1.0, 0.0, C.cpu().numpy(), True, trans_b, oracle_mod,
+                 label=f"ta t{tile} tb={trans_b} padded {pad}")
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("shape", [(4096, 4096, 4096), (4097, 1000, 3001), (300, 257, 129),
+                                   (64, 64, 64)])
+def test_transposed_a_automatic(shape, trans_b, oracle_mod):
+    """Automatic dispatch of C = A^T B and C = A^T B^T (A stored K x M) at
+    benchmark and ragged sizes, sampled rows against the oracle; integer
+    inputs bit-exact."""
+    M, N, K = shape
+    A, B, C0 = workloads.draw(M, N, K, "int4", 1500, True)
+    As, Bs = stored(A, B, True, trans_b)
+    dA, dB, dC = dev(As), dev(Bs), dev(C0)
+    sg.gemm(dA, dB, dC, 0.5, -1.25, trans_a=True, trans_b=trans_b)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 24)
+    got = dC.cpu().numpy()[rows]
+    ref = oracle_mod.sgemm(np.ascontiguousarray(As[:, rows]), Bs, np.ascontiguousarray(C0[rows]),
+                           0.5, -1.25, trans_a=True, trans_b=trans_b)
+    assert np.array_equal(got, ref), f"transposed A {shape} trans_b={trans_b}"
+
+
 SKINNY_CASES = {
     0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
     1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],
@@ -370,10 +476,16 @@ def test_valu_family_full_size(oracle_mod):
 
 
 def test_integer_full_size_every_mfma_tile(oracle_mod):
+    """Every MFMA tile at 4096^3 (the transposed-A tiles on A stored K x M)."""
     A, B, C0 = workloads.inputs("int4096_blas")
     rows = sample_rows(4096, 24)
+    At = np.ascontiguousarray(A.T)
     for tile in tiles(sg.VARIANT_MFMA):
-        C = run_gpu(A, B, C0, 0.5, -1.25, variant=sg.VARIANT_MFMA, tile=tile)
+        kw = dict(variant=sg.VARIANT_MFMA, tile=tile)
+        if sg.tile_info(sg.VARIANT_MFMA, tile)["flags"] & sg.TILE_TRANS_A:
+            C = run_gpu_op(At, B, C0, 0.5, -1.25, True, False, **kw)
+        else:
+            C = run_gpu(A, B, C0, 0.5, -1.25, **kw)
         check(A, B, C0, 0.5, -1.25, C, oracle_mod, rows=rows, exact=True, label=f"tile {tile}")
 
 
