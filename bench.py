@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 MFMA, 2 VALU, 3 skinny")
     ap.add_argument("--tile", type=int, default=-1)
     ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--op", default="NN", choices=["NN", "NT", "TN", "TT"],
+                    help="storage of A and B: N as given, T transposed (sgemm_op)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -207,10 +209,15 @@ def headline(args):
     torch.cuda.set_device(0)
     # memory-bound workloads rotate over operand copies larger than the MALL
     sets = operand_sets(torch, w, A, B, C0, dev, rotate=(w.bound == "hbm"))
+    trans_a, trans_b = args.op[0] == "T", args.op[1] == "T"
+    if trans_a or trans_b:
+        # A stored K x M and/or B stored N x K
+        sets = [(a.t().contiguous() if trans_a else a, b.t().contiguous() if trans_b else b, c)
+                for a, b, c in sets]
     dA, dB, dC = sets[0]
-    kw = {}
+    kw = dict(trans_a=trans_a, trans_b=trans_b)
     if args.variant or args.tile >= 0 or args.group_m:
-        kw = dict(variant=args.variant, tile=args.tile, group_m=args.group_m)
+        kw.update(variant=args.variant, tile=args.tile, group_m=args.group_m)
     counter = [0]
 
     def call():
@@ -218,7 +225,8 @@ def headline(args):
         counter[0] += 1
         sg.gemm(a, b, c, w.alpha, w.beta, **kw)
 
-    chosen = sg.select(w.M, w.N, w.K, dA.data_ptr(), w.K, dB.data_ptr(), w.N, dC.data_ptr(), w.N)
+    chosen = sg.select(w.M, w.N, w.K, dA.data_ptr(), dA.stride(0), dB.data_ptr(), dB.stride(0),
+                       dC.data_ptr(), w.N, trans_a=trans_a, trans_b=trans_b)
     variant = args.variant or chosen.variant
     tile = args.tile if args.tile >= 0 else chosen.tile
     if args.variant and args.tile < 0:
@@ -254,7 +262,8 @@ def headline(args):
         "data": "synthetic",
         "pct_of_peak": round(100 * value / (PEAK_FP32_TFLOPS * 1e3), 2),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
-                   "beta": w.beta, "dist": w.dist, "seed": w.seed, "variant": variant,
+                   "beta": w.beta, "dist": w.dist, "seed": w.seed, "op": args.op,
+                   "variant": variant,
                    "tile": tile, "tile_desc": desc},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -343,7 +352,10 @@ def sweep_transposed(torch, sg, time_graph, w, operands):
         call_i = lambda i: sg.gemm(As, Bs, C, w.alpha, w.beta, trans_a=ta, trans_b=tb)
         med = statistics.median(time_graph(torch, call_i, 5)) / 1e3
         op = ("T" if ta else "N") + ("T" if tb else "N")
+        cfg = sg.select(w.M, w.N, w.K, As.data_ptr(), As.stride(0), Bs.data_ptr(), Bs.stride(0),
+                        C.data_ptr(), C.stride(0), trans_a=ta, trans_b=tb)
         row = {"workload": f"{w.name}_{op}", "M": w.M, "N": w.N, "K": w.K, "op": op,
+               "variant": cfg.variant, "tile": cfg.tile,
                "kernel_ms_median": round(med * 1e3, 4),
                "gflops": round(w.flops / med / 1e9, 1), "bound": w.bound,
                "pct_roofline": round(100 * w.flops / med / 1e9 / (PEAK_FP32_TFLOPS * 1e3), 2)}

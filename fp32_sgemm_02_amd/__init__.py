@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = [
-    "sgemm", "sgemm_ex", "sgemm_op", "gemm", "select", "tile_count", "tile_info", "status_string",
+    "sgemm", "sgemm_ex", "sgemm_op", "sgemm_cblas", "gemm", "select", "tile_count", "tile_info", "status_string",
     "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
     "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A",
@@ -78,6 +78,11 @@ def _load():
                                 ctypes.POINTER(SgemmConfig)]
     lib.sgemm_select.restype = i
     lib.sgemm_select.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_cblas.restype = i
+    lib.sgemm_cblas.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_op_plan.restype = i
+    lib.sgemm_op_plan.argtypes = [i, i, i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig),
+                                  ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.sgemm_plan.restype = i
     lib.sgemm_plan.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig),
                                ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -115,24 +120,33 @@ def sgemm_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, str
                                stream, ctypes.byref(cfg))
 
 
-def select(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None) -> SgemmConfig:
-    """The configuration sgemm() picks for this shape (and these addresses)."""
-    out = SgemmConfig()
-    st = _load().sgemm_select(M, N, K, A, lda or max(K, 1), B, ldb or max(N, 1), C,
-                              ldc or max(N, 1), ctypes.byref(out))
-    if st != 0:
-        raise SgemmError(st)
-    return out
+def sgemm_cblas(order, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                stream=None) -> int:
+    """Raw C-ABI call with cblas_sgemm's conventions (order 101 row-major /
+    102 column-major; trans 111 / 112 / 113)."""
+    return _load().sgemm_cblas(order, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                               ldc, stream)
 
 
-def plan(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None):
-    """(main-part configuration, edge rows, edge columns) of sgemm()'s
-    automatic plan for this shape (and these addresses)."""
+def select(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, *,
+           trans_a=False, trans_b=False) -> SgemmConfig:
+    """The configuration sgemm() (sgemm_op() with transposition flags) picks
+    for this shape (and these addresses); with edge strips, the main part's."""
+    return plan(M, N, K, A, lda, B, ldb, C, ldc, trans_a=trans_a, trans_b=trans_b)[0]
+
+
+def plan(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, *,
+         trans_a=False, trans_b=False):
+    """(main-part configuration, edge rows, edge columns) of the automatic
+    plan for this shape (and these addresses).  Leading dimensions default to
+    the tight ones of the stored operands."""
     out = SgemmConfig()
     rows, cols = ctypes.c_int(0), ctypes.c_int(0)
-    st = _load().sgemm_plan(M, N, K, A, lda or max(K, 1), B, ldb or max(N, 1), C,
-                            ldc or max(N, 1), ctypes.byref(out), ctypes.byref(rows),
-                            ctypes.byref(cols))
+    lda = lda or max(M if trans_a else K, 1)
+    ldb = ldb or max(K if trans_b else N, 1)
+    st = _load().sgemm_op_plan(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C,
+                               ldc or max(N, 1), ctypes.byref(out), ctypes.byref(rows),
+                               ctypes.byref(cols))
     if st != 0:
         raise SgemmError(st)
     return out, rows.value, cols.value

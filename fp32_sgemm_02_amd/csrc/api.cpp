@@ -21,6 +21,23 @@ constexpr int kVersion = 200;   // 0.2.0
 constexpr int kBadConfig = -13;
 constexpr int kBadTransA = -21;
 constexpr int kBadTransB = -22;
+constexpr int kBadOrder = -23;
+
+// A status of the row-major call that serves a column-major one (operands
+// swapped, M and N swapped), renamed after the caller's arguments.
+int colmajor_status(int st) {
+    switch (st) {
+    case -1: return -2;
+    case -2: return -1;
+    case -5: return -7;
+    case -6: return -8;
+    case -7: return -5;
+    case -8: return -6;
+    case kBadTransA: return kBadTransB;
+    case kBadTransB: return kBadTransA;
+    default: return st;
+    }
+}
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -332,13 +349,17 @@ int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, cons
     return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, cfg, trans_a, trans_b);
 }
 
-int sgemm_plan(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-               const float *C, int ldc, sgemm_config *out, int *edge_rows, int *edge_cols) {
+int sgemm_op_plan(int trans_a, int trans_b, int M, int N, int K, const float *A, int lda,
+                  const float *B, int ldb, const float *C, int ldc, sgemm_config *out,
+                  int *edge_rows, int *edge_cols) {
     if (!out) return -14;
+    if (trans_a != 0 && trans_a != 1) return sg::kBadTransA;
+    if (trans_b != 0 && trans_b != 1) return sg::kBadTransB;
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
-    const sg::Problem p{M, N, K, 1.f, 0.f, A, lda, B, ldb, const_cast<float *>(C), ldc};
+    const sg::Problem p{M,   N,   K, 1.f, 0.f, A, lda, B, ldb, const_cast<float *>(C),
+                        ldc, trans_a, trans_b};
     sg::Choice ch;
     sg::Strips sp{0, 0};
     const int st = sg::resolve(p, nullptr, ch, &sp);
@@ -350,6 +371,27 @@ int sgemm_plan(int M, int N, int K, const float *A, int lda, const float *B, int
     if (edge_rows) *edge_rows = sp.rows;
     if (edge_cols) *edge_cols = sp.cols;
     return 0;
+}
+
+int sgemm_plan(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+               const float *C, int ldc, sgemm_config *out, int *edge_rows, int *edge_cols) {
+    return sgemm_op_plan(0, 0, M, N, K, A, lda, B, ldb, C, ldc, out, edge_rows, edge_cols);
+}
+
+int sgemm_cblas(int order, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                const float *A, int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                hipStream_t stream) {
+    auto op = [](int t) { return t == 111 ? 0 : (t == 112 || t == 113) ? 1 : -1; };
+    const int ta = op(trans_a), tb = op(trans_b);
+    if (order != 101 && order != 102) return sg::kBadOrder;
+    if (ta < 0) return sg::kBadTransA;
+    if (tb < 0) return sg::kBadTransB;
+    if (order == 101)
+        return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr, ta, tb);
+    // column-major C = op(A) op(B) is row-major C^T = op(B)^T op(A)^T over the
+    // same memory: B's storage takes A's place and the transposition flags carry over
+    const int st = sg::run(N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream, nullptr, tb, ta);
+    return sg::colmajor_status(st);
 }
 
 int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -385,8 +427,9 @@ const char *sgemm_status_string(int status) {
     case -11: return "invalid argument 11 (ldc < max(1, N))";
     case -13: return "invalid or inapplicable configuration";
     case -14: return "null output pointer";
-    case -21: return "invalid trans_a (0 or 1)";
-    case -22: return "invalid trans_b (0 or 1)";
+    case -21: return "invalid trans_a (0 or 1; CBLAS: 111, 112 or 113)";
+    case -22: return "invalid trans_b (0 or 1; CBLAS: 111, 112 or 113)";
+    case -23: return "invalid order (CBLAS: 101 row-major or 102 column-major)";
     default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -43,7 +43,9 @@
  *     -13               sgemm_ex: the configuration is invalid or does not
  *                       apply to this shape (see sgemm_config); sgemm_op:
  *                       no compiled kernel serves this transposition
- *     -21, -22          sgemm_op: trans_a, trans_b not 0 or 1
+ *     -21, -22          sgemm_op: trans_a, trans_b not 0 or 1 (sgemm_cblas:
+ *                       not 111, 112 or 113)
+ *     -23               sgemm_cblas: order not 101 or 102
  *     > 0               a hipError_t reported by the kernel launch
  * No C++ exception crosses this interface.
  *
@@ -171,6 +173,30 @@ int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const f
 int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
                 int lda, const float *B, int ldb, float beta, float *C, int ldc,
                 hipStream_t stream, const sgemm_config *cfg);
+
+/*
+ * sgemm_cblas: the same product with the argument conventions of
+ * cblas_sgemm: order 101 (row-major) or 102 (column-major), trans_a and
+ * trans_b 111 (no transpose), 112 (transpose) or 113 (conjugate transpose,
+ * the same for real matrices), then M, N, K, alpha, A, lda, B, ldb, beta, C,
+ * ldc and the stream.  Row-major calls are sgemm_op; a column-major call runs
+ * as the row-major product C^T = op(B)^T op(A)^T over the same memory (no
+ * copy).  Leading dimensions follow the order: column-major A (no transpose)
+ * needs lda >= max(1, M), and so on.  Status codes as sgemm_op's, naming the
+ * caller's arguments (-1 M, -2 N, -5 A, -6 lda, -7 B, -8 ldb, -21 trans_a,
+ * -22 trans_b ...), and -23 for an order other than 101 or 102.
+ */
+int sgemm_cblas(int order, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                const float *A, int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                hipStream_t stream);
+
+/*
+ * sgemm_op_plan: sgemm_plan for sgemm_op's transposition flags (0 or 1; -21 /
+ * -22 otherwise).  Transposed problems get no edge strips.
+ */
+int sgemm_op_plan(int trans_a, int trans_b, int M, int N, int K, const float *A, int lda,
+                  const float *B, int ldb, const float *C, int ldc, sgemm_config *out,
+                  int *edge_rows, int *edge_cols);
 
 /*
  * sgemm_plan: sgemm_select plus the edge strips of the automatic plan.  When

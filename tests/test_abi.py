@@ -225,3 +225,54 @@ def test_automatic_selection():
     d = sg.tile_info(cfg.variant, cfg.tile)
     assert cfg.flags & sg.FLAG_SCALAR_IO or d["flags"] & sg.TILE_DIRECT
     assert sg.select(256, 256, 256, 0x10000, 256, 0x20000, 256, 0x30000, 256).flags == 0
+
+
+def test_cblas_entry_point_validation():
+    """sgemm_cblas takes cblas_sgemm's enumerations and names the caller's
+    arguments in its status codes, also for column-major calls (which run as
+    the row-major product with the operands swapped)."""
+    good = 0x10000
+    cb = sg.sgemm_cblas
+    RM, CM, NT, T, CT = 101, 102, 111, 112, 113
+    assert cb(100, NT, NT, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -23
+    assert cb(RM, 0, NT, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -21
+    assert cb(CM, NT, 1, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -22
+    for order in (RM, CM):
+        assert cb(order, NT, NT, -1, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -1
+        assert cb(order, NT, NT, 4, -1, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -2
+        assert cb(order, NT, NT, 4, 4, -1, 1.0, good, 4, good, 4, 0.0, good, 4) == -3
+        assert cb(order, T, CT, 4, 4, 4, 1.0, None, 4, good, 4, 0.0, good, 4) == -5
+        assert cb(order, NT, NT, 4, 4, 4, 1.0, good, 4, None, 4, 0.0, good, 4) == -7
+        assert cb(order, NT, NT, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, None, 4) == -10
+    # column-major A (M x K, no transpose) needs lda >= M; row-major needs lda >= K
+    assert cb(CM, NT, NT, 8, 4, 2, 1.0, good, 4, good, 8, 0.0, good, 8) == -6
+    assert cb(CM, NT, NT, 8, 4, 2, 1.0, good, 8, good, 1, 0.0, good, 8) == -8
+    assert cb(CM, NT, NT, 8, 4, 2, 1.0, good, 8, good, 2, 0.0, good, 4) == -11
+    assert cb(CM, T, NT, 8, 4, 2, 1.0, good, 1, good, 2, 0.0, good, 8) == -6
+    assert cb(CM, NT, T, 8, 4, 2, 1.0, good, 8, good, 2, 0.0, good, 8) == -8
+    # quick returns need no kernel
+    for order in (RM, CM):
+        assert cb(order, T, T, 0, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == 0
+        assert cb(order, NT, T, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, good, 4) == 0
+
+
+def test_op_plan_covers_transpositions():
+    """The automatic plan of a transposed product names a tile that serves
+    that transposition, with no edge strips."""
+    for ta, tb in ((0, 1), (1, 0), (1, 1)):
+        for M, N, K in ((4096, 4096, 4096), (4097, 1000, 3001), (37, 45, 5), (1, 4096, 4096)):
+            cfg, rows, cols = sg.plan(M, N, K, 0x10000, None, 0x10000, None, 0x10000, None,
+                                      trans_a=ta, trans_b=tb)
+            assert cfg.variant == sg.VARIANT_MFMA and (rows, cols) == (0, 0)
+            f = sg.tile_info(sg.VARIANT_MFMA, cfg.tile)["flags"]
+            assert bool(f & sg.TILE_TRANS_A) == bool(ta), (ta, tb, M, N, K)
+            if tb:
+                assert f & sg.TILE_TRANS_B
+    a, b = sg.plan(64, 64, 64, trans_a=False), sg.plan(64, 64, 64)
+    assert (a[0].variant, a[0].tile, a[1:]) == (b[0].variant, b[0].tile, b[1:])
+    out = sg.SgemmConfig()
+    lib = sg._load()
+    assert lib.sgemm_op_plan(2, 0, 4, 4, 4, None, 4, None, 4, None, 4, ctypes.byref(out),
+                             None, None) == -21
+    assert lib.sgemm_op_plan(0, 5, 4, 4, 4, None, 4, None, 4, None, 4, ctypes.byref(out),
+                             None, None) == -22

@@ -412,6 +412,41 @@ def test_transposed_a_automatic(shape, trans_b, oracle_mod):
     assert np.array_equal(got, ref), f"transposed A {shape} trans_b={trans_b}"
 
 
+# ------------------------------------------------------- CBLAS order --
+@pytest.mark.parametrize("order", [101, 102])
+@pytest.mark.parametrize("ta,tb", [(111, 111), (111, 112), (112, 111), (113, 113)])
+def test_cblas_orders(order, ta, tb, oracle_mod):
+    """sgemm_cblas in both storage orders and every transposition: the stored
+    matrices are built from the logical A (M x K), B (K x N), C (M x N) and
+    the result read back through the same order; integer inputs bit-exact."""
+    def store(X, trans):
+        # the matrix the caller stores (X, or X^T when trans) in the given
+        # order, as a row-major array, and its leading dimension
+        S = X.T if trans else X
+        S = S if order == 101 else S.T
+        S = np.ascontiguousarray(S)
+        return S, S.shape[1]
+
+    for i, (M, N, K) in enumerate(((300, 257, 129), (1000, 777, 333), (64, 64, 64), (1, 1, 1),
+                                   (5, 3, 4100))):
+        for dist in ("uniform", "int4"):
+            A, B, C0 = workloads.draw(M, N, K, dist, 1600 + i, True)
+            As, lda = store(A, ta != 111)
+            Bs, ldb = store(B, tb != 111)
+            Cs, ldc = store(C0, False)
+            dA, dB, dC = dev(As), dev(Bs), dev(Cs)
+            torch.cuda.synchronize()
+            st = sg.sgemm_cblas(order, ta, tb, M, N, K, 0.5, dA.data_ptr(), lda, dB.data_ptr(),
+                                ldb, -1.25, dC.data_ptr(), ldc,
+                                torch.cuda.current_stream().cuda_stream)
+            assert st == 0, sg.status_string(st)
+            torch.cuda.synchronize()
+            got = dC.cpu().numpy()
+            got = got if order == 101 else np.ascontiguousarray(got.T)
+            lab = f"cblas order={order} {ta}/{tb} {(M, N, K)} {dist}"
+            check(A, B, C0, 0.5, -1.25, got, oracle_mod, exact=(dist == "int4"), label=lab)
+
+
 SKINNY_CASES = {
     0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
     1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],
