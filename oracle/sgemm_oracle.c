@@ -38,12 +38,40 @@
  * a row of B.  Rows of C are split into contiguous bands, one POSIX thread per
  * band; each cell is produced by exactly one thread, in the same order, so the
  * result does not depend on the thread count.
+ *
+ * Two extensions for the workloads the pages name next to the GEMM ("The GEMM
+ * Scrapbook", introduction: attention projections and the two GEMMs of a
+ * feed-forward block), each the plain definition written out:
+ *   - oracle_sgemm_strided_batched: `batch` independent products, operand b at
+ *     A + b*stride_a, B + b*stride_b, C + b*stride_c (a stride of 0 shares
+ *     one A or B across the batch); batch 0 touches nothing.
+ *   - oracle_sgemm_epilogue: C = act(alpha * op(A) op(B) + beta * C + bias),
+ *     bias[j] added to every cell of column j (the bias of a linear layer
+ *     over its output features), act applied in double to the finished sum,
+ *     then one rounding to float.  The pages name no activation; the codes
+ *     are: 0 none, 1 ReLU max(x, 0), 2 SiLU x / (1 + e^-x) (Elfwing et al.,
+ *     "Sigmoid-weighted linear units", 2018), 3 GELU x * Phi(x), Phi the
+ *     standard normal CDF, 4 GELU's tanh approximation
+ *     x/2 * (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (both from Hendrycks
+ *     and Gimpel, "Gaussian error linear units", 2016).  Phi(x) is evaluated
+ *     as erfc(-x / sqrt 2) / 2 and (1 + tanh u) / 2 as 1 / (1 + e^(-2u)),
+ *     identities that avoid the cancellation of 1 + erf and 1 + tanh for
+ *     negative x.  With alpha == 0 or K == 0 the sum is beta * C + bias (A
+ *     and B not read).
  */
+#include <math.h>
 #include <pthread.h>
 #include <stdlib.h>
 #include <stddef.h>
 
-#define ORACLE_VERSION 2
+#define ORACLE_VERSION 3
+
+/* activation codes of oracle_sgemm_epilogue */
+#define ORACLE_ACT_NONE 0
+#define ORACLE_ACT_RELU 1
+#define ORACLE_ACT_SILU 2
+#define ORACLE_ACT_GELU_ERF 3
+#define ORACLE_ACT_GELU_TANH 4
 
 typedef struct {
     int i0, i1;          /* band of rows [i0, i1) */
@@ -52,8 +80,33 @@ typedef struct {
     const float *A; long long a_row, a_col;   /* op(A)(i,k) = A[i*a_row + k*a_col] */
     const float *B; long long b_row, b_col;   /* op(B)(k,j) = B[k*b_row + j*b_col] */
     float *C;       long long ldc;
+    const float *bias;   /* per column of C, or NULL */
+    int act;             /* ORACLE_ACT_* */
     int status;
 } band_t;
+
+/* The activation of the finished sum, in double. */
+static double activate(int act, double x)
+{
+    switch (act) {
+    case ORACLE_ACT_RELU: return x < 0.0 ? 0.0 : x;
+    case ORACLE_ACT_SILU: return x / (1.0 + exp(-x));
+    case ORACLE_ACT_GELU_ERF: return 0.5 * x * erfc(-x / sqrt(2.0));
+    case ORACLE_ACT_GELU_TANH: {
+        const double pi = 3.14159265358979323846;
+        const double u = sqrt(2.0 / pi) * (x + 0.044715 * x * x * x);
+        return x / (1.0 + exp(-2.0 * u));
+    }
+    default: return x;
+    }
+}
+
+/* The epilogue of one cell: bias and activation of the finished sum. */
+static float finish(const band_t *b, int j, double out)
+{
+    if (b->bias) out += (double)b->bias[j];
+    return (float)activate(b->act, out);
+}
 
 /* C(i,:) for every i in the band. */
 static void *run_band(void *arg)
@@ -67,7 +120,7 @@ static void *run_band(void *arg)
         if (b->alpha == 0.0 || K == 0) {
             /* C = beta * C; A and B are not read. */
             for (int j = 0; j < N; ++j)
-                crow[j] = (b->beta == 0.0) ? 0.0f : (float)(b->beta * (double)crow[j]);
+                crow[j] = finish(b, j, (b->beta == 0.0) ? 0.0 : b->beta * (double)crow[j]);
             continue;
         }
         for (int j = 0; j < N; ++j) acc[j] = 0.0;
@@ -82,7 +135,7 @@ static void *run_band(void *arg)
             double out = b->alpha * acc[j];
             if (b->beta != 0.0)
                 out += b->beta * (double)crow[j];
-            crow[j] = (float)out;
+            crow[j] = finish(b, j, out);
         }
     }
     free(acc);
@@ -93,14 +146,11 @@ static void *run_band(void *arg)
 int oracle_version(void) { return ORACLE_VERSION; }
 
 /*
- * C = alpha * op(A) * op(B) + beta * C with op(A) M x K and op(B) K x N.
- * Returns 0 on success; -i when the i-th argument is invalid (1-based, in the
- * order of the parameter list); -100 when memory for the row accumulators or
- * threads could not be obtained.  nthreads <= 0 means one thread.
+ * Argument checks of oracle_sgemm_op, numbered in its parameter list:
+ * 0 when every argument is valid.
  */
-int oracle_sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
-                    const float *A, int lda, const float *B, int ldb,
-                    float beta, float *C, int ldc, int nthreads)
+static int check_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                    const float *A, int lda, const float *B, int ldb, const float *C, int ldc)
 {
     if (trans_a != 0 && trans_a != 1) return -1;
     if (trans_b != 0 && trans_b != 1) return -2;
@@ -116,7 +166,15 @@ int oracle_sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
     if (reads_ab && !A) return -7;
     if (reads_ab && !B) return -9;
     if (!C) return -12;
+    return 0;
+}
 
+/* One product over valid arguments (checked by the caller). */
+static int sgemm_core(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb,
+                      float beta, float *C, int ldc, const float *bias, int act, int nthreads)
+{
+    if (M == 0 || N == 0) return 0;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > M) nthreads = M;
 
@@ -134,6 +192,7 @@ int oracle_sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
         b->A = A; b->a_row = trans_a ? 1 : lda; b->a_col = trans_a ? lda : 1;
         b->B = B; b->b_row = trans_b ? 1 : ldb; b->b_col = trans_b ? ldb : 1;
         b->C = C; b->ldc = ldc;
+        b->bias = bias; b->act = act;
         b->status = -100;
     }
     int status = 0;
@@ -148,6 +207,71 @@ int oracle_sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
         if (bands[t].status != 0) status = bands[t].status;
     free(bands); free(tids); free(started);
     return status;
+}
+
+/*
+ * C = alpha * op(A) * op(B) + beta * C with op(A) M x K and op(B) K x N.
+ * Returns 0 on success; -i when the i-th argument is invalid (1-based, in the
+ * order of the parameter list); -100 when memory for the row accumulators or
+ * threads could not be obtained.  nthreads <= 0 means one thread.
+ */
+int oracle_sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                    const float *A, int lda, const float *B, int ldb,
+                    float beta, float *C, int ldc, int nthreads)
+{
+    const int st = check_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != 0) return st;
+    return sgemm_core(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, NULL,
+                      ORACLE_ACT_NONE, nthreads);
+}
+
+/*
+ * C = act(alpha * op(A) * op(B) + beta * C + bias): oracle_sgemm_op's
+ * arguments, then bias (N floats, one per column of C; NULL for none) and act
+ * (an ORACLE_ACT_* code).  Returns as oracle_sgemm_op, and -15 for an unknown
+ * act.
+ */
+int oracle_sgemm_epilogue(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                          const float *A, int lda, const float *B, int ldb,
+                          float beta, float *C, int ldc, const float *bias, int act,
+                          int nthreads)
+{
+    const int st = check_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != 0) return st;
+    if (act < ORACLE_ACT_NONE || act > ORACLE_ACT_GELU_TANH) return -15;
+    return sgemm_core(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                      nthreads);
+}
+
+/*
+ * `batch` products C_b = alpha * op(A_b) * op(B_b) + beta * C_b, with
+ * A_b = A + b*stride_a, B_b = B + b*stride_b, C_b = C + b*stride_c (floats).
+ * Arguments, 1-based: trans_a, trans_b, M, N, K, alpha, A, lda, stride_a, B,
+ * ldb, stride_b, beta, C, ldc, stride_c, batch, nthreads.  Returns 0, or -i
+ * for an invalid i-th argument: a negative stride of A or B, a stride of C
+ * that lets two of the batch's C matrices overlap (stride_c < (M-1)*ldc + N
+ * with batch > 1), a negative batch, or any check of oracle_sgemm_op.
+ */
+int oracle_sgemm_strided_batched(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                                 const float *A, int lda, long long stride_a,
+                                 const float *B, int ldb, long long stride_b,
+                                 float beta, float *C, int ldc, long long stride_c,
+                                 int batch, int nthreads)
+{
+    static const int renumber[14] = {0, -1, -2, -3, -4, -5, -6, -7, -8, -10, -11, 0, -14, -15};
+    const int st = check_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (st != 0) return renumber[-st];
+    if (stride_a < 0) return -9;
+    if (stride_b < 0) return -12;
+    if (batch < 0) return -17;
+    if (batch > 1 && M > 0 && N > 0 && stride_c < (long long)(M - 1) * ldc + N) return -16;
+    for (int b = 0; b < batch; ++b) {
+        const int r = sgemm_core(trans_a, trans_b, M, N, K, alpha, A ? A + b * stride_a : A, lda,
+                                 B ? B + b * stride_b : B, ldb, beta, C + b * stride_c, ldc, NULL,
+                                 ORACLE_ACT_NONE, nthreads);
+        if (r != 0) return r;
+    }
+    return 0;
 }
 
 /* The untransposed product, with the argument numbering of its own list. */

@@ -21,6 +21,16 @@ test_oracle.py).  The pins are:
                 every combination of transposed storage, a permutation stored
                 transposed, padded rows of transposed operands, and the
                 argument checks of the transposed leading dimensions.
+  epilogue      (entry point with bias and activation) every cell against the
+                activation of the exact rational sum plus bias, evaluated at
+                40 significant digits (mpmath; GELU through mpmath's normal
+                CDF, its tanh form and SiLU as printed in their papers) and
+                rounded to fp32: within one fp32 ulp; ReLU and bias exact on
+                integers; the alpha = 0 path; act codes checked.
+  batched       (strided-batched entry point) exact rational brute force on
+                every matrix of a batch with padded, shared (stride 0) and
+                transposed operands; batch = 0 touches nothing; stride and
+                batch checks.
 
 The definition pinned: C = alpha * (A * B) + beta * C, each cell a dot product
 of a row of A and a column of B ("a CUDA matmul" section 00; "The GEMM
@@ -30,6 +40,7 @@ from __future__ import annotations
 
 from fractions import Fraction
 
+import mpmath
 import numpy as np
 
 F32 = np.float32
@@ -271,10 +282,12 @@ def pin_transposed(call_op, rng, dims=range(1, 4), square_only=False) -> list[st
     return fails
 
 
-def all_pins(call, seed=1234, square_only=False, call_op=None) -> list[str]:
+def all_pins(call, seed=1234, square_only=False, call_op=None, call_epi=None,
+             call_batched=None) -> list[str]:
     """Every pin; square_only restricts brute force to M = N = K (used for
     broken copies whose indexing is only memory-safe on square shapes).
-    call_op, when given, is the entry point with transposed operands."""
+    call_op, call_epi, call_batched, when given, are the entry points with
+    transposed operands, with bias and activation, and strided-batched."""
     rng = np.random.default_rng(seed)
     fails = []
     if square_only:
@@ -288,6 +301,10 @@ def all_pins(call, seed=1234, square_only=False, call_op=None) -> list[str]:
     fails += pin_ld_padding(call, rng)
     if call_op is not None:
         fails += pin_transposed(call_op, rng)
+    if call_epi is not None:
+        fails += pin_epilogue(call_epi, rng)
+    if call_batched is not None:
+        fails += pin_batched(call_batched, rng)
     return fails
 
 
@@ -302,4 +319,203 @@ def _square_brute(call, rng) -> list[str]:
                 ex, mag = exact_cell(A, B, None, i, j, 1.0, 0.0)
                 if st or not within_fp64_rounding(float(C[i, j]), ex, mag, n):
                     fails.append(f"square brute {n} {(i, j)}")
+    return fails
+
+
+# ------------------------------------------------------------- epilogue --
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3, 4
+
+
+def act_exact(act: int, x: Fraction) -> float:
+    """The activation of an exact rational, at 40 digits, rounded to fp32."""
+    if act == ACT_NONE:
+        return rn32(x)
+    if act == ACT_RELU:
+        return rn32(max(x, Fraction(0)))
+    with mpmath.workdps(40):
+        v = mpmath.mpf(x.numerator) / x.denominator
+        if act == ACT_SILU:
+            y = v / (1 + mpmath.exp(-v))
+        elif act == ACT_GELU_ERF:
+            y = v * mpmath.ncdf(v)
+        elif act == ACT_GELU_TANH:
+            u = mpmath.sqrt(2 / mpmath.pi) * (v + mpmath.mpf("0.044715") * v ** 3)
+            # 1 + tanh(u) loses about 2|u| / ln 10 digits to cancellation for
+            # u < 0: evaluate the printed form with that many digits more
+            with mpmath.workdps(40 + int(2 * abs(u) / mpmath.log(10)) + 10):
+                v = mpmath.mpf(x.numerator) / x.denominator
+                u = mpmath.sqrt(2 / mpmath.pi) * (v + mpmath.mpf("0.044715") * v ** 3)
+                y = v / 2 * (1 + mpmath.tanh(u))
+        else:
+            raise ValueError(act)
+        m, e = mpmath.frexp(y)
+        return rn32(Fraction(int(mpmath.nint(m * 2 ** 80))) * Fraction(2) ** (int(e) - 80))
+
+
+def ulp32(x: float) -> float:
+    x = abs(np.float32(x))
+    return float(np.nextafter(x, F32(np.inf)) - x)
+
+
+def run_epi(call_epi, ta, tb, A, B, C0, alpha, beta, bias, act):
+    """The epilogue entry point on logical A (M x K), B (K x N); bias is passed
+    inside a longer buffer (so that a reading past N stays in memory)."""
+    M, K = A.shape
+    N = B.shape[1]
+    As = np.ascontiguousarray(A.T if ta else A, dtype=F32)
+    Bs = np.ascontiguousarray(B.T if tb else B, dtype=F32)
+    C = (np.ascontiguousarray(C0, dtype=F32).copy() if C0 is not None
+         else np.full((M, N), np.nan, dtype=F32))
+    buf = None
+    if bias is not None:
+        buf = np.concatenate([bias.astype(F32), np.full(M + 8, 1000.0, F32)])
+    st = call_epi(int(ta), int(tb), M, N, K, alpha, As.reshape(-1), max(As.shape[1], 1),
+                  Bs.reshape(-1), max(Bs.shape[1], 1), beta, C.reshape(-1), max(N, 1), buf, act)
+    return st, C
+
+
+def pin_epilogue(call_epi, rng, dims=range(1, 4)) -> list[str]:
+    fails = []
+    for M in dims:
+        for N in dims:
+            for K in dims:
+                A = rng.uniform(-2, 2, (M, K)).astype(F32)
+                B = rng.uniform(-2, 2, (K, N)).astype(F32)
+                C0 = rng.uniform(-2, 2, (M, N)).astype(F32)
+                bias = rng.uniform(-2, 2, N).astype(F32)
+                alpha, beta = float(F32(rng.uniform(-3, 3))), float(F32(rng.uniform(-3, 3)))
+                ta, tb = int(rng.integers(2)), int(rng.integers(2))
+                for act in range(5):
+                    for bz in (bias, None):
+                        st, C = run_epi(call_epi, ta, tb, A, B, C0, alpha, beta, bz, act)
+                        if st != 0:
+                            fails.append(f"epilogue status {st} at {(M, N, K, act)}")
+                            continue
+                        bad = False
+                        for i in range(M):
+                            for j in range(N):
+                                x, _ = exact_cell(A, B, C0, i, j, alpha, beta)
+                                if bz is not None:
+                                    x += Fraction(float(bz[j]))
+                                ref = act_exact(act, x)
+                                if abs(float(C[i, j]) - ref) > ulp32(ref) or \
+                                        (ref == 0.0) != (float(C[i, j]) == 0.0):
+                                    fails.append(f"epilogue act={act} bias={bz is not None} "
+                                                 f"{(M, N, K)} cell {(i, j)}: {C[i, j]!r} vs "
+                                                 f"{ref!r}")
+                                    bad = True
+                                    break
+                            if bad:
+                                break
+    # integers: ReLU and bias are exact, bias goes along columns
+    M, N, K = 5, 7, 6
+    A = rng.integers(-4, 5, (M, K)).astype(F32)
+    B = rng.integers(-4, 5, (K, N)).astype(F32)
+    C0 = rng.integers(-4, 5, (M, N)).astype(F32)
+    bias = rng.integers(-20, 21, N).astype(F32)
+    exact = (A.astype(np.int64) @ B.astype(np.int64)) * 2 - C0.astype(np.int64) + \
+        bias.astype(np.int64)[None, :]
+    st, C = run_epi(call_epi, 0, 0, A, B, C0, 2.0, -1.0, bias, ACT_RELU)
+    if st or not np.array_equal(C, np.maximum(exact, 0).astype(F32)):
+        fails.append("epilogue integer relu+bias")
+    st, C = run_epi(call_epi, 1, 1, A, B, C0, 2.0, -1.0, bias, ACT_NONE)
+    if st or not np.array_equal(C, exact.astype(F32)):
+        fails.append("epilogue integer bias (transposed storage)")
+    # alpha == 0: act(beta * C + bias) without reading A or B
+    An = np.full((M, K), np.nan, F32)
+    st, C = run_epi(call_epi, 0, 0, An, B, C0, 0.0, 0.5, bias, ACT_RELU)
+    if st or not np.array_equal(C, np.maximum(0.5 * C0 + bias[None, :], 0).astype(F32)):
+        fails.append("epilogue alpha0")
+    st, C = run_epi(call_epi, 0, 0, A, B, None, 0.0, 0.0, bias, ACT_NONE)
+    if st or not np.array_equal(C, np.broadcast_to(bias, (M, N))):
+        fails.append("epilogue alpha0 beta0")
+    # beta == 0 never reads C (NaN-filled C)
+    st, C = run_epi(call_epi, 0, 0, A, B, None, 1.0, 0.0, bias, ACT_SILU)
+    if st or not np.all(np.isfinite(C)):
+        fails.append("epilogue beta0 read C")
+    # act codes
+    if run_epi(call_epi, 0, 0, A, B, C0, 1.0, 0.0, bias, 5)[0] != -15 or \
+            run_epi(call_epi, 0, 0, A, B, C0, 1.0, 0.0, bias, -1)[0] != -15:
+        fails.append("epilogue act code check")
+    return fails
+
+
+# -------------------------------------------------------------- batched --
+def pin_batched(call_batched, rng) -> list[str]:
+    """call_batched(ta, tb, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C,
+    ldc, sc, batch) on flat buffers."""
+    fails = []
+    for trial in range(12):
+        M, N, K = (int(v) for v in rng.integers(1, 4, 3))
+        batch = int(rng.integers(1, 4))
+        ta, tb = int(rng.integers(2)), int(rng.integers(2))
+        share_a, share_b = trial % 4 == 1, trial % 4 == 2
+        As = [rng.uniform(-2, 2, (M, K)).astype(F32) for _ in range(batch)]
+        Bs = [rng.uniform(-2, 2, (K, N)).astype(F32) for _ in range(batch)]
+        if share_a:
+            As = [As[0]] * batch
+        if share_b:
+            Bs = [Bs[0]] * batch
+        C0 = [rng.uniform(-2, 2, (M, N)).astype(F32) for _ in range(batch)]
+        alpha, beta = float(F32(rng.uniform(-3, 3))), float(F32(rng.uniform(-3, 3)))
+
+        def pack(mats, trans, pad_rows, pad_gap, share):
+            # stored matrices with padded rows, gap floats between batch entries
+            st = [np.ascontiguousarray(m.T if trans else m) for m in mats]
+            r, c = st[0].shape
+            ld = c + pad_rows
+            stride = 0 if share else r * ld + pad_gap
+            buf = np.full(max(stride * (len(st) - 1), 0) + r * ld + 1, np.nan, F32)
+            for b, m in enumerate(st[:1] if share else st):
+                for i in range(r):
+                    buf[b * stride + i * ld: b * stride + i * ld + c] = m[i]
+            return buf, max(ld, 1), stride
+
+        a, lda, sa = pack(As, ta, int(rng.integers(0, 3)), int(rng.integers(0, 4)), share_a)
+        b, ldb, sb = pack(Bs, tb, int(rng.integers(0, 3)), int(rng.integers(0, 4)), share_b)
+        ldc = N + int(rng.integers(0, 3))
+        sc = M * ldc + int(rng.integers(0, 4))
+        c = np.full(sc * batch + 4, 777.0, F32)
+        for bi in range(batch):
+            for i in range(M):
+                c[bi * sc + i * ldc: bi * sc + i * ldc + N] = C0[bi][i]
+        st = call_batched(ta, tb, M, N, K, alpha, a, lda, sa, b, ldb, sb, beta, c, ldc, sc, batch)
+        if st != 0:
+            fails.append(f"batched status {st}")
+            continue
+        bad = False
+        for bi in range(batch):
+            for i in range(M):
+                row = c[bi * sc + i * ldc: bi * sc + i * ldc + ldc]
+                if np.any(row[N:] != 777.0):
+                    fails.append("batched C padding written")
+                    bad = True
+                for j in range(N):
+                    ex, mag = exact_cell(As[bi], Bs[bi], C0[bi], i, j, alpha, beta)
+                    if not within_fp64_rounding(float(row[j]), ex, mag, K):
+                        fails.append(f"batched {(ta, tb, M, N, K)} batch {bi} cell {(i, j)}")
+                        bad = True
+                        break
+                if bad:
+                    break
+            if bad:
+                break
+        if not bad and np.any(c[sc * batch:] != 777.0):
+            fails.append("batched wrote past the last C")
+    # batch = 0 touches nothing; argument checks (1-based positions)
+    buf = np.full(64, 5.0, F32)
+    if call_batched(0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 2, 4, 0.0, buf, 2, 4, 0) != 0 or \
+            np.any(buf != 5.0):
+        fails.append("batched batch 0")
+    checks = (((0, 0, 2, 2, 2, 1.0, buf, 2, -1, buf, 2, 4, 0.0, buf, 2, 4, 2), -9),
+              ((0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 2, -4, 0.0, buf, 2, 4, 2), -12),
+              ((0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 2, 4, 0.0, buf, 2, 3, 2), -16),
+              ((0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 2, 4, 0.0, buf, 2, 4, -1), -17),
+              ((0, 0, 2, 2, 2, 1.0, buf, 1, 4, buf, 2, 4, 0.0, buf, 2, 4, 2), -8),
+              ((0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 1, 4, 0.0, buf, 2, 4, 2), -11),
+              ((0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 2, 4, 0.0, buf, 1, 4, 2), -15),
+              ((0, 0, 2, 2, 2, 1.0, buf, 2, 4, buf, 2, 4, 0.0, None, 2, 4, 2), -14))
+    for args, code in checks:
+        if call_batched(*args) != code:
+            fails.append(f"batched check {code}")
     return fails

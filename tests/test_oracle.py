@@ -47,6 +47,37 @@ def _op_caller(lib, nthreads=1):
     return call_op
 
 
+def _epi_caller(lib, nthreads=1):
+    fn = lib.oracle_sgemm_epilogue
+    fn.restype = ctypes.c_int
+    i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    fn.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p, i, i]
+
+    def call_epi(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act):
+        q = lambda x: x.ctypes.data if (x is not None and x.size) else None
+        return fn(ta, tb, M, N, K, alpha, q(A), lda, q(B), ldb, beta, q(C), ldc, q(bias), act,
+                  nthreads)
+    return call_epi
+
+
+def _batched_caller(lib, nthreads=1):
+    fn = lib.oracle_sgemm_strided_batched
+    fn.restype = ctypes.c_int
+    i, f, p, ll = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_longlong
+    fn.argtypes = [i, i, i, i, i, f, p, i, ll, p, i, ll, f, p, i, ll, i, i]
+
+    def call_batched(ta, tb, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch):
+        q = lambda x: x.ctypes.data if (x is not None and x.size) else None
+        return fn(ta, tb, M, N, K, alpha, q(A), lda, sa, q(B), ldb, sb, beta, q(C), ldc, sc,
+                  batch, nthreads)
+    return call_batched
+
+
+def _callers(lib, nthreads=1):
+    return dict(call_op=_op_caller(lib, nthreads), call_epi=_epi_caller(lib, nthreads),
+                call_batched=_batched_caller(lib, nthreads))
+
+
 @pytest.fixture(scope="module")
 def call(oracle_mod):
     return _caller(ctypes.CDLL(oracle_mod._LIB), nthreads=3)
@@ -57,8 +88,8 @@ def call_op(oracle_mod):
     return _op_caller(ctypes.CDLL(oracle_mod._LIB), nthreads=2)
 
 
-def test_all_pins_pass(call, call_op):
-    assert all_pins(call, call_op=call_op) == []
+def test_all_pins_pass(call, oracle_mod):
+    assert all_pins(call, **_callers(ctypes.CDLL(oracle_mod._LIB), nthreads=2)) == []
 
 
 def test_transposed_storage_matches_explicit_transpose(oracle_mod):
@@ -196,10 +227,44 @@ MUTANTS = {
     # beta == 0 still reads C
     "beta0_reads_c": ("if (b->beta != 0.0)\n", "if (1)\n", False),
     # alpha == 0 path ignores beta
-    "alpha0_ignores_beta": ("(float)(b->beta * (double)crow[j]);", "crow[j];", False),
+    "alpha0_ignores_beta": ("(b->beta == 0.0) ? 0.0 : b->beta * (double)crow[j]);",
+                            "(b->beta == 0.0) ? 0.0 : (double)crow[j]);", False),
     # epilogue sign error on beta
     "beta_sign": ("out += b->beta * (double)crow[j];", "out -= b->beta * (double)crow[j];",
                   False),
+    # bias dropped
+    "bias_dropped": ("if (b->bias) out += (double)b->bias[j];", "if (0) out += 0.0;", False),
+    # bias taken per row instead of per column (the pins pad the bias buffer)
+    "bias_per_row": ("out += (double)b->bias[j];", "out += (double)b->bias[b->i0];", False),
+    # the activation applied before the bias
+    "act_before_bias": ("    if (b->bias) out += (double)b->bias[j];\n"
+                        "    return (float)activate(b->act, out);",
+                        "    out = activate(b->act, out);\n"
+                        "    if (b->bias) out += (double)b->bias[j];\n    return (float)out;",
+                        False),
+    # alpha == 0 path skips bias and activation
+    "alpha0_no_epilogue": ("crow[j] = finish(b, j, (b->beta == 0.0) ? 0.0 : "
+                           "b->beta * (double)crow[j]);",
+                           "crow[j] = (float)((b->beta == 0.0) ? 0.0 : "
+                           "b->beta * (double)crow[j]);", False),
+    # leaky instead of plain ReLU
+    "relu_leaky": ("return x < 0.0 ? 0.0 : x;", "return x < 0.0 ? 0.01 * x : x;", False),
+    # SiLU with the wrong sign in the exponent
+    "silu_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));", False),
+    # GELU without the 1/sqrt(2) scaling of the erf argument
+    "gelu_no_sqrt2": ("erfc(-x / sqrt(2.0))", "erfc(-x)", False),
+    # GELU tanh form with a perturbed cubic coefficient
+    "gelu_tanh_coeff": ("(x + 0.044715 * x * x * x)", "(x + 0.0447 * x * x * x)", False),
+    # GELU tanh form with the factor 2 of the exponent dropped
+    "gelu_tanh_half": ("return x / (1.0 + exp(-2.0 * u));", "return x / (1.0 + exp(-u));",
+                       False),
+    # the batch stride of A ignored
+    "batch_stride_a_ignored": ("A ? A + b * stride_a : A", "A", False),
+    # the batch stride of C ignored
+    "batch_stride_c_ignored": ("C + b * stride_c, ldc", "C, ldc", False),
+    # the last matrix of the batch skipped
+    "batch_last_skipped": ("for (int b = 0; b < batch; ++b)", "for (int b = 0; b + 1 < batch; ++b)",
+                           False),
 }
 
 
@@ -213,11 +278,49 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     so = tmp_path / f"{name}.so"
     c.write_text(mutated)
     subprocess.run(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-pthread",
-                    str(c), "-o", str(so)], check=True)
+                    str(c), "-o", str(so), "-lm"], check=True)
     lib = ctypes.CDLL(str(so))
-    fails = all_pins(_caller(lib), square_only=square_only, call_op=_op_caller(lib))
+    if square_only:
+        fails = all_pins(_caller(lib), square_only=True, call_op=_op_caller(lib))
+    else:
+        fails = all_pins(_caller(lib), **_callers(lib))
     if square_only:
         # the square subset must catch it; the full suite is not memory-safe here
         assert fails, f"mutant {name} passed every square pin"
     else:
         assert fails, f"mutant {name} passed every pin"
+
+
+def test_batched_wrapper_matches_float64_matmul(oracle_mod):
+    """The batched entry point at a moderate size against numpy's float64
+    batched matmul (a library routine): within one fp32 ulp per cell, with a
+    stacked A and a B shared by the batch."""
+    rng = np.random.default_rng(21)
+    A = rng.uniform(-1, 1, (5, 33, 40)).astype(F32)
+    B = rng.uniform(-1, 1, (40, 29)).astype(F32)
+    C0 = rng.uniform(-1, 1, (5, 33, 29)).astype(F32)
+    got = oracle_mod.sgemm_batched(A, B, C0.copy(), 0.75, -0.5)
+    ref = 0.75 * np.matmul(A.astype(np.float64), B.astype(np.float64)) - 0.5 * C0
+    ulp = np.spacing(np.abs(ref.astype(F32)))
+    assert np.all(np.abs(got - ref) <= ulp)
+    # transposed storage of both operands, per-batch B
+    Bt = rng.uniform(-1, 1, (5, 29, 40)).astype(F32)
+    At = np.ascontiguousarray(np.transpose(A, (0, 2, 1)))
+    got = oracle_mod.sgemm_batched(At, Bt, trans_a=True, trans_b=True)
+    ref = np.matmul(A.astype(np.float64), np.transpose(Bt, (0, 2, 1)).astype(np.float64))
+    assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref.astype(F32))))
+
+
+def test_epilogue_wrapper(oracle_mod):
+    """bias broadcast along rows and the activation codes, through the numpy
+    wrapper, against float64 numpy/scipy evaluations (within a few ulp)."""
+    from scipy.special import expit, ndtr
+    rng = np.random.default_rng(22)
+    A = rng.uniform(-1, 1, (17, 50)).astype(F32)
+    B = rng.uniform(-1, 1, (50, 23)).astype(F32)
+    bias = rng.uniform(-1, 1, 23).astype(F32)
+    x = A.astype(np.float64) @ B.astype(np.float64) + bias
+    refs = {0: x, 1: np.maximum(x, 0), 2: x * expit(x), 3: x * ndtr(x)}
+    for act, ref in refs.items():
+        got = oracle_mod.sgemm(A, B, bias=bias, act=act)
+        assert np.all(np.abs(got - ref) <= 2 * np.spacing(np.abs(ref.astype(F32))) + 1e-30), act
