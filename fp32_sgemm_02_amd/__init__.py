@@ -15,10 +15,12 @@ import ctypes
 import os
 
 __all__ = [
-    "sgemm", "sgemm_ex", "sgemm_op", "sgemm_cblas", "gemm", "select", "tile_count", "tile_info", "status_string",
+    "sgemm", "sgemm_ex", "sgemm_op", "sgemm_cblas", "sgemm_epilogue", "sgemm_strided_batched",
+    "gemm", "gemm_batched", "select", "tile_count", "tile_info", "status_string",
     "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
     "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A",
+    "ACT_NONE", "ACT_RELU", "ACT_SILU", "ACT_GELU_ERF", "ACT_GELU_TANH",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +33,7 @@ TILE_WHOLE = 0x1
 TILE_DIRECT = 0x2
 TILE_TRANS_B = 0x4
 TILE_TRANS_A = 0x8
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3, 4
 
 
 class SgemmConfig(ctypes.Structure):
@@ -78,6 +81,16 @@ def _load():
                                 ctypes.POINTER(SgemmConfig)]
     lib.sgemm_select.restype = i
     lib.sgemm_select.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig)]
+    ll = ctypes.c_longlong
+    lib.sgemm_epilogue.restype = i
+    lib.sgemm_epilogue.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p, i, p]
+    lib.sgemm_epilogue_ex.restype = i
+    lib.sgemm_epilogue_ex.argtypes = lib.sgemm_epilogue.argtypes + [ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_strided_batched.restype = i
+    lib.sgemm_strided_batched.argtypes = [i, i, i, i, i, f, p, i, ll, p, i, ll, f, p, i, ll, i, p]
+    lib.sgemm_strided_batched_ex.restype = i
+    lib.sgemm_strided_batched_ex.argtypes = (lib.sgemm_strided_batched.argtypes +
+                                             [ctypes.POINTER(SgemmConfig)])
     lib.sgemm_cblas.restype = i
     lib.sgemm_cblas.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_op_plan.restype = i
@@ -118,6 +131,26 @@ def sgemm_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, str
                                 stream)
     return _load().sgemm_op_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                stream, ctypes.byref(cfg))
+
+
+def sgemm_epilogue(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                   stream=None, cfg: SgemmConfig | None = None) -> int:
+    """Raw C-ABI call of sgemm_epilogue (cfg given: sgemm_epilogue_ex)."""
+    args = (trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
+    if cfg is None:
+        return _load().sgemm_epilogue(*args)
+    return _load().sgemm_epilogue_ex(*args, ctypes.byref(cfg))
+
+
+def sgemm_strided_batched(trans_a, trans_b, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b,
+                          beta, C, ldc, stride_c, batch, stream=None,
+                          cfg: SgemmConfig | None = None) -> int:
+    """Raw C-ABI call of sgemm_strided_batched (cfg given: the _ex form)."""
+    args = (trans_a, trans_b, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b, beta, C, ldc,
+            stride_c, batch, stream)
+    if cfg is None:
+        return _load().sgemm_strided_batched(*args)
+    return _load().sgemm_strided_batched_ex(*args, ctypes.byref(cfg))
 
 
 def sgemm_cblas(order, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
@@ -183,16 +216,33 @@ def _ld(t) -> int:
     return ld
 
 
+def _check_tensor(name, t, torch, device=None):
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _stream_handle(stream, device, torch):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
-         trans_b: bool = False, variant: int = VARIANT_AUTO, tile: int = -1, flags: int = 0,
-         group_m: int = 0, stream=None):
-    """C = alpha * op(A) @ op(B) + beta * C for 2-D float32 CUDA tensors
-    (row-major views with unit column stride; padded rows are used through
-    their leading dimension).  op(X) is X, or X transposed when trans_x: A is
-    then stored K x M and B N x K (e.g. a linear layer's weight, C = X W^T
-    with B = W, trans_b=True).  C is updated in place when given; otherwise a
-    new tensor is returned (beta must then be 0).  Runs asynchronously on
-    ``stream`` (default: the current stream of A's device)."""
+         trans_b: bool = False, bias=None, act: int = ACT_NONE, variant: int = VARIANT_AUTO,
+         tile: int = -1, flags: int = 0, group_m: int = 0, stream=None):
+    """C = act(alpha * op(A) @ op(B) + beta * C + bias) for 2-D float32 CUDA
+    tensors (row-major views with unit column stride; padded rows are used
+    through their leading dimension).  op(X) is X, or X transposed when
+    trans_x: A is then stored K x M and B N x K (e.g. a linear layer's weight,
+    C = X W^T with B = W, trans_b=True).  bias (N floats, one per column) and
+    act (ACT_*) are optional (sgemm_epilogue).  C is updated in place when
+    given; otherwise a new tensor is returned (beta must then be 0).  Runs
+    asynchronously on ``stream`` (default: the current stream of A's
+    device)."""
     import torch
 
     if A.dim() != 2 or B.dim() != 2:
@@ -201,13 +251,12 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool =
     K2, N = B.shape[::-1] if trans_b else B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
-    for name, t in (("A", A), ("B", B)):
-        if t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-    if B.device != A.device:
-        raise ValueError("A and B must be on the same device")
+    _check_tensor("A", A, torch)
+    _check_tensor("B", B, torch, A.device)
+    if bias is not None:
+        _check_tensor("bias", bias, torch, A.device)
+        if bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
+            raise ValueError(f"bias must be a contiguous vector of {N} floats")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
@@ -216,20 +265,79 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool =
         if C.dtype != torch.float32 or C.device != A.device or tuple(C.shape) != (M, N):
             raise ValueError(f"C must be float32 ({M}, {N}) on {A.device}")
     with torch.cuda.device(A.device):
-        if stream is None:
-            stream = torch.cuda.current_stream(A.device)
-        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        s = _stream_handle(stream, A.device, torch)
         ptr = lambda t: t.data_ptr() if t.numel() else None
         args = (M, N, K, float(alpha), ptr(A), _ld(A), ptr(B), _ld(B), float(beta), ptr(C),
-                _ld(C), s)
+                _ld(C))
         explicit = not (variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0)
         cfg = SgemmConfig(variant, tile, flags, group_m) if explicit else None
-        if trans_a or trans_b:
-            st = sgemm_op(int(trans_a), int(trans_b), *args, cfg=cfg)
+        if bias is not None or act != ACT_NONE:
+            st = sgemm_epilogue(int(trans_a), int(trans_b), *args,
+                                None if bias is None else ptr(bias), int(act), s, cfg=cfg)
+        elif trans_a or trans_b:
+            st = sgemm_op(int(trans_a), int(trans_b), *args, s, cfg=cfg)
         elif explicit:
-            st = sgemm_ex(*args, cfg=cfg)
+            st = sgemm_ex(*args, s, cfg=cfg)
         else:
-            st = sgemm(*args)
+            st = sgemm(*args, s)
+    if st != 0:
+        raise SgemmError(st)
+    return C
+
+
+def _batch_view(name, t, torch):
+    """(batch, rows, cols, leading dimension, batch stride) of a 3-D stack of
+    row-major matrices, or of a 2-D matrix shared by the batch (stride 0)."""
+    if t.dim() == 2:
+        rows, cols = t.shape
+        return None, rows, cols, _ld(t), 0
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 2-D or 3-D")
+    nb, rows, cols = t.shape
+    if cols > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name}: rows must be contiguous (stride(2) == 1)")
+    ld = t.stride(1) if rows > 1 else max(t.stride(1), cols, 1)
+    return nb, rows, cols, max(ld, cols, 1), t.stride(0) if nb > 1 else 0
+
+
+def gemm_batched(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
+                 trans_b: bool = False, variant: int = VARIANT_AUTO, tile: int = -1,
+                 flags: int = 0, group_m: int = 0, stream=None):
+    """C[b] = alpha * op(A[b]) @ op(B[b]) + beta * C[b] for every b
+    (sgemm_strided_batched).  A and B are 3-D float32 CUDA tensors (batch,
+    rows, cols) with unit column stride, or 2-D matrices shared by the whole
+    batch (batch stride 0); C is a 3-D tensor (batch, M, N), updated in place
+    when given (otherwise a new one; beta must then be 0)."""
+    import torch
+
+    _check_tensor("A", A, torch)
+    _check_tensor("B", B, torch, A.device)
+    na, ar, ac, lda, sa = _batch_view("A", A, torch)
+    nb, br, bc, ldb, sb = _batch_view("B", B, torch)
+    M, K = (ac, ar) if trans_a else (ar, ac)
+    K2, N = (bc, br) if trans_b else (br, bc)
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    sizes = {n for n in (na, nb) if n is not None}
+    if len(sizes) > 1:
+        raise ValueError(f"batch sizes differ: {sorted(sizes)}")
+    batch = sizes.pop() if sizes else (C.shape[0] if C is not None and C.dim() == 3 else 1)
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((batch, M, N), dtype=torch.float32, device=A.device)
+    _check_tensor("C", C, torch, A.device)
+    if C.dim() != 3 or tuple(C.shape) != (batch, M, N):
+        raise ValueError(f"C must be ({batch}, {M}, {N})")
+    _, _, _, ldc, sc = _batch_view("C", C, torch)
+    with torch.cuda.device(A.device):
+        s = _stream_handle(stream, A.device, torch)
+        ptr = lambda t: t.data_ptr() if t.numel() else None
+        explicit = not (variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0)
+        cfg = SgemmConfig(variant, tile, flags, group_m) if explicit else None
+        st = sgemm_strided_batched(int(trans_a), int(trans_b), M, N, K, float(alpha), ptr(A), lda,
+                                   sa, ptr(B), ldb, sb, float(beta), ptr(C), ldc, sc, batch, s,
+                                   cfg=cfg)
     if st != 0:
         raise SgemmError(st)
     return C

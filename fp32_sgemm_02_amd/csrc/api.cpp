@@ -17,11 +17,17 @@
 namespace sg {
 namespace {
 
-constexpr int kVersion = 200;   // 0.2.0
+constexpr int kVersion = 300;   // 0.3.0
 constexpr int kBadConfig = -13;
 constexpr int kBadTransA = -21;
 constexpr int kBadTransB = -22;
 constexpr int kBadOrder = -23;
+constexpr int kBadBias = -24;
+constexpr int kBadAct = -25;
+constexpr int kBadStrideA = -26;
+constexpr int kBadStrideB = -27;
+constexpr int kBadStrideC = -28;
+constexpr int kBadBatch = -29;
 
 // A status of the row-major call that serves a column-major one (operands
 // swapped, M and N swapped), renamed after the caller's arguments.
@@ -42,12 +48,13 @@ int colmajor_status(int st) {
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// 16-byte vector I/O needs every row start of A, B and C on a 16-byte
-// boundary ("The GEMM Scrapbook", vectorisation chapter: 128-bit accesses
-// need 16-byte alignment).
-bool vector_io_ok(const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
-    return aligned16(A) && aligned16(B) && aligned16(C) && (lda % 4 == 0) && (ldb % 4 == 0) &&
-           (ldc % 4 == 0);
+// 16-byte vector I/O needs every row start of A, B and C (of every batch
+// entry) on a 16-byte boundary ("The GEMM Scrapbook", vectorisation chapter:
+// 128-bit accesses need 16-byte alignment).
+bool vector_io_ok(const Problem &p) {
+    return rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
+           rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) &&
+           rows_aligned(p.C, p.ldc, p.stride_c, p.batch, 4);
 }
 
 struct Tuned {
@@ -135,12 +142,12 @@ int general_mfma_tile(int M, int N) {
 
 constexpr int kCUs = 256;
 
-// Estimated time of tile t on an M x N output: rounds of workgroups over the
-// 256 CUs, each round costing one tile's work at the tile's measured
+// Estimated time of tile t on `batch` M x N outputs: rounds of workgroups
+// over the 256 CUs, each round costing one tile's work at the tile's measured
 // efficiency.  Rounding up to whole rounds is what makes a 4097-row product
 // with 256-row tiles cost as much as a 4352-row one.
-double tile_cost(const TileEntry &t, int M, int N) {
-    const long long rounds = (tiles_for(t, M, N) + kCUs - 1) / kCUs;
+double tile_cost(const TileEntry &t, int M, int N, int batch = 1) {
+    const long long rounds = (tiles_for(t, M, N) * batch + kCUs - 1) / kCUs;
     return (double)rounds * t.desc.bm * t.desc.bn / (t.eff_pct > 0 ? t.eff_pct : 50);
 }
 
@@ -182,14 +189,14 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
     const TileEntry *tiles = mfma_family(&count);
     const bool trans = p.trans_a || p.trans_b;
     int best = trans ? -1 : general_mfma_tile(p.M, p.N);   // -1: nothing applies
-    double best_cost = trans ? 1e300 : tile_cost(tiles[best], p.M, p.N);
+    double best_cost = trans ? 1e300 : tile_cost(tiles[best], p.M, p.N, p.batch);
     Strips best_strips{0, 0};
     if (trans) strips = nullptr;                          // the skinny family is untransposed
     for (int i = 0; i < count; ++i) {
         const Strips sp = strips ? edge_strips(p, tiles[i]) : Strips{0, 0};
         const Problem m = main_part(p, sp);
         if (!tile_applies(tiles[i], m, io_ok)) continue;
-        double c = tile_cost(tiles[i], m.M, m.N);
+        double c = tile_cost(tiles[i], m.M, m.N, p.batch);
         if (sp.rows || sp.cols) c *= 1.05;
         if (c < best_cost) {
             best = i;
@@ -202,10 +209,10 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
 }
 
 // Automatic choice (in resolve): the measured best configuration for this
-// exact shape (tuned_table.inc), else the skinny family for memory-bound
-// shapes, else the MFMA tile of least estimated time, possibly with edge
-// strips split off.  A choice that cannot run on the actual operands falls
-// back to the general rule.
+// exact shape (tuned_table.inc; single products only), else the skinny family
+// for memory-bound shapes, else the MFMA tile of least estimated time,
+// possibly with edge strips split off.  A choice that cannot run on the
+// actual operands falls back to the general rule.
 
 // The configuration a call runs with: explicit (sgemm_ex) or automatic, with
 // an automatic choice that cannot run on these operands replaced by the
@@ -220,7 +227,7 @@ struct Choice {
 int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *strips = nullptr) {
     const int flags = cfg ? cfg->flags : 0;
     const bool want_vec = !(flags & SGEMM_FLAG_SCALAR_IO);
-    const bool io_ok = want_vec && vector_io_ok(p.A, (int)p.lda, p.B, (int)p.ldb, p.C, (int)p.ldc);
+    const bool io_ok = want_vec && vector_io_ok(p);
     int variant = cfg ? cfg->variant : SGEMM_VARIANT_AUTO;
     int tile = cfg ? cfg->tile : -1;
     int group_m = cfg ? cfg->group_m : 0;
@@ -234,7 +241,8 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
         if (trans) {
             a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok), 0};
             if (a.tile < 0) return kBadConfig;
-        } else if ((flags & SGEMM_FLAG_UNTUNED) || !lookup_tuned(p.M, p.N, p.K, a)) {
+        } else if ((flags & SGEMM_FLAG_UNTUNED) || p.batch > 1 ||
+                   !lookup_tuned(p.M, p.N, p.K, a)) {
             if (skinny_pick(p.M, p.N, p.K) >= 0)
                 a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
             else
@@ -274,52 +282,112 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
 }
 
 
+// One kernel launch per chunk of at most kMaxBatchPerLaunch batch entries.
+// With an epilogue (bias / activation), the tile's fused launcher applies it
+// in the kernel's own epilogue when it serves these operands; otherwise the
+// product is stored first and an elementwise pass applies it (beta = 1).
 int launch(const Problem &p, const Choice &ch, hipStream_t stream) {
     int count = 0;
     const TileEntry &t = family(ch.variant, &count)[ch.tile];
     static const bool log = std::getenv("FP32_SGEMM_LOG") != nullptr;
-    if (log)
-        std::fprintf(stderr, "sgemm M=%d N=%d K=%d variant=%d tile=%d (%dx%dx%d) group_m=%d %s\n",
-                     p.M, p.N, p.K, ch.variant, ch.tile, t.desc.bm, t.desc.bn, t.desc.bk,
-                     ch.group_m, ch.vec ? "vec16" : "scalar");
-    return to_status((ch.vec ? t.vec : t.scalar)(p, ch.group_m, stream));
+    const LaunchFn plain = ch.vec ? t.vec : t.scalar;
+    const LaunchFn fused = (ch.vec && p.has_epilogue()) ? t.fused : nullptr;
+    for (int b0 = 0; b0 < p.batch; b0 += kMaxBatchPerLaunch) {
+        Problem q = p;
+        q.batch = p.batch - b0 < kMaxBatchPerLaunch ? p.batch - b0 : kMaxBatchPerLaunch;
+        q.A += b0 * p.stride_a;
+        q.B += b0 * p.stride_b;
+        q.C += b0 * p.stride_c;
+        hipError_t e = hipErrorNotSupported;
+        if (fused) e = fused(q, ch.group_m, stream);   // hipErrorNotSupported: cannot fuse here
+        const bool done = (e != hipErrorNotSupported);
+        if (log)
+            std::fprintf(stderr,
+                         "sgemm M=%d N=%d K=%d batch=%d variant=%d tile=%d (%dx%dx%d) group_m=%d "
+                         "%s%s\n",
+                         q.M, q.N, q.K, q.batch, ch.variant, ch.tile, t.desc.bm, t.desc.bn,
+                         t.desc.bk, ch.group_m, ch.vec ? "vec16" : "scalar",
+                         !q.has_epilogue() ? "" : done ? " fused-epilogue" : " epilogue-pass");
+        if (!done) {
+            Problem g = q;
+            g.bias = nullptr;
+            g.act = SGEMM_ACT_NONE;
+            e = plain(g, ch.group_m, stream);
+            if (e == hipSuccess && q.has_epilogue()) e = launch_elementwise(q, 1.f, stream);
+        }
+        if (e != hipSuccess) return to_status(e);
+    }
+    return 0;
 }
 
-int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-        float beta, float *C, int ldc, hipStream_t stream, const sgemm_config *cfg,
-        int trans_a = 0, int trans_b = 0) {
-    if (trans_a != 0 && trans_a != 1) return kBadTransA;
-    if (trans_b != 0 && trans_b != 1) return kBadTransB;
-    const int v = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc, trans_a, trans_b);
-    if (v != 0) return v;
-    if (M == 0 || N == 0) return 0;
+// Argument checks shared by every entry point, in sgemm's numbering (a
+// transposed operand is stored K x M (A) or N x K (B), so its leading
+// dimension covers M or K), then those of the batched and epilogue forms.
+int validate(const Problem &p) {
+    if (p.trans_a != 0 && p.trans_a != 1) return kBadTransA;
+    if (p.trans_b != 0 && p.trans_b != 1) return kBadTransB;
+    if (p.act < SGEMM_ACT_NONE || p.act > SGEMM_ACT_GELU_TANH) return kBadAct;
+    if (p.batch < 0) return kBadBatch;
+    if (p.stride_a < 0) return kBadStrideA;
+    if (p.stride_b < 0) return kBadStrideB;
+    const int st = validate(p.M, p.N, p.K, p.alpha, p.A, (int)p.lda, p.B, (int)p.ldb, p.C,
+                            (int)p.ldc, p.trans_a, p.trans_b);
+    if (st != 0) return st;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return 0;
+    if (p.batch > 1 && p.stride_c < (long long)(p.M - 1) * p.ldc + p.N) return kBadStrideC;
+    if (p.bias && !aligned4(p.bias)) return kBadBias;
+    return 0;
+}
 
-    if (alpha == 0.f || K == 0) {
-        if (beta == 1.f) return 0;
-        return to_status(launch_scale(M, N, beta, C, ldc, stream));
+// Validates and runs one call.  The special cases of the reference BLAS:
+// nothing to do for an empty C or batch; alpha == 0 or K == 0 leaves
+// C = beta * C (plus the epilogue), without reading A or B.
+int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
+    const int v = validate(p);
+    if (v != 0) return v;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return 0;
+    if (p.batch == 1) p.stride_a = p.stride_b = p.stride_c = 0;
+
+    if (p.alpha == 0.f || p.K == 0) {
+        if (p.beta == 1.f && !p.has_epilogue()) return 0;
+        return to_status(launch_elementwise(p, p.beta, stream));
     }
 
-    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, trans_a, trans_b};
     Choice ch;
     Strips sp;
     int st = resolve(p, cfg, ch, &sp);
     if (st != 0) return st;
     if (!sp.rows && !sp.cols) return launch(p, ch, stream);
     // main part, then the column strip beside it, then the row strip below
-    const int m1 = M - sp.rows, n1 = N - sp.cols;
+    const int m1 = p.M - sp.rows, n1 = p.N - sp.cols;
     st = launch(main_part(p, sp), ch, stream);
     if (st == 0 && sp.cols) {
-        const Problem cols{m1, sp.cols, K, alpha, beta, A, lda, B + n1, ldb, C + n1, ldc};
+        Problem cols = p;
+        cols.M = m1;
+        cols.N = sp.cols;
+        cols.B = p.B + n1;
+        cols.C = p.C + n1;
+        if (p.bias) cols.bias = p.bias + n1;
         st = resolve(cols, nullptr, ch);
         if (st == 0) st = launch(cols, ch, stream);
     }
     if (st == 0 && sp.rows) {
-        const Problem rows{sp.rows, N, K, alpha, beta, A + (long long)m1 * lda, lda, B, ldb,
-                           C + (long long)m1 * ldc, ldc};
+        Problem rows = p;
+        rows.M = sp.rows;
+        rows.A = p.A + (long long)m1 * p.lda;
+        rows.C = p.C + (long long)m1 * p.ldc;
         st = resolve(rows, nullptr, ch);
         if (st == 0) st = launch(rows, ch, stream);
     }
     return st;
+}
+
+Problem make_problem(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                     int lda, const float *B, int ldb, float beta, float *C, int ldc) {
+    Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    p.trans_a = trans_a;
+    p.trans_b = trans_b;
+    return p;
 }
 
 }  // namespace
@@ -329,24 +397,69 @@ extern "C" {
 
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, hipStream_t stream) {
-    return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+    return sg::run(sg::make_problem(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), stream,
+                   nullptr);
 }
 
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, hipStream_t stream, const sgemm_config *cfg) {
-    return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, cfg);
+    return sg::run(sg::make_problem(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), stream,
+                   cfg);
 }
 
 int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
              int lda, const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
-    return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr, trans_a,
-                   trans_b);
+    return sg::run(sg::make_problem(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                    ldc),
+                   stream, nullptr);
 }
 
 int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
                 int lda, const float *B, int ldb, float beta, float *C, int ldc,
                 hipStream_t stream, const sgemm_config *cfg) {
-    return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, cfg, trans_a, trans_b);
+    return sg::run(sg::make_problem(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                    ldc),
+                   stream, cfg);
+}
+
+int sgemm_epilogue_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                      int ldc, const float *bias, int act, hipStream_t stream,
+                      const sgemm_config *cfg) {
+    sg::Problem p = sg::make_problem(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                     ldc);
+    p.bias = bias;
+    p.act = act;
+    return sg::run(p, stream, cfg);
+}
+
+int sgemm_epilogue(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                   int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                   const float *bias, int act, hipStream_t stream) {
+    return sgemm_epilogue_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias,
+                             act, stream, nullptr);
+}
+
+int sgemm_strided_batched_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                             const float *A, int lda, long long stride_a, const float *B,
+                             int ldb, long long stride_b, float beta, float *C, int ldc,
+                             long long stride_c, int batch, hipStream_t stream,
+                             const sgemm_config *cfg) {
+    sg::Problem p = sg::make_problem(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                     ldc);
+    p.batch = batch;
+    p.stride_a = stride_a;
+    p.stride_b = stride_b;
+    p.stride_c = stride_c;
+    return sg::run(p, stream, cfg);
+}
+
+int sgemm_strided_batched(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                          const float *A, int lda, long long stride_a, const float *B, int ldb,
+                          long long stride_b, float beta, float *C, int ldc, long long stride_c,
+                          int batch, hipStream_t stream) {
+    return sgemm_strided_batched_ex(trans_a, trans_b, M, N, K, alpha, A, lda, stride_a, B, ldb,
+                                    stride_b, beta, C, ldc, stride_c, batch, stream, nullptr);
 }
 
 int sgemm_op_plan(int trans_a, int trans_b, int M, int N, int K, const float *A, int lda,
@@ -387,10 +500,12 @@ int sgemm_cblas(int order, int trans_a, int trans_b, int M, int N, int K, float 
     if (ta < 0) return sg::kBadTransA;
     if (tb < 0) return sg::kBadTransB;
     if (order == 101)
-        return sg::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr, ta, tb);
+        return sg::run(sg::make_problem(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc),
+                       stream, nullptr);
     // column-major C = op(A) op(B) is row-major C^T = op(B)^T op(A)^T over the
     // same memory: B's storage takes A's place and the transposition flags carry over
-    const int st = sg::run(N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream, nullptr, tb, ta);
+    const int st = sg::run(sg::make_problem(tb, ta, N, M, K, alpha, B, ldb, A, lda, beta, C, ldc),
+                           stream, nullptr);
     return sg::colmajor_status(st);
 }
 
@@ -430,6 +545,12 @@ const char *sgemm_status_string(int status) {
     case -21: return "invalid trans_a (0 or 1; CBLAS: 111, 112 or 113)";
     case -22: return "invalid trans_b (0 or 1; CBLAS: 111, 112 or 113)";
     case -23: return "invalid order (CBLAS: 101 row-major or 102 column-major)";
+    case -24: return "bias not 4-byte aligned";
+    case -25: return "invalid activation code";
+    case -26: return "negative batch stride of A";
+    case -27: return "negative batch stride of B";
+    case -28: return "batch stride of C lets two entries of the batch overlap";
+    case -29: return "negative batch count";
     default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -321,6 +321,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
+    select_batch(p);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kg = wave / S::WAVES_MN, wv = wave % S::WAVES_MN;   // k-group, wave within it
@@ -500,8 +501,6 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
         }
 }
 
-bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
-
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
           int BV, bool GUARD>
 hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stream) {
@@ -511,7 +510,8 @@ hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stre
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
     hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AV, BV, GUARD>),
-                       dim3((unsigned)tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m,
+                       dim3((unsigned)tiles, p.batch), dim3(S::NT), 0, stream, p, tiles_m, tiles_n,
+                       group_m,
                        (int)cvec);
     return hipGetLastError();
 }
@@ -528,9 +528,11 @@ template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, boo
           bool VEC>
 hipError_t launch_for(const Problem &p, int group_m, hipStream_t stream) {
     const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
-    const bool av = VEC && aligned16(p.A) && p.lda % 4 == 0 && (TA ? p.M : p.K) % 4 == 0;
-    const bool bv = VEC && aligned16(p.B) && p.ldb % 4 == 0 && (TB ? p.K : p.N) % 4 == 0;
-    const bool cv = VEC && aligned16(p.C) && p.ldc % 4 == 0;
+    const bool av = VEC && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
+                    (TA ? p.M : p.K) % 4 == 0;
+    const bool bv = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) &&
+                    (TB ? p.K : p.N) % 4 == 0;
+    const bool cv = VEC && rows_aligned(p.C, p.ldc, p.stride_c, p.batch, 4);
     if constexpr (!TB && !TA) {
         if (whole && av && bv && cv)
             return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 4, 4, false>(p, group_m, true,

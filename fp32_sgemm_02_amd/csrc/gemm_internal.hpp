@@ -14,6 +14,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // One GEMM problem, C = alpha * (A * B) + beta * C, row-major with leading
 // dimensions (in floats).  Offsets are formed in 64-bit inside the kernels.
+// A batch of `batch` such products runs in one launch: blockIdx.y is the
+// product's index, and its operands start `stride_*` floats further per index.
 struct Problem {
     int M, N, K;
     float alpha, beta;
@@ -25,7 +27,23 @@ struct Problem {
     long long ldc;
     int trans_a = 0;   // A stored transposed (K x M)
     int trans_b = 0;   // B stored transposed (N x K)
+    int batch = 1;
+    long long stride_a = 0, stride_b = 0, stride_c = 0;
+    const float *bias = nullptr;   // epilogue: one float per column of C, or none
+    int act = SGEMM_ACT_NONE;      // epilogue activation
+    bool has_epilogue() const { return bias != nullptr || act != SGEMM_ACT_NONE; }
 };
+
+// Largest grid y (batch entries per launch); larger batches are split.
+constexpr int kMaxBatchPerLaunch = 65535;
+
+// Host: whether every batch entry of an operand has rows starting on
+// `floats`-float boundaries (base aligned, and the leading dimension and the
+// batch stride multiples of `floats`).
+inline bool rows_aligned(const void *ptr, long long ld, long long stride, int batch, int floats) {
+    const unsigned long long a = reinterpret_cast<unsigned long long>(ptr);
+    return a % (4ull * floats) == 0 && ld % floats == 0 && (batch <= 1 || stride % floats == 0);
+}
 
 using LaunchFn = hipError_t (*)(const Problem &, int group_m, hipStream_t);
 
@@ -37,6 +55,10 @@ struct TileEntry {
     LaunchFn vec;
     LaunchFn scalar;
     int eff_pct = 0;   // measured fraction of the fp32 peak at 4096^3 (dispatch cost model)
+    // launcher that applies the problem's bias / activation in the kernel's
+    // own epilogue (16-byte I/O); returns hipErrorNotSupported for operands
+    // it does not serve, and the caller then adds an elementwise pass
+    LaunchFn fused = nullptr;
 };
 
 // Kernel families (each defined in its own .hip file): the compiled tile
@@ -54,11 +76,37 @@ int skinny_pick(int M, int N, int K);
 int skinny_kind(int tile);
 bool skinny_fits(int tile, int M, int N);
 
-// C = beta * C (beta == 0: zero fill without reading C).
-hipError_t launch_scale(int M, int N, float beta, float *C, long long ldc,
-                        hipStream_t stream);
+// C = act(beta * C + bias) over p's batch (beta == 0: C is not read); with
+// no epilogue, C = beta * C.  The alpha == 0 / K == 0 case, and the bias and
+// activation pass after a kernel that does not apply them itself (beta = 1).
+hipError_t launch_elementwise(const Problem &p, float beta, hipStream_t stream);
 
 // ---- device helpers shared by the families ---------------------------------
+
+// Moves the operand pointers to this workgroup's batch entry (blockIdx.y).
+__device__ __forceinline__ void select_batch(Problem &p) {
+    const long long b = blockIdx.y;
+    p.A += b * p.stride_a;
+    p.B += b * p.stride_b;
+    p.C += b * p.stride_c;
+}
+
+// Activation of a finished sum (SGEMM_ACT_*), in fp32.  GELU's normal CDF is
+// evaluated as erfc(-x / sqrt 2) / 2 and (1 + tanh u) / 2 as 1 / (1 + e^-2u):
+// the same functions without the cancellation of 1 + erf and 1 + tanh at
+// negative x.
+__device__ __forceinline__ float activate(int act, float x) {
+    switch (act) {
+    case SGEMM_ACT_RELU: return x < 0.f ? 0.f : x;
+    case SGEMM_ACT_SILU: return x / (1.f + expf(-x));
+    case SGEMM_ACT_GELU_ERF: return 0.5f * x * erfcf(-0.70710678118654752f * x);
+    case SGEMM_ACT_GELU_TANH: {
+        const float u = 0.79788456080286536f * fmaf(0.044715f * x, x * x, x);
+        return x / (1.f + expf(-2.f * u));
+    }
+    default: return x;
+    }
+}
 
 // Ends one software-pipeline step.  The accumulators pass through an empty
 // asm statement, so the arithmetic of this step must be complete at this

@@ -283,6 +283,7 @@ __global__ void __launch_bounds__((MfmaShape<BM, BN, BK, WM, WN, NBUF, OCC>::NT)
 mfma_sgemm_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     using S = MfmaShape<BM, BN, BK, WM, WN, NBUF, OCC>;
     __shared__ __attribute__((aligned(16))) float smem[NBUF * S::STAGE];
+    select_batch(p);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -379,7 +380,7 @@ hipError_t launch_mfma(const Problem &p, int group_m, hipStream_t stream) {
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
     hipLaunchKernelGGL((mfma_sgemm_kernel<BM, BN, BK, WM, WN, NBUF, OCC, VEC>),
-                       dim3((unsigned)tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n,
+                       dim3((unsigned)tiles, p.batch), dim3(S::NT), 0, stream, p, tiles_m, tiles_n,
                        group_m);
     return hipGetLastError();
 }

@@ -109,6 +109,7 @@ template <int VW, int W, int U, bool VA, bool VB>
 __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) {
     using S = RowsShape<VW, W>;
     __shared__ __attribute__((aligned(16))) float red[S::RED];
+    select_batch(p);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, g = lane >> 4;
     // neighbouring strips share cache lines of B: keep them on one XCD's L2
@@ -156,15 +157,11 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     }
 }
 
-bool aligned_to(const void *ptr, unsigned bytes) {
-    return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1)) == 0;
-}
-
 template <int VW, int W, int U, bool VA, bool VB>
 hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB>), dim3(strips), dim3(64 * W), 0, stream, p,
-                       strips);
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB>), dim3(strips, p.batch), dim3(64 * W), 0,
+                       stream, p, strips);
     return hipGetLastError();
 }
 
@@ -172,8 +169,8 @@ hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
 // otherwise 4-byte loads throughout.
 template <int VW, int W, int U, bool VEC>
 hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
-    const bool va = VEC && aligned_to(p.A, 16) && p.lda % 4 == 0;
-    const bool vb = VEC && aligned_to(p.B, 4 * VW) && p.ldb % VW == 0;
+    const bool va = VEC && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
+    const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, VW);
     if (va && vb) return launch_rows_as<VW, W, U, true, true>(p, stream);
     if (va) return launch_rows_as<VW, W, U, true, false>(p, stream);
     if (vb) return launch_rows_as<VW, W, U, false, true>(p, stream);
@@ -240,6 +237,7 @@ __device__ __forceinline__ void cols_fma(const ColsRound<NB, U> &r, float (&acc)
 // few-rows kernel (loads past K read as zero and touch no memory).
 template <int NB, int W, int U, bool VEC, bool BT>
 __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
+    select_batch(p);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * W + wave;
     if (row >= p.M) return;                       // whole wave leaves together; no barrier below
@@ -283,7 +281,8 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
 template <int NB, int W, int U, bool VA, bool BT>
 hipError_t launch_cols_as(const Problem &p, hipStream_t stream) {
     const int blocks = (p.M + W - 1) / W;
-    hipLaunchKernelGGL((cols_kernel<NB, W, U, VA, BT>), dim3(blocks), dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((cols_kernel<NB, W, U, VA, BT>), dim3(blocks, p.batch), dim3(64 * W), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -291,8 +290,9 @@ hipError_t launch_cols_as(const Problem &p, hipStream_t stream) {
 // K x NB block where it is one (decided per operand); otherwise 4-byte loads.
 template <int NB, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
-    const bool va = VEC && aligned_to(p.A, 16) && p.lda % 4 == 0;
-    const bool bt = VEC && aligned_to(p.B, 16) && p.N == NB && p.ldb == NB;
+    const bool va = VEC && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
+    const bool bt = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) && p.N == NB &&
+                    p.ldb == NB;
     if (va && bt) return launch_cols_as<NB, W, U, true, true>(p, stream);
     if (va) return launch_cols_as<NB, W, U, true, false>(p, stream);
     if (bt) return launch_cols_as<NB, W, U, false, true>(p, stream);

@@ -166,6 +166,7 @@ __global__ void __launch_bounds__((ValuShape<BM, BN, BK>::NT), 2)
 valu_sgemm_kernel(Problem p, int tiles_m, int tiles_n, int group_m) {
     using S = ValuShape<BM, BN, BK>;
     __shared__ __attribute__((aligned(16))) float smem[2 * S::STAGE];
+    select_batch(p);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / S::WAVES_N, wc = wave % S::WAVES_N;
@@ -280,7 +281,8 @@ hipError_t launch_valu(const Problem &p, int group_m, hipStream_t stream) {
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 8;
-    hipLaunchKernelGGL((valu_sgemm_kernel<BM, BN, BK, VEC>), dim3((unsigned)tiles), dim3(S::NT),
+    hipLaunchKernelGGL((valu_sgemm_kernel<BM, BN, BK, VEC>), dim3((unsigned)tiles, p.batch),
+                       dim3(S::NT),
                        0, stream, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }

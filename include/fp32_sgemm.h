@@ -46,6 +46,10 @@
  *     -21, -22          sgemm_op: trans_a, trans_b not 0 or 1 (sgemm_cblas:
  *                       not 111, 112 or 113)
  *     -23               sgemm_cblas: order not 101 or 102
+ *     -24, -25          sgemm_epilogue: bias not 4-byte aligned; unknown act
+ *     -26, -27, -28     sgemm_strided_batched: negative stride of A or B; a
+ *                       stride of C that lets two of the batch's C overlap
+ *     -29               sgemm_strided_batched: negative batch
  *     > 0               a hipError_t reported by the kernel launch
  * No C++ exception crosses this interface.
  *
@@ -173,6 +177,65 @@ int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const f
 int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
                 int lda, const float *B, int ldb, float beta, float *C, int ldc,
                 hipStream_t stream, const sgemm_config *cfg);
+
+/*
+ * Activation codes of sgemm_epilogue (applied in fp32 to the finished sum).
+ * The pages name the feed-forward GEMMs of a transformer ("The GEMM
+ * Scrapbook", introduction) but no activation; these are the common ones.
+ */
+#define SGEMM_ACT_NONE 0       /* x */
+#define SGEMM_ACT_RELU 1       /* max(x, 0) */
+#define SGEMM_ACT_SILU 2       /* x / (1 + exp(-x)) */
+#define SGEMM_ACT_GELU_ERF 3   /* x * Phi(x), Phi the standard normal CDF */
+#define SGEMM_ACT_GELU_TANH 4  /* x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+
+/*
+ * sgemm_epilogue: C = act(alpha * op(A) * op(B) + beta * C + bias), the
+ * product of a linear layer with its bias and activation fused ("The GEMM
+ * Scrapbook", introduction: the two GEMMs of a feed-forward block).
+ * Arguments as sgemm_op, then bias (device, N floats: bias[j] is added to
+ * every cell of column j; NULL for none), act (SGEMM_ACT_*) and the stream.
+ * beta == 0 never reads C.  alpha == 0 or K == 0 gives act(beta * C + bias)
+ * without reading A or B.  The direct-load MFMA tiles and the skinny family
+ * apply bias and activation in their own epilogue when every operand allows
+ * 16-byte I/O; otherwise the product is stored and one elementwise pass
+ * applies them.  Status codes as sgemm_op's, -24 for a bias that is not
+ * 4-byte aligned, -25 for an unknown act.
+ */
+int sgemm_epilogue(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                   int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                   const float *bias, int act, hipStream_t stream);
+
+/* sgemm_epilogue with an explicit configuration, as sgemm_op_ex. */
+int sgemm_epilogue_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                      int ldc, const float *bias, int act, hipStream_t stream,
+                      const sgemm_config *cfg);
+
+/*
+ * sgemm_strided_batched: `batch` independent products
+ *     C_b = alpha * op(A_b) * op(B_b) + beta * C_b,  b = 0 .. batch-1,
+ * with A_b = A + b * stride_a, B_b = B + b * stride_b, C_b = C + b * stride_c
+ * (strides in floats; a stride of 0 for A or B shares that operand across
+ * the batch, e.g. one weight matrix for many inputs).  Other arguments as
+ * sgemm_op.  The C matrices must not overlap: stride_c >= (M-1)*ldc + N when
+ * batch > 1 (-28 otherwise).  batch == 0 does nothing.  One kernel launch
+ * serves up to 65535 entries (grid y), larger batches take several.  The
+ * work of attention projections and heads ("The GEMM Scrapbook",
+ * introduction).  Status codes as sgemm_op's, and -26 / -27 for a negative
+ * stride of A / B, -29 for a negative batch.
+ */
+int sgemm_strided_batched(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                          const float *A, int lda, long long stride_a, const float *B, int ldb,
+                          long long stride_b, float beta, float *C, int ldc, long long stride_c,
+                          int batch, hipStream_t stream);
+
+/* sgemm_strided_batched with an explicit configuration, as sgemm_op_ex. */
+int sgemm_strided_batched_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                             const float *A, int lda, long long stride_a, const float *B,
+                             int ldb, long long stride_b, float beta, float *C, int ldc,
+                             long long stride_c, int batch, hipStream_t stream,
+                             const sgemm_config *cfg);
 
 /*
  * sgemm_cblas: the same product with the argument conventions of

@@ -92,6 +92,8 @@ def sgemm_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nthreads=None) -> in
 def _ld(x: np.ndarray) -> int:
     """Leading dimension (in elements) of a row-major 2-D float32 view."""
     assert x.dtype == np.float32 and x.ndim == 2
+    if x.size == 0:
+        return max(x.shape[1], 1)
     assert x.shape[1] <= 1 or x.strides[1] == 4, "rows must be contiguous"
     ld = x.strides[0] // 4
     if x.shape[0] <= 1 or x.shape[1] == 0:

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tables():
-    assert sg.version() == 200
+    assert sg.version() == 300
     for v in (sg.VARIANT_MFMA, sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         n = sg.tile_count(v)
         assert n > 0
@@ -276,3 +276,44 @@ def test_op_plan_covers_transpositions():
                              None, None) == -21
     assert lib.sgemm_op_plan(0, 5, 4, 4, 4, None, 4, None, 4, None, 4, ctypes.byref(out),
                              None, None) == -22
+
+
+def test_epilogue_entry_point_validation():
+    """sgemm_epilogue: act codes, bias alignment, and the quick returns that
+    no longer apply when an epilogue is asked for are checked on the host."""
+    good = 0x10000
+    ep = sg.sgemm_epilogue
+    assert ep(0, 0, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, good, 5) == -25
+    assert ep(0, 0, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, good, -1) == -25
+    assert ep(0, 0, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, good + 2, 1) == -24
+    assert ep(2, 0, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, good, 1) == -21
+    assert ep(0, 0, -1, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, good, 1) == -1
+    assert ep(0, 0, 4, 4, 4, 1.0, None, 4, good, 4, 0.0, good, 4, good, 1) == -5
+    # empty C: nothing to do, whatever the epilogue
+    assert ep(0, 0, 0, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4, good, 1) == 0
+    # no bias and no activation is sgemm_op
+    assert ep(0, 0, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, good, 4, None, 0) == 0
+
+
+def test_batched_entry_point_validation():
+    """sgemm_strided_batched: batch, stride and overlap checks on the host."""
+    good = 0x10000
+    bt = sg.sgemm_strided_batched
+    args = lambda **kw: dict(dict(ta=0, tb=0, M=4, N=4, K=4, alpha=1.0, A=good, lda=4, sa=16,
+                                  B=good, ldb=4, sb=16, beta=0.0, C=good, ldc=4, sc=16, batch=3),
+                             **kw)
+    call = lambda d: bt(d["ta"], d["tb"], d["M"], d["N"], d["K"], d["alpha"], d["A"], d["lda"],
+                        d["sa"], d["B"], d["ldb"], d["sb"], d["beta"], d["C"], d["ldc"], d["sc"],
+                        d["batch"])
+    assert call(args(batch=-1)) == -29
+    assert call(args(sa=-16)) == -26
+    assert call(args(sb=-1)) == -27
+    assert call(args(sc=15)) == -28          # C_1 would overlap C_0
+    assert call(args(sc=0)) == -28
+    assert call(args(tb=3)) == -22
+    assert call(args(M=-2)) == -1
+    assert call(args(ldb=3)) == -8
+    # shared operands (stride 0) are allowed; batch 0 and batch 1 need no C stride
+    assert call(args(batch=0, sc=0)) == 0
+    assert call(args(M=0, sc=0)) == 0
+    assert call(args(alpha=0.0, beta=1.0, A=None, B=None, sa=0, sb=0)) == 0
