@@ -332,8 +332,11 @@ def sweep(args):
             print(json.dumps(row), flush=True)
         if name in TRANSPOSED_SWEEP:
             rows.extend(sweep_transposed(torch, sg, time_graph, w, sets[0]))
+        if name in EPILOGUE_SWEEP:
+            rows.extend(sweep_epilogue(torch, sg, time_graph, w, sets[0]))
         del sets
         torch.cuda.empty_cache()
+    rows.extend(sweep_batched(torch, sg, time_graph))
     with open(args.sweep, "w") as fh:
         json.dump(rows, fh, indent=1)
 
@@ -362,6 +365,70 @@ def sweep_transposed(torch, sg, time_graph, w, operands):
         print(json.dumps(row), flush=True)
         out.append(row)
         del As, Bs
+    return out
+
+
+EPILOGUE_SWEEP = ("mlp_up", "mlp_decode16")
+
+
+def sweep_epilogue(torch, sg, time_graph, w, operands):
+    """The workload as a linear layer, C = act(X W^T + bias) with W stored
+    N x K, for each activation (sgemm_epilogue, automatic dispatch)."""
+    A, B, C = operands
+    Wt = B.t().contiguous()
+    bias = torch.rand(w.N, device=A.device) * 2 - 1
+    out = []
+    for act, label in ((sg.ACT_NONE, "bias"), (sg.ACT_RELU, "relu"), (sg.ACT_SILU, "silu"),
+                       (sg.ACT_GELU_ERF, "gelu"), (sg.ACT_GELU_TANH, "gelu_tanh")):
+        call_i = lambda i: sg.gemm(A, Wt, C, 1.0, 0.0, trans_b=True, bias=bias, act=act)
+        med = statistics.median(time_graph(torch, call_i, 5 if w.flops > 1e11 else 20)) / 1e3
+        row = {"workload": f"{w.name}_NT_{label}", "M": w.M, "N": w.N, "K": w.K, "op": "NT",
+               "epilogue": label, "kernel_ms_median": round(med * 1e3, 4),
+               "gflops": round(w.flops / med / 1e9, 1), "bound": w.bound}
+        if w.bound == "hbm":
+            row["gbs"] = round((w.min_bytes + 4 * w.N) / med / 1e9, 1)
+            row["pct_roofline"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
+        else:
+            row["pct_roofline"] = round(100 * w.flops / med / 1e9 / (PEAK_FP32_TFLOPS * 1e3), 2)
+        print(json.dumps(row), flush=True)
+        out.append(row)
+    return out
+
+
+# batched shapes: (name, batch, M, N, K, trans_b) -- attention over 32 heads
+# of 2048 positions with head dimension 128 (scores Q K^T and the weighted
+# sum P V), and many small products
+BATCHED_SWEEP = (("attn_scores_32x2048x2048x128", 32, 2048, 2048, 128, True),
+                 ("attn_values_32x2048x128x2048", 32, 2048, 128, 2048, False),
+                 ("small_512x128x128x64", 512, 128, 128, 64, True),
+                 ("small_4096x32x32x32", 4096, 32, 32, 32, False))
+
+
+def sweep_batched(torch, sg, time_graph):
+    """Strided-batched products (sgemm_strided_batched), graph-replay device
+    time per call."""
+    out = []
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(7)
+    for name, batch, M, N, K, tb in BATCHED_SWEEP:
+        A = torch.rand((batch, M, K), device="cuda:0", generator=gen) * 2 - 1
+        B = torch.rand((batch, N, K) if tb else (batch, K, N), device="cuda:0", generator=gen)
+        C = torch.empty((batch, M, N), device="cuda:0")
+        call_i = lambda i: sg.gemm_batched(A, B, C, 1.0, 0.0, trans_b=tb)
+        flops = 2.0 * batch * M * N * K
+        med = statistics.median(time_graph(torch, call_i, 5 if flops > 1e11 else 20)) / 1e3
+        byts = 4.0 * batch * (M * K + K * N + M * N)
+        ai = flops / byts
+        bound = "mfma" if ai > PEAK_FP32_TFLOPS * 1e3 / PEAK_HBM_GBS else "hbm"
+        row = {"workload": name, "batch": batch, "M": M, "N": N, "K": K,
+               "op": "NT" if tb else "NN", "kernel_ms_median": round(med * 1e3, 4),
+               "gflops": round(flops / med / 1e9, 1), "gbs": round(byts / med / 1e9, 1),
+               "bound": bound}
+        row["pct_roofline"] = round(100 * (row["gflops"] / (PEAK_FP32_TFLOPS * 1e3)
+                                           if bound == "mfma" else row["gbs"] / PEAK_HBM_GBS), 2)
+        print(json.dumps(row), flush=True)
+        out.append(row)
+        del A, B, C
     return out
 
 

@@ -68,17 +68,27 @@ long long tiles_for(const TileEntry &t, int M, int N) {
 }
 
 // The MFMA family: the general tiles, then the direct-load tiles for
-// untransposed A, then those for transposed A, in one table.
+// untransposed A, then those for transposed A, in one table; the direct-load
+// tiles get their fused-epilogue launchers (compiled separately, same order).
 const TileEntry *mfma_family(int *count) {
     static const std::vector<TileEntry> all = [] {
         std::vector<TileEntry> v;
-        int n = 0;
+        int n = 0, nf = 0;
         const TileEntry *t = mfma_tiles(&n);
         v.insert(v.end(), t, t + n);
+        const LaunchFn *f = nullptr;
         t = mfma_direct_tiles(&n);
-        v.insert(v.end(), t, t + n);
+        f = mfma_direct_epi_launchers(&nf);
+        for (int i = 0; i < n; ++i) {
+            v.push_back(t[i]);
+            if (nf == n) v.back().fused = f[i];
+        }
         t = mfma_direct_ta_tiles(&n);
-        v.insert(v.end(), t, t + n);
+        f = mfma_direct_ta_epi_launchers(&nf);
+        for (int i = 0; i < n; ++i) {
+            v.push_back(t[i]);
+            if (nf == n) v.back().fused = f[i];
+        }
         return v;
     }();
     *count = (int)all.size();

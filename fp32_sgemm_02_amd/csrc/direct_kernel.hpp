@@ -77,8 +77,10 @@ namespace {
 // same way: one 16-byte read gives four 16-row blocks their operand of one
 // MFMA step, so the rows of a 64-row group are interleaved (row 4i + c of
 // the group is row i of block c).
+// EP: the instance applies the fused epilogue (no effect on the shape; it
+// keeps the shape types of the two instances apart).
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4, int KG = 1,
-          bool TB = false, bool TA = false>
+          bool TB = false, bool TA = false, bool EP = false>
 struct DirectShape {
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
@@ -312,12 +314,13 @@ __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S
 
 // GUARD: the problem has edges (M, N or K not tile multiples, or C not fit
 // for 16-byte stores): zero-filled loads outside the matrix and guarded
-// stores.  cvec: C rows allow 16-byte stores (used with GUARD only).
+// stores.  cvec: C rows allow 16-byte stores (used with GUARD only).  EPI:
+// the epilogue adds p.bias and applies p.act.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
-          int BV, bool GUARD>
+          int BV, bool GUARD, bool EPI = false>
 __global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>::NT), 1)
 mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI>;
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
@@ -449,67 +452,98 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     }
 
     // epilogue: alpha/beta (beta == 0 never reads C); 16-byte stores, and
-    // with edges only rows < M and columns < N are touched
+    // with edges only rows < M and columns < N are touched.  With EPI the
+    // bias of each column is added and the activation applied before the
+    // store; the activation is chosen once, outside the unrolled stores.
     const int i = lane & 15, g = lane >> 4;
     const bool read_c = (p.beta != 0.f);
     const int row0 = m0 + wr * WM, col0 = n0 + wc * WN;
+    float bcol[S::CB];   // bias of the column of acc[.][cb] (EPI)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int cb = 0; cb < S::CB; ++cb) {
+        const int gn = col0 + (S::TRANS_B ? cb * 16 + i : (cb / 4) * 64 + 4 * i + cb % 4);
+        bcol[cb] = (EPI && p.bias && (!GUARD || gn < p.N)) ? p.bias[gn] : 0.f;
+    }
+    auto store = [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;   // -1: no epilogue
+        auto finish = [&](float v, int cb) {
+            if constexpr (ACT < 0)
+                return v;
+            else
+                return activate_t<ACT>(v + bcol[cb]);
+        };
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int gm = S::TRANS_A ? row0 + (rb / 4) * 64 + 16 * g + 4 * r + rb % 4
-                                      : row0 + rb * 16 + 4 * g + r;
-            if (GUARD && gm >= p.M) continue;
-            float *crow = p.C + (long long)gm * p.ldc;
-            if constexpr (S::TRANS_B) {
-                // acc[rb][cb][r] is C(gm, col0 + 16cb + i): 16 lanes write 64
-                // contiguous bytes
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int cb = 0; cb < S::CB; ++cb) {
-                    const int gn = col0 + cb * 16 + i;
-                    if (GUARD && gn >= p.N) continue;
-                    float out = p.alpha * acc[rb][cb][r];
-                    if (read_c) out = fmaf(p.beta, crow[gn], out);
-                    crow[gn] = out;
-                }
-                continue;
-            }
+            for (int r = 0; r < 4; ++r) {
+                const int gm = S::TRANS_A ? row0 + (rb / 4) * 64 + 16 * g + 4 * r + rb % 4
+                                          : row0 + rb * 16 + 4 * g + r;
+                if (GUARD && gm >= p.M) continue;
+                float *crow = p.C + (long long)gm * p.ldc;
+                if constexpr (S::TRANS_B) {
+                    // acc[rb][cb][r] is C(gm, col0 + 16cb + i): 16 lanes write 64
+                    // contiguous bytes
 #pragma unroll
-            for (int cg = 0; cg < S::CG; ++cg) {
-                const int gn = col0 + cg * 64 + 4 * i;
-                floatx4 v;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) v[c] = p.alpha * acc[rb][cg * 4 + c][r];
-                if (!GUARD || (cvec && gn + 3 < p.N)) {
-                    floatx4 *dst = reinterpret_cast<floatx4 *>(crow + gn);
-                    if (read_c) {
-                        const floatx4 old = *dst;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) v[c] = fmaf(p.beta, old[c], v[c]);
+                    for (int cb = 0; cb < S::CB; ++cb) {
+                        const int gn = col0 + cb * 16 + i;
+                        if (GUARD && gn >= p.N) continue;
+                        float out = p.alpha * acc[rb][cb][r];
+                        if (read_c) out = fmaf(p.beta, crow[gn], out);
+                        crow[gn] = finish(out, cb);
                     }
-                    *dst = v;
-                } else {
+                    continue;
+                }
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        if (gn + c >= p.N) continue;
-                        float out = v[c];
-                        if (read_c) out = fmaf(p.beta, crow[gn + c], out);
-                        crow[gn + c] = out;
+                for (int cg = 0; cg < S::CG; ++cg) {
+                    const int gn = col0 + cg * 64 + 4 * i;
+                    floatx4 v;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[c] = p.alpha * acc[rb][cg * 4 + c][r];
+                    if (!GUARD || (cvec && gn + 3 < p.N)) {
+                        floatx4 *dst = reinterpret_cast<floatx4 *>(crow + gn);
+                        if (read_c) {
+                            const floatx4 old = *dst;
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) v[c] = fmaf(p.beta, old[c], v[c]);
+                        }
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) v[c] = finish(v[c], cg * 4 + c);
+                        *dst = v;
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            if (gn + c >= p.N) continue;
+                            float out = v[c];
+                            if (read_c) out = fmaf(p.beta, crow[gn + c], out);
+                            crow[gn + c] = finish(out, cg * 4 + c);
+                        }
                     }
                 }
             }
+    };
+    if constexpr (EPI) {
+        switch (p.act) {
+        case SGEMM_ACT_RELU: store(std::integral_constant<int, SGEMM_ACT_RELU>{}); break;
+        case SGEMM_ACT_SILU: store(std::integral_constant<int, SGEMM_ACT_SILU>{}); break;
+        case SGEMM_ACT_GELU_ERF: store(std::integral_constant<int, SGEMM_ACT_GELU_ERF>{}); break;
+        case SGEMM_ACT_GELU_TANH: store(std::integral_constant<int, SGEMM_ACT_GELU_TANH>{}); break;
+        default: store(std::integral_constant<int, SGEMM_ACT_NONE>{}); break;
         }
+    } else {
+        store(std::integral_constant<int, -1>{});
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
-          int BV, bool GUARD>
+          int BV, bool GUARD, bool EPI = false>
 hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stream) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI>;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
-    hipLaunchKernelGGL((mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AV, BV, GUARD>),
+    hipLaunchKernelGGL(
+        (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AV, BV, GUARD, EPI>),
                        dim3((unsigned)tiles, p.batch), dim3(S::NT), 0, stream, p, tiles_m, tiles_n,
                        group_m,
                        (int)cvec);
@@ -568,9 +602,39 @@ hipError_t launch_direct(const Problem &p, int group_m, hipStream_t stream) {
     return launch_for<BM, BN, BK, WM, WN, NBUF, KG, false, TA, EDGES, VEC>(p, group_m, stream);
 }
 
+// The fused-epilogue launcher: bias and activation applied in the kernel's
+// own epilogue, for operands that take dwordx4 loads of A and B (the
+// instances compiled with EPI); hipErrorNotSupported otherwise.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TA, bool EDGES>
+hipError_t launch_direct_epi(const Problem &p, int group_m, hipStream_t stream) {
+    if ((p.trans_a != 0) != TA) return hipErrorInvalidValue;
+    if (!direct_applies(p, BM, BN, BK, EDGES)) return hipErrorInvalidValue;
+    const bool tb = p.trans_b != 0;
+    const bool av = rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) && (TA ? p.M : p.K) % 4 == 0;
+    const bool bv = rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) && (tb ? p.K : p.N) % 4 == 0;
+    const bool cv = rows_aligned(p.C, p.ldc, p.stride_c, p.batch, 4);
+    if (!av || !bv) return hipErrorNotSupported;
+    const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
+    if constexpr (!TA) {
+        if (!tb && whole && cv)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, false, false, 4, 4, false, true>(
+                p, group_m, true, stream);
+    }
+    if constexpr (EDGES) {
+        if (tb)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, TA, 4, 4, true, true>(p, group_m,
+                                                                                      cv, stream);
+        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, false, TA, 4, 4, true, true>(p, group_m,
+                                                                                   cv, stream);
+    }
+    return hipErrorNotSupported;
+}
+
 // Tile-table entry of a direct-load tile.  Tiles without EDGES serve whole
 // tiles of untransposed operands only; tiles with EDGES also serve transposed
-// B.  TA tiles serve transposed A (and only that), with B either way.
+// B.  TA tiles serve transposed A (and only that), with B either way.  The
+// fused-epilogue launchers are compiled in their own translation units and
+// joined to the entries by the dispatcher (fused_launchers).
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES, int KG = 1,
           bool TA = false>
 constexpr TileEntry direct_entry(int eff_pct) {

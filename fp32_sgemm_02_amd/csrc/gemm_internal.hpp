@@ -31,7 +31,9 @@ struct Problem {
     long long stride_a = 0, stride_b = 0, stride_c = 0;
     const float *bias = nullptr;   // epilogue: one float per column of C, or none
     int act = SGEMM_ACT_NONE;      // epilogue activation
-    bool has_epilogue() const { return bias != nullptr || act != SGEMM_ACT_NONE; }
+    __host__ __device__ bool has_epilogue() const {
+        return bias != nullptr || act != SGEMM_ACT_NONE;
+    }
 };
 
 // Largest grid y (batch entries per launch); larger batches are split.
@@ -66,6 +68,9 @@ struct TileEntry {
 const TileEntry *mfma_tiles(int *count);
 const TileEntry *mfma_direct_tiles(int *count);      // direct-load tiles, A untransposed
 const TileEntry *mfma_direct_ta_tiles(int *count);   // ... A transposed
+// their fused-epilogue launchers, one per tile in table order
+const LaunchFn *mfma_direct_epi_launchers(int *count);
+const LaunchFn *mfma_direct_ta_epi_launchers(int *count);
 bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 const TileEntry *valu_tiles(int *count);
 const TileEntry *skinny_tiles(int *count);
@@ -95,15 +100,28 @@ __device__ __forceinline__ void select_batch(Problem &p) {
 // evaluated as erfc(-x / sqrt 2) / 2 and (1 + tanh u) / 2 as 1 / (1 + e^-2u):
 // the same functions without the cancellation of 1 + erf and 1 + tanh at
 // negative x.
-__device__ __forceinline__ float activate(int act, float x) {
-    switch (act) {
-    case SGEMM_ACT_RELU: return x < 0.f ? 0.f : x;
-    case SGEMM_ACT_SILU: return x / (1.f + expf(-x));
-    case SGEMM_ACT_GELU_ERF: return 0.5f * x * erfcf(-0.70710678118654752f * x);
-    case SGEMM_ACT_GELU_TANH: {
+template <int ACT>
+__device__ __forceinline__ float activate_t(float x) {
+    if constexpr (ACT == SGEMM_ACT_RELU) {
+        return x < 0.f ? 0.f : x;
+    } else if constexpr (ACT == SGEMM_ACT_SILU) {
+        return x / (1.f + expf(-x));
+    } else if constexpr (ACT == SGEMM_ACT_GELU_ERF) {
+        return 0.5f * x * erfcf(-0.70710678118654752f * x);
+    } else if constexpr (ACT == SGEMM_ACT_GELU_TANH) {
         const float u = 0.79788456080286536f * fmaf(0.044715f * x, x * x, x);
         return x / (1.f + expf(-2.f * u));
+    } else {
+        return x;
     }
+}
+
+__device__ __forceinline__ float activate(int act, float x) {
+    switch (act) {
+    case SGEMM_ACT_RELU: return activate_t<SGEMM_ACT_RELU>(x);
+    case SGEMM_ACT_SILU: return activate_t<SGEMM_ACT_SILU>(x);
+    case SGEMM_ACT_GELU_ERF: return activate_t<SGEMM_ACT_GELU_ERF>(x);
+    case SGEMM_ACT_GELU_TANH: return activate_t<SGEMM_ACT_GELU_TANH>(x);
     default: return x;
     }
 }

@@ -16,19 +16,10 @@ bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges) {
 
 const TileEntry *mfma_direct_tiles(int *count) {
     static const TileEntry tiles[] = {
-        // argument: % of the fp32 peak measured at 4096^3
-        direct_entry<256, 256, 16, 64, 128, 2, false>(93),
-        direct_entry<256, 256, 16, 128, 64, 2, true>(92),
-        direct_entry<256, 128, 16, 64, 64, 2, true>(91),
-        direct_entry<128, 128, 16, 32, 64, 2, true>(92),
-        direct_entry<128, 128, 16, 64, 64, 2, true>(90),
-        direct_entry<256, 256, 32, 64, 128, 2, false>(93),
-        direct_entry<256, 256, 32, 128, 64, 2, false>(93),
-        direct_entry<128, 128, 32, 32, 64, 2, false>(91),
-        direct_entry<64, 64, 32, 32, 64, 2, true, 2>(90),     // 2 k-groups of 2 waves
-        direct_entry<128, 64, 32, 32, 64, 2, true, 2>(90),    // 2 k-groups of 4 waves
-        direct_entry<64, 128, 32, 32, 64, 2, true, 2>(91),    // 2 k-groups of 4 waves
-        direct_entry<128, 128, 32, 64, 64, 2, true, 2>(89),   // 2 k-groups of 4 waves
+#define DIRECT_TILE(BM, BN, BK, WM, WN, NBUF, EDGES, KG, EFF) \
+    direct_entry<BM, BN, BK, WM, WN, NBUF, EDGES, KG>(EFF),
+#include "direct_tiles.inc"
+#undef DIRECT_TILE
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;

@@ -8,14 +8,10 @@ namespace sg {
 
 const TileEntry *mfma_direct_ta_tiles(int *count) {
     static const TileEntry tiles[] = {
-        // argument: % of the fp32 peak expected at 4096^3 (the untransposed
-        // tile of the same shape)
-        direct_entry<256, 256, 16, 128, 64, 2, true, 1, true>(92),
-        direct_entry<256, 128, 16, 64, 64, 2, true, 1, true>(91),
-        direct_entry<128, 128, 16, 64, 64, 2, true, 1, true>(90),
-        direct_entry<128, 128, 32, 64, 64, 2, true, 2, true>(89),   // 2 k-groups of 4 waves
-        direct_entry<128, 64, 32, 64, 64, 2, true, 2, true>(88),    // 2 k-groups of 2 waves
-        direct_entry<64, 128, 32, 64, 64, 2, true, 2, true>(88),    // 2 k-groups of 2 waves
+#define DIRECT_TILE(BM, BN, BK, WM, WN, NBUF, EDGES, KG, EFF) \
+    direct_entry<BM, BN, BK, WM, WN, NBUF, EDGES, KG, true>(EFF),
+#include "direct_ta_tiles.inc"
+#undef DIRECT_TILE
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;

@@ -141,6 +141,7 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
         *reinterpret_cast<floatx4 *>(red + ((wave * VW + c) * 64 + lane) * 4) = acc[c];
     __syncthreads();
     const bool read_c = (p.beta != 0.f);
+    const bool epi = p.has_epilogue();   // bias / activation applied here
     for (int e = tid; e < VW * 64 * 4; e += S::NT) {
         float sum = 0.f;
 #pragma unroll
@@ -152,6 +153,7 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
             float *dst = p.C + (long long)row * p.ldc + col;
             float out = p.alpha * sum;
             if (read_c) out = fmaf(p.beta, *dst, out);
+            if (epi) out = activate(p.act, p.bias ? out + p.bias[col] : out);
             *dst = out;
         }
     }
@@ -267,12 +269,14 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
         acc[j] = v;
     }
     const bool read_c = (p.beta != 0.f);
+    const bool epi = p.has_epilogue();   // bias / activation applied here
     float *crow = p.C + (long long)row * p.ldc;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         if (lane == j && j < p.N) {
             float out = p.alpha * acc[j];
             if (read_c) out = fmaf(p.beta, crow[j], out);
+            if (epi) out = activate(p.act, p.bias ? out + p.bias[j] : out);
             crow[j] = out;
         }
     }
@@ -302,14 +306,18 @@ hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
 template <int VW, int W, int U>
 constexpr TileEntry rows_entry() {
     using S = RowsShape<VW, W>;
+    // the launchers apply a problem's bias / activation themselves, so the
+    // 16-byte launcher is also the fused one
     return TileEntry{{16, 16 * VW, 16 * W, 16, 16 * VW, 0, 0, S::NT, S::LDS_BYTES, 0, 0},
-                     &launch_rows<VW, W, U, true>, &launch_rows<VW, W, U, false>};
+                     &launch_rows<VW, W, U, true>, &launch_rows<VW, W, U, false>, 0,
+                     &launch_rows<VW, W, U, true>};
 }
 
 template <int NB, int W, int U>
 constexpr TileEntry cols_entry() {
     return TileEntry{{W, NB, 256 * U, 1, NB, 0, 0, 64 * W, 0, 0, 0},
-                     &launch_cols<NB, W, U, true>, &launch_cols<NB, W, U, false>};
+                     &launch_cols<NB, W, U, true>, &launch_cols<NB, W, U, false>, 0,
+                     &launch_cols<NB, W, U, true>};
 }
 
 constexpr int kRowsEntries = 4;   // entries [0, 4) are kind 0
