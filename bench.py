@@ -333,7 +333,7 @@ def sweep(args):
         if name in TRANSPOSED_SWEEP:
             rows.extend(sweep_transposed(torch, sg, time_graph, w, sets[0]))
         if name in EPILOGUE_SWEEP:
-            rows.extend(sweep_epilogue(torch, sg, time_graph, w, sets[0]))
+            rows.extend(sweep_epilogue(torch, sg, time_graph, w, sets))
         del sets
         torch.cuda.empty_cache()
     rows.extend(sweep_batched(torch, sg, time_graph))
@@ -371,19 +371,23 @@ def sweep_transposed(torch, sg, time_graph, w, operands):
 EPILOGUE_SWEEP = ("mlp_up", "mlp_decode16")
 
 
-def sweep_epilogue(torch, sg, time_graph, w, operands):
+def sweep_epilogue(torch, sg, time_graph, w, sets):
     """The workload as a linear layer, C = act(X W^T + bias) with W stored
-    N x K, for each activation (sgemm_epilogue, automatic dispatch)."""
-    A, B, C = operands
-    Wt = B.t().contiguous()
-    bias = torch.rand(w.N, device=A.device) * 2 - 1
+    N x K, for each activation (sgemm_epilogue, automatic dispatch), rotating
+    over the operand copies like the plain rows."""
+    ops = [(A, B.t().contiguous(), C) for A, B, C in sets]
+    bias = torch.rand(w.N, device=ops[0][0].device) * 2 - 1
     out = []
     for act, label in ((sg.ACT_NONE, "bias"), (sg.ACT_RELU, "relu"), (sg.ACT_SILU, "silu"),
                        (sg.ACT_GELU_ERF, "gelu"), (sg.ACT_GELU_TANH, "gelu_tanh")):
-        call_i = lambda i: sg.gemm(A, Wt, C, 1.0, 0.0, trans_b=True, bias=bias, act=act)
-        med = statistics.median(time_graph(torch, call_i, 5 if w.flops > 1e11 else 20)) / 1e3
+        def call_i(i, act=act):
+            A, Wt, C = ops[i % len(ops)]
+            sg.gemm(A, Wt, C, 1.0, 0.0, trans_b=True, bias=bias, act=act)
+        calls = max(len(ops), 5 if w.flops > 1e11 else 20)
+        med = statistics.median(time_graph(torch, call_i, calls)) / 1e3
         row = {"workload": f"{w.name}_NT_{label}", "M": w.M, "N": w.N, "K": w.K, "op": "NT",
-               "epilogue": label, "kernel_ms_median": round(med * 1e3, 4),
+               "epilogue": label, "operand_copies": len(ops),
+               "kernel_ms_median": round(med * 1e3, 4),
                "gflops": round(w.flops / med / 1e9, 1), "bound": w.bound}
         if w.bound == "hbm":
             row["gbs"] = round((w.min_bytes + 4 * w.N) / med / 1e9, 1)

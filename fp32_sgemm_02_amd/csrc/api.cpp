@@ -201,7 +201,7 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
     int best = trans ? -1 : general_mfma_tile(p.M, p.N);   // -1: nothing applies
     double best_cost = trans ? 1e300 : tile_cost(tiles[best], p.M, p.N, p.batch);
     Strips best_strips{0, 0};
-    if (trans) strips = nullptr;                          // the skinny family is untransposed
+    if (p.trans_a) strips = nullptr;   // the few-columns strip kernel reads A untransposed
     for (int i = 0; i < count; ++i) {
         const Strips sp = strips ? edge_strips(p, tiles[i]) : Strips{0, 0};
         const Problem m = main_part(p, sp);
@@ -245,18 +245,16 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     const bool explicit_tile = (variant != SGEMM_VARIANT_AUTO) && tile >= 0;
     if (strips) *strips = Strips{0, 0};
     const bool trans = p.trans_a || p.trans_b;
-    if (trans && variant != SGEMM_VARIANT_AUTO && variant != SGEMM_VARIANT_MFMA) return kBadConfig;
+    if (trans && variant == SGEMM_VARIANT_VALU) return kBadConfig;   // VALU reads untransposed
     if (variant == SGEMM_VARIANT_AUTO) {
         Tuned a;
-        if (trans) {
-            a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok), 0};
-            if (a.tile < 0) return kBadConfig;
-        } else if ((flags & SGEMM_FLAG_UNTUNED) || p.batch > 1 ||
-                   !lookup_tuned(p.M, p.N, p.K, a)) {
-            if (skinny_pick(p.M, p.N, p.K) >= 0)
+        if (trans || (flags & SGEMM_FLAG_UNTUNED) || p.batch > 1 ||
+            !lookup_tuned(p.M, p.N, p.K, a)) {
+            if (skinny_pick(p) >= 0)
                 a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
             else
                 a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok, strips), 0};
+            if (a.tile < 0 && a.variant == SGEMM_VARIANT_MFMA) return kBadConfig;
         }
         variant = a.variant;
         tile = a.tile;
@@ -267,8 +265,8 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     const TileEntry *tiles = family(variant, &count);
     if (!tiles) return kBadConfig;
     if (variant == SGEMM_VARIANT_SKINNY) {
-        if (tile < 0) tile = skinny_pick(p.M, p.N, p.K);
-        if (!skinny_fits(tile, p.M, p.N)) return kBadConfig;   // shape is not skinny
+        if (tile < 0) tile = skinny_pick(p);
+        if (!skinny_fits(tile, p)) return kBadConfig;   // shape is not skinny
     } else if (tile < 0) {
         tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, io_ok) : 0;
     }
@@ -277,7 +275,8 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
         if (explicit_tile || variant != SGEMM_VARIANT_MFMA || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // a tuned row naming a tile that is not compiled
     }
-    if (!tile_applies(tiles[tile], pm, io_ok)) {
+    // (skinny tiles were checked by skinny_fits; they serve any transposition of B)
+    if (variant != SGEMM_VARIANT_SKINNY && !tile_applies(tiles[tile], pm, io_ok)) {
         if (explicit_tile || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // automatic choice that cannot run here
         if (strips) *strips = Strips{0, 0};
@@ -375,7 +374,7 @@ int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
         Problem cols = p;
         cols.M = m1;
         cols.N = sp.cols;
-        cols.B = p.B + n1;
+        cols.B = p.trans_b ? p.B + (long long)n1 * p.ldb : p.B + n1;
         cols.C = p.C + n1;
         if (p.bias) cols.bias = p.bias + n1;
         st = resolve(cols, nullptr, ch);

@@ -77,9 +77,9 @@ const TileEntry *skinny_tiles(int *count);
 
 // Skinny family: which entry serves a shape (-1 if none applies), and which
 // orientation an entry serves (0: few rows of C, M <= 16; 1: few columns, N <= 16).
-int skinny_pick(int M, int N, int K);
+int skinny_pick(const Problem &p);
 int skinny_kind(int tile);
-bool skinny_fits(int tile, int M, int N);
+bool skinny_fits(int tile, const Problem &p);
 
 // C = act(beta * C + bias) over p's batch (beta == 0: C is not read); with
 // no epilogue, C = beta * C.  The alpha == 0 / K == 0 case, and the bias and

@@ -18,6 +18,13 @@
 // loads (neighbouring lanes on neighbouring addresses: "a CUDA matmul"
 // section 04), multiplying by the N <= NB columns of B (small, cache
 // resident), then reduces its 64 lanes.
+//
+// Transposed storage.  B stored N x K (a linear layer's weight, C = X W^T):
+// in kind 0 a lane's four k values of one column are contiguous in that
+// column's row of B^T, one 16-byte load per column (4 lanes cover 64
+// contiguous bytes of a row per chunk); in kind 1 the N <= NB rows of B^T
+// are read 16 bytes at a time like A's row.  A stored K x M is served by
+// kind 0 only (its <= 16 columns are read four bytes at a time; A is small).
 #include <cstdint>
 
 #include "gemm_internal.hpp"
@@ -65,23 +72,48 @@ struct RowsRound {
     floatx4 a[U];
 };
 
-// VA: rows of A allow 16-byte loads; VB: rows of B allow VW-float loads.
-template <int VW, int W, int U, bool VA, bool VB>
+// B^T stored N x K: the four k values k0 .. k0+3 of column n (zero past K or N).
+template <bool VEC>
+__device__ __forceinline__ floatx4 load_bcol(const Problem &p, int k0, int n) {
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+    if (n >= p.N || k0 >= p.K) return t;
+    const float *src = p.B + (long long)n * p.ldb + k0;
+    if (VEC && k0 + 3 < p.K) return *reinterpret_cast<const floatx4 *>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (k0 + e < p.K) t[e] = src[e];
+    return t;
+}
+
+// VA: rows of A allow 16-byte loads (untransposed A); VB: rows of B allow
+// VW-float loads (16-byte loads of B^T's rows with TB).  `arow` walks A's
+// row i in steps of `astep` floats (1, or lda for A stored transposed).
+template <int VW, int W, int U, bool VA, bool VB, bool TB>
 __device__ __forceinline__ void rows_load(const Problem &p, int j, int g, int gn, bool row_ok,
-                                          const float *arow, RowsRound<VW, U> &r) {
+                                          const float *arow, long long astep,
+                                          RowsRound<VW, U> &r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int k0 = (j + u * W) * 16 + 4 * g;
+        if constexpr (TB) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) load_brow<VW, VB>(p, k0 + s, gn, r.b[u][s]);
+            for (int c = 0; c < VW; ++c) {
+                const floatx4 t = load_bcol<VB>(p, k0, gn + c);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) r.b[u][s][c] = t[s];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) load_brow<VW, VB>(p, k0 + s, gn, r.b[u][s]);
+        }
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
         if (row_ok) {
-            if (VA && k0 + 3 < p.K) {
+            if (VA && astep == 1 && k0 + 3 < p.K) {
                 a = *reinterpret_cast<const floatx4 *>(arow + k0);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (k0 + e < p.K) a[e] = arow[k0 + e];
+                    if (k0 + e < p.K) a[e] = arow[(long long)(k0 + e) * astep];
             }
         }
         r.a[u] = a;
@@ -105,7 +137,7 @@ __device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&a
 // before the MFMAs of round r, so a round's memory latency overlaps the
 // previous round's arithmetic (loads past K read as zero, so the extra round
 // at the end touches no memory).
-template <int VW, int W, int U, bool VA, bool VB>
+template <int VW, int W, int U, bool VA, bool VB, bool TB>
 __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) {
     using S = RowsShape<VW, W>;
     __shared__ __attribute__((aligned(16))) float red[S::RED];
@@ -116,7 +148,9 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     const int n0 = xcd_remap(blockIdx.x, strips) * S::STRIP;
     const int gn = n0 + VW * i;
     const bool row_ok = i < p.M;
-    const float *arow = p.A + (long long)(row_ok ? i : 0) * p.lda;
+    // row i of op(A): contiguous, or column i of A stored K x M
+    const long long astep = p.trans_a ? p.lda : 1;
+    const float *arow = p.A + (row_ok ? (p.trans_a ? (long long)i : (long long)i * p.lda) : 0);
 
     floatx4 acc[VW];
 #pragma unroll
@@ -124,13 +158,13 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
 
     const int chunks = (p.K + 15) / 16;
     RowsRound<VW, U> r0, r1;
-    rows_load<VW, W, U, VA, VB>(p, wave, g, gn, row_ok, arow, r0);
+    rows_load<VW, W, U, VA, VB, TB>(p, wave, g, gn, row_ok, arow, astep, r0);
     for (int j = wave; j < chunks; j += 2 * U * W) {
-        rows_load<VW, W, U, VA, VB>(p, j + U * W, g, gn, row_ok, arow, r1);
+        rows_load<VW, W, U, VA, VB, TB>(p, j + U * W, g, gn, row_ok, arow, astep, r1);
         pipeline_fence();
         rows_mfma<VW, U>(r0, acc);
         if (j + U * W >= chunks) break;
-        rows_load<VW, W, U, VA, VB>(p, j + 2 * U * W, g, gn, row_ok, arow, r0);
+        rows_load<VW, W, U, VA, VB, TB>(p, j + 2 * U * W, g, gn, row_ok, arow, astep, r0);
         pipeline_fence();
         rows_mfma<VW, U>(r1, acc);
     }
@@ -159,24 +193,33 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     }
 }
 
-template <int VW, int W, int U, bool VA, bool VB>
+template <int VW, int W, int U, bool VA, bool VB, bool TB>
 hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB>), dim3(strips, p.batch), dim3(64 * W), 0,
-                       stream, p, strips);
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB>), dim3(strips, p.batch), dim3(64 * W),
+                       0, stream, p, strips);
     return hipGetLastError();
+}
+
+template <int VW, int W, int U, bool TB>
+hipError_t launch_rows_tb(const Problem &p, bool va, bool vb, hipStream_t stream) {
+    if (va && vb) return launch_rows_as<VW, W, U, true, true, TB>(p, stream);
+    if (va) return launch_rows_as<VW, W, U, true, false, TB>(p, stream);
+    if (vb) return launch_rows_as<VW, W, U, false, true, TB>(p, stream);
+    return launch_rows_as<VW, W, U, false, false, TB>(p, stream);
 }
 
 // VEC: wide loads wherever an operand's rows allow them (decided per operand);
 // otherwise 4-byte loads throughout.
 template <int VW, int W, int U, bool VEC>
 hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
-    const bool va = VEC && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
+    const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
+    if (p.trans_b) {
+        const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);
+        return launch_rows_tb<VW, W, U, true>(p, va, vb, stream);
+    }
     const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, VW);
-    if (va && vb) return launch_rows_as<VW, W, U, true, true>(p, stream);
-    if (va) return launch_rows_as<VW, W, U, true, false>(p, stream);
-    if (vb) return launch_rows_as<VW, W, U, false, true>(p, stream);
-    return launch_rows_as<VW, W, U, false, false>(p, stream);
+    return launch_rows_tb<VW, W, U, false>(p, va, vb, stream);
 }
 
 // ---------------------------------------------------------------- kind 1 ----
@@ -188,9 +231,12 @@ struct ColsRound {
     float b[U][4][NB];
 };
 
-// BT: B is a tight K x NB block (ldb == N == NB), so the 4*NB values of four
-// consecutive k are contiguous and are read as NB 16-byte loads.
-template <int NB, int U, bool VEC, bool BT>
+// BM (B's mode): 0 any K x N layout, read four bytes at a time; 1 a tight
+// K x NB block (ldb == N == NB), so the 4*NB values of four consecutive k are
+// contiguous and are read as NB 16-byte loads; 2 B stored transposed (N x K),
+// each of its N rows read 16 bytes at a time like A's row; 3 the same, four
+// bytes at a time.  VEC: 16-byte loads of A.
+template <int NB, int U, bool VEC, int BM>
 __device__ __forceinline__ void cols_load(const Problem &p, const float *arow, int kbase,
                                           ColsRound<NB, U> &r) {
 #pragma unroll
@@ -205,7 +251,24 @@ __device__ __forceinline__ void cols_load(const Problem &p, const float *arow, i
                 if (k + e < p.K) a[e] = arow[k + e];
         }
         r.a[u] = a;
-        if (BT && k + 3 < p.K) {
+        if constexpr (BM >= 2) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                if (j < p.N) {
+                    const float *src = p.B + (long long)j * p.ldb + k;
+                    if (BM == 2 && k + 3 < p.K) {
+                        t = *reinterpret_cast<const floatx4 *>(src);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (k + e < p.K) t[e] = src[e];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.b[u][e][j] = t[e];
+            }
+        } else if (BM == 1 && k + 3 < p.K) {
             const floatx4 *src = reinterpret_cast<const floatx4 *>(p.B + (long long)k * NB);
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
@@ -237,7 +300,7 @@ __device__ __forceinline__ void cols_fma(const ColsRound<NB, U> &r, float (&acc)
 
 // One wave per row of A; rounds of U chunks double-buffered as in the
 // few-rows kernel (loads past K read as zero and touch no memory).
-template <int NB, int W, int U, bool VEC, bool BT>
+template <int NB, int W, int U, bool VEC, int BM>
 __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
     select_batch(p);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -249,14 +312,14 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
     for (int j = 0; j < NB; ++j) acc[j] = 0.f;
 
     ColsRound<NB, U> r0, r1;
-    cols_load<NB, U, VEC, BT>(p, arow, 4 * lane, r0);
+    cols_load<NB, U, VEC, BM>(p, arow, 4 * lane, r0);
     // kw: the wave's base column of A for the round in r0 (uniform over lanes)
     for (int kw = 0; kw < p.K; kw += 2 * 256 * U) {
-        cols_load<NB, U, VEC, BT>(p, arow, 4 * lane + kw + 256 * U, r1);
+        cols_load<NB, U, VEC, BM>(p, arow, 4 * lane + kw + 256 * U, r1);
         pipeline_fence();
         cols_fma<NB, U>(r0, acc);
         if (kw + 256 * U >= p.K) break;
-        cols_load<NB, U, VEC, BT>(p, arow, 4 * lane + kw + 2 * 256 * U, r0);
+        cols_load<NB, U, VEC, BM>(p, arow, 4 * lane + kw + 2 * 256 * U, r0);
         pipeline_fence();
         cols_fma<NB, U>(r1, acc);
     }
@@ -282,25 +345,33 @@ __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
     }
 }
 
-template <int NB, int W, int U, bool VA, bool BT>
+template <int NB, int W, int U, bool VA, int BM>
 hipError_t launch_cols_as(const Problem &p, hipStream_t stream) {
     const int blocks = (p.M + W - 1) / W;
-    hipLaunchKernelGGL((cols_kernel<NB, W, U, VA, BT>), dim3(blocks, p.batch), dim3(64 * W), 0,
+    hipLaunchKernelGGL((cols_kernel<NB, W, U, VA, BM>), dim3(blocks, p.batch), dim3(64 * W), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-// VEC: 16-byte loads of A where its rows allow them, and B read as one tight
-// K x NB block where it is one (decided per operand); otherwise 4-byte loads.
+template <int NB, int W, int U, int BM>
+hipError_t launch_cols_bm(const Problem &p, bool va, hipStream_t stream) {
+    return va ? launch_cols_as<NB, W, U, true, BM>(p, stream)
+              : launch_cols_as<NB, W, U, false, BM>(p, stream);
+}
+
+// VEC: 16-byte loads of A where its rows allow them, and of B where it is one
+// tight K x NB block or stored transposed with aligned rows (decided per
+// operand); otherwise 4-byte loads.  A stored transposed is not served.
 template <int NB, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
+    if (p.trans_a) return hipErrorInvalidValue;
     const bool va = VEC && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
-    const bool bt = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) && p.N == NB &&
-                    p.ldb == NB;
-    if (va && bt) return launch_cols_as<NB, W, U, true, true>(p, stream);
-    if (va) return launch_cols_as<NB, W, U, true, false>(p, stream);
-    if (bt) return launch_cols_as<NB, W, U, false, true>(p, stream);
-    return launch_cols_as<NB, W, U, false, false>(p, stream);
+    const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);
+    if (p.trans_b)
+        return vb ? launch_cols_bm<NB, W, U, 2>(p, va, stream)
+                  : launch_cols_bm<NB, W, U, 3>(p, va, stream);
+    if (vb && p.N == NB && p.ldb == NB) return launch_cols_bm<NB, W, U, 1>(p, va, stream);
+    return launch_cols_bm<NB, W, U, 0>(p, va, stream);
 }
 
 template <int VW, int W, int U>
@@ -342,22 +413,23 @@ const TileEntry *skinny_tiles(int *count) {
 
 int skinny_kind(int tile) { return tile < kRowsEntries ? 0 : 1; }
 
-bool skinny_fits(int tile, int M, int N) {
+// Kind 0 serves every transposition; kind 1 does not read A stored transposed.
+bool skinny_fits(int tile, const Problem &p) {
     int count = 0;
     const TileEntry *tiles = skinny_tiles(&count);
     if (tile < 0 || tile >= count) return false;
-    return skinny_kind(tile) == 0 ? M <= 16 : N <= tiles[tile].desc.bn;
+    return skinny_kind(tile) == 0 ? p.M <= 16 : (p.N <= tiles[tile].desc.bn && !p.trans_a);
 }
 
-int skinny_pick(int M, int N, int K) {
-    (void)K;
+int skinny_pick(const Problem &p) {
+    const int M = p.M, N = p.N;
     if (M <= 16) {
         // the widest strip that still gives every CU a workgroup, else 16 columns
         if ((N + 63) / 64 >= 256) return 2;
         if ((N + 31) / 32 >= 256) return 1;
         return 0;
     }
-    if (N <= 16) {
+    if (N <= 16 && !p.trans_a) {
         int count = 0;
         const TileEntry *tiles = skinny_tiles(&count);
         for (int t = kRowsEntries; t < count; ++t)

@@ -126,7 +126,12 @@ def test_transposed_entry_point_validation():
     for variant in (sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         cfg = sg.SgemmConfig(variant, -1, 0, 0)
         assert op(1, 0, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
-    # transposed B: only the MFMA family, only tiles flagged for it
+    # the few-columns skinny kernel does not read A transposed
+    kind1 = sg.tile_count(sg.VARIANT_SKINNY) - 1
+    cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, kind1, 0, 0)
+    assert op(1, 0, 64, 8, 64, 1.0, good, 64, good, 8, 0.0, good, 8, None, cfg) == -13
+    # transposed B: the MFMA tiles flagged for it and the skinny family (on
+    # skinny shapes); never the VALU family
     for variant in (sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         cfg = sg.SgemmConfig(variant, -1, 0, 0)
         assert op(0, 1, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
@@ -258,16 +263,25 @@ def test_cblas_entry_point_validation():
 
 def test_op_plan_covers_transpositions():
     """The automatic plan of a transposed product names a tile that serves
-    that transposition, with no edge strips."""
+    that transposition: the skinny family on skinny shapes (few rows: any
+    transposition; few columns: A untransposed), else an MFMA tile flagged for
+    it; edge strips only with A untransposed."""
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
-        for M, N, K in ((4096, 4096, 4096), (4097, 1000, 3001), (37, 45, 5), (1, 4096, 4096)):
+        for M, N, K in ((4096, 4096, 4096), (4097, 1000, 3001), (2049, 2048, 64), (37, 45, 5),
+                        (1, 4096, 4096), (16, 14336, 4096), (4096, 1, 4096)):
             cfg, rows, cols = sg.plan(M, N, K, 0x10000, None, 0x10000, None, 0x10000, None,
                                       trans_a=ta, trans_b=tb)
-            assert cfg.variant == sg.VARIANT_MFMA and (rows, cols) == (0, 0)
+            lab = (ta, tb, M, N, K)
+            if M <= 16 or (N <= 16 and not ta):
+                assert cfg.variant == sg.VARIANT_SKINNY, lab
+                continue
+            assert cfg.variant == sg.VARIANT_MFMA, lab
             f = sg.tile_info(sg.VARIANT_MFMA, cfg.tile)["flags"]
-            assert bool(f & sg.TILE_TRANS_A) == bool(ta), (ta, tb, M, N, K)
+            assert bool(f & sg.TILE_TRANS_A) == bool(ta), lab
             if tb:
-                assert f & sg.TILE_TRANS_B
+                assert f & sg.TILE_TRANS_B, lab
+            if ta:
+                assert (rows, cols) == (0, 0), lab
     a, b = sg.plan(64, 64, 64, trans_a=False), sg.plan(64, 64, 64)
     assert (a[0].variant, a[0].tile, a[1:]) == (b[0].variant, b[0].tile, b[1:])
     out = sg.SgemmConfig()

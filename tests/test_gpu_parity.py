@@ -473,6 +473,37 @@ def test_skinny_tiles(tile, oracle_mod):
         check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=f"skinny t{tile} int")
 
 
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("tile", range(9))
+def test_skinny_tiles_transposed(tile, ta, tb, oracle_mod):
+    """The skinny family on transposed storage: few rows with A and/or B
+    transposed (B stored N x K is the decode layout of a linear layer), few
+    columns with B transposed; 16-byte and 4-byte paths, integers bit-exact."""
+    if tile >= sg.tile_count(sg.VARIANT_SKINNY):
+        pytest.skip("tile not compiled")
+    desc = sg.tile_info(sg.VARIANT_SKINNY, tile)
+    kind = 0 if desc["wm"] == 16 else 1
+    if kind == 1 and ta:
+        pytest.skip("the few-columns kernel does not read A transposed")
+    for i, (M, N, K) in enumerate(SKINNY_CASES[kind] + [(9, 300, 64) if kind == 0 else
+                                                        (300, 9, 64)]):
+        if kind == 1 and N > desc["bn"]:
+            continue
+        kw = dict(variant=sg.VARIANT_SKINNY, tile=tile)
+        A0, B0, C0 = uniform(M, N, K, 250 + i)
+        As, Bs = stored(A0, B0, ta, tb)
+        lab = f"skinny t{tile} ta={ta} tb={tb} {(M, N, K)}"
+        check_op(As, Bs, C0, 0.5, -1.25, run_gpu_op(As, Bs, C0, 0.5, -1.25, ta, tb, **kw), ta,
+                 tb, oracle_mod, label=lab)
+        check_op(As, Bs, C0, 0.5, -1.25,
+                 run_gpu_op(As, Bs, C0, 0.5, -1.25, ta, tb, flags=sg.FLAG_SCALAR_IO, **kw), ta,
+                 tb, oracle_mod, label=lab + " scalar")
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 350 + i, True)
+        Ai, Bi = stored(Ai, Bi, ta, tb)
+        check_op(Ai, Bi, Ci, 0.5, -1.25, run_gpu_op(Ai, Bi, Ci, 0.5, -1.25, ta, tb, **kw), ta,
+                 tb, oracle_mod, exact=True, label=lab + " int")
+
+
 # ------------------------------------------------------------ tiny shapes --
 def test_tiny_shapes_brute_force(oracle_mod):
     """Every (M, N, K) from a set of tiny sizes, through automatic dispatch,
@@ -482,6 +513,11 @@ def test_tiny_shapes_brute_force(oracle_mod):
         A, B, C0 = workloads.draw(M, N, K, "int4", M * 10007 + N * 101 + K, True)
         C = run_gpu(A, B, C0, 0.5, -1.25)
         check(A, B, C0, 0.5, -1.25, C, oracle_mod, exact=True, label=f"tiny {(M, N, K)}")
+        ta, tb = bool((M + K) % 2), bool((N + K) % 2)
+        if ta or tb:
+            As, Bs = stored(A, B, ta, tb)
+            check_op(As, Bs, C0, 0.5, -1.25, run_gpu_op(As, Bs, C0, 0.5, -1.25, ta, tb), ta, tb,
+                     oracle_mod, exact=True, label=f"tiny {(M, N, K)} ta={ta} tb={tb}")
 
 
 # ------------------------------------------------------- full-size shapes --
