@@ -71,7 +71,9 @@ namespace {
 // It multiplies the waves working on one tile, for problems whose tiles are
 // too few or too small to keep every SIMD busy.
 // TB: B is stored transposed (N x K, k contiguous, ldb >= K); its tile is then
-// held in LDS like A's (BN rows of BK floats, same swizzle).
+// held in LDS like A's (BN rows of BK floats, same swizzle), with the rows of
+// each 64-column group permuted so that lane i's four column blocks are four
+// adjacent columns, as for untransposed B (16-byte stores of C).
 // TA: A is stored transposed (K x M, m contiguous, lda >= M); its tile is held
 // in LDS like untransposed B's (BK rows of BM floats, unswizzled) and read the
 // same way: one 16-byte read gives four 16-row blocks their operand of one
@@ -171,11 +173,14 @@ __device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int m0,
     for (int j = 0; j < S::LB; ++j) {
         const int w = (wave * S::LB + j) * 64 * S::BVEC + S::BVEC * lane;
         if constexpr (S::TRANS_B) {
-            // BN rows (n) of BK floats, swizzled like A
+            // BN rows of BK floats, swizzled like A; LDS row 64q + 16c + i
+            // holds column n = 64q + 4i + c of the tile, so that the 16-row
+            // block c of a 64-column group is columns 4i + c
             const int r = w / BK, kk = w % BK;
             const int k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
+            const int n = (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3);
             d.b_k[j] = k;
-            d.b_off[j] = (GUARD && n0 + r >= p.N) ? kOutOfRange : (r * (int)p.ldb + k) * 4;
+            d.b_off[j] = (GUARD && n0 + n >= p.N) ? kOutOfRange : (n * (int)p.ldb + k) * 4;
         } else {
             const int r = w / (S::CPR_B * 4), n = w % (S::CPR_B * 4);
             d.b_k[j] = r;
@@ -233,8 +238,9 @@ __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, in
 // The B fragments of a chunk, v[]:
 //   B untransposed: v[s * CG + cg] = B(k = 16kc + 4g + s, columns
 //     64cg + 4i + 0..3), the B operand of MFMA step s for 4 column blocks;
-//   B transposed:   v[cb] = B(k = 16kc + 4g + 0..3, column 16cb + i), read
-//     like A, one 16-column block for all four steps.
+//   B transposed:   v[cb] = B(k = 16kc + 4g + 0..3, column 64(cb/4) + 4i +
+//     cb%4), read like A (LDS row 16cb + i holds that column), one 16-column
+//     block for all four steps.
 template <class S>
 __device__ __forceinline__ void read_a(const float *buf, int kc, int rb, int lane, int wr,
                                        floatx4 &a) {
@@ -289,8 +295,8 @@ __device__ __forceinline__ float b_operand(const BFrag<S> &b, int s, int cb) {
 
 // The MFMAs of unit u over one k-chunk (4*CB of them).  acc[rb][cb] covers
 // rows 16rb + i (A untransposed) or 64(rb/4) + 4i + rb%4 (transposed) of the
-// wave tile, and columns 64(cb/4) + 4i + cb%4 (B untransposed) or 16cb + i
-// (transposed), i = lane % 16.
+// wave tile, and columns 64(cb/4) + 4i + cb%4 (B either way), i = lane % 16:
+// lane i holds four adjacent columns of a row, stored with one 16-byte write.
 template <class S>
 __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S> &b,
                                           floatx4 (&acc)[S::RB][S::CB]) {
@@ -461,7 +467,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     float bcol[S::CB];   // bias of the column of acc[.][cb] (EPI)
 #pragma unroll
     for (int cb = 0; cb < S::CB; ++cb) {
-        const int gn = col0 + (S::TRANS_B ? cb * 16 + i : (cb / 4) * 64 + 4 * i + cb % 4);
+        const int gn = col0 + (cb / 4) * 64 + 4 * i + cb % 4;
         bcol[cb] = (EPI && p.bias && (!GUARD || gn < p.N)) ? p.bias[gn] : 0.f;
     }
     auto store = [&](auto act_tag) {
@@ -480,19 +486,6 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
                                           : row0 + rb * 16 + 4 * g + r;
                 if (GUARD && gm >= p.M) continue;
                 float *crow = p.C + (long long)gm * p.ldc;
-                if constexpr (S::TRANS_B) {
-                    // acc[rb][cb][r] is C(gm, col0 + 16cb + i): 16 lanes write 64
-                    // contiguous bytes
-#pragma unroll
-                    for (int cb = 0; cb < S::CB; ++cb) {
-                        const int gn = col0 + cb * 16 + i;
-                        if (GUARD && gn >= p.N) continue;
-                        float out = p.alpha * acc[rb][cb][r];
-                        if (read_c) out = fmaf(p.beta, crow[gn], out);
-                        crow[gn] = finish(out, cb);
-                    }
-                    continue;
-                }
 #pragma unroll
                 for (int cg = 0; cg < S::CG; ++cg) {
                     const int gn = col0 + cg * 64 + 4 * i;

@@ -386,12 +386,11 @@ constexpr TileEntry rows_entry() {
 
 template <int NB, int W, int U>
 constexpr TileEntry cols_entry() {
-    return TileEntry{{W, NB, 256 * U, 1, NB, 0, 0, 64 * W, 0, 0, 0},
+    return TileEntry{{W, NB, 256 * U, 1, NB, 1, 0, 64 * W, 0, 0, 0},
                      &launch_cols<NB, W, U, true>, &launch_cols<NB, W, U, false>, 0,
                      &launch_cols<NB, W, U, true>};
 }
 
-constexpr int kRowsEntries = 4;   // entries [0, 4) are kind 0
 
 }  // namespace
 
@@ -411,7 +410,12 @@ const TileEntry *skinny_tiles(int *count) {
     return tiles;
 }
 
-int skinny_kind(int tile) { return tile < kRowsEntries ? 0 : 1; }
+// The kind is recorded in the tile descriptor's tm field.
+int skinny_kind(int tile) {
+    int count = 0;
+    const TileEntry *tiles = skinny_tiles(&count);
+    return (tile >= 0 && tile < count) ? tiles[tile].desc.tm : -1;
+}
 
 // Kind 0 serves every transposition; kind 1 does not read A stored transposed.
 bool skinny_fits(int tile, const Problem &p) {
@@ -424,16 +428,18 @@ bool skinny_fits(int tile, const Problem &p) {
 int skinny_pick(const Problem &p) {
     const int M = p.M, N = p.N;
     if (M <= 16) {
-        // the widest strip that still gives every CU a workgroup, else 16 columns
-        if ((N + 63) / 64 >= 256) return 2;
+        // the widest strip that still gives three quarters of the CUs a
+        // workgroup (measured best at 16 x 14336 x 4096 for either storage of
+        // B), else 32 or 16 columns
+        if ((N + 63) / 64 >= 192) return 2;
         if ((N + 31) / 32 >= 256) return 1;
         return 0;
     }
     if (N <= 16 && !p.trans_a) {
         int count = 0;
         const TileEntry *tiles = skinny_tiles(&count);
-        for (int t = kRowsEntries; t < count; ++t)
-            if (N <= tiles[t].desc.bn) return t;
+        for (int t = 0; t < count; ++t)
+            if (skinny_kind(t) == 1 && N <= tiles[t].desc.bn) return t;
     }
     return -1;
 }

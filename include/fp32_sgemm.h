@@ -98,7 +98,8 @@ typedef struct sgemm_config {
 typedef struct sgemm_tile_desc {
     int bm, bn, bk;   /* workgroup tile of C (bm x bn) and K step (bk) */
     int wm, wn;       /* per-wave tile of C */
-    int tm, tn;       /* per-lane micro-tile (VALU family; 0 for MFMA) */
+    int tm, tn;       /* per-lane micro-tile (VALU family; 0 for MFMA); skinny family:
+                         tm = kernel kind (0: few rows of C, 1: few columns) */
     int threads;      /* workgroup size */
     int lds_bytes;    /* LDS per workgroup */
     int stages;       /* LDS buffers in the K pipeline (0: no LDS staging) */

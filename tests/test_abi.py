@@ -97,7 +97,9 @@ def test_bad_configuration():
     cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, -1, 0, 0)
     assert sg.sgemm_ex(64, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
     # a few-columns tile cannot serve a few-rows shape with many columns
-    cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, sg.tile_count(sg.VARIANT_SKINNY) - 1, 0, 0)
+    kind1 = [t for t in range(sg.tile_count(sg.VARIANT_SKINNY))
+             if sg.tile_info(sg.VARIANT_SKINNY, t)["tm"] == 1][-1]
+    cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, kind1, 0, 0)
     assert sg.sgemm_ex(8, 64, 4, 1.0, good, 4, good, 64, 0.0, good, 64, None, cfg) == -13
 
 
@@ -127,7 +129,8 @@ def test_transposed_entry_point_validation():
         cfg = sg.SgemmConfig(variant, -1, 0, 0)
         assert op(1, 0, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
     # the few-columns skinny kernel does not read A transposed
-    kind1 = sg.tile_count(sg.VARIANT_SKINNY) - 1
+    kind1 = [t for t in range(sg.tile_count(sg.VARIANT_SKINNY))
+             if sg.tile_info(sg.VARIANT_SKINNY, t)["tm"] == 1][-1]
     cfg = sg.SgemmConfig(sg.VARIANT_SKINNY, kind1, 0, 0)
     assert op(1, 0, 64, 8, 64, 1.0, good, 64, good, 8, 0.0, good, 8, None, cfg) == -13
     # transposed B: the MFMA tiles flagged for it and the skinny family (on

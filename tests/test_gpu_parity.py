@@ -453,12 +453,12 @@ SKINNY_CASES = {
 }
 
 
-@pytest.mark.parametrize("tile", range(9))
+@pytest.mark.parametrize("tile", range(16))
 def test_skinny_tiles(tile, oracle_mod):
     if tile >= sg.tile_count(sg.VARIANT_SKINNY):
         pytest.skip("tile not compiled")
     desc = sg.tile_info(sg.VARIANT_SKINNY, tile)
-    kind = 0 if desc["wm"] == 16 else 1
+    kind = desc["tm"]
     for i, (M, N, K) in enumerate(SKINNY_CASES[kind]):
         if kind == 1 and N > desc["bn"]:
             continue
@@ -474,7 +474,7 @@ def test_skinny_tiles(tile, oracle_mod):
 
 
 @pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
-@pytest.mark.parametrize("tile", range(9))
+@pytest.mark.parametrize("tile", range(16))
 def test_skinny_tiles_transposed(tile, ta, tb, oracle_mod):
     """The skinny family on transposed storage: few rows with A and/or B
     transposed (B stored N x K is the decode layout of a linear layer), few
@@ -482,11 +482,11 @@ def test_skinny_tiles_transposed(tile, ta, tb, oracle_mod):
     if tile >= sg.tile_count(sg.VARIANT_SKINNY):
         pytest.skip("tile not compiled")
     desc = sg.tile_info(sg.VARIANT_SKINNY, tile)
-    kind = 0 if desc["wm"] == 16 else 1
+    kind = desc["tm"]
     if kind == 1 and ta:
         pytest.skip("the few-columns kernel does not read A transposed")
-    for i, (M, N, K) in enumerate(SKINNY_CASES[kind] + [(9, 300, 64) if kind == 0 else
-                                                        (300, 9, 64)]):
+    cases = SKINNY_CASES[kind] + [(9, 300, 64) if kind == 0 else (300, 9, 64)]
+    for i, (M, N, K) in enumerate(cases):
         if kind == 1 and N > desc["bn"]:
             continue
         kw = dict(variant=sg.VARIANT_SKINNY, tile=tile)
