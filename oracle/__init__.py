@@ -59,6 +59,8 @@ def _load():
         i, f, p, ll = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_longlong
         lib.oracle_sgemm_epilogue.restype = i
         lib.oracle_sgemm_epilogue.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p, i, i]
+        lib.oracle_gemm_mixed.restype = i
+        lib.oracle_gemm_mixed.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, i]
         lib.oracle_sgemm_strided_batched.restype = i
         lib.oracle_sgemm_strided_batched.argtypes = [i, i, i, i, i, f, p, i, ll, p, i, ll, f, p,
                                                      i, ll, i, i]
@@ -139,6 +141,42 @@ def sgemm(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None,
                                        threads)
     if st != 0:
         raise RuntimeError(f"oracle returned {st}")
+    return C
+
+
+BF16, F16 = 1, 2
+
+
+def _ld16(x: np.ndarray) -> int:
+    assert x.dtype == np.uint16 and x.ndim == 2
+    if x.size == 0:
+        return max(x.shape[1], 1)
+    assert x.shape[1] <= 1 or x.strides[1] == 2, "rows must be contiguous"
+    ld = x.strides[0] // 2
+    if x.shape[0] <= 1:
+        ld = max(ld, x.shape[1], 1)
+    return ld
+
+
+def gemm_mixed(dtype: int, A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None,
+               alpha: float = 1.0, beta: float = 0.0, nthreads: int | None = None,
+               trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+    """C = alpha * op(A) @ op(B) + beta * C with A and B given as 16-bit float
+    bit patterns (uint16 arrays; dtype BF16 or F16) and C float32, through
+    oracle_gemm_mixed."""
+    lib = _load()
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
+    assert K == K2, "inner dimensions differ"
+    if C is None:
+        assert beta == 0.0
+        C = np.empty((M, N), dtype=np.float32)
+    assert C.shape == (M, N)
+    st = lib.oracle_gemm_mixed(int(dtype), int(trans_a), int(trans_b), M, N, K, float(alpha),
+                               _base(A), _ld16(A), _base(B), _ld16(B), float(beta), _base(C),
+                               _ld(C), int(nthreads or default_threads()))
+    if st != 0:
+        raise RuntimeError(f"oracle_gemm_mixed returned {st}")
     return C
 
 

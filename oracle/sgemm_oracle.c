@@ -58,13 +58,22 @@
  *     identities that avoid the cancellation of 1 + erf and 1 + tanh for
  *     negative x.  With alpha == 0 or K == 0 the sum is beta * C + bias (A
  *     and B not read).
+ *   - oracle_gemm_mixed: the same product with A and B given as 16-bit
+ *     floats (bfloat16: the high half of an IEEE binary32; float16: IEEE
+ *     binary16), C and the scalars in fp32 -- the reduced-precision inputs of
+ *     the tensor-core hardware the fine print of "The GEMM Scrapbook" points
+ *     to (fp16 rates above the fp32 ladder).  Every 16-bit value is decoded exactly
+ *     (both formats embed in binary32) and the product is the definition
+ *     above on the decoded values.
  */
 #include <math.h>
 #include <pthread.h>
+#include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 #include <stddef.h>
 
-#define ORACLE_VERSION 3
+#define ORACLE_VERSION 4
 
 /* activation codes of oracle_sgemm_epilogue */
 #define ORACLE_ACT_NONE 0
@@ -272,6 +281,73 @@ int oracle_sgemm_strided_batched(int trans_a, int trans_b, int M, int N, int K, 
         if (r != 0) return r;
     }
     return 0;
+}
+
+/* 16-bit input formats of oracle_gemm_mixed */
+#define ORACLE_BF16 1
+#define ORACLE_F16 2
+
+/* The exact value of a 16-bit float. */
+static float decode16(int dtype, uint16_t h)
+{
+    if (dtype == ORACLE_BF16) {
+        /* the high 16 bits of a binary32 (sign, 8-bit exponent, 7 stored
+           fraction bits); the low half is zero */
+        const uint32_t bits = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return f;
+    }
+    /* binary16: sign, 5-bit exponent (bias 15), 10 fraction bits */
+    const int sign = (h >> 15) & 1, e = (h >> 10) & 31, frac = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)frac, -24);                   /* zero and subnormals */
+    else if (e == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), e - 25);       /* 1.frac x 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+/*
+ * C = alpha * op(A) * op(B) + beta * C with A and B stored as 16-bit floats
+ * (dtype ORACLE_BF16 or ORACLE_F16; storage and leading dimensions in
+ * elements as oracle_sgemm_op's) and C in fp32.  Arguments: dtype, then
+ * oracle_sgemm_op's.  Returns 0, -1 for an unknown dtype, or oracle_sgemm_op's
+ * codes shifted by one; -100 when memory is short.
+ */
+int oracle_gemm_mixed(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                      const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                      float beta, float *C, int ldc, int nthreads)
+{
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return -1;
+    /* the checks look at the arguments only, not at the data */
+    const int st = check_op(trans_a, trans_b, M, N, K, alpha, (const float *)A, lda,
+                            (const float *)B, ldb, C, ldc);
+    if (st != 0) return st - 1;
+    if (M == 0 || N == 0) return 0;
+    const int reads_ab = (alpha != 0.0f && K > 0);
+    const long long a_rows = trans_a ? K : M, b_rows = trans_b ? N : K;
+    const long long a_cols = trans_a ? M : K, b_cols = trans_b ? K : N;
+    float *a = NULL, *b = NULL;
+    if (reads_ab) {
+        a = (float *)malloc(sizeof(float) * (size_t)(a_rows * a_cols));
+        b = (float *)malloc(sizeof(float) * (size_t)(b_rows * b_cols));
+        if (!a || !b) { free(a); free(b); return -100; }
+        for (long long r = 0; r < a_rows; ++r)
+            for (long long c = 0; c < a_cols; ++c)
+                a[r * a_cols + c] = decode16(dtype, A[r * lda + c]);
+        for (long long r = 0; r < b_rows; ++r)
+            for (long long c = 0; c < b_cols; ++c)
+                b[r * b_cols + c] = decode16(dtype, B[r * ldb + c]);
+    }
+    const int r = sgemm_core(trans_a, trans_b, M, N, K, alpha, a, (int)(a_cols > 1 ? a_cols : 1),
+                             b, (int)(b_cols > 1 ? b_cols : 1), beta, C, ldc, NULL,
+                             ORACLE_ACT_NONE, nthreads);
+    free(a);
+    free(b);
+    return r;
 }
 
 /* The untransposed product, with the argument numbering of its own list. */

@@ -27,6 +27,11 @@ test_oracle.py).  The pins are:
                 CDF, its tanh form and SiLU as printed in their papers) and
                 rounded to fp32: within one fp32 ulp; ReLU and bias exact on
                 integers; the alpha = 0 path; act codes checked.
+  mixed         (16-bit inputs) the decoding of listed bfloat16 / float16 bit
+                patterns against the values their formats define, every finite
+                pattern against numpy's binary16 (float16) or the binary32
+                embedding (bfloat16), and exact rational brute force on
+                random 16-bit inputs for every transposition.
   batched       (strided-batched entry point) exact rational brute force on
                 every matrix of a batch with padded, shared (stride 0) and
                 transposed operands; batch = 0 touches nothing; stride and
@@ -283,7 +288,7 @@ def pin_transposed(call_op, rng, dims=range(1, 4), square_only=False) -> list[st
 
 
 def all_pins(call, seed=1234, square_only=False, call_op=None, call_epi=None,
-             call_batched=None) -> list[str]:
+             call_batched=None, call_mixed=None) -> list[str]:
     """Every pin; square_only restricts brute force to M = N = K (used for
     broken copies whose indexing is only memory-safe on square shapes).
     call_op, call_epi, call_batched, when given, are the entry points with
@@ -305,6 +310,8 @@ def all_pins(call, seed=1234, square_only=False, call_op=None, call_epi=None,
         fails += pin_epilogue(call_epi, rng)
     if call_batched is not None:
         fails += pin_batched(call_batched, rng)
+    if call_mixed is not None:
+        fails += pin_mixed(call_mixed, rng)
     return fails
 
 
@@ -518,4 +525,91 @@ def pin_batched(call_batched, rng) -> list[str]:
     for args, code in checks:
         if call_batched(*args) != code:
             fails.append(f"batched check {code}")
+    return fails
+
+
+# ---------------------------------------------------------- 16-bit inputs --
+BF16, F16 = 1, 2
+
+# bit patterns with the values their formats define (closed forms)
+DECODE_CASES = {
+    BF16: [(0x3F80, 1.0), (0xC000, -2.0), (0x3F81, 1.0 + 2.0 ** -7), (0x0001, 2.0 ** -133),
+           (0x0080, 2.0 ** -126), (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127), (0x0000, 0.0),
+           (0x8000, -0.0), (0x7F80, np.inf), (0xFF80, -np.inf), (0x7FC0, np.nan),
+           (0x4049, 3.140625)],
+    F16: [(0x3C00, 1.0), (0xC000, -2.0), (0x3C01, 1.0 + 2.0 ** -10), (0x0001, 2.0 ** -24),
+          (0x03FF, 1023 * 2.0 ** -24), (0x0400, 2.0 ** -14), (0x7BFF, 65504.0), (0x0000, 0.0),
+          (0x8000, -0.0), (0x7C00, np.inf), (0xFC00, -np.inf), (0x7E00, np.nan),
+          (0x4248, 3.140625)],
+}
+
+
+def decode_ref(dtype, bits: np.ndarray) -> np.ndarray:
+    """Test-side decoding: numpy's binary16 for F16; for BF16 the binary32
+    whose high half the pattern is."""
+    with np.errstate(invalid="ignore"):
+        if dtype == F16:
+            return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_mixed(call_mixed, rng) -> list[str]:
+    """call_mixed(dtype, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
+    on flat buffers (A, B uint16 bit patterns, C float32)."""
+    fails = []
+    for dtype in (BF16, F16):
+        # decoding: every listed pattern times 1.0 (K = 1) gives its value
+        pats = np.array([b for b, _ in DECODE_CASES[dtype]], np.uint16)
+        vals = np.array([v for _, v in DECODE_CASES[dtype]], np.float64)
+        one = np.array([DECODE_CASES[dtype][0][0]], np.uint16)
+        C = np.full(len(pats), 7.0, np.float32)
+        st = call_mixed(dtype, 0, 0, len(pats), 1, 1, 1.0, pats, 1, one, 1, 0.0, C, 1)
+        # (a lone -0 product sums to +0 from the zero accumulator: compare values)
+        ok = st == 0 and np.array_equal(np.isnan(C), np.isnan(vals)) and \
+            np.all((C == vals) | np.isnan(vals))
+        if not ok:
+            fails.append(f"mixed decode dtype {dtype}")
+        # every finite pattern through the same route, against the test-side decode
+        allp = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        ref = decode_ref(dtype, allp)
+        fin = np.isfinite(ref) & (np.abs(ref) < 3e38)
+        allp = allp[fin]
+        C = np.empty(len(allp), np.float32)
+        st = call_mixed(dtype, 0, 0, len(allp), 1, 1, 1.0, allp, 1, one, 1, 0.0, C, 1)
+        if st or not np.array_equal(C.astype(np.float64), ref[fin]):
+            fails.append(f"mixed decode all patterns dtype {dtype}")
+        # exact rational brute force over small shapes and every transposition
+        for trial in range(24):
+            M, N, K = (int(v) for v in rng.integers(1, 4, 3))
+            ta, tb = int(rng.integers(2)), int(rng.integers(2))
+            # finite values of moderate size: random sign, exponent, fraction
+            def draw(shape):
+                x = rng.uniform(-4, 4, shape)
+                if dtype == F16:
+                    return x.astype(np.float16).view(np.uint16)
+                return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            Ab, Bb = draw((M, K)), draw((K, N))
+            Av, Bv = decode_ref(dtype, Ab), decode_ref(dtype, Bb)
+            C0 = rng.uniform(-2, 2, (M, N)).astype(F32)
+            alpha, beta = float(F32(rng.uniform(-3, 3))), float(F32(rng.uniform(-3, 3)))
+            As = np.ascontiguousarray(Ab.T if ta else Ab)
+            Bs = np.ascontiguousarray(Bb.T if tb else Bb)
+            C = C0.copy()
+            st = call_mixed(dtype, ta, tb, M, N, K, alpha, As.reshape(-1), As.shape[1],
+                            Bs.reshape(-1), Bs.shape[1], beta, C.reshape(-1), N)
+            if st:
+                fails.append(f"mixed status {st}")
+                continue
+            for i in range(M):
+                for j in range(N):
+                    ex, mag = exact_cell(Av.astype(F32), Bv.astype(F32), C0, i, j, alpha, beta)
+                    if not within_fp64_rounding(float(C[i, j]), ex, mag, K):
+                        fails.append(f"mixed dtype {dtype} {(ta, tb, M, N, K)} cell {(i, j)}")
+                        break
+    buf = np.zeros(16, np.uint16)
+    cb = np.zeros(16, np.float32)
+    if call_mixed(3, 0, 0, 2, 2, 2, 1.0, buf, 2, buf, 2, 0.0, cb, 2) != -1:
+        fails.append("mixed dtype check")
+    if call_mixed(BF16, 0, 0, 2, 2, 4, 1.0, buf, 2, buf, 2, 0.0, cb, 2) != -9:   # lda < K
+        fails.append("mixed lda check")
     return fails

@@ -73,9 +73,22 @@ def _batched_caller(lib, nthreads=1):
     return call_batched
 
 
+def _mixed_caller(lib, nthreads=1):
+    fn = lib.oracle_gemm_mixed
+    fn.restype = ctypes.c_int
+    i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    fn.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, i]
+
+    def call_mixed(dtype, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+        q = lambda x: x.ctypes.data if (x is not None and x.size) else None
+        return fn(dtype, ta, tb, M, N, K, alpha, q(A), lda, q(B), ldb, beta, q(C), ldc, nthreads)
+    return call_mixed
+
+
 def _callers(lib, nthreads=1):
     return dict(call_op=_op_caller(lib, nthreads), call_epi=_epi_caller(lib, nthreads),
-                call_batched=_batched_caller(lib, nthreads))
+                call_batched=_batched_caller(lib, nthreads),
+                call_mixed=_mixed_caller(lib, nthreads))
 
 
 @pytest.fixture(scope="module")
@@ -262,6 +275,16 @@ MUTANTS = {
     "batch_stride_a_ignored": ("A ? A + b * stride_a : A", "A", False),
     # the batch stride of C ignored
     "batch_stride_c_ignored": ("C + b * stride_c, ldc", "C, ldc", False),
+    # bfloat16 decoded from the wrong bits
+    "bf16_shift": ("const uint32_t bits = (uint32_t)h << 16;",
+                   "const uint32_t bits = (uint32_t)h << 15;", False),
+    # float16 exponent bias off by one
+    "f16_bias": ("v = ldexp((double)(1024 + frac), e - 25);",
+                 "v = ldexp((double)(1024 + frac), e - 24);", False),
+    # float16 subnormals scaled wrongly
+    "f16_subnormal": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -23);", False),
+    # float16 sign dropped
+    "f16_sign": ("return (float)(sign ? -v : v);", "return (float)v;", False),
     # the last matrix of the batch skipped
     "batch_last_skipped": ("for (int b = 0; b < batch; ++b)", "for (int b = 0; b + 1 < batch; ++b)",
                            False),
