@@ -16,9 +16,10 @@ import os
 
 __all__ = [
     "sgemm", "sgemm_ex", "sgemm_op", "sgemm_cblas", "sgemm_epilogue", "sgemm_strided_batched",
-    "gemm", "gemm_batched", "select", "tile_count", "tile_info", "status_string",
+    "sgemm_mixed", "gemm", "gemm_batched", "gemm_mixed", "select", "tile_count", "tile_info", "status_string",
     "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
-    "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
+    "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "VARIANT_MFMA16",
+    "VARIANT_GENERIC16", "DTYPE_BF16", "DTYPE_F16", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
     "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A",
     "ACT_NONE", "ACT_RELU", "ACT_SILU", "ACT_GELU_ERF", "ACT_GELU_TANH",
 ]
@@ -27,6 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp32sgemm.so")
 
 VARIANT_AUTO, VARIANT_MFMA, VARIANT_VALU, VARIANT_SKINNY = 0, 1, 2, 3
+VARIANT_MFMA16, VARIANT_GENERIC16 = 4, 5
+DTYPE_BF16, DTYPE_F16 = 1, 2
 FLAG_SCALAR_IO = 0x1
 FLAG_UNTUNED = 0x2
 TILE_WHOLE = 0x1
@@ -91,6 +94,10 @@ def _load():
     lib.sgemm_strided_batched_ex.restype = i
     lib.sgemm_strided_batched_ex.argtypes = (lib.sgemm_strided_batched.argtypes +
                                              [ctypes.POINTER(SgemmConfig)])
+    lib.sgemm_mixed.restype = i
+    lib.sgemm_mixed.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_mixed_ex.restype = i
+    lib.sgemm_mixed_ex.argtypes = lib.sgemm_mixed.argtypes + [ctypes.POINTER(SgemmConfig)]
     lib.sgemm_cblas.restype = i
     lib.sgemm_cblas.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_op_plan.restype = i
@@ -151,6 +158,15 @@ def sgemm_strided_batched(trans_a, trans_b, M, N, K, alpha, A, lda, stride_a, B,
     if cfg is None:
         return _load().sgemm_strided_batched(*args)
     return _load().sgemm_strided_batched_ex(*args, ctypes.byref(cfg))
+
+
+def sgemm_mixed(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                stream=None, cfg: SgemmConfig | None = None) -> int:
+    """Raw C-ABI call of sgemm_mixed (cfg given: sgemm_mixed_ex)."""
+    args = (dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    if cfg is None:
+        return _load().sgemm_mixed(*args)
+    return _load().sgemm_mixed_ex(*args, ctypes.byref(cfg))
 
 
 def sgemm_cblas(order, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
@@ -280,6 +296,44 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool =
             st = sgemm_ex(*args, s, cfg=cfg)
         else:
             st = sgemm(*args, s)
+    if st != 0:
+        raise SgemmError(st)
+    return C
+
+
+def gemm_mixed(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
+               trans_b: bool = False, variant: int = VARIANT_AUTO, tile: int = -1, group_m: int = 0,
+               stream=None):
+    """C = alpha * op(A) @ op(B) + beta * C for 2-D bfloat16 or float16 CUDA
+    tensors A and B (the same dtype) and a float32 C (sgemm_mixed: fp32
+    accumulation).  Layout and stream handling as gemm()."""
+    import torch
+
+    codes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+    if A.dtype not in codes or B.dtype != A.dtype:
+        raise ValueError("A and B must both be bfloat16 or both float16")
+    if not A.is_cuda or B.device != A.device:
+        raise ValueError("A and B must be GPU tensors on one device")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _check_tensor("C", C, torch, A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"C must be ({M}, {N})")
+    with torch.cuda.device(A.device):
+        s = _stream_handle(stream, A.device, torch)
+        ptr = lambda t: t.data_ptr() if t.numel() else None
+        explicit = not (variant == VARIANT_AUTO and tile < 0 and group_m == 0)
+        cfg = SgemmConfig(variant, tile, 0, group_m) if explicit else None
+        st = sgemm_mixed(codes[A.dtype], int(trans_a), int(trans_b), M, N, K, float(alpha),
+                         ptr(A), _ld(A), ptr(B), _ld(B), float(beta), ptr(C), _ld(C), s, cfg=cfg)
     if st != 0:
         raise SgemmError(st)
     return C

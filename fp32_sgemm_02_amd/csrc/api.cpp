@@ -28,6 +28,7 @@ constexpr int kBadStrideA = -26;
 constexpr int kBadStrideB = -27;
 constexpr int kBadStrideC = -28;
 constexpr int kBadBatch = -29;
+constexpr int kBadDtype = -30;
 
 // A status of the row-major call that serves a column-major one (operands
 // swapped, M and N swapped), renamed after the caller's arguments.
@@ -391,6 +392,87 @@ int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
     return st;
 }
 
+// ---- 16-bit inputs -----------------------------------------------------------
+// The 16-bit tile of least estimated time for the word problem pw (the fp32
+// cost model over the 16-bit tile list), or -1.
+int pick_tile16(const Problem &pw) {
+    int best = -1;
+    double best_cost = 1e300;
+    for (int t = 0; t < tiles16_count(); ++t) {
+        const sgemm_tile_desc &d = *tile16_desc(t);
+        if (!direct_applies(pw, d.bm, d.bn, d.bk / 2, true)) continue;
+        const long long tiles = (long long)((pw.M + d.bm - 1) / d.bm) * ((pw.N + d.bn - 1) / d.bn);
+        const double c = (double)((tiles * pw.batch + kCUs - 1) / kCUs) * d.bm * d.bn /
+                         tile16_eff(t);
+        if (c < best_cost) {
+            best = t;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
+// C = alpha * op(A) * op(B) + beta * C with A, B 16-bit (dtype) and C fp32.
+// Argument checks as sgemm_op's (A and B need 2-byte alignment), -30 for an
+// unknown dtype.  The matrix-core tiles serve A untransposed with B
+// transposed when K, lda, ldb are even and A, B 4-byte aligned (the operands
+// are then word matrices along k); everything else runs the generic kernel.
+int run16(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha, const void *A,
+          int lda, const void *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
+          const sgemm_config *cfg) {
+    if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return kBadDtype;
+    if (trans_a != 0 && trans_a != 1) return kBadTransA;
+    if (trans_b != 0 && trans_b != 1) return kBadTransB;
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    const int a_cols = trans_a ? M : K, b_cols = trans_b ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1)) return -6;
+    if (ldb < (b_cols > 1 ? b_cols : 1)) return -8;
+    if (ldc < (N > 1 ? N : 1)) return -11;
+    if (M == 0 || N == 0) return 0;
+    const bool reads_ab = (alpha != 0.f) && K > 0;
+    auto aligned2 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 1u) == 0; };
+    if (reads_ab && (!A || !aligned2(A))) return -5;
+    if (reads_ab && (!B || !aligned2(B))) return -7;
+    if (!C || !aligned4(C)) return -10;
+    if (!reads_ab) {
+        if (beta == 1.f) return 0;
+        Problem p{M, N, K, alpha, beta, nullptr, 1, nullptr, 1, C, ldc};
+        return to_status(launch_elementwise(p, beta, stream));
+    }
+    int variant = cfg ? cfg->variant : SGEMM_VARIANT_AUTO;
+    int tile = cfg ? cfg->tile : -1;
+    const int group_m = cfg ? cfg->group_m : 0;
+    const bool mfma_ok = !trans_a && trans_b && K % 2 == 0 && lda % 2 == 0 && ldb % 2 == 0 &&
+                         aligned4(A) && aligned4(B);
+    Problem pw{M,   N,   K / 2, alpha, beta, static_cast<const float *>(A), lda / 2,
+               static_cast<const float *>(B), ldb / 2, C, ldc};
+    pw.trans_b = 1;
+    if (variant == SGEMM_VARIANT_AUTO)
+        variant = (mfma_ok && pick_tile16(pw) >= 0) ? SGEMM_VARIANT_MFMA16
+                                                    : SGEMM_VARIANT_GENERIC16;
+    if (variant == SGEMM_VARIANT_MFMA16) {
+        if (!mfma_ok) return kBadConfig;
+        if (tile < 0) tile = pick_tile16(pw);
+        if (tile < 0 || tile >= tiles16_count()) return kBadConfig;
+        const sgemm_tile_desc &d = *tile16_desc(tile);
+        if (!direct_applies(pw, d.bm, d.bn, d.bk / 2, true)) return kBadConfig;
+        return to_status(launch_tile16(tile, dtype, pw, group_m, stream));
+    }
+    if (variant == SGEMM_VARIANT_GENERIC16 && tile <= 0) {
+        Problem16 q{M,   N,   K, alpha, beta, static_cast<const unsigned short *>(A), lda,
+                    static_cast<const unsigned short *>(B), ldb, C, ldc};
+        q.trans_a = trans_a;
+        q.trans_b = trans_b;
+        return to_status(launch_generic16(dtype, q, stream));
+    }
+    return kBadConfig;
+}
+
+// The descriptor of the generic 16-bit kernel (one configuration).
+const sgemm_tile_desc kGeneric16Desc{64, 64, 16, 64, 64, 4, 4, 256, 2 * 16 * 65 * 4, 1, 0};
+
 Problem make_problem(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
                      int lda, const float *B, int ldb, float beta, float *C, int ldc) {
     Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
@@ -523,16 +605,44 @@ int sgemm_select(int M, int N, int K, const float *A, int lda, const float *B, i
     return sgemm_plan(M, N, K, A, lda, B, ldb, C, ldc, out, nullptr, nullptr);
 }
 
+int sgemm_mixed_ex(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                   const void *A, int lda, const void *B, int ldb, float beta, float *C, int ldc,
+                   hipStream_t stream, const sgemm_config *cfg) {
+    return sg::run16(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     stream, cfg);
+}
+
+int sgemm_mixed(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                const void *A, int lda, const void *B, int ldb, float beta, float *C, int ldc,
+                hipStream_t stream) {
+    return sg::run16(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     stream, nullptr);
+}
+
 int sgemm_tile_count(int variant) {
+    if (variant == SGEMM_VARIANT_MFMA16) return sg::tiles16_count();
+    if (variant == SGEMM_VARIANT_GENERIC16) return 1;
     int count = 0;
     sg::family(variant, &count);
     return count;
 }
 
 int sgemm_tile_info(int variant, int tile, sgemm_tile_desc *out) {
+    if (!out) return sg::kBadConfig;
+    if (variant == SGEMM_VARIANT_MFMA16) {
+        const sgemm_tile_desc *d = sg::tile16_desc(tile);
+        if (!d) return sg::kBadConfig;
+        *out = *d;
+        return 0;
+    }
+    if (variant == SGEMM_VARIANT_GENERIC16) {
+        if (tile != 0) return sg::kBadConfig;
+        *out = sg::kGeneric16Desc;
+        return 0;
+    }
     int count = 0;
     const sg::TileEntry *t = sg::family(variant, &count);
-    if (!t || tile < 0 || tile >= count || !out) return sg::kBadConfig;
+    if (!t || tile < 0 || tile >= count) return sg::kBadConfig;
     *out = t[tile].desc;
     return 0;
 }
@@ -560,6 +670,7 @@ const char *sgemm_status_string(int status) {
     case -27: return "negative batch stride of B";
     case -28: return "batch stride of C lets two entries of the batch overlap";
     case -29: return "negative batch count";
+    case -30: return "invalid input format (SGEMM_DTYPE_BF16 or SGEMM_DTYPE_F16)";
     default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -81,8 +81,15 @@ namespace {
 // the group is row i of block c).
 // EP: the instance applies the fused epilogue (no effect on the shape; it
 // keeps the shape types of the two instances apart).
+// IN: input format, 0 fp32; 1 bfloat16, 2 float16 (16-bit inputs, fp32
+// accumulation): A and B^T are then read as matrices of 32-bit words, each
+// word two adjacent k values, so every size along k below (BK, K, lda, ldb,
+// the 16-byte chunks) counts words, the LDS image and its loads are those of
+// the fp32 kernel, and a lane's 16-byte fragment is the 8 k values of one
+// v_mfma_f32_16x16x32 instead of the 4 k-steps of v_mfma_f32_16x16x4.  Only
+// k-contiguous operands (A untransposed, B transposed) have that word form.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4, int KG = 1,
-          bool TB = false, bool TA = false, bool EP = false>
+          bool TB = false, bool TA = false, bool EP = false, int IN = 0>
 struct DirectShape {
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
@@ -94,6 +101,8 @@ struct DirectShape {
     static constexpr int CB = WN / 16;                  // 16-column blocks of a wave tile
     static constexpr bool TRANS_B = TB;
     static constexpr bool TRANS_A = TA;
+    static constexpr int INPUT = IN;
+    static_assert(IN == 0 || (TB && !TA), "16-bit inputs: A untransposed, B transposed");
     static_assert(!TA || WM % 64 == 0, "transposed A: 64-row groups per wave");
     static constexpr int CPR_A = BK / 4;                // 16-byte chunks per A-tile row
     static constexpr int CPR_B = BN / 4;                // ... per B-tile row
@@ -297,10 +306,26 @@ __device__ __forceinline__ float b_operand(const BFrag<S> &b, int s, int cb) {
 // rows 16rb + i (A untransposed) or 64(rb/4) + 4i + rb%4 (transposed) of the
 // wave tile, and columns 64(cb/4) + 4i + cb%4 (B either way), i = lane % 16:
 // lane i holds four adjacent columns of a row, stored with one 16-byte write.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 template <class S>
 __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S> &b,
                                           floatx4 (&acc)[S::RB][S::CB]) {
-    if constexpr (S::TRANS_A) {
+    if constexpr (S::INPUT == 1) {
+        // 16-bit inputs: one MFMA per 16-column block covers the chunk's 32 k
+#pragma unroll
+        for (int cb = 0; cb < S::CB; ++cb)
+            acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b.v[cb]), acc[u][cb], 0,
+                0, 0);
+    } else if constexpr (S::INPUT == 2) {
+#pragma unroll
+        for (int cb = 0; cb < S::CB; ++cb)
+            acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b.v[cb]), acc[u][cb], 0,
+                0, 0);
+    } else if constexpr (S::TRANS_A) {
         const int s = u % 4, rg = u / 4;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -323,10 +348,10 @@ __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S
 // stores.  cvec: C rows allow 16-byte stores (used with GUARD only).  EPI:
 // the epilogue adds p.bias and applies p.act.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
-          int BV, bool GUARD, bool EPI = false>
+          int BV, bool GUARD, bool EPI = false, int IN = 0>
 __global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>::NT), 1)
 mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI, IN>;
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
@@ -528,15 +553,15 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
-          int BV, bool GUARD, bool EPI = false>
+          int BV, bool GUARD, bool EPI = false, int IN = 0>
 hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stream) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI>;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI, IN>;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
     hipLaunchKernelGGL(
-        (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AV, BV, GUARD, EPI>),
+        (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AV, BV, GUARD, EPI, IN>),
                        dim3((unsigned)tiles, p.batch), dim3(S::NT), 0, stream, p, tiles_m, tiles_n,
                        group_m,
                        (int)cvec);
@@ -621,6 +646,24 @@ hipError_t launch_direct_epi(const Problem &p, int group_m, hipStream_t stream) 
                                                                                    cv, stream);
     }
     return hipErrorNotSupported;
+}
+
+// The launcher for 16-bit inputs (IN = 1 or 2).  `pw` is the problem in
+// 32-bit words along k (K, lda, ldb halved; A untransposed, B transposed, so
+// each word holds two adjacent k values); it takes dwordx4 loads of an
+// operand whose word rows allow them, as launch_for does.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, int IN>
+hipError_t launch_direct16(const Problem &pw, int group_m, hipStream_t stream) {
+    if (pw.trans_a || !pw.trans_b) return hipErrorInvalidValue;
+    if (!direct_applies(pw, BM, BN, BK, true)) return hipErrorInvalidValue;
+    const bool av = rows_aligned(pw.A, pw.lda, pw.stride_a, pw.batch, 4) && pw.K % 4 == 0;
+    const bool bv = rows_aligned(pw.B, pw.ldb, pw.stride_b, pw.batch, 4) && pw.K % 4 == 0;
+    const bool cv = rows_aligned(pw.C, pw.ldc, pw.stride_c, pw.batch, 4);
+    if (av && bv)
+        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, false, 4, 4, true, false, IN>(
+            pw, group_m, cv, stream);
+    return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, false, 1, 1, true, false, IN>(
+        pw, group_m, cv, stream);
 }
 
 // Tile-table entry of a direct-load tile.  Tiles without EDGES serve whole

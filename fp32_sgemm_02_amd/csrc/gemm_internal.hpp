@@ -36,6 +36,22 @@ struct Problem {
     }
 };
 
+// A product with 16-bit A and B (bfloat16 or float16 bit patterns; sizes and
+// leading dimensions in elements) and fp32 C, for the generic 16-bit kernel.
+struct Problem16 {
+    int M, N, K;
+    float alpha, beta;
+    const unsigned short *A;
+    long long lda;
+    const unsigned short *B;
+    long long ldb;
+    float *C;
+    long long ldc;
+    int trans_a = 0, trans_b = 0;
+    int batch = 1;
+    long long stride_a = 0, stride_b = 0, stride_c = 0;
+};
+
 // Largest grid y (batch entries per launch); larger batches are split.
 constexpr int kMaxBatchPerLaunch = 65535;
 
@@ -74,6 +90,15 @@ const LaunchFn *mfma_direct_ta_epi_launchers(int *count);
 bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 const TileEntry *valu_tiles(int *count);
 const TileEntry *skinny_tiles(int *count);
+
+// 16-bit-input family (mfma_gemm16.hip): the direct-load MFMA tiles for A
+// untransposed and B transposed, over the problem in 32-bit words along k, and
+// the generic kernel for every layout.
+int tiles16_count();
+const sgemm_tile_desc *tile16_desc(int tile);
+int tile16_eff(int tile);
+hipError_t launch_tile16(int tile, int dtype, const Problem &pw, int group_m, hipStream_t stream);
+hipError_t launch_generic16(int dtype, const Problem16 &p, hipStream_t stream);
 
 // Skinny family: which entry serves a shape (-1 if none applies), and which
 // orientation an entry serves (0: few rows of C, M <= 16; 1: few columns, N <= 16).

@@ -50,6 +50,7 @@
  *     -26, -27, -28     sgemm_strided_batched: negative stride of A or B; a
  *                       stride of C that lets two of the batch's C overlap
  *     -29               sgemm_strided_batched: negative batch
+ *     -30               sgemm_mixed: dtype not SGEMM_DTYPE_BF16 / _F16
  *     > 0               a hipError_t reported by the kernel launch
  * No C++ exception crosses this interface.
  *
@@ -73,8 +74,14 @@ enum sgemm_variant {
     SGEMM_VARIANT_MFMA = 1,    /* fp32 matrix-core (v_mfma_f32_*_f32) tiles */
     SGEMM_VARIANT_VALU = 2,    /* per-thread register micro-tiles of fp32 FMAs */
     SGEMM_VARIANT_SKINNY = 3,  /* memory-bound shapes: M <= 16 or N <= 16 */
-    SGEMM_VARIANT_COUNT = 4
+    SGEMM_VARIANT_MFMA16 = 4,  /* sgemm_mixed: 16-bit-input matrix-core tiles */
+    SGEMM_VARIANT_GENERIC16 = 5, /* sgemm_mixed: the generic 16-bit-input kernel */
+    SGEMM_VARIANT_COUNT = 6
 };
+
+/* Input formats of sgemm_mixed. */
+#define SGEMM_DTYPE_BF16 1   /* bfloat16: the high 16 bits of an IEEE binary32 */
+#define SGEMM_DTYPE_F16 2    /* IEEE binary16 */
 
 /* sgemm_config.flags bits */
 #define SGEMM_FLAG_SCALAR_IO 0x1   /* force 4-byte loads/stores (no 16-byte vectors) */
@@ -237,6 +244,32 @@ int sgemm_strided_batched_ex(int trans_a, int trans_b, int M, int N, int K, floa
                              int ldb, long long stride_b, float beta, float *C, int ldc,
                              long long stride_c, int batch, hipStream_t stream,
                              const sgemm_config *cfg);
+
+/*
+ * sgemm_mixed: C = alpha * op(A) * op(B) + beta * C with A and B given as
+ * 16-bit floats (dtype SGEMM_DTYPE_BF16 or SGEMM_DTYPE_F16; device arrays of
+ * 16-bit values, leading dimensions in elements) and C, alpha, beta in fp32.
+ * Every product of two 16-bit values is exact in fp32; sums are accumulated
+ * in fp32 (the matrix instructions v_mfma_f32_16x16x32_bf16 / _f16).  The
+ * reduced-precision matrix hardware of the tensor-core fine print of "The
+ * GEMM Scrapbook".  Arguments after dtype as sgemm_op's.  The matrix-core
+ * tiles (family SGEMM_VARIANT_MFMA16) serve trans_a = 0, trans_b = 1 (C = X
+ * W^T with W stored N x K) when K, lda and ldb are even and A, B are 4-byte
+ * aligned; every other case runs the generic kernel
+ * (SGEMM_VARIANT_GENERIC16: 16-bit values decoded to fp32 in LDS, fp32
+ * FMAs; correct for any layout, not tuned).  A and B need 2-byte alignment
+ * (-5, -7).  Status codes as sgemm_op's, -30 for an unknown dtype, -13 when
+ * an explicit configuration cannot serve the operands.
+ */
+int sgemm_mixed(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                const void *A, int lda, const void *B, int ldb, float beta, float *C, int ldc,
+                hipStream_t stream);
+
+/* sgemm_mixed with an explicit configuration (variant SGEMM_VARIANT_MFMA16
+ * with a tile index, or SGEMM_VARIANT_GENERIC16 with tile 0 or -1). */
+int sgemm_mixed_ex(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                   const void *A, int lda, const void *B, int ldb, float beta, float *C, int ldc,
+                   hipStream_t stream, const sgemm_config *cfg);
 
 /*
  * sgemm_cblas: the same product with the argument conventions of

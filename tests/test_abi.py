@@ -334,3 +334,32 @@ def test_batched_entry_point_validation():
     assert call(args(batch=0, sc=0)) == 0
     assert call(args(M=0, sc=0)) == 0
     assert call(args(alpha=0.0, beta=1.0, A=None, B=None, sa=0, sb=0)) == 0
+
+
+def test_mixed_entry_point_validation():
+    """sgemm_mixed: dtype and argument checks on the host; the 16-bit tile
+    tables are described."""
+    good = 0x10000
+    mx = sg.sgemm_mixed
+    assert mx(0, 0, 1, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -30
+    assert mx(3, 0, 1, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -30
+    assert mx(sg.DTYPE_BF16, 2, 1, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -21
+    assert mx(sg.DTYPE_F16, 0, 1, -1, 4, 4, 1.0, good, 4, good, 4, 0.0, good, 4) == -1
+    assert mx(sg.DTYPE_F16, 0, 1, 4, 4, 4, 1.0, good, 3, good, 4, 0.0, good, 4) == -6
+    assert mx(sg.DTYPE_F16, 0, 1, 4, 4, 4, 1.0, good + 1, 4, good, 4, 0.0, good, 4) == -5
+    assert mx(sg.DTYPE_BF16, 0, 1, 4, 4, 4, 1.0, good, 4, good, 4, 0.0, good + 2, 4) == -10
+    assert mx(sg.DTYPE_BF16, 0, 1, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4) == 0
+    assert mx(sg.DTYPE_BF16, 0, 1, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, good, 4) == 0
+    # the matrix-core tiles need A untransposed, B transposed, even K
+    cfg = sg.SgemmConfig(sg.VARIANT_MFMA16, 0, 0, 0)
+    assert mx(sg.DTYPE_BF16, 0, 0, 64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64,
+              None, cfg) == -13
+    assert mx(sg.DTYPE_BF16, 0, 1, 64, 64, 63, 1.0, good, 63, good, 63, 0.0, good, 64,
+              None, cfg) == -13
+    assert sg.tile_count(sg.VARIANT_MFMA16) > 0 and sg.tile_count(sg.VARIANT_GENERIC16) == 1
+    for t in range(sg.tile_count(sg.VARIANT_MFMA16)):
+        d = sg.tile_info(sg.VARIANT_MFMA16, t)
+        assert d["flags"] & sg.TILE_TRANS_B and d["bk"] % 2 == 0
+    # fp32 entry points refuse the 16-bit families
+    cfg = sg.SgemmConfig(sg.VARIANT_MFMA16, 0, 0, 0)
+    assert sg.sgemm_ex(64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
