@@ -337,6 +337,7 @@ def sweep(args):
         del sets
         torch.cuda.empty_cache()
     rows.extend(sweep_batched(torch, sg, time_graph))
+    rows.extend(sweep_mixed(torch, sg, time_graph))
     with open(args.sweep, "w") as fh:
         json.dump(rows, fh, indent=1)
 
@@ -433,6 +434,45 @@ def sweep_batched(torch, sg, time_graph):
         print(json.dumps(row), flush=True)
         out.append(row)
         del A, B, C
+    return out
+
+
+PEAK_16BIT_TFLOPS = 2500.0     # MI355X dense bf16 / fp16 matrix peak
+MIXED_SWEEP = ((4096, 4096, 4096), (8192, 14336, 4096), (8192, 4096, 14336), (16, 14336, 4096))
+
+
+def sweep_mixed(torch, sg, time_graph):
+    """16-bit inputs (sgemm_mixed) as a linear layer, C = X W^T with W stored
+    N x K, fp32 C; graph-replay device time per call.  The decode shape
+    rotates over operand copies larger than the Infinity Cache."""
+    out = []
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(11)
+    for M, N, K in MIXED_SWEEP:
+        for label, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+            per_set = 2 * (M * K + N * K) + 4 * M * N
+            copies = 1 if M > 16 else max(2, -(-2 * MALL_BYTES // per_set) + 1)
+            ops = [((torch.rand((M, K), device="cuda:0", generator=gen) * 2 - 1).to(dt),
+                    (torch.rand((N, K), device="cuda:0", generator=gen) * 2 - 1).to(dt),
+                    torch.empty((M, N), device="cuda:0")) for _ in range(copies)]
+
+            def call_i(i):
+                A, W, C = ops[i % len(ops)]
+                sg.gemm_mixed(A, W, C, trans_b=True)
+            flops = 2.0 * M * N * K
+            med = statistics.median(time_graph(torch, call_i, max(copies, 5))) / 1e3
+            byts = per_set
+            bound = "mfma" if flops / byts > PEAK_16BIT_TFLOPS * 1e3 / PEAK_HBM_GBS else "hbm"
+            row = {"workload": f"mixed_{label}_{M}x{N}x{K}_NT", "M": M, "N": N, "K": K,
+                   "op": "NT", "inputs": label, "kernel_ms_median": round(med * 1e3, 4),
+                   "gflops": round(flops / med / 1e9, 1), "gbs": round(byts / med / 1e9, 1),
+                   "bound": bound, "operand_copies": copies}
+            row["pct_roofline"] = round(100 * (row["gflops"] / (PEAK_16BIT_TFLOPS * 1e3)
+                                               if bound == "mfma" else row["gbs"] / PEAK_HBM_GBS),
+                                        2)
+            print(json.dumps(row), flush=True)
+            out.append(row)
+            del ops
     return out
 
 

@@ -20,15 +20,16 @@ namespace {
 
 // ---- direct-load tiles ---------------------------------------------------------
 // TILE16(BM, BN, BK_WORDS, WM, WN, NBUF, KG, EFF): the fp32 kernel's tile
-// with BK counted in words (2 k values each).  EFF: expected % of the 16-bit
-// peak (dispatch cost model).
+// with BK counted in words (2 k values each).  EFF: % of the 16-bit peak
+// measured on whole-GPU shapes (4096^3 and the MLP shapes; dispatch cost
+// model).
 #define TILES16(X)                              \
-    X(256, 256, 32, 128, 64, 2, 1, 60)          \
-    X(256, 256, 16, 128, 64, 2, 1, 55)          \
-    X(256, 128, 32, 64, 64, 2, 1, 55)           \
-    X(128, 128, 32, 32, 64, 2, 1, 50)           \
-    X(128, 128, 32, 64, 64, 2, 2, 45)           \
-    X(64, 64, 32, 32, 64, 2, 2, 40)
+    X(256, 256, 32, 128, 64, 2, 1, 48)          \
+    X(256, 256, 16, 128, 64, 2, 1, 44)          \
+    X(256, 128, 32, 64, 64, 2, 1, 41)           \
+    X(128, 128, 32, 32, 64, 2, 1, 41)           \
+    X(128, 128, 32, 64, 64, 2, 2, 38)           \
+    X(64, 64, 32, 32, 64, 2, 2, 35)
 
 struct Tile16 {
     sgemm_tile_desc desc;
