@@ -416,7 +416,9 @@ int pick_tile16(const Problem &pw) {
 // Argument checks as sgemm_op's (A and B need 2-byte alignment), -30 for an
 // unknown dtype.  The matrix-core tiles serve A untransposed with B
 // transposed when K, lda, ldb are even and A, B 4-byte aligned (the operands
-// are then word matrices along k); everything else runs the generic kernel.
+// are then word matrices along k), and so does the few-rows skinny kernel
+// for M <= 8 (automatic choice only); everything else runs the generic
+// kernel.
 int run16(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha, const void *A,
           int lda, const void *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
           const sgemm_config *cfg) {
@@ -449,9 +451,13 @@ int run16(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
     Problem pw{M,   N,   K / 2, alpha, beta, static_cast<const float *>(A), lda / 2,
                static_cast<const float *>(B), ldb / 2, C, ldc};
     pw.trans_b = 1;
-    if (variant == SGEMM_VARIANT_AUTO)
+    if (variant == SGEMM_VARIANT_AUTO) {
+        // up to 8 rows in word form: the skinny kernel streams W once (at
+        // 16 rows the 64 x 64 k-group tile was measured faster)
+        if (mfma_ok && M <= 8) return to_status(launch_skinny16(dtype, pw, stream));
         variant = (mfma_ok && pick_tile16(pw) >= 0) ? SGEMM_VARIANT_MFMA16
                                                     : SGEMM_VARIANT_GENERIC16;
+    }
     if (variant == SGEMM_VARIANT_MFMA16) {
         if (!mfma_ok) return kBadConfig;
         if (tile < 0) tile = pick_tile16(pw);

@@ -99,6 +99,8 @@ const sgemm_tile_desc *tile16_desc(int tile);
 int tile16_eff(int tile);
 hipError_t launch_tile16(int tile, int dtype, const Problem &pw, int group_m, hipStream_t stream);
 hipError_t launch_generic16(int dtype, const Problem16 &p, hipStream_t stream);
+// ... and the few-rows skinny kernel over the same word form (M <= 8).
+hipError_t launch_skinny16(int dtype, const Problem &pw, hipStream_t stream);
 
 // Skinny family: which entry serves a shape (-1 if none applies), and which
 // orientation an entry serves (0: few rows of C, M <= 16; 1: few columns, N <= 16).

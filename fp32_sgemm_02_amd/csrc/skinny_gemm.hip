@@ -120,8 +120,31 @@ __device__ __forceinline__ void rows_load(const Problem &p, int j, int g, int gn
     }
 }
 
-template <int VW, int U>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// IN = 1 / 2: 16-bit inputs in word form (see the 16-bit family): a lane's
+// four k-words of A and of column c are the 8 k values of one
+// v_mfma_f32_16x16x32 (bfloat16 / float16).
+template <int VW, int U, int IN = 0>
 __device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&acc)[VW]) {
+    if constexpr (IN != 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < VW; ++c) {
+                const floatx4 b = {r.b[u][0][c], r.b[u][1][c], r.b[u][2][c], r.b[u][3][c]};
+                if constexpr (IN == 1)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, r.a[u]), __builtin_bit_cast(bf16x8, b), acc[c],
+                        0, 0, 0);
+                else
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8, r.a[u]), __builtin_bit_cast(f16x8, b), acc[c],
+                        0, 0, 0);
+            }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -137,8 +160,9 @@ __device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&a
 // before the MFMAs of round r, so a round's memory latency overlaps the
 // previous round's arithmetic (loads past K read as zero, so the extra round
 // at the end touches no memory).
-template <int VW, int W, int U, bool VA, bool VB, bool TB>
+template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0>
 __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) {
+    static_assert(IN == 0 || TB, "16-bit inputs: B transposed (word form)");
     using S = RowsShape<VW, W>;
     __shared__ __attribute__((aligned(16))) float red[S::RED];
     select_batch(p);
@@ -162,11 +186,11 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     for (int j = wave; j < chunks; j += 2 * U * W) {
         rows_load<VW, W, U, VA, VB, TB>(p, j + U * W, g, gn, row_ok, arow, astep, r1);
         pipeline_fence();
-        rows_mfma<VW, U>(r0, acc);
+        rows_mfma<VW, U, IN>(r0, acc);
         if (j + U * W >= chunks) break;
         rows_load<VW, W, U, VA, VB, TB>(p, j + 2 * U * W, g, gn, row_ok, arow, astep, r0);
         pipeline_fence();
-        rows_mfma<VW, U>(r1, acc);
+        rows_mfma<VW, U, IN>(r1, acc);
     }
 
     // fixed-order reduction over the W waves
@@ -193,12 +217,24 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     }
 }
 
-template <int VW, int W, int U, bool VA, bool VB, bool TB>
+template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0>
 hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB>), dim3(strips, p.batch), dim3(64 * W),
-                       0, stream, p, strips);
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB, IN>), dim3(strips, p.batch),
+                       dim3(64 * W), 0, stream, p, strips);
     return hipGetLastError();
+}
+
+// 16-bit inputs, few rows: pw is the word-form problem (A untransposed, B
+// transposed, K / lda / ldb in 32-bit words); 16-column strips (measured
+// faster than 64-column ones for 16-bit inputs at 1 x 14336 x 4096 and
+// 16 x 14336 x 4096).
+template <int IN>
+hipError_t launch_rows16_as(const Problem &pw, hipStream_t stream) {
+    const bool va = rows_aligned(pw.A, pw.lda, pw.stride_a, pw.batch, 4);
+    const bool vb = rows_aligned(pw.B, pw.ldb, pw.stride_b, pw.batch, 4);
+    if (va && vb) return launch_rows_as<1, 16, 4, true, true, true, IN>(pw, stream);
+    return launch_rows_as<1, 16, 4, false, false, true, IN>(pw, stream);
 }
 
 template <int VW, int W, int U, bool TB>
@@ -393,6 +429,12 @@ constexpr TileEntry cols_entry() {
 
 
 }  // namespace
+
+hipError_t launch_skinny16(int dtype, const Problem &pw, hipStream_t stream) {
+    if (pw.M > 16 || pw.trans_a || !pw.trans_b) return hipErrorInvalidValue;
+    return dtype == SGEMM_DTYPE_BF16 ? launch_rows16_as<1>(pw, stream)
+                                     : launch_rows16_as<2>(pw, stream);
+}
 
 const TileEntry *skinny_tiles(int *count) {
     static const TileEntry tiles[] = {

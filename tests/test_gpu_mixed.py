@@ -109,6 +109,19 @@ def test_mixed_automatic_every_layout(ta, tb, dtype, tname, oracle_mod):
 
 
 @pytest.mark.parametrize("dtype,tname", DTYPES)
+def test_mixed_few_rows(dtype, tname, oracle_mod):
+    """Decode-like shapes (M <= 16) with W stored N x K: the few-rows skinny
+    kernel in word form (M <= 8), 16-byte and 4-byte loads, and the k-group
+    tiles above that."""
+    rng = np.random.default_rng(40 + dtype)
+    for M, N, K in ((1, 5000, 4096), (8, 300, 64), (5, 4100, 66), (3, 17, 2), (16, 14336, 512),
+                    (9, 300, 64)):
+        lab = f"{tname} few rows {(M, N, K)}"
+        run_check(rng, dtype, tname, M, N, K, False, True, False, oracle_mod, lab)
+        run_check(rng, dtype, tname, M, N, K, False, True, True, oracle_mod, lab + " int")
+
+
+@pytest.mark.parametrize("dtype,tname", DTYPES)
 def test_mixed_generic_explicit_and_unaligned(dtype, tname, oracle_mod):
     """The generic kernel asked for explicitly on the matrix-core layout, and
     operands that are only 2-byte aligned (the matrix-core tiles cannot take
