@@ -19,8 +19,8 @@ __all__ = [
     "sgemm_mixed", "gemm", "gemm_batched", "gemm_mixed", "select", "tile_count", "tile_info", "status_string",
     "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "VARIANT_MFMA16",
-    "VARIANT_GENERIC16", "DTYPE_BF16", "DTYPE_F16", "FLAG_SCALAR_IO", "FLAG_UNTUNED",
-    "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A",
+    "VARIANT_GENERIC16", "DTYPE_BF16", "DTYPE_F16", "FLAG_SCALAR_IO", "FLAG_UNTUNED", "FLAG_STREAMK",
+    "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A", "TILE_STREAMK",
     "ACT_NONE", "ACT_RELU", "ACT_SILU", "ACT_GELU_ERF", "ACT_GELU_TANH",
 ]
 
@@ -32,10 +32,12 @@ VARIANT_MFMA16, VARIANT_GENERIC16 = 4, 5
 DTYPE_BF16, DTYPE_F16 = 1, 2
 FLAG_SCALAR_IO = 0x1
 FLAG_UNTUNED = 0x2
+FLAG_STREAMK = 0x4
 TILE_WHOLE = 0x1
 TILE_DIRECT = 0x2
 TILE_TRANS_B = 0x4
 TILE_TRANS_A = 0x8
+TILE_STREAMK = 0x10
 ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3, 4
 
 

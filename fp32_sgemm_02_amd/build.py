@@ -26,6 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "scale.hip", "mfma_gemm.hip", "mfma_direct.hip", "mfma_direct_epi.hip",
+           "mfma_direct_sk.hip",
            "mfma_direct_ta.hip", "mfma_direct_ta_epi.hip", "mfma_gemm16.hip", "valu_gemm.hip",
            "skinny_gemm.hip"]
 PROBE_SOURCES = ["peak_probes.hip"]

@@ -70,7 +70,8 @@ long long tiles_for(const TileEntry &t, int M, int N) {
 
 // The MFMA family: the general tiles, then the direct-load tiles for
 // untransposed A, then those for transposed A, in one table; the direct-load
-// tiles get their fused-epilogue launchers (compiled separately, same order).
+// tiles get their fused-epilogue and stream-K launchers (compiled separately,
+// same order).
 const TileEntry *mfma_family(int *count) {
     static const std::vector<TileEntry> all = [] {
         std::vector<TileEntry> v;
@@ -80,15 +81,26 @@ const TileEntry *mfma_family(int *count) {
         const LaunchFn *f = nullptr;
         t = mfma_direct_tiles(&n);
         f = mfma_direct_epi_launchers(&nf);
+        int nsk = 0;
+        const LaunchFn *sk = mfma_direct_sk_launchers(&nsk);
         for (int i = 0; i < n; ++i) {
             v.push_back(t[i]);
             if (nf == n) v.back().fused = f[i];
+            if (nsk == n && sk[i]) {
+                v.back().streamk = sk[i];
+                v.back().desc.flags |= SGEMM_TILE_STREAMK;
+            }
         }
         t = mfma_direct_ta_tiles(&n);
         f = mfma_direct_ta_epi_launchers(&nf);
+        sk = mfma_direct_ta_sk_launchers(&nsk);
         for (int i = 0; i < n; ++i) {
             v.push_back(t[i]);
             if (nf == n) v.back().fused = f[i];
+            if (nsk == n && sk[i]) {
+                v.back().streamk = sk[i];
+                v.back().desc.flags |= SGEMM_TILE_STREAMK;
+            }
         }
         return v;
     }();
@@ -152,6 +164,7 @@ int general_mfma_tile(int M, int N) {
 }
 
 constexpr int kCUs = 256;
+constexpr double kPeakFlops = 157.3e12;   // fp32 MFMA, dense
 
 // Estimated time of tile t on `batch` M x N outputs: rounds of workgroups
 // over the 256 CUs, each round costing one tile's work at the tile's measured
@@ -190,12 +203,41 @@ Problem main_part(const Problem &p, Strips s) {
     return m;
 }
 
+// Stream-K (the tile's persistent runs over evenly split k-iterations, plus
+// a fixup): its launcher serves single products whose A and B take dwordx4
+// loads.  Estimated time, in the units of tile_cost: the whole rounds before
+// the split wave plus each workgroup's share of the split iterations, and the
+// partial sums (written and read once, at about 4 TB/s) with the second
+// launch (about 4 us).
+bool streamk_ok(const Problem &p) {
+    return p.batch == 1 && rows_aligned(p.A, p.lda, p.stride_a, 1, 4) &&
+           rows_aligned(p.B, p.ldb, p.stride_b, 1, 4) &&
+           (p.trans_a ? p.M : p.K) % 4 == 0 && (p.trans_b ? p.K : p.N) % 4 == 0;
+}
+
+double streamk_cost(const TileEntry &t, const Problem &p) {
+    const long long tiles = tiles_for(t, p.M, p.N);
+    const long long iters = (p.K + t.desc.bk - 1) / t.desc.bk;
+    const long long dp = tiles >= kCUs ? (tiles / kCUs - 1) * kCUs : 0;
+    const long long sk = tiles - dp;
+    const long long share = (sk * iters + kCUs - 1) / kCUs;
+    const double eff = t.eff_pct > 0 ? t.eff_pct : 50;
+    const double rounds = (double)dp / kCUs + (double)share / iters;
+    // seconds per cost unit: one round of tiles at `eff` % of the peak
+    const double unit_s = 2.0 * p.K * kCUs * 100.0 / kPeakFlops;
+    const long long partials = sk < kCUs ? sk + kCUs : 2 * kCUs;
+    const double extra_s = 2.0 * partials * t.desc.bm * t.desc.bn * 4 / 4e12 + 4e-6;
+    return rounds * t.desc.bm * t.desc.bn / eff + extra_s / unit_s;
+}
+
 // The MFMA tile for a shape that is not in the tuned table: the applicable
 // tile of least estimated time (ties: the earlier, i.e. general, tile),
 // counting for each tile the option of handing its edge strips to the skinny
 // family (`strips`, when not null, receives the chosen tile's strips; a strip
-// is charged 5 % of the main part, far below the round it saves).
-int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
+// is charged 5 % of the main part, far below the round it saves) and, where
+// the tile offers it, stream-K (`*streamk` set when chosen).
+int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr,
+                      bool *streamk = nullptr) {
     int count = 0;
     const TileEntry *tiles = mfma_family(&count);
     const bool trans = p.trans_a || p.trans_b;
@@ -213,6 +255,17 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
             best = i;
             best_cost = c;
             best_strips = sp;
+            if (streamk) *streamk = false;
+        }
+        if (streamk && tiles[i].streamk && io_ok && streamk_ok(p) &&
+            tile_applies(tiles[i], p, io_ok)) {
+            const double cs = streamk_cost(tiles[i], p);
+            if (cs < best_cost) {
+                best = i;
+                best_cost = cs;
+                best_strips = Strips{0, 0};
+                *streamk = true;
+            }
         }
     }
     if (strips) *strips = best_strips;
@@ -233,6 +286,7 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr) {
 struct Choice {
     int variant, tile, group_m;
     bool vec;
+    bool streamk = false;
 };
 
 int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *strips = nullptr) {
@@ -247,6 +301,8 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     if (strips) *strips = Strips{0, 0};
     const bool trans = p.trans_a || p.trans_b;
     if (trans && variant == SGEMM_VARIANT_VALU) return kBadConfig;   // VALU reads untransposed
+    bool streamk = (flags & SGEMM_FLAG_STREAMK) != 0;
+    if (streamk && !explicit_tile) return kBadConfig;   // stream-K is asked for with a tile
     if (variant == SGEMM_VARIANT_AUTO) {
         Tuned a;
         if (trans || (flags & SGEMM_FLAG_UNTUNED) || p.batch > 1 ||
@@ -254,7 +310,7 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
             if (skinny_pick(p) >= 0)
                 a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
             else
-                a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok, strips), 0};
+                a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok, strips, &streamk), 0};
             if (a.tile < 0 && a.variant == SGEMM_VARIANT_MFMA) return kBadConfig;
         }
         variant = a.variant;
@@ -281,13 +337,16 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
         if (explicit_tile || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // automatic choice that cannot run here
         if (strips) *strips = Strips{0, 0};
+        streamk = false;
     }
+    if (streamk && (variant != SGEMM_VARIANT_MFMA || !tiles[tile].streamk)) return kBadConfig;
     // direct-load and skinny tiles pick 16-byte paths per operand themselves
     const bool per_operand =
         (tiles[tile].desc.flags & SGEMM_TILE_DIRECT) || variant == SGEMM_VARIANT_SKINNY;
     const bool vec = per_operand ? want_vec : io_ok;
     if (!(vec ? tiles[tile].vec : tiles[tile].scalar)) return kBadConfig;
-    out = Choice{variant, tile, group_m, vec};
+    if (streamk && (!vec || !streamk_ok(p))) return kBadConfig;   // (automatic: never so)
+    out = Choice{variant, tile, group_m, vec, streamk};
     return 0;
 }
 
@@ -309,15 +368,27 @@ int launch(const Problem &p, const Choice &ch, hipStream_t stream) {
         q.B += b0 * p.stride_b;
         q.C += b0 * p.stride_c;
         hipError_t e = hipErrorNotSupported;
-        if (fused) e = fused(q, ch.group_m, stream);   // hipErrorNotSupported: cannot fuse here
-        const bool done = (e != hipErrorNotSupported);
+        bool sk_ran = false;
+        if (ch.streamk && t.streamk) {
+            // stream-K stores the product; an epilogue then takes the elementwise pass
+            Problem g = q;
+            g.bias = nullptr;
+            g.act = SGEMM_ACT_NONE;
+            e = t.streamk(g, ch.group_m, stream);   // hipErrorNotSupported: operands it cannot take
+            sk_ran = (e != hipErrorNotSupported);
+            if (sk_ran && e == hipSuccess && q.has_epilogue()) e = launch_elementwise(q, 1.f, stream);
+        }
+        if (!sk_ran && fused) e = fused(q, ch.group_m, stream);   // NotSupported: cannot fuse
+        const bool done = sk_ran || (fused && e != hipErrorNotSupported);
         if (log)
             std::fprintf(stderr,
                          "sgemm M=%d N=%d K=%d batch=%d variant=%d tile=%d (%dx%dx%d) group_m=%d "
-                         "%s%s\n",
+                         "%s%s%s\n",
                          q.M, q.N, q.K, q.batch, ch.variant, ch.tile, t.desc.bm, t.desc.bn,
                          t.desc.bk, ch.group_m, ch.vec ? "vec16" : "scalar",
-                         !q.has_epilogue() ? "" : done ? " fused-epilogue" : " epilogue-pass");
+                         sk_ran ? " stream-k" : "",
+                         !q.has_epilogue() ? "" : (done && !sk_ran) ? " fused-epilogue"
+                                                                    : " epilogue-pass");
         if (!done) {
             Problem g = q;
             g.bias = nullptr;
@@ -577,7 +648,7 @@ int sgemm_op_plan(int trans_a, int trans_b, int M, int N, int K, const float *A,
     out->variant = ch.variant;
     out->tile = ch.tile;
     out->group_m = ch.group_m;
-    out->flags = ch.vec ? 0 : SGEMM_FLAG_SCALAR_IO;
+    out->flags = (ch.vec ? 0 : SGEMM_FLAG_SCALAR_IO) | (ch.streamk ? SGEMM_FLAG_STREAMK : 0);
     if (edge_rows) *edge_rows = sp.rows;
     if (edge_cols) *edge_cols = sp.cols;
     return 0;

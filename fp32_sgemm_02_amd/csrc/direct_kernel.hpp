@@ -88,8 +88,10 @@ namespace {
 // the fp32 kernel, and a lane's 16-byte fragment is the 8 k values of one
 // v_mfma_f32_16x16x32 instead of the 4 k-steps of v_mfma_f32_16x16x4.  Only
 // k-contiguous operands (A untransposed, B transposed) have that word form.
+// MD: the kernel's mode (0 one tile per workgroup, 1 stream-K runs, 2
+// stream-K fixup); like EP it only keeps the shape types of instances apart.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int AV = 4, int BV = 4, int KG = 1,
-          bool TB = false, bool TA = false, bool EP = false, int IN = 0>
+          bool TB = false, bool TA = false, bool EP = false, int IN = 0, int MD = 0>
 struct DirectShape {
     static constexpr int WAVES_M = BM / WM;
     static constexpr int WAVES_N = BN / WN;
@@ -343,17 +345,47 @@ __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S
     }
 }
 
+// Stream-K plan (MODE 1 and 2).  The first dp_tiles tiles (in tile order)
+// are computed whole, tile g, g + groups, ... by workgroup g; the k-iterations
+// (BK-wide stages) of the next sk_tiles tiles, iters each, are laid end to
+// end and split into `groups` consecutive runs of per_wg, one per workgroup.
+// A run's middle tiles are whole and stored directly; its first and last
+// tile may be partial, and their un-scaled partial sums go to workspace slots
+// 2g and 2g + 1 of workgroup g.  The fixup launch (MODE 2, one workgroup per
+// split tile) adds a tile's pieces in k order and stores C.  No workgroup
+// waits for another.
+struct StreamK {
+    int dp_tiles = 0, sk_tiles = 0, iters = 0, per_wg = 0, groups = 0;
+    float *ws = nullptr;
+};
+
+// Number of runs that touch stream-K tile `tl`.
+__device__ __forceinline__ int sk_pieces(const StreamK &sk, int tl) {
+    const long long first = (long long)tl * sk.iters, last = first + sk.iters - 1;
+    return 1 + (int)(last / sk.per_wg - first / sk.per_wg);
+}
+// Workspace slot of the q-th run touching tile `tl`: the run of workgroup
+// g = first / per_wg + q; the tile is g's first (slot 2g) unless g's run
+// started in an earlier tile (slot 2g + 1, only possible for q == 0).
+__device__ __forceinline__ int sk_slot(const StreamK &sk, int tl, int q) {
+    const long long first = (long long)tl * sk.iters;
+    const long long g = first / sk.per_wg + q;
+    return (int)(2 * g + (g * sk.per_wg < first ? 1 : 0));
+}
+
 // GUARD: the problem has edges (M, N or K not tile multiples, or C not fit
 // for 16-byte stores): zero-filled loads outside the matrix and guarded
 // stores.  cvec: C rows allow 16-byte stores (used with GUARD only).  EPI:
-// the epilogue adds p.bias and applies p.act.
+// the epilogue adds p.bias and applies p.act.  MODE: 0 one tile per
+// workgroup (blockIdx.x), 1 the stream-K runs, 2 the stream-K fixup.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
-          int BV, bool GUARD, bool EPI = false, int IN = 0>
+          int BV, bool GUARD, bool EPI = false, int IN = 0, int MODE = 0>
 __global__ void __launch_bounds__((DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, KG>::NT), 1)
-mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
-    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI, IN>;
+mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, StreamK sk) {
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, AV, BV, KG, TB, TA, EPI, IN, MODE>;
     constexpr int RB = S::RB, H = RB / 2;
     static_assert(RB % 2 == 0, "two halves of row blocks");
+    static_assert(MODE == 0 || KG == 1, "stream-K tiles have one k-group");
     __shared__ __attribute__((aligned(1024))) float smem[NBUF * S::STAGE];
     select_batch(p);
 
@@ -361,96 +393,102 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     const int kg = wave / S::WAVES_MN, wv = wave % S::WAVES_MN;   // k-group, wave within it
     const int wr = wv / S::WAVES_N, wc = wv % S::WAVES_N;
     const int kc0 = kg * S::KCW;                                 // this wave's first chunk
-    int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (p.K + BK - 1) / BK;
-    const DirectLanes<S> d = direct_lanes<S, GUARD>(p, m0, n0, wave, lane);
 
     floatx4 acc[RB][S::CB];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int a = 0; a < RB; ++a)
+        for (int x = 0; x < RB; ++x)
 #pragma unroll
-        for (int b = 0; b < S::CB; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // prologue: stages 0 .. NBUF-1 in flight; stage 0 complete and published
-#pragma unroll
-    for (int t = 0; t < NBUF; ++t)
-        if (t < nk) issue_stage<S, GUARD>(p, m0, n0, t, smem + t * S::STAGE, wave, d, 0, S::L);
-    if (nk >= NBUF)
-        wait_vmcnt<(NBUF - 1) * S::L>();
-    else
-        wait_vmcnt<0>();
-    __syncthreads();
-
+            for (int y = 0; y < S::CB; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
     floatx4 a[RB];
     BFrag<S> b0, b1;
-#pragma unroll
-    for (int rb = 0; rb < H; ++rb) read_a<S>(smem, kc0, rb, lane, wr, a[rb]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) read_b_part<S>(smem, kc0, s, lane, wc, b0);
 
-    // One k-chunk: the MFMAs of this wave's chunk kc0 + kc of stage t with B
-    // fragments bc, and the fragments of its following chunk (of this stage,
-    // or its first chunk of the next) read into a[] and bn.  A wave's last
-    // chunk of a stage holds the barrier and issues the loads of stage t+NBUF.
-    auto chunk = [&](int t, int kcw, const BFrag<S> &bc, BFrag<S> &bn) {
-        const float *cbuf = smem + (t % NBUF) * S::STAGE;
-        const bool last = (kcw == S::KCW - 1);
-        const int kc = kc0 + kcw;
+    // The MFMAs of stages [tb, te) of the tile at (m0, n0), added to acc;
+    // stage t sits in LDS buffer (t - tb) % NBUF.
+    auto mainloop = [&](int m0, int n0, int tb, int te) {
+        const DirectLanes<S> d = direct_lanes<S, GUARD>(p, m0, n0, wave, lane);
+        // prologue: stages tb .. tb+NBUF-1 in flight; stage tb complete and published
 #pragma unroll
-        for (int rb = 0; rb < H; ++rb) {
-            read_a<S>(cbuf, kc, rb + H, lane, wr, a[rb + H]);
-            roll_unit<S>(rb, a[rb], bc, acc);
-            pipeline_fence();
-        }
-        const bool more = !last || (t + 1 < nk);     // a following chunk exists
-        const float *nbuf = cbuf;
-        int nkc = kc + 1;
-        if (last) {
-            if (more) {
-                if (t + NBUF <= nk)
-                    wait_vmcnt<(NBUF - 2) * S::L>();
-                else
-                    wait_vmcnt<0>();
+        for (int i = 0; i < NBUF; ++i)
+            if (tb + i < te)
+                issue_stage<S, GUARD>(p, m0, n0, tb + i, smem + i * S::STAGE, wave, d, 0, S::L);
+        if (te - tb >= NBUF)
+            wait_vmcnt<(NBUF - 1) * S::L>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+
+#pragma unroll
+        for (int rb = 0; rb < H; ++rb) read_a<S>(smem, kc0, rb, lane, wr, a[rb]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) read_b_part<S>(smem, kc0, s, lane, wc, b0);
+
+        // One k-chunk: the MFMAs of this wave's chunk kc0 + kc of stage t with B
+        // fragments bc, and the fragments of its following chunk (of this stage,
+        // or its first chunk of the next) read into a[] and bn.  A wave's last
+        // chunk of a stage holds the barrier and issues the loads of stage t+NBUF.
+        auto chunk = [&](int t, int kcw, const BFrag<S> &bc, BFrag<S> &bn) {
+            const float *cbuf = smem + ((t - tb) % NBUF) * S::STAGE;
+            const bool last = (kcw == S::KCW - 1);
+            const int kc = kc0 + kcw;
+#pragma unroll
+            for (int rb = 0; rb < H; ++rb) {
+                read_a<S>(cbuf, kc, rb + H, lane, wr, a[rb + H]);
+                roll_unit<S>(rb, a[rb], bc, acc);
+                pipeline_fence();
             }
-            __syncthreads();
-            nbuf = smem + ((t + 1) % NBUF) * S::STAGE;
-            nkc = kc0;
-        }
-        const int tf = t + NBUF;
-        float *fbuf = smem + (t % NBUF) * S::STAGE;
-#pragma unroll
-        for (int j = 0; j < H; ++j) {
-            if (more) {
-                read_a<S>(nbuf, nkc, j, lane, wr, a[j]);
-#pragma unroll
-                for (int s = (4 * j) / H; s < (4 * (j + 1)) / H; ++s)
-                    read_b_part<S>(nbuf, nkc, s, lane, wc, bn);
+            const bool more = !last || (t + 1 < te);     // a following chunk exists
+            const float *nbuf = cbuf;
+            int nkc = kc + 1;
+            if (last) {
+                if (more) {
+                    if (t + NBUF <= te)
+                        wait_vmcnt<(NBUF - 2) * S::L>();
+                    else
+                        wait_vmcnt<0>();
+                }
+                __syncthreads();
+                nbuf = smem + ((t + 1 - tb) % NBUF) * S::STAGE;
+                nkc = kc0;
             }
-            if (last && tf < nk)
-                issue_stage<S, GUARD>(p, m0, n0, tf, fbuf, wave, d, (S::L * j) / H,
-                                      (S::L * (j + 1)) / H);
-            roll_unit<S>(H + j, a[H + j], bc, acc);
-            pipeline_fence();
+            const int tf = t + NBUF;
+            float *fbuf = smem + ((t - tb) % NBUF) * S::STAGE;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                if (more) {
+                    read_a<S>(nbuf, nkc, j, lane, wr, a[j]);
+#pragma unroll
+                    for (int s = (4 * j) / H; s < (4 * (j + 1)) / H; ++s)
+                        read_b_part<S>(nbuf, nkc, s, lane, wc, bn);
+                }
+                if (last && tf < te)
+                    issue_stage<S, GUARD>(p, m0, n0, tf, fbuf, wave, d, (S::L * j) / H,
+                                          (S::L * (j + 1)) / H);
+                roll_unit<S>(H + j, a[H + j], bc, acc);
+                pipeline_fence();
+            }
+        };
+        if (S::KCW == 2) {
+            // an even number of chunks per stage and wave: the B sets are back in place
+            for (int t = tb; t < te; ++t) {
+                chunk(t, 0, b0, b1);
+                chunk(t, 1, b1, b0);
+            }
+        } else {
+            // one chunk per stage and wave: two stages per iteration swap the B sets back
+            int t = tb;
+            for (; t + 1 < te; t += 2) {
+                chunk(t, 0, b0, b1);
+                chunk(t + 1, 0, b1, b0);
+            }
+            if (t < te) chunk(t, 0, b0, b1);
         }
     };
-    if (S::KCW == 2) {
-        // an even number of chunks per stage and wave: the B sets are back in place
-        for (int t = 0; t < nk; ++t) {
-            chunk(t, 0, b0, b1);
-            chunk(t, 1, b1, b0);
-        }
-    } else {
-        // one chunk per stage and wave: two stages per iteration swap the B sets back
-        int t = 0;
-        for (; t + 1 < nk; t += 2) {
-            chunk(t, 0, b0, b1);
-            chunk(t + 1, 0, b1, b0);
-        }
-        if (t < nk) chunk(t, 0, b0, b1);
-    }
 
+    // k-group reduction and the epilogue of the tile at (m0, n0): C from acc
+    auto finish = [&](int m0, int n0) {
     // k-groups: groups 1.. leave their partial sums in LDS (the ring is free
     // once every wave has left the loop); group 0 adds them in group order
     // and writes C
@@ -550,6 +588,79 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec) {
     } else {
         store(std::integral_constant<int, -1>{});
     }
+    };   // finish
+
+    // the stream-K workspace: slot `slot` holds RB*CB floatx4 per thread,
+    // laid out so that neighbouring threads touch neighbouring 16 bytes
+    auto ws_at = [&](int slot, int j) {
+        return reinterpret_cast<floatx4 *>(sk.ws) +
+               ((long long)slot * (RB * S::CB) + j) * S::NT + tid;
+    };
+    auto coords = [&](int tile, int &m0, int &n0) {
+        int tm, tn;
+        tile_coords(tile, tiles_m, tiles_n, group_m, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    };
+
+    if constexpr (MODE == 0) {
+        int tm, tn;
+        tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+        zero_acc();
+        mainloop(tm * BM, tn * BN, 0, nk);
+        finish(tm * BM, tn * BN);
+    } else if constexpr (MODE == 1) {
+        int m0, n0;
+        for (int tile = blockIdx.x; tile < sk.dp_tiles; tile += sk.groups) {
+            coords(tile, m0, n0);
+            zero_acc();
+            mainloop(m0, n0, 0, nk);
+            finish(m0, n0);
+            __syncthreads();   // LDS free for the next tile's loads
+        }
+        const long long total = (long long)sk.sk_tiles * sk.iters;
+        long long it = (long long)blockIdx.x * sk.per_wg;
+        const long long end = it + sk.per_wg < total ? it + sk.per_wg : total;
+        while (it < end) {
+            const int tl = (int)(it / sk.iters);
+            const int k0 = (int)(it - (long long)tl * sk.iters);
+            const int k1 = (long long)sk.iters - k0 < end - it ? sk.iters : k0 + (int)(end - it);
+            coords(sk.dp_tiles + tl, m0, n0);
+            zero_acc();
+            mainloop(m0, n0, k0, k1);
+            if (k0 == 0 && k1 == sk.iters) {
+                finish(m0, n0);
+            } else {
+                const int slot = 2 * blockIdx.x + (it == (long long)blockIdx.x * sk.per_wg ? 0 : 1);
+#pragma unroll
+                for (int x = 0; x < RB; ++x)
+#pragma unroll
+                    for (int y = 0; y < S::CB; ++y) *ws_at(slot, x * S::CB + y) = acc[x][y];
+            }
+            it += k1 - k0;
+            __syncthreads();   // LDS free for the next piece's loads
+        }
+    } else {
+        // fixup: one workgroup per stream-K tile; tiles of one piece are done
+        const int tl = blockIdx.x;
+        const int pieces = sk_pieces(sk, tl);
+        if (pieces == 1) return;
+        zero_acc();
+        for (int q = 0; q < pieces; ++q) {
+            const int slot = sk_slot(sk, tl, q);
+#pragma unroll
+            for (int x = 0; x < RB; ++x)
+#pragma unroll
+                for (int y = 0; y < S::CB; ++y) {
+                    const floatx4 v = *ws_at(slot, x * S::CB + y);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[x][y][e] += v[e];
+                }
+        }
+        int m0, n0;
+        coords(sk.dp_tiles + tl, m0, n0);
+        finish(m0, n0);
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, int AV,
@@ -562,9 +673,8 @@ hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stre
     if (group_m <= 0) group_m = 4;
     hipLaunchKernelGGL(
         (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AV, BV, GUARD, EPI, IN>),
-                       dim3((unsigned)tiles, p.batch), dim3(S::NT), 0, stream, p, tiles_m, tiles_n,
-                       group_m,
-                       (int)cvec);
+        dim3((unsigned)tiles, p.batch), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m,
+        (int)cvec, StreamK{});
     return hipGetLastError();
 }
 
@@ -664,6 +774,80 @@ hipError_t launch_direct16(const Problem &pw, int group_m, hipStream_t stream) {
             pw, group_m, cv, stream);
     return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, false, 1, 1, true, false, IN>(
         pw, group_m, cv, stream);
+}
+
+// Workgroups of a stream-K launch: one per CU (the tiles that offer stream-K
+// run one 8-wave workgroup per CU).
+constexpr int kStreamKGroups = 256;
+
+// Stream-K launch of a tile with one k-group (dwordx4 loads of A and B, the
+// guarded instance): the plan, a workspace from the stream-ordered allocator
+// (freed on the stream after the fixup), the runs and the fixup.  The last
+// full wave of tiles and the remainder are split (the tiles before them run
+// whole), so every workgroup gets the same number of k-iterations.
+// hipErrorNotSupported when the operands do not take dwordx4 loads or the
+// problem is batched.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool TA>
+hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
+    if ((p.trans_a != 0) != TA) return hipErrorInvalidValue;
+    if (!direct_applies(p, BM, BN, BK, true)) return hipErrorInvalidValue;
+    const bool tb = p.trans_b != 0;
+    const bool av = rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) && (TA ? p.M : p.K) % 4 == 0;
+    const bool bv = rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) && (tb ? p.K : p.N) % 4 == 0;
+    const bool cv = rows_aligned(p.C, p.ldc, p.stride_c, p.batch, 4);
+    if (!av || !bv || p.batch != 1) return hipErrorNotSupported;
+    using S = DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, 1, false, TA>;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const long long tiles = (long long)tiles_m * tiles_n;
+    const int G = kStreamKGroups;
+    if (tiles > 0x7fffffffLL / 16) return hipErrorInvalidConfiguration;
+    if (group_m <= 0) group_m = 4;
+    StreamK sk;
+    sk.groups = G;
+    sk.dp_tiles = tiles >= G ? (int)((tiles / G - 1) * G) : 0;
+    sk.sk_tiles = (int)(tiles - sk.dp_tiles);
+    sk.iters = (p.K + BK - 1) / BK;
+    const long long sk_iters = (long long)sk.sk_tiles * sk.iters;
+    if (sk_iters / G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    sk.per_wg = (int)((sk_iters + G - 1) / G);
+    const size_t bytes = (size_t)2 * G * (S::RB * S::CB) * S::NT * 16;   // two slots a run
+    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&sk.ws), bytes, stream);
+    if (e != hipSuccess) return e;
+    if (tb)
+        hipLaunchKernelGGL(
+            (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, true, TA, 4, 4, true, false, 0, 1>),
+            dim3(G), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv, sk);
+    else
+        hipLaunchKernelGGL(
+            (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, false, TA, 4, 4, true, false, 0, 1>),
+            dim3(G), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv, sk);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        if (tb)
+            hipLaunchKernelGGL(
+                (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, true, TA, 4, 4, true, false, 0, 2>),
+                dim3(sk.sk_tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv,
+                sk);
+        else
+            hipLaunchKernelGGL(
+                (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, false, TA, 4, 4, true, false, 0,
+                                    2>),
+                dim3(sk.sk_tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv,
+                sk);
+        e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(sk.ws, stream);
+    return e != hipSuccess ? e : f;
+}
+
+// The stream-K launcher of a tile table entry, or none: offered by the
+// 256-row tiles with edges and one k-group.
+template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool EDGES, int KG, bool TA>
+constexpr LaunchFn streamk_launcher() {
+    if constexpr (EDGES && KG == 1 && BM == 256)
+        return &launch_streamk<BM, BN, BK, WM, WN, NBUF, TA>;
+    else
+        return nullptr;
 }
 
 // Tile-table entry of a direct-load tile.  Tiles without EDGES serve whole

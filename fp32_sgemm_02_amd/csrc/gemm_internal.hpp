@@ -77,6 +77,9 @@ struct TileEntry {
     // own epilogue (16-byte I/O); returns hipErrorNotSupported for operands
     // it does not serve, and the caller then adds an elementwise pass
     LaunchFn fused = nullptr;
+    // stream-K launcher (persistent runs over split k-iterations and a
+    // fixup); hipErrorNotSupported for operands it does not serve
+    LaunchFn streamk = nullptr;
 };
 
 // Kernel families (each defined in its own .hip file): the compiled tile
@@ -87,6 +90,9 @@ const TileEntry *mfma_direct_ta_tiles(int *count);   // ... A transposed
 // their fused-epilogue launchers, one per tile in table order
 const LaunchFn *mfma_direct_epi_launchers(int *count);
 const LaunchFn *mfma_direct_ta_epi_launchers(int *count);
+// their stream-K launchers (null where a tile offers none), same order
+const LaunchFn *mfma_direct_sk_launchers(int *count);
+const LaunchFn *mfma_direct_ta_sk_launchers(int *count);
 bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 const TileEntry *valu_tiles(int *count);
 const TileEntry *skinny_tiles(int *count);

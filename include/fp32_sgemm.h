@@ -20,8 +20,14 @@
  * written in C.
  *
  * Memory and ownership: A, B and C are DEVICE pointers owned by the caller.
- * The library keeps no pointer after a call returns and allocates no device
- * memory.  Work is enqueued on `stream` (NULL = the null stream) and the call
+ * The library keeps no pointer after a call returns.  It allocates device
+ * memory in one case only: a stream-K launch (SGEMM_FLAG_STREAMK, or chosen
+ * by automatic dispatch for a single product whose tile count leaves the
+ * last wave of workgroups partly idle) takes a workspace for partial sums
+ * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
+ * stream (at most 256 x 3 tiles' accumulators, e.g. 12 MiB for 256 x 256
+ * tiles); an allocation failure is returned as its hipError_t.  Work is
+ * enqueued on `stream` (NULL = the null stream) and the call
  * returns without synchronising: the caller keeps A, B and C alive and
  * unmodified until that stream's work has completed.  C must not overlap A
  * or B (A and B may alias each other).  Calls are thread-safe.
@@ -86,6 +92,8 @@ enum sgemm_variant {
 /* sgemm_config.flags bits */
 #define SGEMM_FLAG_SCALAR_IO 0x1   /* force 4-byte loads/stores (no 16-byte vectors) */
 #define SGEMM_FLAG_UNTUNED 0x2     /* automatic choice: skip the tuned table, use the cost model */
+#define SGEMM_FLAG_STREAMK 0x4     /* with an explicit MFMA tile that offers it: stream-K
+                                      (see sgemm_ex); reported by sgemm_plan when chosen */
 
 /*
  * Explicit configuration for sgemm_ex: which kernel family, which compiled
@@ -129,6 +137,17 @@ typedef struct sgemm_tile_desc {
 /* sgemm_tile_desc.flags: the tile serves A stored transposed (sgemm_op with
  * trans_a = 1), and only that; such tiles need bk * lda below 2^29 elements. */
 #define SGEMM_TILE_TRANS_A 0x8
+/* sgemm_tile_desc.flags: the tile can also run as stream-K: 256 persistent
+ * workgroups take the tiles of the last one or two waves (whole waves before
+ * them run as usual) as one list of k-steps cut into 256 equal runs; a run
+ * that ends or starts inside a tile leaves that tile's partial sums in a
+ * workspace, and a second launch adds each tile's pieces in k order and
+ * applies alpha, beta and C.  Offered for single products (no batch) whose A
+ * and B take 16-byte loads (rows 16-byte aligned, the stored row length a
+ * multiple of 4); asked for with SGEMM_FLAG_STREAMK, otherwise sgemm_ex
+ * returns -13.  The k-sum order then depends on the split, which is fixed for
+ * a shape: results stay bitwise repeatable. */
+#define SGEMM_TILE_STREAMK 0x10
 
 /*
  * sgemm: C = alpha * (A * B) + beta * C, kernel family and tile chosen from
@@ -145,8 +164,10 @@ int sgemm(int M, int N, int K, float alpha,
  * sgemm_ex: as sgemm, with the kernel family and tile taken from *cfg
  * (NULL = automatic, identical to sgemm).  Returns -13 when cfg names an
  * unknown family or tile index, or a family that does not apply to the shape
- * (SGEMM_VARIANT_SKINNY requires M <= 16 or N <= 16).  Used by the tuner,
- * the benchmark and the tests to reach each family directly.
+ * (SGEMM_VARIANT_SKINNY requires M <= 16 or N <= 16), or SGEMM_FLAG_STREAMK
+ * without an MFMA tile flagged SGEMM_TILE_STREAMK, with SGEMM_FLAG_SCALAR_IO,
+ * or for operands stream-K does not take.  Used by the tuner, the benchmark
+ * and the tests to reach each family directly.
  */
 int sgemm_ex(int M, int N, int K, float alpha,
              const float *A, int lda, const float *B, int ldb,

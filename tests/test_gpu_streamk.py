@@ -1,0 +1,179 @@
+"""GPU parity of the stream-K launches (tiles flagged TILE_STREAMK, asked
+for with FLAG_STREAMK) against the CPU oracle.
+
+Stream-K cuts the k-steps of the last waves' tiles into 256 equal runs; a
+tile touched by several runs is summed by a second launch from partial sums.
+The shapes below make every case of that split happen: all tiles split (few
+tiles), whole waves before the split ones (more than 512 tiles), a tile cut
+into hundreds of one-step pieces, K under one step (nothing split), and
+M, N, K that are not tile multiples (each stays a multiple of 4: stream-K
+takes operands whose stored rows allow 16-byte loads).  Integer-valued
+inputs must match the oracle bit for bit (every partial sum is exact in
+fp32, so the split cannot change them); random inputs are held to the
+tolerance in parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import fp32_sgemm_02_amd as sg
+import workloads
+from parity import epilogue_err_ratio, max_err_ratio, sample_rows
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def sk_tiles(trans_a):
+    out = []
+    for t in range(sg.tile_count(sg.VARIANT_MFMA)):
+        d = sg.tile_info(sg.VARIANT_MFMA, t)
+        if d["flags"] & sg.TILE_STREAMK and bool(d["flags"] & sg.TILE_TRANS_A) == trans_a:
+            out.append(t)
+    return out
+
+
+def stored(A, B, trans_a, trans_b):
+    return (np.ascontiguousarray(A.T) if trans_a else A,
+            np.ascontiguousarray(B.T) if trans_b else B)
+
+
+def run(As, Bs, C0, alpha, beta, ta, tb, tile, rows=None, **kw):
+    M = As.shape[1] if ta else As.shape[0]
+    N = Bs.shape[0] if tb else Bs.shape[1]
+    C = dev(C0) if C0 is not None else torch.full((M, N), float("nan"), device=DEV)
+    sg.gemm(dev(As), dev(Bs), C, alpha, beta, trans_a=ta, trans_b=tb, variant=sg.VARIANT_MFMA,
+            tile=tile, flags=sg.FLAG_STREAMK, **kw)
+    torch.cuda.synchronize()
+    out = C.cpu().numpy()
+    return out if rows is None else out[rows]
+
+
+def oracle_rows(oracle_mod, As, Bs, C0, alpha, beta, ta, tb, rows, **kw):
+    Ar = np.ascontiguousarray(As[:, rows] if ta else As[rows])
+    Cr = None if C0 is None else np.ascontiguousarray(C0[rows])
+    return oracle_mod.sgemm(Ar, Bs, Cr, alpha, beta if C0 is not None else 0.0, trans_a=ta,
+                            trans_b=tb, **kw)
+
+
+def shapes_for(tile):
+    d = sg.tile_info(sg.VARIANT_MFMA, tile)
+    bm, bn, bk = d["bm"], d["bn"], d["bk"]
+    return bk, [
+        (3 * bm + 4, 2 * bn - 4, 3004),        # 6 tiles, each cut into ~43 pieces
+        (bm, bn, 250 * bk),                    # one tile, 250 one-step pieces
+        (5 * bm - 8, 3 * bn + 12, 40 * bk + 4),  # ragged, a few pieces a tile
+        (2 * bm, 2 * bn, 4),                   # K under one step: no tile is split
+        (17 * bm, 16 * bn + 8, 64),            # 289 tiles: one split wave of 289
+        (24 * bm, 24 * bn, 2 * bk + 4),        # 576 tiles: 256 whole, 320 split
+    ]
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("trans_a", [False, True])
+def test_streamk_tiles(trans_a, trans_b, oracle_mod):
+    """Every stream-K tile, B either way (A as the tile serves it): random
+    inputs with alpha/beta and beta = 0 over a NaN C within tolerance,
+    integer inputs bit-exact; large shapes on sampled rows."""
+    tiles = sk_tiles(trans_a)
+    if not tiles:
+        pytest.skip("no stream-K tile for this A")
+    for tile in tiles:
+        bk, shapes = shapes_for(tile)
+        for i, (M, N, K) in enumerate(shapes):
+            lab = f"sk t{tile} ta={trans_a} tb={trans_b} {(M, N, K)}"
+            print(lab, flush=True)
+            rows = sample_rows(M, 40) if M * N > 2_000_000 else np.arange(M)
+            A, B, C0 = workloads.draw(M, N, K, "uniform", 2100 + i, True)
+            As, Bs = stored(A, B, trans_a, trans_b)
+            got = run(As, Bs, C0, 0.5, -1.25, trans_a, trans_b, tile, rows)
+            ref = oracle_rows(oracle_mod, As, Bs, C0, 0.5, -1.25, trans_a, trans_b, rows)
+            r = max_err_ratio(got, ref, K, 0.5, -1.25, As, Bs, C0[rows])
+            assert r <= 1.0, f"{lab}: max err/tol = {r}"
+            got = run(As, Bs, None, 1.0, 0.0, trans_a, trans_b, tile, rows)
+            ref = oracle_rows(oracle_mod, As, Bs, None, 1.0, 0.0, trans_a, trans_b, rows)
+            r = max_err_ratio(got, ref, K, 1.0, 0.0, As, Bs, None)
+            assert r <= 1.0, f"{lab} b0: max err/tol = {r}"
+            Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 2200 + i, True)
+            Ai, Bi = stored(Ai, Bi, trans_a, trans_b)
+            got = run(Ai, Bi, Ci, 0.5, -1.25, trans_a, trans_b, tile, rows)
+            ref = oracle_rows(oracle_mod, Ai, Bi, Ci, 0.5, -1.25, trans_a, trans_b, rows)
+            assert np.array_equal(got, ref), f"{lab} int: not bit-exact"
+
+
+def test_streamk_repeatable_and_epilogue(oracle_mod):
+    """Two stream-K calls give the same bits; bias + GELU after stream-K (the
+    elementwise pass) within the epilogue tolerance."""
+    tiles = sk_tiles(False)
+    if not tiles:
+        pytest.skip("no stream-K tile")
+    tile = tiles[0]
+    M, N, K = 700, 900, 4004
+    A, B, C0 = workloads.draw(M, N, K, "uniform", 2300, True)
+    c1 = run(A, B, C0, 1.0, 0.5, False, False, tile)
+    c2 = run(A, B, C0, 1.0, 0.5, False, False, tile)
+    assert np.array_equal(c1, c2), "stream-K results differ between calls"
+    bias = np.random.default_rng(2301).uniform(-1, 1, N).astype(F32)
+    Bs = np.ascontiguousarray(B.T)
+    got = run(A, Bs, C0, 1.0, 0.5, False, True, tile, bias=dev(bias), act=sg.ACT_GELU_ERF)
+    ref = oracle_mod.sgemm(A, Bs, C0.copy(), 1.0, 0.5, trans_b=True, bias=bias,
+                           act=sg.ACT_GELU_ERF)
+    x = oracle_mod.sgemm(A, Bs, C0.copy(), 1.0, 0.5, trans_b=True, bias=bias)
+    r = epilogue_err_ratio(got, ref, x, K, 1.0, 0.5, A, Bs, C0, bias, sg.ACT_GELU_ERF)
+    assert r <= 1.0, f"stream-K + GELU: max err/tol = {r}"
+
+
+def test_streamk_rejected_configs():
+    """FLAG_STREAMK without a stream-K tile, with 4-byte I/O, or for A rows
+    that cannot take 16-byte loads is an invalid configuration (-13)."""
+    tiles = sk_tiles(False)
+    if not tiles:
+        pytest.skip("no stream-K tile")
+    plain = [t for t in range(sg.tile_count(sg.VARIANT_MFMA))
+             if not sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_STREAMK]
+    A = torch.zeros((256, 258), device=DEV)
+    B = torch.zeros((258, 256), device=DEV)
+    C = torch.zeros((256, 256), device=DEV)
+    for tile, flags, a in ((plain[0], sg.FLAG_STREAMK, A[:, :256]),
+                           (tiles[0], sg.FLAG_STREAMK | sg.FLAG_SCALAR_IO, A[:, :256]),
+                           (tiles[0], sg.FLAG_STREAMK, A[:, :255])):
+        K = a.shape[1]
+        with pytest.raises(sg.SgemmError) as e:
+            sg.gemm(a, B[:K], C, variant=sg.VARIANT_MFMA, tile=tile, flags=flags)
+        assert e.value.status == -13
+    with pytest.raises(sg.SgemmError):
+        sg.gemm(A[:, :256], B[:256], C, flags=sg.FLAG_STREAMK)   # no explicit tile
+
+
+@pytest.mark.parametrize("ta,tb,shape", [(False, False, (1536, 1536, 8192)),
+                                         (False, True, (768, 768, 65536)),
+                                         (True, False, (3000, 3000, 3000))])
+def test_streamk_automatic(ta, tb, shape, oracle_mod):
+    """Shapes whose automatic plan is stream-K: the plan reports it, and
+    integer inputs match the oracle bit for bit on sampled rows."""
+    M, N, K = shape
+    cfg = sg.plan(M, N, K, trans_a=ta, trans_b=tb)[0]
+    assert cfg.flags & sg.FLAG_STREAMK, f"plan for {shape} is not stream-K"
+    A, B, C0 = workloads.draw(M, N, K, "int4", 2400, True)
+    As, Bs = stored(A, B, ta, tb)
+    dC = dev(C0)
+    sg.gemm(dev(As), dev(Bs), dC, 0.5, -1.25, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 24)
+    ref = oracle_rows(oracle_mod, As, Bs, C0, 0.5, -1.25, ta, tb, rows)
+    assert np.array_equal(dC.cpu().numpy()[rows], ref), f"automatic stream-K {shape}"
