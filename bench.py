@@ -336,6 +336,7 @@ def sweep(args):
             rows.extend(sweep_epilogue(torch, sg, time_graph, w, sets))
         del sets
         torch.cuda.empty_cache()
+    rows.extend(sweep_streamk(torch, sg, time_graph))
     rows.extend(sweep_batched(torch, sg, time_graph))
     rows.extend(sweep_mixed(torch, sg, time_graph))
     with open(args.sweep, "w") as fh:
@@ -407,6 +408,51 @@ BATCHED_SWEEP = (("attn_scores_32x2048x2048x128", 32, 2048, 2048, 128, True),
                  ("attn_values_32x2048x128x2048", 32, 2048, 128, 2048, False),
                  ("small_512x128x128x64", 512, 128, 128, 64, True),
                  ("small_4096x32x32x32", 4096, 32, 32, 32, False))
+
+
+# Few tiles of C with a long K: the automatic plan runs them as stream-K
+# (M, N, K, A stored transposed, B stored transposed).
+STREAMK_SWEEP = ((512, 512, 32768, False, False), (768, 768, 65536, False, True),
+                 (1536, 1536, 8192, False, False), (3000, 3000, 3000, True, False))
+
+
+def sweep_streamk(torch, sg, time_graph):
+    """Shapes whose automatic plan is stream-K, beside the fastest compiled
+    MFMA tile run one workgroup per tile (every applicable tile timed, no
+    stream-K flag); graph-replay device time per call."""
+    out = []
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(13)
+    for M, N, K, ta, tb in STREAMK_SWEEP:
+        A = torch.rand((K, M) if ta else (M, K), device="cuda:0", generator=gen) * 2 - 1
+        B = torch.rand((N, K) if tb else (K, N), device="cuda:0", generator=gen) * 2 - 1
+        C = torch.empty((M, N), device="cuda:0")
+        cfg = sg.plan(M, N, K, trans_a=ta, trans_b=tb)[0]
+        op = ("T" if ta else "N") + ("T" if tb else "N")
+        flops = 2.0 * M * N * K
+
+        def timed(**kw):
+            call_i = lambda i: sg.gemm(A, B, C, trans_a=ta, trans_b=tb, **kw)
+            return statistics.median(time_graph(torch, call_i, 10, replays=3)) / 1e3
+        best = None
+        for t in range(sg.tile_count(sg.VARIANT_MFMA)):
+            try:
+                sec = timed(variant=sg.VARIANT_MFMA, tile=t)
+            except sg.SgemmError:
+                continue   # the tile does not serve this transposition
+            if best is None or sec < best[1]:
+                best = (t, sec)
+        for label, tile, sec, sk in (("auto", cfg.tile, timed(), bool(cfg.flags & sg.FLAG_STREAMK)),
+                                     ("fastest tile, one per workgroup", best[0], best[1], False)):
+            row = {"workload": f"longk_{M}x{N}x{K}_{op}", "M": M, "N": N, "K": K, "op": op,
+                   "plan": label, "variant": sg.VARIANT_MFMA, "tile": tile, "streamk": sk,
+                   "kernel_ms_median": round(sec * 1e3, 4),
+                   "gflops": round(flops / sec / 1e9, 1), "bound": "mfma",
+                   "pct_roofline": round(100 * flops / sec / 1e12 / PEAK_FP32_TFLOPS, 2)}
+            print(json.dumps(row), flush=True)
+            out.append(row)
+        del A, B, C
+    return out
 
 
 def sweep_batched(torch, sg, time_graph):

@@ -352,8 +352,8 @@ __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S
 // A run's middle tiles are whole and stored directly; its first and last
 // tile may be partial, and their un-scaled partial sums go to workspace slots
 // 2g and 2g + 1 of workgroup g.  The fixup launch (MODE 2, one workgroup per
-// split tile) adds a tile's pieces in k order and stores C.  No workgroup
-// waits for another.
+// split tile and row block of the waves) adds a tile's pieces in k order and
+// stores C.  No workgroup waits for another.
 struct StreamK {
     int dp_tiles = 0, sk_tiles = 0, iters = 0, per_wg = 0, groups = 0;
     float *ws = nullptr;
@@ -488,7 +488,8 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
     };
 
     // k-group reduction and the epilogue of the tile at (m0, n0): C from acc
-    auto finish = [&](int m0, int n0) {
+    // finish(m0, n0, rlo, rhi): store row blocks [rlo, rhi) of every wave
+    auto finish = [&](int m0, int n0, int rlo, int rhi) {
     // k-groups: groups 1.. leave their partial sums in LDS (the ring is free
     // once every wave has left the loop); group 0 adds them in group order
     // and writes C
@@ -545,6 +546,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
+                if (rb < rlo || rb >= rhi) continue;
                 const int gm = S::TRANS_A ? row0 + (rb / 4) * 64 + 16 * g + 4 * r + rb % 4
                                           : row0 + rb * 16 + 4 * g + r;
                 if (GUARD && gm >= p.M) continue;
@@ -608,14 +610,14 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
         tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
         zero_acc();
         mainloop(tm * BM, tn * BN, 0, nk);
-        finish(tm * BM, tn * BN);
+        finish(tm * BM, tn * BN, 0, RB);
     } else if constexpr (MODE == 1) {
         int m0, n0;
         for (int tile = blockIdx.x; tile < sk.dp_tiles; tile += sk.groups) {
             coords(tile, m0, n0);
             zero_acc();
             mainloop(m0, n0, 0, nk);
-            finish(m0, n0);
+            finish(m0, n0, 0, RB);
             __syncthreads();   // LDS free for the next tile's loads
         }
         const long long total = (long long)sk.sk_tiles * sk.iters;
@@ -629,7 +631,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
             zero_acc();
             mainloop(m0, n0, k0, k1);
             if (k0 == 0 && k1 == sk.iters) {
-                finish(m0, n0);
+                finish(m0, n0, 0, RB);
             } else {
                 const int slot = 2 * blockIdx.x + (it == (long long)blockIdx.x * sk.per_wg ? 0 : 1);
 #pragma unroll
@@ -641,25 +643,28 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
             __syncthreads();   // LDS free for the next piece's loads
         }
     } else {
-        // fixup: one workgroup per stream-K tile; tiles of one piece are done
-        const int tl = blockIdx.x;
+        // fixup: workgroup (tl, z) adds row block z of every wave over the
+        // pieces of stream-K tile tl and stores it; tiles of one piece are done
+        const int tl = blockIdx.x, z = blockIdx.y;
         const int pieces = sk_pieces(sk, tl);
         if (pieces == 1) return;
         zero_acc();
         for (int q = 0; q < pieces; ++q) {
             const int slot = sk_slot(sk, tl, q);
 #pragma unroll
-            for (int x = 0; x < RB; ++x)
+            for (int x = 0; x < RB; ++x) {
+                if (x != z) continue;
 #pragma unroll
                 for (int y = 0; y < S::CB; ++y) {
                     const floatx4 v = *ws_at(slot, x * S::CB + y);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[x][y][e] += v[e];
                 }
+            }
         }
         int m0, n0;
         coords(sk.dp_tiles + tl, m0, n0);
-        finish(m0, n0);
+        finish(m0, n0, z, z + 1);
     }
 }
 
@@ -826,13 +831,13 @@ hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
         if (tb)
             hipLaunchKernelGGL(
                 (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, true, TA, 4, 4, true, false, 0, 2>),
-                dim3(sk.sk_tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv,
+                dim3(sk.sk_tiles, S::RB), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv,
                 sk);
         else
             hipLaunchKernelGGL(
                 (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, false, TA, 4, 4, true, false, 0,
                                     2>),
-                dim3(sk.sk_tiles), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv,
+                dim3(sk.sk_tiles, S::RB), dim3(S::NT), 0, stream, p, tiles_m, tiles_n, group_m, (int)cv,
                 sk);
         e = hipGetLastError();
     }

@@ -177,3 +177,41 @@ def test_streamk_automatic(ta, tb, shape, oracle_mod):
     rows = sample_rows(M, 24)
     ref = oracle_rows(oracle_mod, As, Bs, C0, 0.5, -1.25, ta, tb, rows)
     assert np.array_equal(dC.cpu().numpy()[rows], ref), f"automatic stream-K {shape}"
+
+
+def test_streamk_graph_capture():
+    """Stream-K calls captured in a HIP graph (workspace taken and returned by
+    stream-ordered allocation inside the graph): every replay, with eager
+    work and synchronisation between replays, gives the eager call's bits."""
+    tiles = sk_tiles(False)
+    if not tiles:
+        pytest.skip("no stream-K tile")
+    M, N, K = 512, 512, 8192
+    A, B, C0 = workloads.draw(M, N, K, "uniform", 2500, True)
+    dA, dB = dev(A), dev(B)
+    cfg = sg.plan(M, N, K)[0]
+    assert cfg.flags & sg.FLAG_STREAMK, "plan for 512x512x8192 is not stream-K"
+    eager = torch.empty((M, N), device=DEV)
+    sg.gemm(dA, dB, eager)
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy()
+    C = torch.empty((M, N), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sg.gemm(dA, dB, C)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        C.fill_(float("nan"))
+        sg.gemm(dA, dB, C)
+    for r in range(3):
+        C.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), want), f"replay {r} differs from the eager call"
+        sg.gemm(dA, dB, eager, 1.0, 0.0)   # eager work between replays
+        torch.cuda.synchronize()
+    del g
