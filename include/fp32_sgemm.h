@@ -25,8 +25,9 @@
  * by automatic dispatch for a single product whose tile count leaves the
  * last wave of workgroups partly idle) takes a workspace for partial sums
  * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
- * stream (at most 256 x 3 tiles' accumulators, e.g. 12 MiB for 256 x 256
- * tiles); an allocation failure is returned as its hipError_t.  Work is
+ * stream (two tile accumulators for each of 256 workgroups: 64 MiB with
+ * 256 x 128 tiles, 128 MiB with 256 x 256); an allocation failure is
+ * returned as its hipError_t.  Work is
  * enqueued on `stream` (NULL = the null stream) and the call
  * returns without synchronising: the caller keeps A, B and C alive and
  * unmodified until that stream's work has completed.  C must not overlap A
