@@ -17,7 +17,7 @@ import os
 __all__ = [
     "sgemm", "sgemm_ex", "sgemm_op", "sgemm_cblas", "sgemm_epilogue", "sgemm_strided_batched",
     "sgemm_mixed", "gemm", "gemm_batched", "gemm_mixed", "select", "tile_count", "tile_info", "status_string",
-    "version", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
+    "version", "workspace_release", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "VARIANT_MFMA16",
     "VARIANT_GENERIC16", "DTYPE_BF16", "DTYPE_F16", "FLAG_SCALAR_IO", "FLAG_UNTUNED", "FLAG_STREAMK",
     "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A", "TILE_STREAMK",
@@ -116,6 +116,8 @@ def _load():
     lib.sgemm_status_string.argtypes = [i]
     lib.sgemm_version.restype = i
     lib.sgemm_version.argtypes = []
+    lib.sgemm_workspace_release.restype = i
+    lib.sgemm_workspace_release.argtypes = []
     _lib = lib
     return lib
 
@@ -221,6 +223,14 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return _load().sgemm_version()
+
+
+def workspace_release() -> None:
+    """Synchronise the current device and free the workspaces the library
+    keeps for it (stream-K and split-K partial sums, one per stream)."""
+    st = _load().sgemm_workspace_release()
+    if st != 0:
+        raise SgemmError(st)
 
 
 def _ld(t) -> int:

@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "scale.hip", "mfma_gemm.hip", "mfma_direct.hip", "mfma_direct_epi.hip",
+SOURCES = ["api.cpp", "workspace.cpp", "scale.hip", "mfma_gemm.hip", "mfma_direct.hip", "mfma_direct_epi.hip",
            "mfma_direct_sk.hip",
            "mfma_direct_ta.hip", "mfma_direct_ta_epi.hip", "mfma_gemm16.hip", "valu_gemm.hip",
            "skinny_gemm.hip"]

@@ -756,4 +756,6 @@ const char *sgemm_status_string(int status) {
 
 int sgemm_version(void) { return sg::kVersion; }
 
+int sgemm_workspace_release(void) { return static_cast<int>(sg::workspace_release_all()); }
+
 }  // extern "C"

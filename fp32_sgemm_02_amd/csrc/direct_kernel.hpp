@@ -816,8 +816,10 @@ hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
     if (sk_iters / G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     sk.per_wg = (int)((sk_iters + G - 1) / G);
     const size_t bytes = (size_t)2 * G * (S::RB * S::CB) * S::NT * 16;   // two slots a run
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&sk.ws), bytes, stream);
+    Workspace w;
+    hipError_t e = workspace_acquire(bytes, stream, w);
     if (e != hipSuccess) return e;
+    sk.ws = static_cast<float *>(w.ptr);
     if (tb)
         hipLaunchKernelGGL(
             (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, true, TA, 4, 4, true, false, 0, 1>),
@@ -841,7 +843,7 @@ hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
                 sk);
         e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(sk.ws, stream);
+    const hipError_t f = workspace_release(w, stream);
     return e != hipSuccess ? e : f;
 }
 

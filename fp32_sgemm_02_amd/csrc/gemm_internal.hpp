@@ -90,6 +90,18 @@ const TileEntry *mfma_direct_ta_tiles(int *count);   // ... A transposed
 // their fused-epilogue launchers, one per tile in table order
 const LaunchFn *mfma_direct_epi_launchers(int *count);
 const LaunchFn *mfma_direct_ta_epi_launchers(int *count);
+// Device workspace of a launch that keeps partial sums (workspace.cpp):
+// outside graph capture the buffer cached for the (device, stream), reused by
+// every call on that stream; under capture a stream-ordered allocation of the
+// graph's own.  Release after the launches that use it.
+struct Workspace {
+    void *ptr = nullptr;
+    bool owned = false;   // allocated for this call (graph capture)
+};
+hipError_t workspace_acquire(size_t bytes, hipStream_t stream, Workspace &w);
+hipError_t workspace_release(const Workspace &w, hipStream_t stream);
+hipError_t workspace_release_all();   // the current device's cached buffers
+
 // their stream-K launchers (null where a tile offers none), same order
 const LaunchFn *mfma_direct_sk_launchers(int *count);
 const LaunchFn *mfma_direct_ta_sk_launchers(int *count);

@@ -160,12 +160,24 @@ __device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&a
 // before the MFMAs of round r, so a round's memory latency overlaps the
 // previous round's arithmetic (loads past K read as zero, so the extra round
 // at the end touches no memory).
-template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0>
-__global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) {
+//
+// SPLIT: workgroup (strip, 0, z) runs its strip over rows [z*kslice,
+// (z+1)*kslice) of K only, as a product of its own (A and B advanced to the
+// slice, K its length), and stores to C + z*stride_c (the split launcher
+// points C at a workspace of partial results).
+template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0, bool SPLIT = false>
+__global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips, int kslice) {
     static_assert(IN == 0 || TB, "16-bit inputs: B transposed (word form)");
     using S = RowsShape<VW, W>;
     __shared__ __attribute__((aligned(16))) float red[S::RED];
     select_batch(p);
+    if constexpr (SPLIT) {
+        const long long k0 = (long long)blockIdx.z * kslice;
+        p.A += p.trans_a ? k0 * p.lda : k0;
+        p.B += p.trans_b ? k0 : k0 * p.ldb;
+        p.K = (int)((long long)kslice < p.K - k0 ? (long long)kslice : p.K - k0);
+        p.C += (long long)blockIdx.z * p.stride_c;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, g = lane >> 4;
     // neighbouring strips share cache lines of B: keep them on one XCD's L2
@@ -217,12 +229,78 @@ __global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips) 
     }
 }
 
-template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0>
+// Split-K of a few-rows product: the sum over the slices in slice order, then
+// C = act(alpha * sum + beta * C + bias) as the unsplit kernel's epilogue.
+__global__ void __launch_bounds__(256) rows_split_reduce(Problem p, const float *ws, int splits) {
+    const long long mn = (long long)p.M * p.N;
+    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < mn;
+         e += (long long)gridDim.x * blockDim.x) {
+        float sum = 0.f;
+        for (int z = 0; z < splits; ++z) sum += ws[z * mn + e];
+        const int row = (int)(e / p.N), col = (int)(e % p.N);
+        float *dst = p.C + (long long)row * p.ldc + col;
+        float out = p.alpha * sum;
+        if (p.beta != 0.f) out = fmaf(p.beta, *dst, out);
+        if (p.has_epilogue()) out = activate(p.act, p.bias ? out + p.bias[col] : out);
+        *dst = out;
+    }
+}
+
+// Slices for a split-K launch of a few-rows product, or 1: single products
+// whose strips fill under 192 CUs, cut into about 512 workgroups with at
+// least two rounds of U chunks per wave in every slice.  kslice: rows of K
+// per slice (a multiple of 16, so 16-byte alignment carries over).
+template <int VW, int W, int U>
+int rows_splits(const Problem &p, int &kslice) {
+    kslice = p.K;
+    if (p.batch != 1 || p.K == 0) return 1;
+    const long long strips = (p.N + 16 * VW - 1) / (16 * VW);
+    if (strips >= 192) return 1;
+    const long long chunks = (p.K + 15) / 16;
+    long long s = (512 + strips - 1) / strips;
+    const long long most = chunks / (2LL * W * U);
+    if (s > most) s = most;
+    if (s < 2) return 1;
+    const long long per = (chunks + s - 1) / s;
+    kslice = (int)(per * 16);
+    return (int)((p.K + kslice - 1) / kslice);
+}
+
+template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0, bool SPLIT = false>
 hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB, IN>), dim3(strips, p.batch),
-                       dim3(64 * W), 0, stream, p, strips);
-    return hipGetLastError();
+    int kslice = p.K;
+    const int splits = SPLIT ? rows_splits<VW, W, U>(p, kslice) : 1;
+    if (splits == 1) {
+        hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB, IN>), dim3(strips, p.batch),
+                           dim3(64 * W), 0, stream, p, strips, kslice);
+        return hipGetLastError();
+    }
+    // partial results of the slices: splits x M x N floats
+    const long long mn = (long long)p.M * p.N;
+    Workspace w;
+    hipError_t e = workspace_acquire((size_t)splits * mn * 4, stream, w);
+    if (e != hipSuccess) return e;
+    float *ws = static_cast<float *>(w.ptr);
+    Problem q = p;
+    q.C = ws;
+    q.ldc = p.N;
+    q.stride_c = mn;
+    q.alpha = 1.f;
+    q.beta = 0.f;
+    q.bias = nullptr;
+    q.act = SGEMM_ACT_NONE;
+    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB, IN, true>), dim3(strips, 1, splits),
+                       dim3(64 * W), 0, stream, q, strips, kslice);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        const long long blocks = (mn + 255) / 256 < 1024 ? (mn + 255) / 256 : 1024;
+        hipLaunchKernelGGL(rows_split_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+                           static_cast<const float *>(ws), splits);
+        e = hipGetLastError();
+    }
+    const hipError_t f = workspace_release(w, stream);
+    return e != hipSuccess ? e : f;
 }
 
 // 16-bit inputs, few rows: pw is the word-form problem (A untransposed, B
@@ -237,25 +315,25 @@ hipError_t launch_rows16_as(const Problem &pw, hipStream_t stream) {
     return launch_rows_as<1, 16, 4, false, false, true, IN>(pw, stream);
 }
 
-template <int VW, int W, int U, bool TB>
+template <int VW, int W, int U, bool TB, bool SPLIT>
 hipError_t launch_rows_tb(const Problem &p, bool va, bool vb, hipStream_t stream) {
-    if (va && vb) return launch_rows_as<VW, W, U, true, true, TB>(p, stream);
-    if (va) return launch_rows_as<VW, W, U, true, false, TB>(p, stream);
-    if (vb) return launch_rows_as<VW, W, U, false, true, TB>(p, stream);
-    return launch_rows_as<VW, W, U, false, false, TB>(p, stream);
+    if (va && vb) return launch_rows_as<VW, W, U, true, true, TB, 0, SPLIT>(p, stream);
+    if (va) return launch_rows_as<VW, W, U, true, false, TB, 0, SPLIT>(p, stream);
+    if (vb) return launch_rows_as<VW, W, U, false, true, TB, 0, SPLIT>(p, stream);
+    return launch_rows_as<VW, W, U, false, false, TB, 0, SPLIT>(p, stream);
 }
 
 // VEC: wide loads wherever an operand's rows allow them (decided per operand);
 // otherwise 4-byte loads throughout.
-template <int VW, int W, int U, bool VEC>
+template <int VW, int W, int U, bool VEC, bool SPLIT = false>
 hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
     const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
     if (p.trans_b) {
         const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);
-        return launch_rows_tb<VW, W, U, true>(p, va, vb, stream);
+        return launch_rows_tb<VW, W, U, true, SPLIT>(p, va, vb, stream);
     }
     const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, VW);
-    return launch_rows_tb<VW, W, U, false>(p, va, vb, stream);
+    return launch_rows_tb<VW, W, U, false, SPLIT>(p, va, vb, stream);
 }
 
 // ---------------------------------------------------------------- kind 1 ----
@@ -410,14 +488,14 @@ hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
     return launch_cols_bm<NB, W, U, 0>(p, va, stream);
 }
 
-template <int VW, int W, int U>
+template <int VW, int W, int U, bool SPLIT = false>
 constexpr TileEntry rows_entry() {
     using S = RowsShape<VW, W>;
     // the launchers apply a problem's bias / activation themselves, so the
     // 16-byte launcher is also the fused one
     return TileEntry{{16, 16 * VW, 16 * W, 16, 16 * VW, 0, 0, S::NT, S::LDS_BYTES, 0, 0},
-                     &launch_rows<VW, W, U, true>, &launch_rows<VW, W, U, false>, 0,
-                     &launch_rows<VW, W, U, true>};
+                     &launch_rows<VW, W, U, true, SPLIT>, &launch_rows<VW, W, U, false, SPLIT>, 0,
+                     &launch_rows<VW, W, U, true, SPLIT>};
 }
 
 template <int NB, int W, int U>
@@ -447,6 +525,8 @@ const TileEntry *skinny_tiles(int *count) {
         cols_entry<4, 4, 4>(),    // 6
         cols_entry<8, 4, 2>(),    // 7
         cols_entry<16, 4, 2>(),   // 8
+        rows_entry<4, 4, 4, true>(),    // 9: 64-column strips, split-K when strips are few
+        rows_entry<4, 8, 2, true>(),    // 10: the same, 8 waves
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;
@@ -467,15 +547,23 @@ bool skinny_fits(int tile, const Problem &p) {
     return skinny_kind(tile) == 0 ? p.M <= 16 : (p.N <= tiles[tile].desc.bn && !p.trans_a);
 }
 
+// Few-rows tile choice, from graph-replay and eager timings over M = 1..16,
+// N = 256..14336, K = 1024..16384 with operands larger than the Infinity
+// Cache: 64-column strips once they give most CUs a workgroup; 16-column
+// strips for B stored transposed (4 lanes read 64 contiguous bytes of a
+// column's K run), 32-column strips otherwise; split-K (tile 10) where those
+// leave most CUs idle for a long K.
 int skinny_pick(const Problem &p) {
-    const int M = p.M, N = p.N;
+    const int M = p.M, N = p.N, K = p.K;
     if (M <= 16) {
-        // the widest strip that still gives three quarters of the CUs a
-        // workgroup (measured best at 16 x 14336 x 4096 for either storage of
-        // B), else 32 or 16 columns
-        if ((N + 63) / 64 >= 192) return 2;
-        if ((N + 31) / 32 >= 256) return 1;
-        return 0;
+        if ((N + 63) / 64 >= 160) return 2;
+        const bool split_ok = p.batch == 1;
+        if (p.trans_b) {
+            if (split_ok && K >= 8192 && N <= 2048) return 10;
+            return N >= 8192 ? 1 : 0;
+        }
+        if (split_ok && ((K >= 4096 && N <= 2048) || (K >= 8192 && N <= 4096))) return 10;
+        return 1;
     }
     if (N <= 16 && !p.trans_a) {
         int count = 0;

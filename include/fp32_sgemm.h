@@ -20,14 +20,19 @@
  * written in C.
  *
  * Memory and ownership: A, B and C are DEVICE pointers owned by the caller.
- * The library keeps no pointer after a call returns.  It allocates device
- * memory in one case only: a stream-K launch (SGEMM_FLAG_STREAMK, or chosen
- * by automatic dispatch for a single product whose tile count leaves the
- * last wave of workgroups partly idle) takes a workspace for partial sums
- * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
- * stream (two tile accumulators for each of 256 workgroups: 64 MiB with
- * 256 x 128 tiles, 128 MiB with 256 x 256); an allocation failure is
- * returned as its hipError_t.  Work is
+ * The library keeps no pointer to them after a call returns.  It allocates
+ * device memory in two cases only, both for partial sums: a stream-K launch
+ * (SGEMM_FLAG_STREAMK, or chosen by automatic dispatch for a single product
+ * whose tile count leaves the last wave of workgroups partly idle; two tile
+ * accumulators for each of 256 workgroups: 64 MiB with 256 x 128 tiles,
+ * 128 MiB with 256 x 256), and a split-K launch of the few-rows skinny tiles
+ * (a K-slice count times M x N floats).  Outside graph capture the workspace
+ * is kept per device and stream and reused by later calls on that stream
+ * (taken with hipMallocAsync on the stream, grown when a call needs more, the
+ * old buffer returned with hipFreeAsync on the same stream; held until
+ * sgemm_workspace_release or process exit).  Under graph capture each call
+ * records its own allocation and free on the capturing stream.  An
+ * allocation failure is returned as its hipError_t.  Work is
  * enqueued on `stream` (NULL = the null stream) and the call
  * returns without synchronising: the caller keeps A, B and C alive and
  * unmodified until that stream's work has completed.  C must not overlap A
@@ -339,6 +344,15 @@ const char *sgemm_status_string(int status);
 
 /* Library version: major * 10000 + minor * 100 + patch. */
 int sgemm_version(void);
+
+/*
+ * sgemm_workspace_release: synchronise the current device and free the
+ * workspaces the library keeps for it (one per stream that has run a
+ * stream-K or split-K launch; see "Memory and ownership").  Later calls take
+ * new ones as needed.  Returns 0 or a hipError_t.  Not to be called while
+ * another thread runs sgemm calls on the same device.
+ */
+int sgemm_workspace_release(void);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,7 @@
-"""GPU parity of the stream-K launches (tiles flagged TILE_STREAMK, asked
-for with FLAG_STREAMK) against the CPU oracle.
+"""GPU parity of the launches that keep partial sums in a workspace against
+the CPU oracle: stream-K (tiles flagged TILE_STREAMK, asked for with
+FLAG_STREAMK) and split-K of the few-rows skinny tiles; and the workspace
+cache itself (streams, growth, release, graph capture).
 
 Stream-K cuts the k-steps of the last waves' tiles into 256 equal runs; a
 tile touched by several runs is summed by a second launch from partial sums.
@@ -215,3 +217,95 @@ def test_streamk_graph_capture():
         sg.gemm(dA, dB, eager, 1.0, 0.0)   # eager work between replays
         torch.cuda.synchronize()
     del g
+
+
+def test_workspace_streams_grow_and_release():
+    """The cached workspaces: stream-K and split-K calls on two streams at
+    once (each stream its own workspace), a larger call after a smaller one
+    on the same stream (the workspace grows while earlier work may still
+    use the old one), and calls after workspace_release; every result
+    matches a call made alone on the default stream, bit for bit."""
+    tiles = sk_tiles(False)
+    if not tiles:
+        pytest.skip("no stream-K tile")
+    rng = np.random.default_rng(2600)
+    cases = [(512, 512, 8192, dict(variant=sg.VARIANT_MFMA, tile=tiles[0], flags=sg.FLAG_STREAMK)),
+             (768, 640, 16384, dict(variant=sg.VARIANT_MFMA, tile=tiles[0], flags=sg.FLAG_STREAMK)),
+             (4, 1024, 8192, dict(variant=sg.VARIANT_SKINNY, tile=9)),
+             (16, 2048, 16384, dict(variant=sg.VARIANT_SKINNY, tile=9))]
+    ops = []
+    for M, N, K, kw in cases:
+        A = dev(rng.uniform(-1, 1, (M, K)).astype(F32))
+        B = dev(rng.uniform(-1, 1, (K, N)).astype(F32))
+        ref = torch.empty((M, N), device=DEV)
+        sg.gemm(A, B, ref, **kw)
+        ops.append((A, B, ref, kw))
+    torch.cuda.synchronize()
+    want = [r.cpu().numpy() for _, _, r, _ in ops]
+    for rnd in range(2):
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        outs = [[torch.full_like(r, float("nan")) for _, _, r, _ in ops] for _ in streams]
+        for rep in range(3):
+            for si, st in enumerate(streams):
+                with torch.cuda.stream(st):
+                    # small before large on each stream: the workspace grows in order
+                    for (A, B, _, kw), C in zip(ops, outs[si]):
+                        sg.gemm(A, B, C, **kw)
+        torch.cuda.synchronize()
+        for si in range(len(streams)):
+            for j, C in enumerate(outs[si]):
+                assert np.array_equal(C.cpu().numpy(), want[j]), \
+                    f"round {rnd} stream {si} case {cases[j][:3]} differs"
+        sg.workspace_release()
+
+
+SPLIT_CASES = [(1, 1000, 3001), (7, 77, 4097), (16, 2000, 8192), (3, 300, 16384), (1, 64, 1024)]
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
+@pytest.mark.parametrize("tile", [9, 10])
+def test_skinny_split_k(tile, ta, tb, oracle_mod):
+    """The few-rows tiles that split K over workgroups (partial sums in a
+    workspace, summed in slice order by a second kernel): random inputs with
+    alpha/beta and with bias + GELU within tolerance, 4-byte loads, integer
+    inputs bit-exact, and two calls give the same bits."""
+    if tile >= sg.tile_count(sg.VARIANT_SKINNY):
+        pytest.skip("tile not compiled")
+    kw = dict(variant=sg.VARIANT_SKINNY, tile=tile)
+    for i, (M, N, K) in enumerate(SPLIT_CASES):
+        lab = f"split t{tile} ta={ta} tb={tb} {(M, N, K)}"
+        print(lab, flush=True)
+        A, B, C0 = workloads.draw(M, N, K, "uniform", 2700 + i, True)
+        As, Bs = stored(A, B, ta, tb)
+        for flags in (0, sg.FLAG_SCALAR_IO):
+            C = dev(C0)
+            sg.gemm(dev(As), dev(Bs), C, 0.5, -1.25, trans_a=ta, trans_b=tb, flags=flags, **kw)
+            torch.cuda.synchronize()
+            got = C.cpu().numpy()
+            ref = oracle_mod.sgemm(As, Bs, C0.copy(), 0.5, -1.25, trans_a=ta, trans_b=tb)
+            r = max_err_ratio(got, ref, K, 0.5, -1.25, As, Bs, C0)
+            assert r <= 1.0, f"{lab} flags {flags}: max err/tol = {r}"
+        C2 = dev(C0)
+        sg.gemm(dev(As), dev(Bs), C2, 0.5, -1.25, trans_a=ta, trans_b=tb, **kw)
+        C3 = dev(C0)
+        sg.gemm(dev(As), dev(Bs), C3, 0.5, -1.25, trans_a=ta, trans_b=tb, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(C2, C3), f"{lab}: two calls differ"
+        bias = np.random.default_rng(2750 + i).uniform(-1, 1, N).astype(F32)
+        C = dev(C0)
+        sg.gemm(dev(As), dev(Bs), C, 1.0, 0.5, trans_a=ta, trans_b=tb, bias=dev(bias),
+                act=sg.ACT_GELU_ERF, **kw)
+        torch.cuda.synchronize()
+        ref = oracle_mod.sgemm(As, Bs, C0.copy(), 1.0, 0.5, trans_a=ta, trans_b=tb, bias=bias,
+                               act=sg.ACT_GELU_ERF)
+        x = oracle_mod.sgemm(As, Bs, C0.copy(), 1.0, 0.5, trans_a=ta, trans_b=tb, bias=bias)
+        r = epilogue_err_ratio(C.cpu().numpy(), ref, x, K, 1.0, 0.5, As, Bs, C0, bias,
+                               sg.ACT_GELU_ERF)
+        assert r <= 1.0, f"{lab} GELU: max err/tol = {r}"
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 2800 + i, True)
+        Ai, Bi = stored(Ai, Bi, ta, tb)
+        C = dev(Ci)
+        sg.gemm(dev(Ai), dev(Bi), C, 0.5, -1.25, trans_a=ta, trans_b=tb, **kw)
+        torch.cuda.synchronize()
+        ref = oracle_mod.sgemm(Ai, Bi, Ci.copy(), 0.5, -1.25, trans_a=ta, trans_b=tb)
+        assert np.array_equal(C.cpu().numpy(), ref), f"{lab} int: not bit-exact"
