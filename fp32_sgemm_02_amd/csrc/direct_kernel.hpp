@@ -612,14 +612,28 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
         mainloop(tm * BM, tn * BN, 0, nk);
         finish(tm * BM, tn * BN, 0, RB);
     } else if constexpr (MODE == 1) {
+        // whole tiles, numbered over the batch entries (the grid has one row):
+        // each XCD takes a contiguous range of them, so the panels its tiles
+        // share stay in its L2
         int m0, n0;
+        const int per_entry = tiles_m * tiles_n;
+        const float *A0 = p.A, *B0 = p.B;
+        float *C0 = p.C;
         for (int tile = blockIdx.x; tile < sk.dp_tiles; tile += sk.groups) {
-            coords(tile, m0, n0);
+            const int lt = xcd_remap(tile, sk.dp_tiles);
+            const int b = lt / per_entry;
+            p.A = A0 + b * p.stride_a;
+            p.B = B0 + b * p.stride_b;
+            p.C = C0 + b * p.stride_c;
+            coords(lt - b * per_entry, m0, n0);
             zero_acc();
             mainloop(m0, n0, 0, nk);
             finish(m0, n0, 0, RB);
             __syncthreads();   // LDS free for the next tile's loads
         }
+        p.A = A0;
+        p.B = B0;
+        p.C = C0;
         const long long total = (long long)sk.sk_tiles * sk.iters;
         long long it = (long long)blockIdx.x * sk.per_wg;
         const long long end = it + sk.per_wg < total ? it + sk.per_wg : total;
@@ -786,12 +800,13 @@ hipError_t launch_direct16(const Problem &pw, int group_m, hipStream_t stream) {
 constexpr int kStreamKGroups = 256;
 
 // Stream-K launch of a tile with one k-group (dwordx4 loads of A and B, the
-// guarded instance): the plan, a workspace from the stream-ordered allocator
-// (freed on the stream after the fixup), the runs and the fixup.  The last
-// full wave of tiles and the remainder are split (the tiles before them run
-// whole), so every workgroup gets the same number of k-iterations.
-// hipErrorNotSupported when the operands do not take dwordx4 loads or the
-// problem is batched.
+// guarded instance): the plan, the workspace (workspace_acquire), the runs
+// and the fixup.  The last full wave of tiles and the remainder are split
+// (the tiles before them run whole), so every workgroup gets the same number
+// of k-iterations.  A batch (at most kMaxBatchPerLaunch entries) runs the
+// same persistent workgroups over the whole tiles of all its entries, with
+// no split.  hipErrorNotSupported when the operands do not take dwordx4
+// loads.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, bool TA>
 hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
     if ((p.trans_a != 0) != TA) return hipErrorInvalidValue;
@@ -800,14 +815,34 @@ hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
     const bool av = rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) && (TA ? p.M : p.K) % 4 == 0;
     const bool bv = rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) && (tb ? p.K : p.N) % 4 == 0;
     const bool cv = rows_aligned(p.C, p.ldc, p.stride_c, p.batch, 4);
-    if (!av || !bv || p.batch != 1) return hipErrorNotSupported;
+    if (!av || !bv) return hipErrorNotSupported;
     using S = DirectShape<BM, BN, BK, WM, WN, NBUF, 4, 4, 1, false, TA>;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const long long tiles = (long long)tiles_m * tiles_n;
     const int G = kStreamKGroups;
-    if (tiles > 0x7fffffffLL / 16) return hipErrorInvalidConfiguration;
+    if (tiles * p.batch > 0x7fffffffLL / 16) return hipErrorInvalidConfiguration;
     if (group_m <= 0) group_m = 4;
     StreamK sk;
+    if (p.batch > 1) {
+        // a batch: persistent workgroups over the whole tiles of every entry
+        // (a tile's stores drain while the workgroup loads its next tile); no
+        // split, no workspace
+        sk.dp_tiles = (int)(tiles * p.batch);
+        sk.groups = sk.dp_tiles < G ? sk.dp_tiles : G;
+        sk.iters = (p.K + BK - 1) / BK;
+        sk.per_wg = 1;
+        Problem q = p;
+        q.batch = 1;   // the grid has one row; the kernel walks the entries
+        if (tb)
+            hipLaunchKernelGGL(
+                (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, true, TA, 4, 4, true, false, 0, 1>),
+                dim3(sk.groups), dim3(S::NT), 0, stream, q, tiles_m, tiles_n, group_m, (int)cv, sk);
+        else
+            hipLaunchKernelGGL(
+                (mfma_direct_kernel<BM, BN, BK, WM, WN, NBUF, 1, false, TA, 4, 4, true, false, 0, 1>),
+                dim3(sk.groups), dim3(S::NT), 0, stream, q, tiles_m, tiles_n, group_m, (int)cv, sk);
+        return hipGetLastError();
+    }
     sk.groups = G;
     sk.dp_tiles = tiles >= G ? (int)((tiles / G - 1) * G) : 0;
     sk.sk_tiles = (int)(tiles - sk.dp_tiles);

@@ -148,11 +148,13 @@ typedef struct sgemm_tile_desc {
  * them run as usual) as one list of k-steps cut into 256 equal runs; a run
  * that ends or starts inside a tile leaves that tile's partial sums in a
  * workspace, and a second launch adds each tile's pieces in k order and
- * applies alpha, beta and C.  Offered for single products (no batch) whose A
- * and B take 16-byte loads (rows 16-byte aligned, the stored row length a
- * multiple of 4); asked for with SGEMM_FLAG_STREAMK, otherwise sgemm_ex
- * returns -13.  The k-sum order then depends on the split, which is fixed for
- * a shape: results stay bitwise repeatable. */
+ * applies alpha, beta and C.  A batch (sgemm_strided_batched) runs the same
+ * persistent workgroups over the whole tiles of all its entries, with no
+ * split and no workspace.  Offered where A and B take 16-byte loads (rows
+ * 16-byte aligned, the stored row length a multiple of 4); asked for with
+ * SGEMM_FLAG_STREAMK, otherwise sgemm_ex returns -13.  The k-sum order then
+ * depends on the split, which is fixed for a shape: results stay bitwise
+ * repeatable. */
 #define SGEMM_TILE_STREAMK 0x10
 
 /*

@@ -309,3 +309,52 @@ def test_skinny_split_k(tile, ta, tb, oracle_mod):
         torch.cuda.synchronize()
         ref = oracle_mod.sgemm(Ai, Bi, Ci.copy(), 0.5, -1.25, trans_a=ta, trans_b=tb)
         assert np.array_equal(C.cpu().numpy(), ref), f"{lab} int: not bit-exact"
+
+
+@pytest.mark.parametrize("tb", [False, True])
+def test_persistent_batched(tb, oracle_mod):
+    """A batch through the stream-K launchers (persistent workgroups over the
+    whole tiles of every entry): ragged entries, more tiles than workgroups,
+    a shared B (stride 0); integers bit-exact, random inputs within
+    tolerance, the same bits as one workgroup per tile."""
+    tiles = sk_tiles(False)
+    if not tiles:
+        pytest.skip("no stream-K tile")
+    rng = np.random.default_rng(2900)
+    for tile in tiles:
+        d = sg.tile_info(sg.VARIANT_MFMA, tile)
+        for batch, M, N, K, shared_b in ((5, d["bm"] + 4, 3 * d["bn"] - 8, 68, False),
+                                        (40, 2 * d["bm"], 2 * d["bn"], 128, False),
+                                        (3, 300, 520, 36, True)):
+            lab = f"persistent t{tile} tb={tb} {(batch, M, N, K)} shared_b={shared_b}"
+            print(lab, flush=True)
+            for dist in ("int4", "uniform"):
+                if dist == "int4":
+                    A = rng.integers(-4, 5, (batch, M, K)).astype(F32)
+                    B = rng.integers(-4, 5, (1 if shared_b else batch, N if tb else K,
+                                             K if tb else N)).astype(F32)
+                    C0 = rng.integers(-4, 5, (batch, M, N)).astype(F32)
+                else:
+                    A = rng.uniform(-1, 1, (batch, M, K)).astype(F32)
+                    B = rng.uniform(-1, 1, (1 if shared_b else batch, N if tb else K,
+                                            K if tb else N)).astype(F32)
+                    C0 = rng.uniform(-1, 1, (batch, M, N)).astype(F32)
+                dA, dB = dev(A), dev(B[0] if shared_b else B)
+                C = dev(C0)
+                sg.gemm_batched(dA, dB, C, 0.5, -1.25, trans_b=tb, variant=sg.VARIANT_MFMA,
+                                tile=tile, flags=sg.FLAG_STREAMK)
+                C1 = dev(C0)
+                sg.gemm_batched(dA, dB, C1, 0.5, -1.25, trans_b=tb, variant=sg.VARIANT_MFMA,
+                                tile=tile)
+                torch.cuda.synchronize()
+                got = C.cpu().numpy()
+                assert np.array_equal(got, C1.cpu().numpy()), f"{lab} {dist}: differs from plain"
+                Bb = np.broadcast_to(B, (batch,) + B.shape[1:]) if shared_b else B
+                ref = oracle_mod.sgemm_batched(A, np.ascontiguousarray(Bb), C0.copy(), 0.5, -1.25,
+                                               trans_b=tb)
+                if dist == "int4":
+                    assert np.array_equal(got, ref), f"{lab}: not bit-exact"
+                else:
+                    for b in range(batch):
+                        r = max_err_ratio(got[b], ref[b], K, 0.5, -1.25, A[b], Bb[b], C0[b])
+                        assert r <= 1.0, f"{lab} entry {b}: max err/tol = {r}"
