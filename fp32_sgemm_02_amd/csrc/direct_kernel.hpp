@@ -351,7 +351,8 @@ __device__ __forceinline__ void roll_unit(int u, const floatx4 &a, const BFrag<S
 // end and split into `groups` consecutive runs of per_wg, one per workgroup.
 // A run's middle tiles are whole and stored directly; its first and last
 // tile may be partial, and their un-scaled partial sums go to workspace slots
-// 2g and 2g + 1 of workgroup g.  The fixup launch (MODE 2, one workgroup per
+// 2g and 2g + 1 of run g (run g is taken by the workgroup that xcd_remap
+// maps to g).  The fixup launch (MODE 2, one workgroup per
 // split tile and row block of the waves) adds a tile's pieces in k order and
 // stores C.  No workgroup waits for another.
 struct StreamK {
@@ -634,8 +635,11 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
         p.A = A0;
         p.B = B0;
         p.C = C0;
+        // run v of the split tiles: consecutive runs (and so neighbouring
+        // tiles, which share panels of A and B) on one XCD
+        const int v = xcd_remap(blockIdx.x, sk.groups);
         const long long total = (long long)sk.sk_tiles * sk.iters;
-        long long it = (long long)blockIdx.x * sk.per_wg;
+        long long it = (long long)v * sk.per_wg;
         const long long end = it + sk.per_wg < total ? it + sk.per_wg : total;
         while (it < end) {
             const int tl = (int)(it / sk.iters);
@@ -647,7 +651,7 @@ mfma_direct_kernel(Problem p, int tiles_m, int tiles_n, int group_m, int cvec, S
             if (k0 == 0 && k1 == sk.iters) {
                 finish(m0, n0, 0, RB);
             } else {
-                const int slot = 2 * blockIdx.x + (it == (long long)blockIdx.x * sk.per_wg ? 0 : 1);
+                const int slot = 2 * v + (it == (long long)v * sk.per_wg ? 0 : 1);
 #pragma unroll
                 for (int x = 0; x < RB; ++x)
 #pragma unroll
