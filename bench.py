@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W]            # headline line (4096^3)
     python bench.py --workload mlp_up                   # another named workload
-    python bench.py --sweep gpurun_out/sweep.json        # every workload, table
+    python bench.py --sweep sweep.json                  # every workload, table
                                                         # (memory-bound shapes rotate over
                                                         # operand copies > the 256 MB MALL)
     python bench.py --copy-bytes 1073741824              # plain copy (counter calibration)
