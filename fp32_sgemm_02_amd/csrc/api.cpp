@@ -273,6 +273,31 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr,
             }
         }
     }
+    // Short K (at most 256) with A untransposed, C at least 256 x 256 and two
+    // or more rounds of 128 x 128 tiles that fill at least 85 % of their last
+    // round and of their area: the 8-wave 128 x 128 tile, measured fastest there (batched attention scores
+    // 32 x 2048 x 2048 x 128: 308 us against 321 for the cost model's pick;
+    // 8192^2 x 64..256: 3-13 %; 5632^2 x 256: 2-4 %).  At short K the
+    // per-workgroup cost of the first loads and of the C store weighs more
+    // than the 4096^3 efficiencies of the table.
+    if (!p.trans_a && p.K <= 256) {
+        for (int i = 0; i < count; ++i) {
+            const sgemm_tile_desc &d = tiles[i].desc;
+            if (!((d.flags & SGEMM_TILE_DIRECT) && !(d.flags & SGEMM_TILE_TRANS_A) && d.bm == 128 &&
+                  d.bn == 128 && d.bk == 16 && d.wm == 32 && d.wn == 64))
+                continue;
+            const long long n = tiles_for(tiles[i], p.M, p.N) * p.batch;
+            const long long rounds = (n + kCUs - 1) / kCUs;
+            const double fill = (double)p.M * p.N * p.batch / ((double)n * 128 * 128);
+            if (tile_applies(tiles[i], p, io_ok) && p.M >= 256 && p.N >= 256 && rounds >= 2 &&
+                n * 100 >= 85 * rounds * kCUs && fill >= 0.85) {
+                best = i;
+                best_strips = Strips{0, 0};
+                if (streamk) *streamk = false;
+                break;
+            }
+        }
+    }
     if (strips) *strips = best_strips;
     return best;
 }
