@@ -11,6 +11,7 @@ every cell of C is the dot product of a row of A and a column of B.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -253,6 +254,14 @@ def _check_tensor(name, t, torch, device=None):
         raise ValueError(f"{name} must be on {device}")
 
 
+def _on_device(device, torch):
+    """A context that makes `device` current: a no-op when it already is
+    (the common case, and the switch costs host time on every call)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _stream_handle(stream, device, torch):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -292,7 +301,7 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool =
     else:
         if C.dtype != torch.float32 or C.device != A.device or tuple(C.shape) != (M, N):
             raise ValueError(f"C must be float32 ({M}, {N}) on {A.device}")
-    with torch.cuda.device(A.device):
+    with _on_device(A.device, torch):
         s = _stream_handle(stream, A.device, torch)
         ptr = lambda t: t.data_ptr() if t.numel() else None
         args = (M, N, K, float(alpha), ptr(A), _ld(A), ptr(B), _ld(B), float(beta), ptr(C),
@@ -339,7 +348,7 @@ def gemm_mixed(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: 
     _check_tensor("C", C, torch, A.device)
     if tuple(C.shape) != (M, N):
         raise ValueError(f"C must be ({M}, {N})")
-    with torch.cuda.device(A.device):
+    with _on_device(A.device, torch):
         s = _stream_handle(stream, A.device, torch)
         ptr = lambda t: t.data_ptr() if t.numel() else None
         explicit = not (variant == VARIANT_AUTO and tile < 0 and group_m == 0)
@@ -396,7 +405,7 @@ def gemm_batched(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a
     if C.dim() != 3 or tuple(C.shape) != (batch, M, N):
         raise ValueError(f"C must be ({batch}, {M}, {N})")
     _, _, _, ldc, sc = _batch_view("C", C, torch)
-    with torch.cuda.device(A.device):
+    with _on_device(A.device, torch):
         s = _stream_handle(stream, A.device, torch)
         ptr = lambda t: t.data_ptr() if t.numel() else None
         explicit = not (variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0)
