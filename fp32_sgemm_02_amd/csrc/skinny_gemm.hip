@@ -235,8 +235,17 @@ __global__ void __launch_bounds__(256) rows_split_reduce(Problem p, const float 
     const long long mn = (long long)p.M * p.N;
     for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < mn;
          e += (long long)gridDim.x * blockDim.x) {
+        // slice order kept; loads eight slices ahead of the adds
         float sum = 0.f;
-        for (int z = 0; z < splits; ++z) sum += ws[z * mn + e];
+        int z = 0;
+        for (; z + 8 <= splits; z += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ws[(z + u) * mn + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; z < splits; ++z) sum += ws[z * mn + e];
         const int row = (int)(e / p.N), col = (int)(e % p.N);
         float *dst = p.C + (long long)row * p.ldc + col;
         float out = p.alpha * sum;
