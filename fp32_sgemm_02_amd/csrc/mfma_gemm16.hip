@@ -29,7 +29,8 @@ namespace {
     X(256, 128, 32, 64, 64, 2, 1, 41)           \
     X(128, 128, 32, 32, 64, 2, 1, 41)           \
     X(128, 128, 32, 64, 64, 2, 2, 38)           \
-    X(64, 64, 32, 32, 64, 2, 2, 35)
+    X(64, 64, 32, 32, 64, 2, 2, 35)            \
+    X(256, 256, 32, 64, 128, 2, 1, 50)
 
 struct Tile16 {
     sgemm_tile_desc desc;
