@@ -36,6 +36,7 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and packed vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TILE_DIRECT = 0x2  # sgemm_tile_desc.flags bit of the direct-load MFMA tiles
+TILE_TRANS_B = 0x4  # ... of those compiled with edges (they also read B stored transposed)
 TILE_TRANS_A = 0x8  # ... of those that read A stored transposed
 KERNEL_SOURCES = {
     1: ["mfma_gemm.hip", "gemm_internal.hpp"],
@@ -64,8 +65,9 @@ def kernel_name(variant: int, desc: dict) -> str:
         return fam
     if variant == 1 and desc.get("flags", 0) & TILE_DIRECT:
         fam = "mfma_direct_ta" if desc["flags"] & TILE_TRANS_A else "mfma_direct"
+    edges = "_edges" if variant == 1 and desc.get("flags", 0) & TILE_TRANS_B else ""
     return (f"{fam}_{desc['bm']}x{desc['bn']}x{desc['bk']}_w{desc['wm']}x{desc['wn']}"
-            f"_s{desc.get('stages', 0)}_t{desc['threads']}")
+            f"_s{desc.get('stages', 0)}_t{desc['threads']}{edges}")
 
 
 def parse():
