@@ -42,7 +42,7 @@ struct RowsShape {
 };
 
 // Rows of B in the few-rows kernel and the row of A in the few-columns kernel
-// are streamed exactly once: their 16-byte loads are non-temporal (measured
+// are streamed exactly once: their 8- and 16-byte loads are non-temporal (measured
 // +2-6 % on 16 x 14336 x 4096, 4096 x 1 x 4096 and 1 x 2048 x 8192).  The
 // column runs of B^T are not: 4 lanes share each 64-byte run, and the hint
 // cost 6 % there.
@@ -59,7 +59,7 @@ __device__ __forceinline__ void load_brow(const Problem &p, int k, int gn, float
             return;
         } else if constexpr (VW == 2) {
             typedef float floatx2 __attribute__((ext_vector_type(2)));
-            const floatx2 t = *reinterpret_cast<const floatx2 *>(src);
+            const floatx2 t = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(src));
             v[0] = t[0]; v[1] = t[1];
             return;
         }
