@@ -188,3 +188,27 @@ def test_batched_attention_shapes(oracle_mod):
     torch.cuda.synchronize()
     ref = oracle_mod.sgemm_batched(P, V, None, 1.0, 0.0)
     check(P, V, None, 1.0, 0.0, out.cpu().numpy(), ref, False, "weighted sum")
+
+
+def test_batched_short_k_automatic(oracle_mod):
+    """Attention scores at a size where the automatic plan takes the
+    short-K rule (K = 128, two full rounds of 128 x 128 tiles): 8 heads of
+    1024 x 1024 x 128 with B stored transposed, and the same through the
+    persistent schedule of a 256-row tile; small-integer inputs, so every
+    result must equal the oracle's bit for bit."""
+    rng = np.random.default_rng(23)
+    heads, S, D = 8, 1024, 128
+    Q = rng.integers(-4, 5, (heads, S, D)).astype(F32)
+    Kt = rng.integers(-4, 5, (heads, S, D)).astype(F32)
+    ref = oracle_mod.sgemm_batched(Q, Kt, None, 0.5, 0.0, trans_b=True)
+    got = sg.gemm_batched(dev(Q), dev(Kt), None, 0.5, 0.0, trans_b=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref), "automatic plan differs from the oracle"
+    sk = [t for t in range(sg.tile_count(sg.VARIANT_MFMA))
+          if sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_STREAMK
+          and not sg.tile_info(sg.VARIANT_MFMA, t)["flags"] & sg.TILE_TRANS_A]
+    if sk:
+        got = sg.gemm_batched(dev(Q), dev(Kt), None, 0.5, 0.0, trans_b=True,
+                              variant=sg.VARIANT_MFMA, tile=sk[0], flags=sg.FLAG_STREAMK)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), ref), "persistent schedule differs"
