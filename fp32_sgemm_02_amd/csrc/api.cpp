@@ -17,7 +17,7 @@
 namespace sg {
 namespace {
 
-constexpr int kVersion = 300;   // 0.3.0
+constexpr int kVersion = 400;   // 0.4.0
 constexpr int kBadConfig = -13;
 constexpr int kBadTransA = -21;
 constexpr int kBadTransB = -22;
@@ -215,6 +215,13 @@ bool streamk_ok(const Problem &p) {
            (p.trans_a ? p.M : p.K) % 4 == 0 && (p.trans_b ? p.K : p.N) % 4 == 0;
 }
 
+// Workspace bytes (after the counters) of a stream-K launch of tile t: two
+// tile accumulators for each of the 256 persistent workgroups (none for a
+// batch, which runs whole tiles only).
+size_t streamk_workspace_bytes(const TileEntry &t, const Problem &p) {
+    return p.batch > 1 ? 0 : (size_t)2 * 256 * 4 * t.desc.bm * t.desc.bn;
+}
+
 double streamk_cost(const TileEntry &t, const Problem &p) {
     const long long tiles = tiles_for(t, p.M, p.N);
     const long long iters = (p.K + t.desc.bk - 1) / t.desc.bk;
@@ -257,8 +264,10 @@ int default_mfma_tile(const Problem &p, bool io_ok, Strips *strips = nullptr,
             best_strips = sp;
             if (streamk) *streamk = false;
         }
+        // (with a caller's scratch: only where its workspace fits)
         if (streamk && tiles[i].streamk && io_ok && streamk_ok(p) &&
             tile_applies(tiles[i], p, io_ok) &&
+            (!p.scratch || streamk_workspace_bytes(tiles[i], p) <= p.scratch_bytes) &&
             (p.batch == 1 || (p.K <= 256 && tiles_for(tiles[i], p.M, p.N) * p.batch >= 2 * kCUs))) {
             // a batch runs persistent whole tiles: measured 3-5 % faster than
             // one workgroup per tile when K is short and tiles span several
@@ -450,9 +459,20 @@ int validate(const Problem &p) {
     return 0;
 }
 
+// Workspace bytes (after the counters) that launching choice ch on p takes.
+size_t choice_workspace(const Problem &p, const Choice &ch) {
+    int count = 0;
+    const TileEntry *t = family(ch.variant, &count);
+    if (ch.variant == SGEMM_VARIANT_SKINNY) return skinny_workspace_bytes(ch.tile, p, ch.group_m);
+    if (ch.streamk && t && ch.tile < count) return streamk_workspace_bytes(t[ch.tile], p);
+    return 0;
+}
+
 // Validates and runs one call.  The special cases of the reference BLAS:
 // nothing to do for an empty C or batch; alpha == 0 or K == 0 leaves
-// C = beta * C (plus the epilogue), without reading A or B.
+// C = beta * C (plus the epilogue), without reading A or B.  A problem that
+// brings its own scratch for partial sums runs only plans whose partial sums
+// fit it, and is rejected before anything is launched otherwise.
 int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
     const int v = validate(p);
     if (v != 0) return v;
@@ -468,28 +488,37 @@ int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
     Strips sp;
     int st = resolve(p, cfg, ch, &sp);
     if (st != 0) return st;
-    if (!sp.rows && !sp.cols) return launch(p, ch, stream);
-    // main part, then the column strip beside it, then the row strip below
+    // the parts of the plan: the main part, the column strip beside it, the
+    // row strip below it
     const int m1 = p.M - sp.rows, n1 = p.N - sp.cols;
-    st = launch(main_part(p, sp), ch, stream);
-    if (st == 0 && sp.cols) {
-        Problem cols = p;
+    Problem cols = p, rows = p;
+    Choice ch_cols, ch_rows;
+    if (sp.cols) {
         cols.M = m1;
         cols.N = sp.cols;
         cols.B = p.trans_b ? p.B + (long long)n1 * p.ldb : p.B + n1;
         cols.C = p.C + n1;
         if (p.bias) cols.bias = p.bias + n1;
-        st = resolve(cols, nullptr, ch);
-        if (st == 0) st = launch(cols, ch, stream);
+        st = resolve(cols, nullptr, ch_cols);
+        if (st != 0) return st;
     }
-    if (st == 0 && sp.rows) {
-        Problem rows = p;
+    if (sp.rows) {
         rows.M = sp.rows;
         rows.A = p.A + (long long)m1 * p.lda;
         rows.C = p.C + (long long)m1 * p.ldc;
-        st = resolve(rows, nullptr, ch);
-        if (st == 0) st = launch(rows, ch, stream);
+        st = resolve(rows, nullptr, ch_rows);
+        if (st != 0) return st;
     }
+    const Problem main = main_part(p, sp);
+    if (p.scratch) {
+        if (choice_workspace(main, ch) > p.scratch_bytes ||
+            (sp.cols && choice_workspace(cols, ch_cols) > p.scratch_bytes) ||
+            (sp.rows && choice_workspace(rows, ch_rows) > p.scratch_bytes))
+            return kBadConfig;
+    }
+    st = launch(main, ch, stream);
+    if (st == 0 && sp.cols) st = launch(cols, ch_cols, stream);
+    if (st == 0 && sp.rows) st = launch(rows, ch_rows, stream);
     return st;
 }
 
@@ -677,7 +706,10 @@ int sgemm_op_plan(int trans_a, int trans_b, int M, int N, int K, const float *A,
     if (st != 0) return st;
     out->variant = ch.variant;
     out->tile = ch.tile;
-    out->group_m = ch.group_m;
+    // a few-rows skinny plan reports the K slices it splits into
+    out->group_m = (ch.variant == SGEMM_VARIANT_SKINNY && sg::skinny_kind(ch.tile) == 0)
+                       ? sg::skinny_slices(ch.tile, p, ch.group_m)
+                       : ch.group_m;
     out->flags = (ch.vec ? 0 : SGEMM_FLAG_SCALAR_IO) | (ch.streamk ? SGEMM_FLAG_STREAMK : 0);
     if (edge_rows) *edge_rows = sp.rows;
     if (edge_cols) *edge_cols = sp.cols;

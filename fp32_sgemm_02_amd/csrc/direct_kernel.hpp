@@ -858,7 +858,7 @@ hipError_t launch_streamk(const Problem &p, int group_m, hipStream_t stream) {
     sk.per_wg = (int)((sk_iters + G - 1) / G);
     const size_t bytes = (size_t)2 * G * (S::RB * S::CB) * S::NT * 16;   // two slots a run
     Workspace w;
-    hipError_t e = workspace_acquire(bytes, stream, w);
+    hipError_t e = workspace_acquire(bytes, stream, p, w);
     if (e != hipSuccess) return e;
     sk.ws = static_cast<float *>(w.ptr);
     if (tb)

@@ -31,6 +31,12 @@ struct Problem {
     long long stride_a = 0, stride_b = 0, stride_c = 0;
     const float *bias = nullptr;   // epilogue: one float per column of C, or none
     int act = SGEMM_ACT_NONE;      // epilogue activation
+    // Device memory that partial sums of this call take instead of the
+    // library's workspace (the entry point that allocates nothing): arrival
+    // counters first (kWorkspaceCounterBytes, zero between launches), then
+    // scratch_bytes for the sums.  Null: the workspace of workspace_acquire.
+    void *scratch = nullptr;
+    size_t scratch_bytes = 0;
     __host__ __device__ bool has_epilogue() const {
         return bias != nullptr || act != SGEMM_ACT_NONE;
     }
@@ -90,15 +96,23 @@ const TileEntry *mfma_direct_ta_tiles(int *count);   // ... A transposed
 // their fused-epilogue launchers, one per tile in table order
 const LaunchFn *mfma_direct_epi_launchers(int *count);
 const LaunchFn *mfma_direct_ta_epi_launchers(int *count);
-// Device workspace of a launch that keeps partial sums (workspace.cpp):
-// outside graph capture the buffer cached for the (device, stream), reused by
-// every call on that stream; under capture a stream-ordered allocation of the
-// graph's own.  Release after the launches that use it.
+// Device workspace of a launch that keeps partial sums (workspace.cpp): the
+// problem's scratch when it has one; otherwise, outside graph capture, the
+// buffer cached for the (device, stream), reused by every call on that
+// stream; under capture a stream-ordered allocation of the graph's own.
+// Every workspace starts with kWorkspaceCounters arrival counters, zero
+// between launches (a launch that counts arrivals sets them back to zero),
+// followed by `bytes` for the partial sums.  Release after the launches that
+// use it.
+constexpr int kWorkspaceCounters = 4096;
+constexpr size_t kWorkspaceCounterBytes = 4 * kWorkspaceCounters;
 struct Workspace {
-    void *ptr = nullptr;
-    bool owned = false;   // allocated for this call (graph capture)
+    void *ptr = nullptr;            // the partial sums
+    unsigned *counters = nullptr;   // kWorkspaceCounters arrival counters
+    void *base = nullptr;           // the allocation (graph capture)
+    bool owned = false;             // allocated for this call (graph capture)
 };
-hipError_t workspace_acquire(size_t bytes, hipStream_t stream, Workspace &w);
+hipError_t workspace_acquire(size_t bytes, hipStream_t stream, const Problem &p, Workspace &w);
 hipError_t workspace_release(const Workspace &w, hipStream_t stream);
 hipError_t workspace_release_all();   // the current device's cached buffers
 
@@ -125,6 +139,11 @@ hipError_t launch_skinny16(int dtype, const Problem &pw, hipStream_t stream);
 int skinny_pick(const Problem &p);
 int skinny_kind(int tile);
 bool skinny_fits(int tile, const Problem &p);
+// Workspace bytes (after the counters) of a skinny launch of `tile`, with
+// group_m as passed to its launcher; 0 when it needs none.
+size_t skinny_workspace_bytes(int tile, const Problem &p, int group_m);
+// K slices of a few-rows skinny launch (group_m as passed to its launcher).
+int skinny_slices(int tile, const Problem &p, int group_m);
 
 // C = act(beta * C + bias) over p's batch (beta == 0: C is not read); with
 // no epilogue, C = beta * C.  The alpha == 0 / K == 0 case, and the bias and

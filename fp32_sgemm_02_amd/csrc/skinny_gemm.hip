@@ -1,30 +1,48 @@
 // skinny_gemm.hip -- SGEMM shapes with few rows (M <= 16) or few columns
 // (N <= 16) of C.  They do O(1) flops per byte of the large operand, far below
 // the ridge point of the roofline ("The GEMM Scrapbook", roofline paragraph:
-// peak flops over memory bandwidth), so they are bound by HBM and the kernels
-// are built to stream the large operand exactly once with wide, coalesced
-// loads, with K split over the waves of a workgroup and a fixed-order LDS
-// reduction (no atomics, so results are bitwise repeatable).
+// peak flops over memory bandwidth), so they are bound by HBM: the kernels
+// stream the large operand exactly once, with every wave keeping several
+// 16-byte loads per lane in flight.
+//
+// Every load is a buffer load whose offset is computed without branches: a
+// lane whose element lies outside the matrix (or outside its K slice) gets an
+// offset past the buffer's range, and the hardware returns zeros without
+// touching memory ("The 1% kernel" section 6: idle threads past the matrix).
+// Per-lane branches around the loads would make the compiler wait for every
+// load in flight at each branch join, one load at a time.
 //
 // Few rows (kind 0): C (M x N) = A (M x K) * B (K x N), B streamed.  The M <= 16
 // rows of A are the A operand of v_mfma_f32_16x16x4_f32 (rows >= M read as
-// zero); each workgroup owns a strip of 16*VW columns.  Lane l (i = l % 16,
-// g = l / 16) in MFMA step s of a 16-wide k-chunk supplies k = 4g + s, and VW
-// consecutive B values of row k (columns VW*i + c, c < VW, feed MFMA column
-// block c), so a row of the strip is one contiguous 64*VW-byte run per 16
-// lanes.  The result register r of block c is C[4g + r][VW*i + c].
+// zero).  A wave owns 64*Q columns of C; lane l (i = l % 16, g = l / 16)
+// supplies, in MFMA step s of a 16-row k-chunk, k = 4g + s, and loads four
+// consecutive B values of row k at columns 64q + 4i .. +3 for each q < Q:
+// the 16 lanes of a row group read 256 contiguous bytes per load, 256*Q per
+// row in all ("a CUDA matmul" section 04: neighbouring lanes on neighbouring
+// addresses).  Column 64q + 4i + c feeds MFMA column block 4q + c, whose
+// result register r is C[4g + r][64q + 4i + c].  The WK waves of a
+// workgroup share its columns and take turns over the 16-row k-chunks; their
+// sums meet in LDS in a fixed order.
 //
-// Few columns (kind 1): each wave owns one row of A and walks it with 16-byte
-// loads (neighbouring lanes on neighbouring addresses: "a CUDA matmul"
-// section 04), multiplying by the N <= NB columns of B (small, cache
-// resident), then reduces its 64 lanes.
+// Schedule.  A workgroup owns one strip of 64*Q columns and one slice of K.
+// With S > 1 slices the slices' partial sums go to a workspace and the last
+// workgroup of a strip to arrive (an atomic counter per strip) adds them in
+// slice order and writes C: the result does not depend on which workgroup
+// finishes last, and one launch does the whole product.  HBM is saturated
+// only when every CU streams, so skinny products whose strips are fewer than
+// the CUs are split; the small tiles fit several workgroups per CU, so that
+// one workgroup's closing reduction overlaps the others' loads.
+//
+// Few columns (kind 1): each wave owns R rows of A and walks them with 16-byte
+// loads along k, multiplying by the N <= NB columns of B (small, cache
+// resident; one load of B serves the R rows), then reduces its 64 lanes.
 //
 // Transposed storage.  B stored N x K (a linear layer's weight, C = X W^T):
-// in kind 0 a lane's four k values of one column are contiguous in that
-// column's row of B^T, one 16-byte load per column (4 lanes cover 64
-// contiguous bytes of a row per chunk); in kind 1 the N <= NB rows of B^T
-// are read 16 bytes at a time like A's row.  A stored K x M is served by
-// kind 0 only (its <= 16 columns are read four bytes at a time; A is small).
+// in kind 0 a lane loads the four k values 4g .. 4g+3 of a column from that
+// column's row of B^T (one 16-byte load per column, the MFMA operand of all
+// four steps); in kind 1 the N <= NB rows of B^T are read 16 bytes at a time
+// like A's rows.  A stored K x M is served by kind 0 only (its <= 16 columns
+// are read four bytes at a time; A is small).
 #include <cstdint>
 
 #include "gemm_internal.hpp"
@@ -32,96 +50,142 @@
 namespace sg {
 namespace {
 
-// ---------------------------------------------------------------- kind 0 ----
-template <int VW, int W>
-struct RowsShape {
-    static constexpr int NT = 64 * W;
-    static constexpr int STRIP = 16 * VW;
-    static constexpr int RED = W * VW * 64 * 4;      // floats of the reduction buffer
-    static constexpr int LDS_BYTES = RED * 4;
-};
+// A buffer offset past every resource's range (records are below 2^31).
+constexpr int kOff = (int)0x80000000u;
 
-// Rows of B in the few-rows kernel and the row of A in the few-columns kernel
-// are streamed exactly once: their 8- and 16-byte loads are non-temporal (measured
-// +2-6 % on 16 x 14336 x 4096, 4096 x 1 x 4096 and 1 x 2048 x 8192).  The
-// column runs of B^T are not: 4 lanes share each 64-byte run, and the hint
-// cost 6 % there.
-template <int VW, bool VEC>
-__device__ __forceinline__ void load_brow(const Problem &p, int k, int gn, float (&v)[VW]) {
-#pragma unroll
-    for (int c = 0; c < VW; ++c) v[c] = 0.f;
-    if (k >= p.K) return;
-    const float *src = p.B + (long long)k * p.ldb + gn;
-    if (VEC && gn + VW - 1 < p.N) {
-        if constexpr (VW == 4) {
-            const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(src));
-            v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
-            return;
-        } else if constexpr (VW == 2) {
-            typedef float floatx2 __attribute__((ext_vector_type(2)));
-            const floatx2 t = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(src));
-            v[0] = t[0]; v[1] = t[1];
-            return;
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < VW; ++c)
-        if (gn + c < p.N) v[c] = src[c];
+// Raw buffer resource over [base, base + bytes), capped at 2^31 - 1 bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, long long bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n, 0x00020000);
 }
 
-// One round of a wave's loads: U 16-wide k-chunks (chunk indices j, j + W,
-// ..., j + (U-1)W), for each 4 B rows of VW values and a 4-value A sliver.
-template <int VW, int U>
+// 16-byte and 4-byte buffer loads; NT: non-temporal (data streamed once).
+template <bool NT>
+__device__ __forceinline__ floatx4 ld4(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(floatx4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
+}
+__device__ __forceinline__ float ld1(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// The finished value of one cell: alpha * sum (+ beta * C) (+ bias, act).
+__device__ __forceinline__ void store_cell(const Problem &p, float *dst, int col, float sum) {
+    float out = p.alpha * sum;
+    if (p.beta != 0.f) out = fmaf(p.beta, *dst, out);
+    if (p.has_epilogue()) out = activate(p.act, p.bias ? out + p.bias[col] : out);
+    *dst = out;
+}
+
+// ---------------------------------------------------------------- kind 0 ----
+// The split of a few-rows launch: workgroup w owns strip w % strips and K
+// slice w / strips, rows [slice * kslice, min(K, (slice + 1) * kslice)).
+struct RowsGrid {
+    int strips;        // column strips of 64*Q
+    int slices;        // K slices (1: no split, no workspace)
+    int kslice;        // rows of K per slice, a multiple of 16
+    float *part;       // slices x M x N partial sums (row-major, leading dimension N)
+    unsigned *count;   // one arrival counter per strip, zero between launches
+};
+
+template <int Q, int WK, int U>
+struct RowsShape {
+    static constexpr int NT = 64 * WK;
+    static constexpr int COLS = 64 * Q;
+    static constexpr int ACC = 4 * Q;                    // floatx4 accumulators per lane
+    static constexpr int LDS_BYTES = WK * ACC * 64 * 16;
+    static_assert(LDS_BYTES <= 64 * 1024, "wave sums of a workgroup fit 64 KB of LDS");
+};
+
+// One round of a wave's loads: U consecutive 16-row k-chunks.
+// B untransposed: b[u][s][q] = B(k0 + s, 64q + 4i + 0..3);
+// B transposed:   b[u][c][q] = B(k0 + 0..3, 64q + 4i + c);
+// a[u] = A(row i, k0 + 0..3); k0 = 16 * chunk + 4g.
+template <int Q, int U>
 struct RowsRound {
-    float b[U][4][VW];
+    floatx4 b[U][4][Q];
     floatx4 a[U];
 };
 
-// B^T stored N x K: the four k values k0 .. k0+3 of column n (zero past K or N).
-template <bool VEC>
-__device__ __forceinline__ floatx4 load_bcol(const Problem &p, int k0, int n) {
-    floatx4 t = {0.f, 0.f, 0.f, 0.f};
-    if (n >= p.N || k0 >= p.K) return t;
-    const float *src = p.B + (long long)n * p.ldb + k0;
-    if (VEC && k0 + 3 < p.K) return *reinterpret_cast<const floatx4 *>(src);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (k0 + e < p.K) t[e] = src[e];
-    return t;
-}
-
-// VA: rows of A allow 16-byte loads (untransposed A); VB: rows of B allow
-// VW-float loads (16-byte loads of B^T's rows with TB).  `arow` walks A's
-// row i in steps of `astep` floats (1, or lda for A stored transposed).
-template <int VW, int W, int U, bool VA, bool VB, bool TB>
-__device__ __forceinline__ void rows_load(const Problem &p, int j, int g, int gn, bool row_ok,
-                                          const float *arow, long long astep,
-                                          RowsRound<VW, U> &r) {
+// VA / VB: 16-byte loads of A / B (rows 16-byte aligned, the stored row length
+// a multiple of 4, so a group of four never straddles the edge).  kr0 is the
+// first row of K of the round's U consecutive chunks (uniform over the
+// wave): for B stored transposed, the four lanes of a column read 64
+// contiguous bytes per chunk, so a round reads 64*U per column.  Each
+// chunk (and, for B^T, each 64-column group) gets a resource of its own that
+// starts at its first row (column), so the per-lane offsets stay below 2^31
+// for any K: under 16 * ldb floats for B, 64 * ldb for B^T, 16 * lda for A.
+template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB>
+__device__ __forceinline__ void rows_load(const Problem &p, int ke, int n0, int ncols, int kr0,
+                                          int i, int g, RowsRound<Q, U> &r) {
+    const int ldb = (int)p.ldb, lda = (int)p.lda;
+    const int kk = 4 * g;   // this lane's first row of a chunk
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int k0 = (j + u * W) * 16 + 4 * g;
+        const int kr = kr0 + 16 * u;   // the chunk's first row
+        const int krem = ke - kr;            // rows of the slice from kr on
         if constexpr (TB) {
 #pragma unroll
-            for (int c = 0; c < VW; ++c) {
-                const floatx4 t = load_bcol<VB>(p, k0, gn + c);
+            for (int q = 0; q < Q; ++q) {
+                const __amdgpu_buffer_rsrc_t rb =
+                    make_rsrc(p.B + (long long)(n0 + 64 * q) * p.ldb + kr,
+                              4 * ((long long)(ncols - 64 * q - 1) * p.ldb + krem));
 #pragma unroll
-                for (int s = 0; s < 4; ++s) r.b[u][s][c] = t[s];
+                for (int c = 0; c < 4; ++c) {
+                    const int col = 4 * i + c;   // within the 64-column group
+                    const bool ok = 64 * q + col < ncols;
+                    if constexpr (VB) {
+                        r.b[u][c][q] = ld4<false>(rb, (ok && kk < krem) ? (col * ldb + kk) * 4 : kOff);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            r.b[u][c][q][e] =
+                                ld1(rb, (ok && kk + e < krem) ? (col * ldb + kk + e) * 4 : kOff);
+                    }
+                }
             }
         } else {
+            // rows of the chunk past the slice fall outside the resource (its
+            // records end at row min(krem, 16)), so the 16-byte loads' offsets
+            // depend on the lane only and stay in registers across rounds
+            const int rows = krem < 16 ? (krem > 0 ? krem : 0) : 16;
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(p.B + (long long)kr * p.ldb + n0, 4LL * rows * p.ldb);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) load_brow<VW, VB>(p, k0 + s, gn, r.b[u][s]);
+            for (int s = 0; s < 4; ++s) {
+                const bool rok = kk + s < krem;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int col = 64 * q + 4 * i;
+                    if constexpr (VB) {
+                        r.b[u][s][q] = ld4<true>(rb, col < ncols ? ((kk + s) * ldb + col) * 4 : kOff);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            r.b[u][s][q][c] = ld1(
+                                rb, (rok && col + c < ncols) ? ((kk + s) * ldb + col + c) * 4 : kOff);
+                    }
+                }
+            }
         }
-        floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) {
-            if (VA && astep == 1 && k0 + 3 < p.K) {
-                a = *reinterpret_cast<const floatx4 *>(arow + k0);
+        const bool mok = i < p.M;
+        if constexpr (TA) {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+                p.A + (long long)kr * p.lda, 4 * ((long long)(krem - 1) * p.lda + p.M));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r.a[u][e] = ld1(ra, (mok && kk + e < krem) ? ((kk + e) * lda + i) * 4 : kOff);
+        } else {
+            const __amdgpu_buffer_rsrc_t ra =
+                make_rsrc(p.A + kr, 4 * ((long long)(p.M - 1) * p.lda + krem));
+            if constexpr (VA) {
+                r.a[u] = ld4<false>(ra, (mok && kk < krem) ? (i * lda + kk) * 4 : kOff);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (k0 + e < p.K) a[e] = arow[(long long)(k0 + e) * astep];
+                    r.a[u][e] = ld1(ra, (mok && kk + e < krem) ? (i * lda + kk + e) * 4 : kOff);
             }
         }
-        r.a[u] = a;
     }
 }
 
@@ -129,396 +193,452 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // IN = 1 / 2: 16-bit inputs in word form (see the 16-bit family): a lane's
-// four k-words of A and of column c are the 8 k values of one
+// four k-words of A and of a column are the 8 k values of one
 // v_mfma_f32_16x16x32 (bfloat16 / float16).
-template <int VW, int U, int IN = 0>
-__device__ __forceinline__ void rows_mfma(const RowsRound<VW, U> &r, floatx4 (&acc)[VW]) {
-    if constexpr (IN != 0) {
+template <int Q, int U, bool TB, int IN>
+__device__ __forceinline__ void rows_mfma(const RowsRound<Q, U> &r, floatx4 (&acc)[4 * Q]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+        if constexpr (IN != 0) {
 #pragma unroll
-            for (int c = 0; c < VW; ++c) {
-                const floatx4 b = {r.b[u][0][c], r.b[u][1][c], r.b[u][2][c], r.b[u][3][c]};
-                if constexpr (IN == 1)
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, r.a[u]), __builtin_bit_cast(bf16x8, b), acc[c],
-                        0, 0, 0);
-                else
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(f16x8, r.a[u]), __builtin_bit_cast(f16x8, b), acc[c],
-                        0, 0, 0);
-            }
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if constexpr (IN == 1)
+                        acc[4 * q + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, r.a[u]),
+                            __builtin_bit_cast(bf16x8, r.b[u][c][q]), acc[4 * q + c], 0, 0, 0);
+                    else
+                        acc[4 * q + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, r.a[u]),
+                            __builtin_bit_cast(f16x8, r.b[u][c][q]), acc[4 * q + c], 0, 0, 0);
+                }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float b = TB ? r.b[u][c][q][s] : r.b[u][s][q][c];
+                        acc[4 * q + c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            r.a[u][s], b, acc[4 * q + c], 0, 0, 0);
+                    }
+        }
+    }
+}
+
+// Cell (m, col) of a strip from the waves' sums in LDS, added in wave
+// order: register m % 4 of accumulator 4 (col / 64) + col % 4 of lane
+// 16 (m / 4) + (col % 64) / 4.
+template <int Q, int WK>
+__device__ __forceinline__ float wave_sum(const floatx4 (&red)[WK][4 * Q][64], int m, int col) {
+    const int a = 4 * (col >> 6) + (col & 3), l = 16 * (m >> 2) + ((col & 63) >> 2);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WK; ++w) sum += red[w][a][l][m & 3];
+    return sum;
+}
+
+// Each wave walks its chunks of a strip segment in rounds of U with two
+// register sets: the loads of round r + 1 are issued before the MFMAs of
+// round r, so a round's memory latency overlaps the previous round's
+// arithmetic (chunks past the segment read as zero and touch no memory).
+//
+// Partial sums are written and read as device-coherent (agent-scope)
+// accesses, which bypass the per-XCD caches that are not coherent with each
+// other; every wave waits for its stores to complete before the workgroup
+// counts its arrival, so the workgroup that counts last finds every partial
+// sum in memory.  (A release fence would also write back each XCD's whole L2,
+// once per wave: measured to cost more than the split saves.)
+template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0>
+__global__ void __launch_bounds__(64 * WK) rows_kernel(Problem p, RowsGrid grid) {
+    static_assert(IN == 0 || (TB && !TA), "16-bit inputs: B transposed (word form)");
+    using S = RowsShape<Q, WK, U>;
+    __shared__ floatx4 red[WK][S::ACC][64];
+    __shared__ int last;
+    select_batch(p);
+    // the wave index is uniform over the wave: in a scalar register, so the
+    // buffer resources built from it are too
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int strip = blockIdx.x % grid.strips, slice = blockIdx.x / grid.strips;
+    const int n0 = strip * S::COLS, ncols = min(S::COLS, p.N - n0);
+    const int kb = slice * grid.kslice, ke = min(p.K, kb + grid.kslice);
+    const int c1 = (ke - kb + 15) / 16;   // chunks of the slice
+
+    floatx4 acc[S::ACC];
+#pragma unroll
+    for (int a = 0; a < S::ACC; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // wave w takes the groups of U consecutive chunks w, w + WK, ...
+    const int groups = (c1 + U - 1) / U;
+    RowsRound<Q, U> r0, r1;
+    rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * wave, i, g, r0);
+    for (int j = wave; j < groups; j += 2 * WK) {
+        rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * (j + WK), i, g, r1);
+        pipeline_fence();
+        rows_mfma<Q, U, TB, IN>(r0, acc);
+        if (j + WK >= groups) break;
+        rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * (j + 2 * WK), i, g, r0);
+        pipeline_fence();
+        rows_mfma<Q, U, TB, IN>(r1, acc);
+    }
+#pragma unroll
+    for (int a = 0; a < S::ACC; ++a) red[wave][a][lane] = acc[a];
+    __syncthreads();
+    const int cells = p.M * S::COLS;
+    if (grid.slices == 1) {
+        for (int f = tid; f < cells; f += S::NT) {
+            const int m = f / S::COLS, col = f % S::COLS;
+            if (col < ncols)
+                store_cell(p, p.C + (long long)m * p.ldc + n0 + col, n0 + col,
+                           wave_sum<Q, WK>(red, m, col));
+        }
         return;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int c = 0; c < VW; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.a[u][s], r.b[u][s][c], acc[c], 0, 0,
-                                                              0);
-}
-
-// The strip's B columns are streamed once.  Each wave walks its chunks in
-// rounds of U with two register sets: the loads of round r + 1 are issued
-// before the MFMAs of round r, so a round's memory latency overlaps the
-// previous round's arithmetic (loads past K read as zero, so the extra round
-// at the end touches no memory).
-//
-// SPLIT: workgroup (strip, 0, z) runs its strip over rows [z*kslice,
-// (z+1)*kslice) of K only, as a product of its own (A and B advanced to the
-// slice, K its length), and stores to C + z*stride_c (the split launcher
-// points C at a workspace of partial results).
-template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0, bool SPLIT = false>
-__global__ void __launch_bounds__(64 * W, 1) rows_kernel(Problem p, int strips, int kslice) {
-    static_assert(IN == 0 || TB, "16-bit inputs: B transposed (word form)");
-    using S = RowsShape<VW, W>;
-    __shared__ __attribute__((aligned(16))) float red[S::RED];
-    select_batch(p);
-    if constexpr (SPLIT) {
-        const long long k0 = (long long)blockIdx.z * kslice;
-        p.A += p.trans_a ? k0 * p.lda : k0;
-        p.B += p.trans_b ? k0 : k0 * p.ldb;
-        p.K = (int)((long long)kslice < p.K - k0 ? (long long)kslice : p.K - k0);
-        p.C += (long long)blockIdx.z * p.stride_c;
+    float *part = grid.part + (long long)slice * p.M * p.N;
+    for (int f = tid; f < cells; f += S::NT) {
+        const int m = f / S::COLS, col = f % S::COLS;
+        if (col < ncols)
+            __hip_atomic_store(part + (long long)m * p.N + n0 + col, wave_sum<Q, WK>(red, m, col),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int i = lane & 15, g = lane >> 4;
-    // neighbouring strips share cache lines of B: keep them on one XCD's L2
-    const int n0 = xcd_remap(blockIdx.x, strips) * S::STRIP;
-    const int gn = n0 + VW * i;
-    const bool row_ok = i < p.M;
-    // row i of op(A): contiguous, or column i of A stored K x M
-    const long long astep = p.trans_a ? p.lda : 1;
-    const float *arow = p.A + (row_ok ? (p.trans_a ? (long long)i : (long long)i * p.lda) : 0);
-
-    floatx4 acc[VW];
-#pragma unroll
-    for (int c = 0; c < VW; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    const int chunks = (p.K + 15) / 16;
-    RowsRound<VW, U> r0, r1;
-    rows_load<VW, W, U, VA, VB, TB>(p, wave, g, gn, row_ok, arow, astep, r0);
-    for (int j = wave; j < chunks; j += 2 * U * W) {
-        rows_load<VW, W, U, VA, VB, TB>(p, j + U * W, g, gn, row_ok, arow, astep, r1);
-        pipeline_fence();
-        rows_mfma<VW, U, IN>(r0, acc);
-        if (j + U * W >= chunks) break;
-        rows_load<VW, W, U, VA, VB, TB>(p, j + 2 * U * W, g, gn, row_ok, arow, astep, r0);
-        pipeline_fence();
-        rows_mfma<VW, U, IN>(r1, acc);
-    }
-
-    // fixed-order reduction over the W waves
-#pragma unroll
-    for (int c = 0; c < VW; ++c)
-        *reinterpret_cast<floatx4 *>(red + ((wave * VW + c) * 64 + lane) * 4) = acc[c];
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial sums have completed
     __syncthreads();
-    const bool read_c = (p.beta != 0.f);
-    const bool epi = p.has_epilogue();   // bias / activation applied here
-    for (int e = tid; e < VW * 64 * 4; e += S::NT) {
+    if (tid == 0)
+        last = __hip_atomic_fetch_add(grid.count + strip, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(grid.slices - 1);
+    __syncthreads();
+    if (!last) return;
+    const long long step = (long long)p.M * p.N;
+    for (int f = tid; f < cells; f += S::NT) {
+        const int m = f / S::COLS, col = f % S::COLS;
+        if (col >= ncols) continue;
+        const float *src = grid.part + (long long)m * p.N + n0 + col;
+        // slice order kept; sixteen slices' loads in flight at a time
         float sum = 0.f;
+        for (int z = 0; z < grid.slices; z += 16) {
+            float v[16];
 #pragma unroll
-        for (int w = 0; w < W; ++w) sum += red[w * VW * 64 * 4 + e];
-        const int r = e & 3, l = (e >> 2) & 63, c = e >> 8;
-        const int row = 4 * (l >> 4) + r;
-        const int col = n0 + VW * (l & 15) + c;
-        if (row < p.M && col < p.N) {
-            float *dst = p.C + (long long)row * p.ldc + col;
-            float out = p.alpha * sum;
-            if (read_c) out = fmaf(p.beta, *dst, out);
-            if (epi) out = activate(p.act, p.bias ? out + p.bias[col] : out);
-            *dst = out;
+            for (int x = 0; x < 16; ++x)
+                v[x] = z + x < grid.slices
+                           ? __hip_atomic_load(src + (z + x) * step, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+#pragma unroll
+            for (int x = 0; x < 16; ++x)
+                if (z + x < grid.slices) sum += v[x];
         }
+        store_cell(p, p.C + (long long)m * p.ldc + n0 + col, n0 + col, sum);
     }
+    if (tid == 0)   // ready for the next launch on the stream
+        __hip_atomic_store(grid.count + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Split-K of a few-rows product: the sum over the slices in slice order, then
-// C = act(alpha * sum + beta * C + bias) as the unsplit kernel's epilogue.
-__global__ void __launch_bounds__(256) rows_split_reduce(Problem p, const float *ws, int splits) {
-    const long long mn = (long long)p.M * p.N;
-    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < mn;
-         e += (long long)gridDim.x * blockDim.x) {
-        // slice order kept; loads eight slices ahead of the adds
-        float sum = 0.f;
-        int z = 0;
-        for (; z + 8 <= splits; z += 8) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = ws[(z + u) * mn + e];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) sum += v[u];
-        }
-        for (; z < splits; ++z) sum += ws[z * mn + e];
-        const int row = (int)(e / p.N), col = (int)(e % p.N);
-        float *dst = p.C + (long long)row * p.ldc + col;
-        float out = p.alpha * sum;
-        if (p.beta != 0.f) out = fmaf(p.beta, *dst, out);
-        if (p.has_epilogue()) out = activate(p.act, p.bias ? out + p.bias[col] : out);
-        *dst = out;
-    }
-}
+// Counters of the workspace: one per strip, so a split launch has at most
+// this many strips.
+constexpr int kMaxSplitStrips = kWorkspaceCounters;
 
-// Slices for a split-K launch of a few-rows product, or 1: single products
-// whose strips fill under 192 CUs, cut into about 512 workgroups with at
-// least two rounds of U chunks per wave in every slice.  kslice: rows of K
-// per slice (a multiple of 16, so 16-byte alignment carries over).
-template <int VW, int W, int U>
-int rows_splits(const Problem &p, int &kslice) {
-    kslice = p.K;
-    if (p.batch != 1 || p.K == 0) return 1;
-    const long long strips = (p.N + 16 * VW - 1) / (16 * VW);
-    if (strips >= 192) return 1;
+// K slices of a few-rows launch: `want` when given (at most 64, and one
+// 16-row chunk per wave and slice), else the library's choice for single
+// products whose strips are fewer than the CUs: as many slices as keep the
+// grid within about one workgroup per CU (measured best over M = 1..16,
+// N = 256..14336, K = 3001..16384: HBM is saturated only while every CU
+// streams, and a second round of workgroups costs more than it balances),
+// with every wave still running two rounds of loads or more and the partial
+// sums (written and read once) under ~3 % of B's bytes.
+template <int Q, int WK, int U>
+int rows_slices(const Problem &p, int want) {
+    using S = RowsShape<Q, WK, U>;
+    const long long strips = (p.N + S::COLS - 1) / S::COLS;
+    if (p.batch != 1 || p.K == 0 || strips > kMaxSplitStrips) return 1;
     const long long chunks = (p.K + 15) / 16;
-    long long s = (512 + strips - 1) / strips;
-    const long long most = chunks / (2LL * W * U);
-    if (s > most) s = most;
-    if (s < 2) return 1;
-    const long long per = (chunks + s - 1) / s;
-    kslice = (int)(per * 16);
-    return (int)((p.K + kslice - 1) / kslice);
+    long long s;
+    if (want > 0) {
+        s = want < 64 ? want : 64;
+        if (s > (chunks + WK - 1) / WK) s = (chunks + WK - 1) / WK;
+    } else {
+        s = 256 / strips;
+        const long long rounds = chunks / (2LL * WK * U);
+        if (s > rounds) s = rounds;
+        const long long by_bytes = (long long)(0.015 * p.K / (p.M > 0 ? p.M : 1));
+        if (s > by_bytes) s = by_bytes;
+        if (s > 64) s = 64;
+    }
+    return s < 2 ? 1 : (int)s;
 }
 
-template <int VW, int W, int U, bool VA, bool VB, bool TB, int IN = 0, bool SPLIT = false>
-hipError_t launch_rows_as(const Problem &p, hipStream_t stream) {
-    const int strips = (p.N + 16 * VW - 1) / (16 * VW);
-    int kslice = p.K;
-    const int splits = SPLIT ? rows_splits<VW, W, U>(p, kslice) : 1;
-    if (splits == 1) {
-        hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB, IN>), dim3(strips, p.batch),
-                           dim3(64 * W), 0, stream, p, strips, kslice);
+// Rows of K per slice (a multiple of 16) and the resulting slice count.
+template <int Q, int WK, int U>
+int rows_kslice(const Problem &p, int want, int *slices) {
+    const int s = rows_slices<Q, WK, U>(p, want);
+    const int kslice = 16 * (int)(((p.K + 15) / 16 + s - 1) / s);
+    *slices = s == 1 ? 1 : (p.K + kslice - 1) / kslice;
+    return *slices == 1 ? 16 * ((p.K + 15) / 16) : kslice;
+}
+
+template <int Q, int WK, int U>
+int rows_slice_count(const Problem &p, int group_m) {
+    int slices = 1;
+    rows_kslice<Q, WK, U>(p, group_m, &slices);
+    return slices;
+}
+
+template <int Q, int WK, int U>
+size_t rows_workspace(const Problem &p, int group_m) {
+    int slices = 1;
+    rows_kslice<Q, WK, U>(p, group_m, &slices);
+    return slices == 1 ? 0 : (size_t)slices * p.M * p.N * 4;
+}
+
+template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0>
+hipError_t launch_rows_as(const Problem &p, int want_slices, hipStream_t stream) {
+    using S = RowsShape<Q, WK, U>;
+    RowsGrid grid{(p.N + S::COLS - 1) / S::COLS, 1, 0, nullptr, nullptr};
+    grid.kslice = rows_kslice<Q, WK, U>(p, want_slices, &grid.slices);
+    if (grid.slices == 1) {
+        hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>), dim3(grid.strips, p.batch),
+                           dim3(S::NT), 0, stream, p, grid);
         return hipGetLastError();
     }
-    // partial results of the slices: splits x M x N floats
-    const long long mn = (long long)p.M * p.N;
     Workspace w;
-    hipError_t e = workspace_acquire((size_t)splits * mn * 4, stream, w);
+    hipError_t e = workspace_acquire(rows_workspace<Q, WK, U>(p, want_slices), stream, p, w);
     if (e != hipSuccess) return e;
-    float *ws = static_cast<float *>(w.ptr);
-    Problem q = p;
-    q.C = ws;
-    q.ldc = p.N;
-    q.stride_c = mn;
-    q.alpha = 1.f;
-    q.beta = 0.f;
-    q.bias = nullptr;
-    q.act = SGEMM_ACT_NONE;
-    hipLaunchKernelGGL((rows_kernel<VW, W, U, VA, VB, TB, IN, true>), dim3(strips, 1, splits),
-                       dim3(64 * W), 0, stream, q, strips, kslice);
+    grid.part = static_cast<float *>(w.ptr);
+    grid.count = w.counters;
+    hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>),
+                       dim3(grid.strips * grid.slices), dim3(S::NT), 0, stream, p, grid);
     e = hipGetLastError();
-    if (e == hipSuccess) {
-        const long long blocks = (mn + 255) / 256 < 1024 ? (mn + 255) / 256 : 1024;
-        hipLaunchKernelGGL(rows_split_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, p,
-                           static_cast<const float *>(ws), splits);
-        e = hipGetLastError();
-    }
     const hipError_t f = workspace_release(w, stream);
     return e != hipSuccess ? e : f;
 }
 
-// 16-bit inputs, few rows: pw is the word-form problem (A untransposed, B
-// transposed, K / lda / ldb in 32-bit words); 16-column strips (measured
-// faster than 64-column ones for 16-bit inputs at 1 x 14336 x 4096 and
-// 16 x 14336 x 4096).
-template <int IN>
-hipError_t launch_rows16_as(const Problem &pw, hipStream_t stream) {
-    const bool va = rows_aligned(pw.A, pw.lda, pw.stride_a, pw.batch, 4);
-    const bool vb = rows_aligned(pw.B, pw.ldb, pw.stride_b, pw.batch, 4);
-    if (va && vb) return launch_rows_as<1, 16, 4, true, true, true, IN>(pw, stream);
-    return launch_rows_as<1, 16, 4, false, false, true, IN>(pw, stream);
+template <int Q, int WK, int U, bool TA, bool TB>
+hipError_t launch_rows_ab(const Problem &p, int groups, bool va, bool vb, hipStream_t stream) {
+    if (va && vb) return launch_rows_as<Q, WK, U, true, true, TA, TB>(p, groups, stream);
+    if (va) return launch_rows_as<Q, WK, U, true, false, TA, TB>(p, groups, stream);
+    if (vb) return launch_rows_as<Q, WK, U, false, true, TA, TB>(p, groups, stream);
+    return launch_rows_as<Q, WK, U, false, false, TA, TB>(p, groups, stream);
 }
 
-template <int VW, int W, int U, bool TB, bool SPLIT>
-hipError_t launch_rows_tb(const Problem &p, bool va, bool vb, hipStream_t stream) {
-    if (va && vb) return launch_rows_as<VW, W, U, true, true, TB, 0, SPLIT>(p, stream);
-    if (va) return launch_rows_as<VW, W, U, true, false, TB, 0, SPLIT>(p, stream);
-    if (vb) return launch_rows_as<VW, W, U, false, true, TB, 0, SPLIT>(p, stream);
-    return launch_rows_as<VW, W, U, false, false, TB, 0, SPLIT>(p, stream);
-}
-
-// VEC: wide loads wherever an operand's rows allow them (decided per operand);
-// otherwise 4-byte loads throughout.
-template <int VW, int W, int U, bool VEC, bool SPLIT = false>
-hipError_t launch_rows(const Problem &p, int, hipStream_t stream) {
-    const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
-    if (p.trans_b) {
-        const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);
-        return launch_rows_tb<VW, W, U, true, SPLIT>(p, va, vb, stream);
+// VEC: 16-byte loads wherever an operand allows them (decided per operand:
+// rows 16-byte aligned and the stored row length a multiple of 4); otherwise
+// 4-byte loads throughout.  group_m, when positive, asks for that many K
+// slices.
+template <int Q, int WK, int U, bool VEC>
+hipError_t launch_rows(const Problem &p, int group_m, hipStream_t stream) {
+    const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
+                    p.K % 4 == 0;
+    const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) &&
+                    (p.trans_b ? p.K : p.N) % 4 == 0;
+    if (p.trans_a) {
+        return p.trans_b ? launch_rows_ab<Q, WK, U, true, true>(p, group_m, false, vb, stream)
+                         : launch_rows_ab<Q, WK, U, true, false>(p, group_m, false, vb, stream);
     }
-    const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, VW);
-    return launch_rows_tb<VW, W, U, false, SPLIT>(p, va, vb, stream);
+    return p.trans_b ? launch_rows_ab<Q, WK, U, false, true>(p, group_m, va, vb, stream)
+                     : launch_rows_ab<Q, WK, U, false, false>(p, group_m, va, vb, stream);
 }
 
 // ---------------------------------------------------------------- kind 1 ----
-// One round of a lane's loads: U 4-float chunks of its row of A (k = 4*lane +
-// 256u + 0..3) and the matching 4 x NB values of B.
-template <int NB, int U>
+// One round of a wave's loads: U chunks of 256 k (lane l: k = 256 * chunk +
+// 4l + 0..3): a[u][rr] = A(row rr, k .. k+3), b[u][j] = B(k .. k+3, column j).
+template <int NB, int R, int U>
 struct ColsRound {
-    floatx4 a[U];
-    float b[U][4][NB];
+    floatx4 a[U][R];
+    floatx4 b[U][NB];
 };
 
-// BM (B's mode): 0 any K x N layout, read four bytes at a time; 1 a tight
-// K x NB block (ldb == N == NB), so the 4*NB values of four consecutive k are
-// contiguous and are read as NB 16-byte loads; 2 B stored transposed (N x K),
-// each of its N rows read 16 bytes at a time like A's row; 3 the same, four
-// bytes at a time.  VEC: 16-byte loads of A.
-template <int NB, int U, bool VEC, int BM>
-__device__ __forceinline__ void cols_load(const Problem &p, const float *arow, int kbase,
-                                          ColsRound<NB, U> &r) {
+// BM (B's layout): 0 any K x N layout, read four bytes at a time; 1 a tight
+// K x NB block (ldb == N == NB, 16-byte aligned, K a multiple of 4), so the
+// 4*NB values of four consecutive k are contiguous and are read as NB 16-byte
+// loads; 2 B stored transposed (N x K), each of its N rows read 16 bytes at a
+// time like A's rows; 3 the same, four bytes at a time.  VA: 16-byte loads of
+// A.  Each 256-k chunk gets resources of its own starting at its first k, so
+// the per-lane offsets stay below 2^31: under R * lda floats for A, 256 * ldb
+// for B, 16 * ldb for B^T.
+template <int NB, int R, int U, bool VA, int BM>
+__device__ __forceinline__ void cols_load(const Problem &p, int row0, int kc0, int lane,
+                                          ColsRound<NB, R, U> &r) {
+    const int ldb = (int)p.ldb, lda = (int)p.lda;
+    const int rows = min(R, p.M - row0);
+    const int kk = 4 * lane;   // this lane's first k of a chunk
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int k = kbase + 256 * u;
-        floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        if (VEC && k + 3 < p.K) {
-            a = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(arow + k));
-        } else {
+        const int kr = 256 * (kc0 + u);   // the chunk's first k (uniform)
+        const int krem = p.K - kr;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            p.A + (long long)row0 * p.lda + kr, 4 * ((long long)(rows - 1) * p.lda + krem));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (k + e < p.K) a[e] = arow[k + e];
+        for (int rr = 0; rr < R; ++rr) {
+            const bool ok = rr < rows;
+            if constexpr (VA) {
+                r.a[u][rr] = ld4<true>(ra, (ok && kk < krem) ? (rr * lda + kk) * 4 : kOff);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    r.a[u][rr][e] = ld1(ra, (ok && kk + e < krem) ? (rr * lda + kk + e) * 4 : kOff);
+            }
         }
-        r.a[u] = a;
         if constexpr (BM >= 2) {
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(p.B + kr, 4 * ((long long)(p.N - 1) * p.ldb + krem));
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                if (j < p.N) {
-                    const float *src = p.B + (long long)j * p.ldb + k;
-                    if (BM == 2 && k + 3 < p.K) {
-                        t = *reinterpret_cast<const floatx4 *>(src);
-                    } else {
+            for (int jj = 0; jj < NB; ++jj) {
+                const bool ok = jj < p.N;
+                if constexpr (BM == 2) {
+                    r.b[u][jj] = ld4<false>(rb, (ok && kk < krem) ? (jj * ldb + kk) * 4 : kOff);
+                } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (k + e < p.K) t[e] = src[e];
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        r.b[u][jj][e] = ld1(rb, (ok && kk + e < krem) ? (jj * ldb + kk + e) * 4 : kOff);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r.b[u][e][j] = t[e];
-            }
-        } else if (BM == 1 && k + 3 < p.K) {
-            const floatx4 *src = reinterpret_cast<const floatx4 *>(p.B + (long long)k * NB);
-#pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const floatx4 v = src[q];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) r.b[u][(4 * q + x) / NB][(4 * q + x) % NB] = v[x];
             }
         } else {
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+                p.B + (long long)kr * p.ldb, 4 * ((long long)(krem - 1) * p.ldb + p.N));
+            if constexpr (BM == 1) {
+                // B(kk + e, j) at float kk * NB + e * NB + j of the chunk
+                floatx4 v[NB];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float *brow = p.B + (long long)(k + e) * p.ldb;
+                for (int q = 0; q < NB; ++q)
+                    v[q] = ld4<false>(rb, kk < krem ? (kk * NB + 4 * q) * 4 : kOff);
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    r.b[u][e][j] = (k + e < p.K && j < p.N) ? brow[j] : 0.f;
+                for (int x = 0; x < 4 * NB; ++x) r.b[u][x % NB][x / NB] = v[x / 4][x % 4];
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < NB; ++jj) {
+                    const bool ok = jj < p.N;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        r.b[u][jj][e] =
+                            ld1(rb, (ok && kk + e < krem) ? ((kk + e) * ldb + jj) * 4 : kOff);
+                }
             }
         }
     }
 }
 
-template <int NB, int U>
-__device__ __forceinline__ void cols_fma(const ColsRound<NB, U> &r, float (&acc)[NB]) {
+template <int NB, int R, int U>
+__device__ __forceinline__ void cols_fma(const ColsRound<NB, R, U> &r, float (&acc)[R][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[j] = fmaf(r.a[u][e], r.b[u][e][j], acc[j]);
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int jj = 0; jj < NB; ++jj)
+                    acc[rr][jj] = fmaf(r.a[u][rr][e], r.b[u][jj][e], acc[rr][jj]);
 }
 
-// One wave per row of A; rounds of U chunks double-buffered as in the
-// few-rows kernel (loads past K read as zero and touch no memory).
-template <int NB, int W, int U, bool VEC, int BM>
+// R rows of A per wave; rounds of U chunks double-buffered as in the
+// few-rows kernel (chunks past K read as zero and touch no memory).
+template <int NB, int R, int W, int U, bool VA, int BM>
 __global__ void __launch_bounds__(64 * W) cols_kernel(Problem p) {
     select_batch(p);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * W + wave;
-    if (row >= p.M) return;                       // whole wave leaves together; no barrier below
-    const float *arow = p.A + (long long)row * p.lda;
-    float acc[NB];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * W + wave) * R;
+    if (row0 >= p.M) return;                      // whole wave leaves together; no barrier below
+    float acc[R][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = 0.f;
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) acc[rr][jj] = 0.f;
 
-    ColsRound<NB, U> r0, r1;
-    cols_load<NB, U, VEC, BM>(p, arow, 4 * lane, r0);
-    // kw: the wave's base column of A for the round in r0 (uniform over lanes)
-    for (int kw = 0; kw < p.K; kw += 2 * 256 * U) {
-        cols_load<NB, U, VEC, BM>(p, arow, 4 * lane + kw + 256 * U, r1);
+    const int chunks = (p.K + 255) / 256;
+    ColsRound<NB, R, U> r0, r1;
+    cols_load<NB, R, U, VA, BM>(p, row0, 0, lane, r0);
+    for (int kc = 0; kc < chunks; kc += 2 * U) {
+        cols_load<NB, R, U, VA, BM>(p, row0, kc + U, lane, r1);
         pipeline_fence();
-        cols_fma<NB, U>(r0, acc);
-        if (kw + 256 * U >= p.K) break;
-        cols_load<NB, U, VEC, BM>(p, arow, 4 * lane + kw + 2 * 256 * U, r0);
+        cols_fma<NB, R, U>(r0, acc);
+        if (kc + U >= chunks) break;
+        cols_load<NB, R, U, VA, BM>(p, row0, kc + 2 * U, lane, r0);
         pipeline_fence();
-        cols_fma<NB, U>(r1, acc);
+        cols_fma<NB, R, U>(r1, acc);
     }
     // butterfly reduction over the 64 lanes (fixed order)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        float v = acc[j];
+    for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        acc[j] = v;
-    }
-    const bool read_c = (p.beta != 0.f);
-    const bool epi = p.has_epilogue();   // bias / activation applied here
-    float *crow = p.C + (long long)row * p.ldc;
+        for (int jj = 0; jj < NB; ++jj) {
+            float v = acc[rr][jj];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        if (lane == j && j < p.N) {
-            float out = p.alpha * acc[j];
-            if (read_c) out = fmaf(p.beta, crow[j], out);
-            if (epi) out = activate(p.act, p.bias ? out + p.bias[j] : out);
-            crow[j] = out;
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            acc[rr][jj] = v;
         }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        if (row0 + rr >= p.M) break;
+        float *crow = p.C + (long long)(row0 + rr) * p.ldc;
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj)
+            if (lane == jj && jj < p.N) store_cell(p, crow + jj, jj, acc[rr][jj]);
     }
 }
 
-template <int NB, int W, int U, bool VA, int BM>
+template <int NB, int R, int W, int U, bool VA, int BM>
 hipError_t launch_cols_as(const Problem &p, hipStream_t stream) {
-    const int blocks = (p.M + W - 1) / W;
-    hipLaunchKernelGGL((cols_kernel<NB, W, U, VA, BM>), dim3(blocks, p.batch), dim3(64 * W), 0,
+    const int blocks = (p.M + W * R - 1) / (W * R);
+    hipLaunchKernelGGL((cols_kernel<NB, R, W, U, VA, BM>), dim3(blocks, p.batch), dim3(64 * W), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-template <int NB, int W, int U, int BM>
+template <int NB, int R, int W, int U, int BM>
 hipError_t launch_cols_bm(const Problem &p, bool va, hipStream_t stream) {
-    return va ? launch_cols_as<NB, W, U, true, BM>(p, stream)
-              : launch_cols_as<NB, W, U, false, BM>(p, stream);
+    return va ? launch_cols_as<NB, R, W, U, true, BM>(p, stream)
+              : launch_cols_as<NB, R, W, U, false, BM>(p, stream);
 }
 
 // VEC: 16-byte loads of A where its rows allow them, and of B where it is one
 // tight K x NB block or stored transposed with aligned rows (decided per
-// operand); otherwise 4-byte loads.  A stored transposed is not served.
-template <int NB, int W, int U, bool VEC>
+// operand; K a multiple of 4); otherwise 4-byte loads.  A stored transposed is
+// not served.
+template <int NB, int R, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
     if (p.trans_a) return hipErrorInvalidValue;
-    const bool va = VEC && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
-    const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);
+    const bool k4 = p.K % 4 == 0;
+    const bool va = VEC && k4 && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
+    const bool vb = VEC && k4 && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);
     if (p.trans_b)
-        return vb ? launch_cols_bm<NB, W, U, 2>(p, va, stream)
-                  : launch_cols_bm<NB, W, U, 3>(p, va, stream);
-    if (vb && p.N == NB && p.ldb == NB) return launch_cols_bm<NB, W, U, 1>(p, va, stream);
-    return launch_cols_bm<NB, W, U, 0>(p, va, stream);
+        return vb ? launch_cols_bm<NB, R, W, U, 2>(p, va, stream)
+                  : launch_cols_bm<NB, R, W, U, 3>(p, va, stream);
+    // a tight K x NB block: 16-byte aligned, and so is every batch entry
+    if (VEC && k4 && p.N == NB && p.ldb == NB && rows_aligned(p.B, 4, p.stride_b, p.batch, 4))
+        return launch_cols_bm<NB, R, W, U, 1>(p, va, stream);
+    return launch_cols_bm<NB, R, W, U, 0>(p, va, stream);
 }
 
-template <int VW, int W, int U, bool SPLIT = false>
+template <int Q, int WK, int U>
 constexpr TileEntry rows_entry() {
-    using S = RowsShape<VW, W>;
+    using S = RowsShape<Q, WK, U>;
     // the launchers apply a problem's bias / activation themselves, so the
     // 16-byte launcher is also the fused one
-    return TileEntry{{16, 16 * VW, 16 * W, 16, 16 * VW, 0, 0, S::NT, S::LDS_BYTES, 0, 0},
-                     &launch_rows<VW, W, U, true, SPLIT>, &launch_rows<VW, W, U, false, SPLIT>, 0,
-                     &launch_rows<VW, W, U, true, SPLIT>};
+    return TileEntry{{16, S::COLS, 16 * U, 16, S::COLS, 0, 0, S::NT, S::LDS_BYTES, 0, 0},
+                     &launch_rows<Q, WK, U, true>, &launch_rows<Q, WK, U, false>, 0,
+                     &launch_rows<Q, WK, U, true>};
 }
 
-template <int NB, int W, int U>
+template <int NB, int R, int W, int U>
 constexpr TileEntry cols_entry() {
-    return TileEntry{{W, NB, 256 * U, 1, NB, 1, 0, 64 * W, 0, 0, 0},
-                     &launch_cols<NB, W, U, true>, &launch_cols<NB, W, U, false>, 0,
-                     &launch_cols<NB, W, U, true>};
+    return TileEntry{{W * R, NB, 256 * U, R, NB, 1, 0, 64 * W, 0, 0, 0},
+                     &launch_cols<NB, R, W, U, true>, &launch_cols<NB, R, W, U, false>, 0,
+                     &launch_cols<NB, R, W, U, true>};
 }
 
+// The few-rows tiles, in table order, with their workspace size functions.
+#define SG_ROWS_TILES(X) X(2, 8, 1) X(2, 4, 2) X(1, 4, 2) X(1, 16, 1) X(1, 4, 4)
+
+// 16-bit inputs, few rows: pw is the word-form problem (A untransposed, B
+// transposed, K / lda / ldb in 32-bit words).
+template <int IN>
+hipError_t launch_rows16_as(const Problem &pw, hipStream_t stream) {
+    const bool va = rows_aligned(pw.A, pw.lda, pw.stride_a, pw.batch, 4) && pw.K % 4 == 0;
+    const bool vb = rows_aligned(pw.B, pw.ldb, pw.stride_b, pw.batch, 4) && pw.K % 4 == 0;
+    if (va && vb) return launch_rows_as<1, 8, 4, true, true, false, true, IN>(pw, 0, stream);
+    return launch_rows_as<1, 8, 4, false, false, false, true, IN>(pw, 0, stream);
+}
 
 }  // namespace
 
@@ -529,21 +649,40 @@ hipError_t launch_skinny16(int dtype, const Problem &pw, hipStream_t stream) {
 }
 
 const TileEntry *skinny_tiles(int *count) {
+#define SG_ROWS_ENTRY(Q, WK, U) rows_entry<Q, WK, U>(),
     static const TileEntry tiles[] = {
-        rows_entry<1, 16, 4>(),   // 0: 16-column strips
-        rows_entry<2, 16, 2>(),   // 1: 32-column strips
-        rows_entry<4, 16, 1>(),   // 2: 64-column strips
-        rows_entry<2, 8, 4>(),    // 3: 32-column strips, 8 waves
-        cols_entry<1, 4, 4>(),    // 4
-        cols_entry<2, 4, 4>(),    // 5
-        cols_entry<4, 4, 4>(),    // 6
-        cols_entry<8, 4, 2>(),    // 7
-        cols_entry<16, 4, 2>(),   // 8
-        rows_entry<4, 4, 4, true>(),    // 9: 64-column strips, split-K when strips are few
-        rows_entry<4, 8, 2, true>(),    // 10: the same, 8 waves
+        SG_ROWS_TILES(SG_ROWS_ENTRY)   // 0-4: few rows (128-, 128-, 64-, 64-, 64-column strips)
+        cols_entry<1, 2, 4, 4>(),      // 5-9: few columns
+        cols_entry<2, 2, 4, 4>(),
+        cols_entry<4, 2, 4, 2>(),
+        cols_entry<8, 2, 4, 2>(),
+        cols_entry<16, 2, 4, 1>(),
     };
+#undef SG_ROWS_ENTRY
     *count = sizeof(tiles) / sizeof(tiles[0]);
     return tiles;
+}
+
+// K slices of a few-rows launch of `tile` with `group_m` asked-for slices
+// (0: the library's choice); 1 for unsplit launches and kind 1.
+int skinny_slices(int tile, const Problem &p, int group_m) {
+    using SlFn = int (*)(const Problem &, int);
+#define SG_ROWS_SL(Q, WK, U) &rows_slice_count<Q, WK, U>,
+    static const SlFn fns[] = {SG_ROWS_TILES(SG_ROWS_SL)};
+#undef SG_ROWS_SL
+    constexpr int n = sizeof(fns) / sizeof(fns[0]);
+    return (tile >= 0 && tile < n) ? fns[tile](p, group_m) : 1;
+}
+
+// Workspace bytes of a few-rows launch of `tile` with `group_m` asked-for
+// K slices (0: the library's choice); 0 for unsplit launches and kind 1.
+size_t skinny_workspace_bytes(int tile, const Problem &p, int group_m) {
+    using WsFn = size_t (*)(const Problem &, int);
+#define SG_ROWS_WS(Q, WK, U) &rows_workspace<Q, WK, U>,
+    static const WsFn fns[] = {SG_ROWS_TILES(SG_ROWS_WS)};
+#undef SG_ROWS_WS
+    constexpr int n = sizeof(fns) / sizeof(fns[0]);
+    return (tile >= 0 && tile < n) ? fns[tile](p, group_m) : 0;
 }
 
 // The kind is recorded in the tile descriptor's tm field.
@@ -554,30 +693,33 @@ int skinny_kind(int tile) {
 }
 
 // Kind 0 serves every transposition; kind 1 does not read A stored transposed.
+// Both need the per-lane offsets of a chunk's resource below 2^31 bytes:
+// kind 0 under 64 rows of B^T or 16 rows of B or A, kind 1 under its rows of
+// A and 256 rows of B (16 of B^T).
 bool skinny_fits(int tile, const Problem &p) {
     int count = 0;
     const TileEntry *tiles = skinny_tiles(&count);
     if (tile < 0 || tile >= count) return false;
-    return skinny_kind(tile) == 0 ? p.M <= 16 : (p.N <= tiles[tile].desc.bn && !p.trans_a);
+    constexpr long long lim = 1LL << 29;   // floats
+    if (skinny_kind(tile) == 0)
+        return p.M <= 16 && 16 * p.lda < lim && (p.trans_b ? 64 : 16) * p.ldb < lim;
+    return p.N <= tiles[tile].desc.bn && !p.trans_a && tiles[tile].desc.wm * p.lda < lim &&
+           (p.trans_b ? 16 : 256) * p.ldb < lim;
 }
 
-// Few-rows tile choice, from graph-replay and eager timings over M = 1..16,
-// N = 256..14336, K = 1024..16384 with operands larger than the Infinity
-// Cache: 64-column strips once they give most CUs a workgroup; 16-column
-// strips for B stored transposed (4 lanes read 64 contiguous bytes of a
-// column's K run), 32-column strips otherwise; split-K (tile 10) where those
-// leave most CUs idle for a long K.
-int skinny_pick(const Problem &p) {
-    const int M = p.M, N = p.N, K = p.K;
+namespace {
+
+// Few-rows tile choice (measured with operands rotated past the Infinity
+// Cache, graph-replayed): 128-column strips of 8 waves where many rows of
+// A would otherwise be re-read per 64 columns of B (M > 4, wide N); 64-column
+// strips otherwise, 16 waves for narrow products (few strips, split deeply)
+// and 4 waves (several workgroups per CU) for the rest.  Few columns: the
+// narrowest tile that holds N.
+int choose_skinny(const Problem &p) {
+    const int M = p.M, N = p.N;
     if (M <= 16) {
-        if ((N + 63) / 64 >= 160) return 2;
-        const bool split_ok = p.batch == 1;
-        if (p.trans_b) {
-            if (split_ok && K >= 8192 && N <= 2048) return 10;
-            return N >= 8192 ? 1 : 0;
-        }
-        if (split_ok && ((K >= 4096 && N <= 2048) || (K >= 8192 && N <= 4096))) return 10;
-        return 1;
+        if (!p.trans_b && M > 4 && N >= 8192) return 0;
+        return N <= 2048 ? 3 : 2;
     }
     if (N <= 16 && !p.trans_a) {
         int count = 0;
@@ -586,6 +728,14 @@ int skinny_pick(const Problem &p) {
             if (skinny_kind(t) == 1 && N <= tiles[t].desc.bn) return t;
     }
     return -1;
+}
+
+}  // namespace
+
+// The skinny tile for a shape, or -1 when the family does not serve it.
+int skinny_pick(const Problem &p) {
+    const int t = choose_skinny(p);
+    return skinny_fits(t, p) ? t : -1;
 }
 
 }  // namespace sg

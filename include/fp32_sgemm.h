@@ -23,14 +23,17 @@
  * The library keeps no pointer to them after a call returns.  It allocates
  * device memory in two cases only, both for partial sums: a stream-K launch
  * (SGEMM_FLAG_STREAMK, or chosen by automatic dispatch for a single product
- * whose tile count leaves the last wave of workgroups partly idle; two tile
- * accumulators for each of 256 workgroups: 64 MiB with 256 x 128 tiles,
- * 128 MiB with 256 x 256), and a split-K launch of the few-rows skinny tiles
- * (a K-slice count times M x N floats).  Outside graph capture the workspace
- * is kept per device and stream and reused by later calls on that stream
- * (taken with hipMallocAsync on the stream, grown when a call needs more, the
- * old buffer returned with hipFreeAsync on the same stream; held until
- * sgemm_workspace_release or process exit).  Under graph capture each call
+ * with few tiles of C and a long K, whose last wave of workgroups would be
+ * partly idle; two tile accumulators for each of 256 workgroups: 64 MiB with
+ * 256 x 128 tiles, 128 MiB with 256 x 256), and a few-rows skinny launch split
+ * over K (automatic dispatch splits single products of M <= 16 rows whose
+ * column strips leave most CUs idle, e.g. 1 x 4096 x 4096; a slice count
+ * times M x N floats).  The workspace also holds 16 KiB of arrival counters.
+ * Outside graph capture it is kept per device and stream and reused by later
+ * calls on that stream (taken with hipMallocAsync on the stream, grown when a
+ * call needs more, the old buffer returned with hipFreeAsync on the same
+ * stream; held until sgemm_workspace_release or process exit; the per-thread
+ * default stream gets one per host thread).  Under graph capture each call
  * records its own allocation and free on the capturing stream.  An
  * allocation failure is returned as its hipError_t.  Work is
  * enqueued on `stream` (NULL = the null stream) and the call
@@ -106,7 +109,10 @@ enum sgemm_variant {
  * tile configuration of that family (`tile` indexes the list reported by
  * sgemm_tile_info; -1 = the family's choice for the shape), and flag bits.
  * `group_m` sets the number of tile-rows per block of the tile-ordering
- * swizzle (0 = the library's choice).
+ * swizzle (0 = the library's choice).  For the few-rows tiles of the skinny
+ * family it is instead the number of K slices to split a single product
+ * over (at most 64, and at most one per 16-row k-chunk of each wave; 1 = no
+ * split; 0 = the library's choice; batches are not split).
  */
 typedef struct sgemm_config {
     int variant;
@@ -185,7 +191,9 @@ int sgemm_ex(int M, int N, int K, float alpha,
 /*
  * sgemm_select: the configuration sgemm() would use for this shape and these
  * pointers/leading dimensions, written to *out (variant, tile, flags,
- * group_m).  When sgemm() also hands edge strips to the skinny family (see
+ * group_m; for a few-rows skinny tile, group_m is the number of K slices the
+ * product is split into, 1 for none, so that *out passed to sgemm_ex runs
+ * the same plan).  When sgemm() also hands edge strips to the skinny family (see
  * sgemm_plan), *out describes the main part.  Reads no memory behind A, B or
  * C.  Returns 0; -1, -2 or -3 for a negative M, N or K; -14 when out is NULL.
  */
@@ -352,7 +360,9 @@ int sgemm_version(void);
  * workspaces the library keeps for it (one per stream that has run a
  * stream-K or split-K launch; see "Memory and ownership").  Later calls take
  * new ones as needed.  Returns 0 or a hipError_t.  Not to be called while
- * another thread runs sgemm calls on the same device.
+ * another thread runs sgemm calls on the same device.  Call it before
+ * destroying a stream that has run such launches: a stream created later
+ * may receive the same handle value and would otherwise inherit the buffer.
  */
 int sgemm_workspace_release(void);
 

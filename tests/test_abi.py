@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tables():
-    assert sg.version() == 300
+    assert sg.version() == 400
     for v in (sg.VARIANT_MFMA, sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         n = sg.tile_count(v)
         assert n > 0
@@ -363,3 +363,46 @@ def test_mixed_entry_point_validation():
     # fp32 entry points refuse the 16-bit families
     cfg = sg.SgemmConfig(sg.VARIANT_MFMA16, 0, 0, 0)
     assert sg.sgemm_ex(64, 64, 64, 1.0, good, 64, good, 64, 0.0, good, 64, None, cfg) == -13
+
+
+# The shapes of the named workloads: (M, N, K).  Square sweep 128 .. 8192.
+NAMED_SHAPES = ([(256, 256, 256), (4096, 4096, 4096), (4097, 1000, 3001), (1, 4096, 4096),
+                 (4096, 1, 4096), (777, 777, 33), (8192, 14336, 4096), (8192, 4096, 14336),
+                 (16, 14336, 4096)] + [(n, n, n) for n in (128, 256, 512, 1024, 2048, 4096, 8192)])
+STATIC_SCRATCH_BYTES = 16 << 20   # sgemm_op_ex_noalloc's array, after its counters
+
+
+def plan_partial_bytes(M, N, K, a=0x10000, b=0x20000, c=0x30000, lda=None, ldb=None, ldc=None):
+    """(configuration, partial-sum bytes) of one part of an automatic plan:
+    a stream-K launch keeps two tile accumulators per workgroup, a few-rows
+    skinny launch split into S K-slices keeps S x M x N floats."""
+    cfg, rows, cols = sg.plan(M, N, K, a, lda or K, b, ldb or N, c, ldc or N)
+    d = sg.tile_info(cfg.variant, cfg.tile)
+    if cfg.flags & sg.FLAG_STREAMK:
+        return cfg, rows, cols, 2 * 256 * 4 * d["bm"] * d["bn"]
+    if cfg.variant == sg.VARIANT_SKINNY and d["tm"] == 0 and cfg.group_m > 1:
+        return cfg, rows, cols, cfg.group_m * M * N * 4
+    return cfg, rows, cols, 0
+
+
+def test_named_workload_plans_take_no_stream_k_and_fit_the_static_scratch():
+    """Which automatic plans of the named workloads keep partial sums in
+    device memory: none is stream-K (64-128 MiB); the few-rows products
+    whose strips leave CUs idle are split over K (1 x 4096 x 4096, the
+    16-row decode shape, the one-row edge strip of 4097 x 1000 x 3001), and
+    their partial sums fit the static scratch of the entry point that
+    allocates nothing, so that entry point runs the same plans."""
+    split = {}
+    for M, N, K in NAMED_SHAPES:
+        cfg, rows, cols, ws = plan_partial_bytes(M, N, K)
+        assert not cfg.flags & sg.FLAG_STREAMK, (M, N, K)
+        assert ws <= STATIC_SCRATCH_BYTES, (M, N, K, ws)
+        if ws:
+            split[(M, N, K)] = ws
+        if rows:   # the edge strip below the main part: its own plan
+            _, _, _, ws_rows = plan_partial_bytes(rows, N, K, a=0x10000 + 4 * (M - rows) * K)
+            assert ws_rows <= STATIC_SCRATCH_BYTES
+            if ws_rows:
+                split[(rows, N, K, "edge rows")] = ws_rows
+    assert set(split) == {(1, 4096, 4096), (16, 14336, 4096), (1, 1000, 3001, "edge rows")}, split
+    assert split[(1, 4096, 4096)] <= 1 << 20

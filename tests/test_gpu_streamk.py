@@ -231,8 +231,8 @@ def test_workspace_streams_grow_and_release():
     rng = np.random.default_rng(2600)
     cases = [(512, 512, 8192, dict(variant=sg.VARIANT_MFMA, tile=tiles[0], flags=sg.FLAG_STREAMK)),
              (768, 640, 16384, dict(variant=sg.VARIANT_MFMA, tile=tiles[0], flags=sg.FLAG_STREAMK)),
-             (4, 1024, 8192, dict(variant=sg.VARIANT_SKINNY, tile=9)),
-             (16, 2048, 16384, dict(variant=sg.VARIANT_SKINNY, tile=9))]
+             (4, 1024, 8192, dict(variant=sg.VARIANT_SKINNY, tile=0, group_m=8)),
+             (16, 2048, 16384, dict(variant=sg.VARIANT_SKINNY, tile=2, group_m=16))]
     ops = []
     for M, N, K, kw in cases:
         A = dev(rng.uniform(-1, 1, (M, K)).astype(F32))
@@ -259,21 +259,29 @@ def test_workspace_streams_grow_and_release():
         sg.workspace_release()
 
 
-SPLIT_CASES = [(1, 1000, 3001), (7, 77, 4097), (16, 2000, 8192), (3, 300, 16384), (1, 64, 1024)]
+SPLIT_CASES = [(1, 1000, 3001, 5), (7, 77, 4097, 0), (16, 2000, 8192, 7), (3, 300, 16384, 0),
+               (1, 64, 1024, 3), (2, 4100, 999, 64)]
+
+
+def rows_tiles():
+    return [t for t in range(sg.tile_count(sg.VARIANT_SKINNY))
+            if sg.tile_info(sg.VARIANT_SKINNY, t)["tm"] == 0]
 
 
 @pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
-@pytest.mark.parametrize("tile", [9, 10])
+@pytest.mark.parametrize("tile", range(6))
 def test_skinny_split_k(tile, ta, tb, oracle_mod):
-    """The few-rows tiles that split K over workgroups (partial sums in a
-    workspace, summed in slice order by a second kernel): random inputs with
-    alpha/beta and with bias + GELU within tolerance, 4-byte loads, integer
-    inputs bit-exact, and two calls give the same bits."""
-    if tile >= sg.tile_count(sg.VARIANT_SKINNY):
+    """The few-rows tiles split over K (group_m slices, 0: the library's
+    choice; partial sums in a workspace, added in slice order by the last
+    workgroup of each strip): random inputs with alpha/beta and with bias +
+    GELU within tolerance, 4-byte loads, integer inputs bit-exact, and two
+    calls give the same bits."""
+    if tile >= len(rows_tiles()):
         pytest.skip("tile not compiled")
-    kw = dict(variant=sg.VARIANT_SKINNY, tile=tile)
-    for i, (M, N, K) in enumerate(SPLIT_CASES):
-        lab = f"split t{tile} ta={ta} tb={tb} {(M, N, K)}"
+    tile = rows_tiles()[tile]
+    for i, (M, N, K, slices) in enumerate(SPLIT_CASES):
+        kw = dict(variant=sg.VARIANT_SKINNY, tile=tile, group_m=slices)
+        lab = f"split t{tile} s{slices} ta={ta} tb={tb} {(M, N, K)}"
         print(lab, flush=True)
         A, B, C0 = workloads.draw(M, N, K, "uniform", 2700 + i, True)
         As, Bs = stored(A, B, ta, tb)
@@ -309,6 +317,26 @@ def test_skinny_split_k(tile, ta, tb, oracle_mod):
         torch.cuda.synchronize()
         ref = oracle_mod.sgemm(Ai, Bi, Ci.copy(), 0.5, -1.25, trans_a=ta, trans_b=tb)
         assert np.array_equal(C.cpu().numpy(), ref), f"{lab} int: not bit-exact"
+
+
+def test_skinny_split_repeated_bit_exact(oracle_mod):
+    """Many-slice splits, repeated: each slice's partial sums are read back by
+    whichever workgroup of the strip arrives last, so a partial sum that was
+    not yet visible would show as a wrong cell.  Integer inputs make every
+    order exact: 40 calls per case must all equal the oracle bit for bit."""
+    cases = [(1, 4096, 4096, 0, 32), (4, 1000, 3001, 1, 16), (16, 2048, 4096, 2, 8),
+             (3, 700, 8192, 3, 64), (16, 14336, 4096, 4, 3)]
+    for M, N, K, tile, slices in cases:
+        A, B, C0 = workloads.draw(M, N, K, "int4", 3100 + M + K, True)
+        ref = oracle_mod.sgemm(A, B, C0.copy(), 0.5, -1.25)
+        dA, dB = dev(A), dev(B)
+        outs = [dev(C0) for _ in range(40)]
+        for C in outs:
+            sg.gemm(dA, dB, C, 0.5, -1.25, variant=sg.VARIANT_SKINNY, tile=tile, group_m=slices)
+        torch.cuda.synchronize()
+        for n, C in enumerate(outs):
+            assert np.array_equal(C.cpu().numpy(), ref), \
+                f"call {n} of {(M, N, K)} tile {tile} slices {slices} is not bit-exact"
 
 
 @pytest.mark.parametrize("tb", [False, True])
