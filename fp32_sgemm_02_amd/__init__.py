@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = [
-    "sgemm", "sgemm_ex", "sgemm_op", "sgemm_cblas", "sgemm_epilogue", "sgemm_strided_batched",
+    "sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_noalloc", "sgemm_cblas", "sgemm_epilogue", "sgemm_strided_batched",
     "sgemm_mixed", "gemm", "gemm_batched", "gemm_mixed", "select", "tile_count", "tile_info", "status_string",
     "version", "workspace_release", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "VARIANT_MFMA16",
@@ -85,6 +85,8 @@ def _load():
     lib.sgemm_op_ex.restype = i
     lib.sgemm_op_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p,
                                 ctypes.POINTER(SgemmConfig)]
+    lib.sgemm_op_ex_noalloc.restype = i
+    lib.sgemm_op_ex_noalloc.argtypes = lib.sgemm_op_ex.argtypes
     lib.sgemm_select.restype = i
     lib.sgemm_select.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.POINTER(SgemmConfig)]
     ll = ctypes.c_longlong
@@ -143,6 +145,15 @@ def sgemm_op(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, str
                                 stream)
     return _load().sgemm_op_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                stream, ctypes.byref(cfg))
+
+
+def sgemm_op_noalloc(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     stream=None, cfg: SgemmConfig | None = None) -> int:
+    """Raw C-ABI call of sgemm_op_ex_noalloc (partial sums in the library's
+    static scratch array; no device allocation)."""
+    return _load().sgemm_op_ex_noalloc(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                       ldc, stream,
+                                       ctypes.byref(cfg) if cfg is not None else None)
 
 
 def sgemm_epilogue(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
@@ -270,7 +281,7 @@ def _stream_handle(stream, device, torch):
 
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
          trans_b: bool = False, bias=None, act: int = ACT_NONE, variant: int = VARIANT_AUTO,
-         tile: int = -1, flags: int = 0, group_m: int = 0, stream=None):
+         tile: int = -1, flags: int = 0, group_m: int = 0, stream=None, noalloc: bool = False):
     """C = act(alpha * op(A) @ op(B) + beta * C + bias) for 2-D float32 CUDA
     tensors (row-major views with unit column stride; padded rows are used
     through their leading dimension).  op(X) is X, or X transposed when
@@ -279,7 +290,7 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool =
     act (ACT_*) are optional (sgemm_epilogue).  C is updated in place when
     given; otherwise a new tensor is returned (beta must then be 0).  Runs
     asynchronously on ``stream`` (default: the current stream of A's
-    device)."""
+    device).  noalloc: run through sgemm_op_ex_noalloc (no bias or act)."""
     import torch
 
     if A.dim() != 2 or B.dim() != 2:
@@ -308,7 +319,11 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool =
                 _ld(C))
         explicit = not (variant == VARIANT_AUTO and tile < 0 and flags == 0 and group_m == 0)
         cfg = SgemmConfig(variant, tile, flags, group_m) if explicit else None
-        if bias is not None or act != ACT_NONE:
+        if noalloc:
+            if bias is not None or act != ACT_NONE:
+                raise ValueError("noalloc: no bias or activation")
+            st = sgemm_op_noalloc(int(trans_a), int(trans_b), *args, s, cfg=cfg)
+        elif bias is not None or act != ACT_NONE:
             st = sgemm_epilogue(int(trans_a), int(trans_b), *args,
                                 None if bias is None else ptr(bias), int(act), s, cfg=cfg)
         elif trans_a or trans_b:

@@ -29,6 +29,7 @@ constexpr int kBadStrideB = -27;
 constexpr int kBadStrideC = -28;
 constexpr int kBadBatch = -29;
 constexpr int kBadDtype = -30;
+constexpr int kBadScratch = -31;
 
 // A status of the row-major call that serves a column-major one (operands
 // swapped, M and N swapped), renamed after the caller's arguments.
@@ -470,10 +471,12 @@ size_t choice_workspace(const Problem &p, const Choice &ch) {
 
 // Validates and runs one call.  The special cases of the reference BLAS:
 // nothing to do for an empty C or batch; alpha == 0 or K == 0 leaves
-// C = beta * C (plus the epilogue), without reading A or B.  A problem that
-// brings its own scratch for partial sums runs only plans whose partial sums
-// fit it, and is rejected before anything is launched otherwise.
-int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
+// C = beta * C (plus the epilogue), without reading A or B.  With
+// `noalloc`, partial sums take the static scratch array instead of the
+// library's workspace: plans are chosen among those whose partial sums fit
+// it, and a call whose plan (an explicit configuration) needs more is
+// rejected before anything is launched.
+int run(Problem p, hipStream_t stream, const sgemm_config *cfg, bool noalloc = false) {
     const int v = validate(p);
     if (v != 0) return v;
     if (p.M == 0 || p.N == 0 || p.batch == 0) return 0;
@@ -482,6 +485,10 @@ int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
     if (p.alpha == 0.f || p.K == 0) {
         if (p.beta == 1.f && !p.has_epilogue()) return 0;
         return to_status(launch_elementwise(p, p.beta, stream));
+    }
+    if (noalloc) {
+        const hipError_t e = static_scratch(&p.scratch, &p.scratch_bytes);
+        if (e != hipSuccess) return to_status(e);
     }
 
     Choice ch;
@@ -514,7 +521,7 @@ int run(Problem p, hipStream_t stream, const sgemm_config *cfg) {
         if (choice_workspace(main, ch) > p.scratch_bytes ||
             (sp.cols && choice_workspace(cols, ch_cols) > p.scratch_bytes) ||
             (sp.rows && choice_workspace(rows, ch_rows) > p.scratch_bytes))
-            return kBadConfig;
+            return kBadScratch;
     }
     st = launch(main, ch, stream);
     if (st == 0 && sp.cols) st = launch(cols, ch_cols, stream);
@@ -647,6 +654,14 @@ int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, cons
     return sg::run(sg::make_problem(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
                                     ldc),
                    stream, cfg);
+}
+
+int sgemm_op_ex_noalloc(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                        int ldc, hipStream_t stream, const sgemm_config *cfg) {
+    return sg::run(sg::make_problem(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                    ldc),
+                   stream, cfg, true);
 }
 
 int sgemm_epilogue_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
@@ -810,6 +825,7 @@ const char *sgemm_status_string(int status) {
     case -28: return "batch stride of C lets two entries of the batch overlap";
     case -29: return "negative batch count";
     case -30: return "invalid input format (SGEMM_DTYPE_BF16 or SGEMM_DTYPE_F16)";
+    case -31: return "the plan's partial sums need more memory than the static scratch holds";
     default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

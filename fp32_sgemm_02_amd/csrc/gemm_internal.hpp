@@ -115,6 +115,9 @@ struct Workspace {
 hipError_t workspace_acquire(size_t bytes, hipStream_t stream, const Problem &p, Workspace &w);
 hipError_t workspace_release(const Workspace &w, hipStream_t stream);
 hipError_t workspace_release_all();   // the current device's cached buffers
+// The static scratch array of the current device (workspace.cpp): its device
+// address (counters first, as in a workspace) and the bytes after the counters.
+hipError_t static_scratch(void **ptr, size_t *bytes);
 
 // their stream-K launchers (null where a tile offers none), same order
 const LaunchFn *mfma_direct_sk_launchers(int *count);

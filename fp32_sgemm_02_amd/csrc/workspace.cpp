@@ -1,6 +1,7 @@
 // workspace.cpp -- device memory for launches that leave partial sums in
 // memory (stream-K runs of the direct-load tiles, K slices of the few-rows
-// skinny kernel).
+// skinny kernel), and the static scratch array of the entry point that
+// allocates nothing.
 //
 // Layout of every workspace: kWorkspaceCounters arrival counters (zero
 // between launches: a launch that counts arrivals on them sets each one back
@@ -24,8 +25,8 @@
 // counters cleared by a recorded fill kernel), so replays of the graph never
 // share memory with eager calls.
 //
-// A problem that brings its own scratch (Problem::scratch) takes it instead,
-// with no allocation at all.
+// A problem that brings its own scratch (Problem::scratch, set by the entry
+// point that allocates nothing) takes it instead, with no allocation at all.
 #include <map>
 #include <mutex>
 #include <thread>
@@ -35,6 +36,13 @@
 
 namespace sg {
 namespace {
+
+// The static scratch: counters, then 16 MiB for partial sums.  Zero at load
+// (so its counters start at zero); each device holds its own copy until the
+// process ends.
+constexpr size_t kStaticScratchBytes = kWorkspaceCounterBytes + ((size_t)16 << 20);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
 
 __global__ void __launch_bounds__(256) zero_counters(unsigned *c, int n) {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -72,6 +80,27 @@ void fill(Workspace &w, void *base, bool owned) {
 }
 
 }  // namespace
+
+hipError_t static_scratch(void **ptr, size_t *bytes) {
+    static std::mutex m;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(m);
+    if (!addr[dev]) {
+        // the array's device address on this device (the name itself is a
+        // host-side stand-in and must never reach a kernel)
+        void *q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = q;
+    }
+    *ptr = addr[dev];
+    *bytes = kStaticScratchBytes - kWorkspaceCounterBytes;
+    return hipSuccess;
+}
 
 hipError_t workspace_acquire(size_t bytes, hipStream_t stream, const Problem &p, Workspace &w) {
     w = Workspace{};

@@ -35,7 +35,8 @@
  * stream; held until sgemm_workspace_release or process exit; the per-thread
  * default stream gets one per host thread).  Under graph capture each call
  * records its own allocation and free on the capturing stream.  An
- * allocation failure is returned as its hipError_t.  Work is
+ * allocation failure is returned as its hipError_t.  Callers that cannot
+ * allocate use sgemm_op_ex_noalloc.  Work is
  * enqueued on `stream` (NULL = the null stream) and the call
  * returns without synchronising: the caller keeps A, B and C alive and
  * unmodified until that stream's work has completed.  C must not overlap A
@@ -66,6 +67,8 @@
  *                       stride of C that lets two of the batch's C overlap
  *     -29               sgemm_strided_batched: negative batch
  *     -30               sgemm_mixed: dtype not SGEMM_DTYPE_BF16 / _F16
+ *     -31               sgemm_op_ex_noalloc: the plan's partial sums need
+ *                       more memory than the static scratch holds
  *     > 0               a hipError_t reported by the kernel launch
  * No C++ exception crosses this interface.
  *
@@ -222,6 +225,26 @@ int sgemm_op(int trans_a, int trans_b, int M, int N, int K, float alpha, const f
 int sgemm_op_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
                 int lda, const float *B, int ldb, float beta, float *C, int ldc,
                 hipStream_t stream, const sgemm_config *cfg);
+
+/*
+ * sgemm_op_ex_noalloc: sgemm_op_ex for callers that cannot allocate device
+ * memory -- code under HIP graph capture (where sgemm_op would record an
+ * allocation and a free node for every split or stream-K call), tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no hipMalloc, hipFree or
+ * allocating routine: the partial sums of split launches go to a static
+ * device array of the library (16 MiB plus 16 KiB of arrival counters), held
+ * by every device the library runs on until the process ends.  Arguments,
+ * results and status codes as sgemm_op_ex (cfg NULL = automatic); the
+ * automatic plan is sgemm_op's among the plans whose partial sums fit the
+ * array (stream-K, which needs 64 MiB or more, is then never chosen), and a
+ * call whose explicit configuration needs more returns -31 before launching
+ * anything.  Every call on a device shares that device's array: calls that
+ * may overlap on one device (on different streams, or from several host
+ * threads) race on it, and must be ordered by the caller.
+ */
+int sgemm_op_ex_noalloc(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                        int ldc, hipStream_t stream, const sgemm_config *cfg);
 
 /*
  * Activation codes of sgemm_epilogue (applied in fp32 to the finished sum).
