@@ -23,9 +23,12 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -82,13 +85,80 @@ def parse():
     ap.add_argument("--op", default="NN", choices=["NN", "NT", "TN", "TT"],
                     help="storage of A and B: N as given, T transposed (sgemm_op)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the graphics clock with amd-smi (for runs under a "
+                         "profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--sweep", metavar="JSON_OUT", default=None)
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    default=None,
+                    help="write the HBM traffic record of the workload's kernel from two "
+                         "rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
+                         "WRITE_SIZE) of this same command")
+    ap.add_argument("--traffic-out", default=None,
+                    help="traffic record file to update (default: profiles/traffic.json)")
     ap.add_argument("--probes", action="store_true",
-                    help="measure the MFMA-f32 and VALU-FMA ceilings with register-only loops")
+                    help="measure the MFMA-f32 and VALU-FMA ceilings with register-only loops, "
+                         "and the HBM read rate of a plain streaming read")
     return ap.parse_args()
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_sclk_mhz() -> float | None:
+    """The mean of the GPU's graphics clocks (one per XCD) now, in MHz, from
+    `amd-smi metric -g 0 -c --json`; None when the tool is not there."""
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                             text=True, timeout=10).stdout
+        data = json.loads(out)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                  if k.startswith("gfx") and isinstance(v, dict) and "clk" in v]
+        vals = [float(c) for c in clocks if isinstance(c, (int, float))]
+        return sum(vals) / len(vals) if vals else None
+    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+        return None
+
+
+def sustained_sclk(torch, call, seconds: float = 1.5) -> dict:
+    """SCLK sampled (amd-smi, one sample about every 0.2 s) while `call` runs
+    back to back for about `seconds`: the clock the kernel runs at."""
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            stop.wait(0.2)
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            call()
+        n += 20
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return {"sclk_mhz": None, "samples": 0}
+    return {"sclk_mhz": round(statistics.median(samples), 1), "samples": len(samples),
+            "calls": n}
 
 
 def cpu_baseline(w, A, B, C0, target_s: float):
@@ -110,7 +180,7 @@ def cpu_baseline(w, A, B, C0, target_s: float):
         rows = min(w.M, max(rows + 1, int(rows * target_s / max(dt, 1e-3))))
     flops = 2.0 * rows * w.N * w.K
     out = {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
-           "kind": "oracle", "seconds": round(dt, 3),
+           "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
            "sample": f"rows 0..{rows - 1} of {w.name} ({rows} x {w.N} x {w.K}, "
                      f"{flops / 1e9:.2f} GFLOP), fp64-accumulating C oracle on {threads} threads"}
     return out, ref
@@ -129,6 +199,23 @@ def cpu_baseline_one_core(target: str = "square256") -> dict:
     dt = time.perf_counter() - t0
     return {"workload": w.name, "value": round(w.flops / dt / 1e9, 3), "unit": "GFLOP/s",
             "cores": 1, "seconds": round(dt, 4)}
+
+
+def time_each(torch, call, steps, per: int = 1):
+    """Device times (ms per call) of `steps` samples, each sample `per` calls
+    back to back bracketed by its own pair of events on torch's current
+    stream (the stream the library launches on).  Short kernels take several
+    calls per sample, so that the events' own cost and the host's launch
+    path stay small beside the sample."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s, e in ev:
+        s.record()
+        for _ in range(per):
+            call()
+        e.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) / per for s, e in ev]
 
 
 def time_calls(torch, call, steps, warmup):
@@ -233,8 +320,20 @@ def headline(args):
     tile = args.tile if args.tile >= 0 else chosen.tile
     if args.variant and args.tile < 0:
         tile = -1
+    # The register-only MFMA probe runs first: it is reported beside the
+    # kernel's rate, and its ~35 ms of matrix work brings the graphics clock
+    # from idle (~160 MHz) to its working value, so that the timed steps
+    # measure the kernel rather than the clock ramp (measured: with only the
+    # warm-up steps before them, the first timed 4096^3 launches took up to
+    # 1.12 ms against a 0.93 ms median).
+    probe = measure_probe(torch, "mfma_f32")
+    if variant == 2:
+        probe = measure_probe(torch, "valu_fma_f32")
     wall, kern_ms = time_calls(torch, call, args.steps, args.warmup)
     torch.cuda.synchronize()
+    # after the timed region: per-call durations, and the clock the kernel runs at
+    each = time_each(torch, call, args.steps, per=max(1, math.ceil(0.2 / kern_ms)))
+    clock = {"sclk_mhz": None} if args.no_clock else sustained_sclk(torch, call)
 
     flops = w.flops
     value = flops * args.steps / wall / 1e9
@@ -246,6 +345,9 @@ def headline(args):
         achieved = w.min_bytes / kern_s / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     else:
+        # the VALU family runs on the vector ALUs: the same 157.3 TFLOP/s
+        # (256 CUs x 2.4 GHz x 256 FLOP per clock per CU), priced as "alu"
+        bound = "alu" if variant == 2 else bound
         achieved = flops / kern_s / 1e12
         peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
     traffic = traffic_for(variant, kernel, desc)
@@ -269,12 +371,19 @@ def headline(args):
                    "tile": tile, "tile_desc": desc},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel, "kernel_ms_mean": round(kern_s * 1e3, 4)},
+                     "kernel": kernel, "kernel_ms_mean": round(kern_s * 1e3, 4),
+                     "kernel_ms_median": round(statistics.median(each), 4),
+                     "kernel_ms_min": round(min(each), 4)},
     }
-    probe = measure_probe(torch, "mfma_f32")
     if bound != "hbm":
         out["roofline"]["probe_tflops"] = probe["tflops"]
         out["roofline"]["frac_of_probe"] = round(achieved / probe["tflops"], 4)
+        # the spec peak scaled to the graphics clock sampled while the kernel ran
+        out["roofline"]["sclk_mhz"] = clock["sclk_mhz"]
+        if clock["sclk_mhz"]:
+            peak_at_clock = 256 * 256 * clock["sclk_mhz"] * 1e6 / 1e12
+            out["roofline"]["peak_at_sclk"] = round(peak_at_clock, 2)
+            out["roofline"]["frac_at_sclk"] = round(achieved / peak_at_clock, 4)
     if not args.no_cpu_baseline:
         base, ref = cpu_baseline(w, A, B, C0, args.cpu_seconds)
         # the GPU's rows of one more call on the original C, against the oracle's
@@ -295,7 +404,12 @@ def sweep(args):
     """Every named workload through automatic dispatch.  `kernel_ms_median` is
     the device time per call from HIP-graph replay (calls back to back with no
     host launch gaps); `eager_call_ms_median` brackets single eager calls with
-    events and includes the host launch path, which dominates small shapes."""
+    events and includes the host launch path, which dominates small shapes.
+    Plans that keep partial sums also record `noalloc_kernel_ms_median`, the
+    same plan replayed through sgemm_op_ex_noalloc (a captured sgemm call
+    records an allocation and a free node, the no-alloc entry point none).
+    Each workload's oracle is timed on a bounded band of rows
+    (`oracle_gflops`, on `oracle_cores` threads of the host CPU)."""
     import numpy as np
     import torch
     import fp32_sgemm_02_amd as sg
@@ -304,7 +418,8 @@ def sweep(args):
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
-    rows = []
+    rows = [{"host_cpu": cpu_model(), "sclk_mhz_idle": read_sclk_mhz()}]
+    print(json.dumps(rows[0]), flush=True)
     names = [n for n in workloads.WORKLOADS if n != "probe256"]
     for name in names:
         w = workloads.WORKLOADS[name]
@@ -318,14 +433,26 @@ def sweep(args):
             eager = statistics.median(time_rotating(torch, call_i, 30 if hbm else 20, 5)) / 1e3
             calls = max(len(sets), 20 if w.flops < 1e11 else 5)
             med = statistics.median(time_graph(torch, call_i, calls)) / 1e3
-            cfg = sg.select(w.M, w.N, w.K)
+            cfg, erows, ecols = sg.plan(w.M, w.N, w.K)
             row = {"workload": name, "M": w.M, "N": w.N, "K": w.K,
                    "variant": v or cfg.variant, "tile": cfg.tile if v == 0 else -1,
+                   "group_m": cfg.group_m if v == 0 else 0, "edge_rows": erows,
                    "kernel_ms_median": round(med * 1e3, 4),
                    "eager_call_ms_median": round(eager * 1e3, 4),
                    "gflops": round(w.flops / med / 1e9, 1),
-                   "gbs": round(w.min_bytes / med / 1e9, 1), "bound": w.bound,
+                   "gbs": round(w.min_bytes / med / 1e9, 1),
+                   "bound": "alu" if v == 2 else w.bound,
                    "operand_copies": len(sets)}
+            keeps_sums = v == 0 and (cfg.flags & sg.FLAG_STREAMK or erows or
+                                     (cfg.variant == sg.VARIANT_SKINNY and cfg.group_m > 1))
+            if keeps_sums:
+                call_n = lambda i: sg.gemm(*sets[i % len(sets)], w.alpha, w.beta, noalloc=True)
+                row["noalloc_kernel_ms_median"] = round(
+                    statistics.median(time_graph(torch, call_n, calls)), 4)
+            if v == 0:
+                base, _ = cpu_baseline(w, A, B, C0, 1.5)
+                row.update(oracle_gflops=base["value"], oracle_cores=base["cores"],
+                           oracle_sample=base["sample"])
             if hbm:
                 row["pct_roofline"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
             else:
@@ -524,6 +651,74 @@ def sweep_mixed(torch, sg, time_graph):
     return out
 
 
+# FETCH_SIZE / WRITE_SIZE counter bytes -> true bytes, from a 1 GiB device
+# copy of known size (profiles/hbm_counter_calibration_copy1GiB.md)
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
+
+
+def read_counter_csv(path: str) -> dict:
+    """{kernel name: (dispatches, mean counter KiB per dispatch, summed
+    duration ns)} from a rocprofv3 counter_collection.csv with one counter."""
+    import csv
+
+    acc = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            name = row["Kernel_Name"]
+            d = acc.setdefault(name, {})
+            disp = row["Dispatch_Id"]
+            v, dur = float(row["Counter_Value"]), int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            prev = d.get(disp, (0.0, dur))
+            d[disp] = (prev[0] + v, dur)
+    out = {}
+    for name, d in acc.items():
+        vals = [v for v, _ in d.values()]
+        out[name] = (len(vals), sum(vals) / len(vals), sum(t for _, t in d.values()))
+    return out
+
+
+def record_traffic(args):
+    """The HBM traffic record of the kernel this command times: the dominant
+    kernel (largest summed duration, probes excluded) of two counter runs,
+    scaled by the copy calibration, keyed by the kernel's name and the hash
+    of its source files, so that bench.py reports it only while the source is
+    unchanged."""
+    import fp32_sgemm_02_amd as sg
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    trans_a, trans_b = args.op[0] == "T", args.op[1] == "T"
+    chosen = sg.select(w.M, w.N, w.K, trans_a=trans_a, trans_b=trans_b)
+    variant = args.variant or chosen.variant
+    tile = args.tile if args.tile >= 0 else chosen.tile
+    desc = sg.tile_info(variant, tile) if tile >= 0 else {}
+    fetch, write = (read_counter_csv(f) for f in args.record_traffic)
+    names = [n for n in fetch if "probe_" not in n]
+    main = max(names, key=lambda n: fetch[n][2])
+    f_kib, w_kib = fetch[main][1], write[main][1]
+    rec = {"kernel": main, "workload": w.name, "source_hash": kernel_source_hash(variant, desc),
+           "dispatches": fetch[main][0], "fetch_kib_per_dispatch": round(f_kib, 1),
+           "write_kib_per_dispatch": round(w_kib, 1), "fetch_factor": FETCH_FACTOR,
+           "write_factor": WRITE_FACTOR, "fetch_bytes": int(f_kib * 1024 * FETCH_FACTOR),
+           "write_bytes": int(w_kib * 1024 * WRITE_FACTOR),
+           "bytes_per_launch": int(f_kib * 1024 * FETCH_FACTOR + w_kib * 1024 * WRITE_FACTOR),
+           "algorithmic_bytes": w.min_bytes}
+    path = args.traffic_out or TRAFFIC_FILE
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        data = {}
+    data.setdefault("_about", "HBM/fabric bytes per launch from rocprofv3 --pmc FETCH_SIZE and "
+                              "WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps "
+                              "the same counter onto a 1 GiB device copy of known size. "
+                              "source_hash covers the kernel's source files; bench.py reports "
+                              "traffic only while it matches.")
+    data[kernel_name(variant, desc)] = rec
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1)
+    print(json.dumps({kernel_name(variant, desc): rec}), flush=True)
+
+
 def copy_calibration(args):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -552,26 +747,64 @@ def measure_probe(torch, name: str, steps: int = 10, warmup: int = 3) -> dict:
                                                  ctypes.c_void_p]
     blocks = 256 * 8
     iters = 2000 if kind == "mfma" else 20000
-    peak = PEAK_FP32_TFLOPS if kind == "mfma" else PEAK_FP32_TFLOPS / 2
+    peak = PEAK_FP32_TFLOPS
     out = torch.empty(blocks * 256, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     flops = getattr(lib, f"probe_{kind}_flops")(blocks, iters)
     launch = getattr(lib, f"probe_{kind}_f32")
     _, ms = time_calls(torch, lambda: launch(blocks, iters, out.data_ptr(), stream), steps, warmup)
     tf = flops / (ms / 1e3) / 1e12
-    per_cu_clk = 256 if kind == "mfma" else 128
-    return {"probe": name, "tflops": round(tf, 2), "peak_tflops": peak,
-            "frac": round(tf / peak, 4), "kernel_ms_mean": round(ms, 4),
-            "implied_clock_ghz": round(tf * 1e12 / (256 * per_cu_clk) / 1e9, 3)}
+    out = {"probe": name, "tflops": round(tf, 2), "peak_tflops": peak,
+           "frac": round(tf / peak, 4), "kernel_ms_mean": round(ms, 4)}
+    if kind == "mfma":
+        # the matrix cores retire 256 FP32 FLOP per clock per CU
+        out["implied_clock_ghz"] = round(tf * 1e12 / (256 * 256) / 1e9, 3)
+    return out
+
+
+def measure_read_probe(torch, floats: int, blocks: int) -> dict:
+    """The streaming-read probe over `floats` floats with `blocks` workgroups,
+    graph-replayed back to back over copies larger than twice the Infinity
+    Cache (so every launch reads HBM)."""
+    import ctypes
+    from fp32_sgemm_02_amd.tune import time_graph
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp32_sgemm_02_amd", "libfp32probes.so"))
+    lib.probe_read_f32.restype = ctypes.c_int
+    lib.probe_read_f32.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    copies = max(2, -(-2 * MALL_BYTES // (4 * floats)) + 1)
+    bufs = [torch.ones(floats, device="cuda:0") for _ in range(copies)]
+    out = torch.empty(blocks * 256, device="cuda:0")
+
+    def call_i(i):
+        st = lib.probe_read_f32(bufs[i % copies].data_ptr(), floats, blocks, out.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"probe_read_f32: {st}")
+    ms = statistics.median(time_graph(torch, call_i, 2 * copies))
+    del bufs
+    return {"probe": "read_f32", "MB": round(4 * floats / 1e6, 1), "workgroups": blocks,
+            "us": round(ms * 1e3, 2), "TBs": round(4 * floats / (ms / 1e3) / 1e12, 3),
+            "frac_of_8TBs": round(4 * floats / (ms / 1e3) / 8e12, 4)}
 
 
 def probes(args):
-    """Register-only MFMA and FMA loops: the rates the chip sustains on this machine."""
+    """Register-only MFMA and FMA loops: the rates the chip sustains on this
+    box; and a streaming read of 67 MB (one 4096 x 4096 operand) and 235 MB
+    (the 4096 x 14336 weight of the decode shape) with 224 .. 2048
+    workgroups: what a memory-bound kernel can reach, and how many
+    workgroups it takes."""
     import torch
 
     torch.cuda.set_device(0)
     for name in ("mfma_f32", "valu_fma_f32"):
         print(json.dumps(measure_probe(torch, name)), flush=True)
+    for floats in (4096 * 4096, 4096 * 14336):
+        for blocks in (224, 256, 512, 1024, 2048):
+            if floats % (4 * blocks) == 0:
+                print(json.dumps(measure_read_probe(torch, floats, blocks)), flush=True)
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -580,7 +813,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.probes:
+    if args.record_traffic:
+        record_traffic(args)
+    elif args.probes:
         probes(args)
     elif args.copy_bytes:
         copy_calibration(args)

@@ -6,6 +6,11 @@
 //     2048 flops per instruction.
 //   * probe_valu_f32: chains of independent fp32 FMAs per lane (built, like
 //     the library, with packed fp32 disabled), 2 flops per lane per FMA.
+//   * probe_read_f32: a plain streaming read, each workgroup one contiguous
+//     chunk, 16-byte non-temporal loads, eight in flight per lane: the HBM
+//     read rate a memory-bound kernel can reach with a given number of
+//     workgroups (the roofline paragraph of "The GEMM Scrapbook" bounds such
+//     kernels by bandwidth, not flops).
 // The achieved rate divided by (256 CUs x 256 flops/clock) gives the
 // effective matrix-core clock during a long fp32 MFMA run.  Not part of the
 // SGEMM library: built into libfp32probes.so and used by bench.py --probes.
@@ -48,9 +53,43 @@ __global__ void __launch_bounds__(256) probe_valu_kernel(int iters, float *out) 
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Workgroup b reads floats [b * chunk, (b + 1) * chunk) of src (chunk a
+// multiple of 4); lanes past the chunk load its first element and discard it
+// (no branch around the loads, so all eight stay in flight together).  Each
+// thread writes its sum, so the loads cannot be removed.
+__global__ void __launch_bounds__(256) probe_read_kernel(const float *src, long long chunk,
+                                                         float *out) {
+    const floatx4 *p = reinterpret_cast<const floatx4 *>(src + (long long)blockIdx.x * chunk);
+    const long long n4 = chunk / 4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (long long i = threadIdx.x; i < n4; i += 256 * 8) {
+        floatx4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const long long j = i + 256LL * u;
+            const bool ok = j < n4;
+            const floatx4 t = __builtin_nontemporal_load(ok ? p + j : p);
+            v[u] = ok ? t : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Streaming read of n floats by `blocks` workgroups of 256 threads; n must be
+// a multiple of 4 * blocks and `out` hold blocks * 256 floats.  Returns a
+// hipError_t, or -1 for a size that does not divide.
+int probe_read_f32(const float *src, long long n, int blocks, float *out, hipStream_t stream) {
+    if (blocks <= 0 || n <= 0 || n % (4LL * blocks) != 0) return -1;
+    hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(256), 0, stream, src, n / blocks,
+                       out);
+    return (int)hipGetLastError();
+}
 
 // Flops performed by one launch of each probe with `blocks` workgroups of 256
 // threads (4 waves) and `iters` iterations.

@@ -16,6 +16,19 @@ tests against the CPU oracle; as a guard against a mis-tuned table the tuner
 also requires each candidate's output to agree with the automatic
 configuration's output on the same inputs (same tolerance rule as the
 tests) before it may win.
+
+Graph-replayed timing (--graph) runs every candidate through
+sgemm_op_ex_noalloc, so plans that keep partial sums (K-split skinny tiles,
+stream-K) are not charged the allocation and free nodes a captured sgemm
+call records; those the static scratch cannot hold (stream-K) are timed
+eagerly after a warm-up call instead, and the cost of the nodes is reported
+beside them as `graph_with_alloc_ms`.
+
+    python -m fp32_sgemm_02_amd.tune --mixed bf16 --shapes 4096x4096x4096 --graph
+
+times every 16-bit-input tile (sgemm_mixed, W stored N x K) instead; its
+`eff_pct` (percent of the 2.5 PFLOP/s 16-bit matrix peak) is what the
+16-bit tile table's efficiencies are read from.
 """
 from __future__ import annotations
 
@@ -37,18 +50,29 @@ def parse_shape(text: str):
     return m, n, k
 
 
+SLICES = (1, 2, 4, 8, 16, 32)   # K slices of the few-rows skinny tiles
+
+
 def candidates(sg, M, N, K, sweep_groups: bool):
     """(variant, tile, group_m, flags) to time.  The first is the automatic
     plan without the tuned table (the cost model, edge strips included); when
-    it wins, the shape needs no table row."""
+    it wins, the shape needs no table row.  Then every MFMA tile (and its
+    stream-K form where it has one), every VALU tile, and for skinny shapes
+    every skinny tile (the few-rows ones at each K-slice count)."""
     out = [(sg.VARIANT_AUTO, -1, 0, sg.FLAG_UNTUNED)]
     for tile in range(sg.tile_count(sg.VARIANT_MFMA)):
         groups = GROUPS if sweep_groups else (0,)
         for g in groups:
             out.append((sg.VARIANT_MFMA, tile, g, 0))
+        if sg.tile_info(sg.VARIANT_MFMA, tile)["flags"] & sg.TILE_STREAMK:
+            out.append((sg.VARIANT_MFMA, tile, 0, sg.FLAG_STREAMK))
+    for tile in range(sg.tile_count(sg.VARIANT_VALU)):
+        out.append((sg.VARIANT_VALU, tile, 0, 0))
     if M <= 16 or N <= 16:
         for tile in range(sg.tile_count(sg.VARIANT_SKINNY)):
-            out.append((sg.VARIANT_SKINNY, tile, 0, 0))
+            rows_kind = sg.tile_info(sg.VARIANT_SKINNY, tile)["tm"] == 0
+            for g in (SLICES if rows_kind else (0,)):
+                out.append((sg.VARIANT_SKINNY, tile, g, 0))
     return out
 
 
@@ -117,11 +141,26 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
         if not agree(torch, C, ref, K, 1.0, 1.0):
             print(f"  rejected v{variant} t{tile} g{group}: output differs", flush=True)
             continue
-        call_i = lambda i: sg.gemm(As[i % copies], Bs[i % copies], C, variant=variant, tile=tile,
-                                   group_m=group, flags=flags)
+        kw = dict(variant=variant, tile=tile, group_m=group, flags=flags)
+        call_i = lambda i, kw=kw: sg.gemm(As[i % copies], Bs[i % copies], C, **kw)
+        call_n = lambda i, kw=kw: sg.gemm(As[i % copies], Bs[i % copies], C, noalloc=True, **kw)
+        timing = "eager"
+        alloc_ms = None
         if graph:
-            ms = statistics.median(time_graph(torch, call_i, max(reps, copies)))
-        else:
+            try:
+                call_n(0)
+                fits = True
+            except sg.SgemmError as ex:
+                if ex.status != -31:
+                    raise
+                fits = False   # partial sums beyond the static scratch: time eagerly
+            if fits:
+                ms = statistics.median(time_graph(torch, call_n, max(reps, copies)))
+                timing = "graph, no allocation"
+                if keeps_partial_sums(sg, M, N, K, variant, tile, group, flags):
+                    alloc_ms = round(statistics.median(
+                        time_graph(torch, call_i, max(reps, copies))), 5)
+        if timing == "eager":
             for i in range(warmup):
                 call_i(i)
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -140,8 +179,72 @@ def tune_shape(sg, torch, M, N, K, warmup, reps, sweep_groups, seed=0, rotate=Fa
         else:
             desc = sg.tile_info(variant, tile)
         results.append({"variant": variant, "tile": tile, "group_m": group, "flags": flags,
-                        "ms": round(ms, 5), "gflops": round(gf, 1), "desc": desc})
+                        "ms": round(ms, 5), "gflops": round(gf, 1), "timing": timing,
+                        "graph_with_alloc_ms": alloc_ms, "desc": desc})
         print(f"  v{variant} t{tile} g{group} f{flags}: {ms:.4f} ms  {gf:,.0f} GFLOP/s", flush=True)
+    results.sort(key=lambda r: r["ms"])
+    return results
+
+
+def keeps_partial_sums(sg, M, N, K, variant, tile, group, flags) -> bool:
+    """Whether a candidate's plan keeps partial sums in device memory: a
+    stream-K launch, or a few-rows skinny launch split over K (the automatic
+    plan as sgemm_plan reports it)."""
+    if flags & sg.FLAG_STREAMK:
+        return True
+    if variant == sg.VARIANT_AUTO:
+        cfg, rows, _ = sg.plan(M, N, K)
+        return bool(cfg.flags & sg.FLAG_STREAMK or rows or
+                    (cfg.variant == sg.VARIANT_SKINNY and cfg.group_m > 1))
+    return (variant == sg.VARIANT_SKINNY and sg.tile_info(variant, tile)["tm"] == 0 and
+            group != 1)
+
+
+PEAK_16BIT_GFLOPS = 2.5e6   # MI355X dense bf16 / fp16 matrix peak
+
+
+def tune_mixed(sg, torch, M, N, K, dtype: str, reps: int, seed: int = 0):
+    """Every 16-bit-input configuration (sgemm_mixed with W stored N x K: the
+    automatic choice, each 16-bit MFMA tile, the generic kernel) on
+    (M, N, K), graph-replayed; `eff_pct` is the percent of the 16-bit matrix
+    peak, the figure the 16-bit tile table's cost model uses."""
+    dev = "cuda:0"
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    A = (torch.rand((M, K), device=dev, generator=gen) * 2 - 1).to(dt)
+    W = (torch.rand((N, K), device=dev, generator=gen) * 2 - 1).to(dt)
+    C = torch.empty((M, N), device=dev)
+    ref = torch.empty((M, N), device=dev)
+    sg.gemm_mixed(A, W, ref, trans_b=True)
+    torch.cuda.synchronize()
+    cands = [(sg.VARIANT_AUTO, -1)] + [(sg.VARIANT_MFMA16, t)
+                                       for t in range(sg.tile_count(sg.VARIANT_MFMA16))]
+    cands.append((sg.VARIANT_GENERIC16, 0))
+    results = []
+    for variant, tile in cands:
+        kw = {} if variant == sg.VARIANT_AUTO else dict(variant=variant, tile=tile)
+        try:
+            C.fill_(float("nan"))
+            sg.gemm_mixed(A, W, C, trans_b=True, **kw)
+            torch.cuda.synchronize()
+        except sg.SgemmError:
+            continue
+        if not agree(torch, C, ref, K, 1.0, 1.0):
+            print(f"  rejected v{variant} t{tile}: output differs", flush=True)
+            continue
+        call_i = lambda i, kw=kw: sg.gemm_mixed(A, W, C, trans_b=True, **kw)
+        # the first timing of a process runs slower (clock and power ramp):
+        # one untimed graph replay first
+        time_graph(torch, call_i, reps, replays=1)
+        ms = statistics.median(time_graph(torch, call_i, reps))
+        gf = 2.0 * M * N * K / (ms / 1e3) / 1e9
+        results.append({"variant": variant, "tile": tile, "inputs": dtype, "ms": round(ms, 5),
+                        "gflops": round(gf, 1), "eff_pct": round(100 * gf / PEAK_16BIT_GFLOPS, 1),
+                        "desc": (sg.tile_info(variant, tile) if variant == sg.VARIANT_MFMA16
+                                 else {})})
+        print(f"  v{variant} t{tile}: {ms:.4f} ms  {gf:,.0f} GFLOP/s  "
+              f"{100 * gf / PEAK_16BIT_GFLOPS:.1f} %", flush=True)
     results.sort(key=lambda r: r["ms"])
     return results
 
@@ -212,6 +315,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time calls replayed from a HIP graph (no host launch gaps; for "
                          "shapes whose kernels are shorter than the host launch path)")
+    ap.add_argument("--mixed", choices=["bf16", "f16"], default=None,
+                    help="time the 16-bit-input tiles (sgemm_mixed, W stored N x K) instead")
     ap.add_argument("--out", default=None)
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--from-json", default=None,
@@ -234,6 +339,10 @@ def main():
     report, best = {}, {}
     for (M, N, K) in shapes:
         print(f"shape {M}x{N}x{K}", flush=True)
+        if args.mixed:
+            report[f"{M}x{N}x{K}"] = tune_mixed(sg, torch, M, N, K, args.mixed, args.reps)
+            torch.cuda.empty_cache()
+            continue
         res = tune_shape(sg, torch, M, N, K, args.warmup, args.reps, args.groups,
                          rotate=args.rotate, graph=args.graph)
         report[f"{M}x{N}x{K}"] = res
@@ -245,7 +354,7 @@ def main():
     if args.out:
         with open(args.out, "w") as fh:
             json.dump(report, fh, indent=1)
-    if args.write_table:
+    if args.write_table and not args.mixed:
         write_table(best)
 
 

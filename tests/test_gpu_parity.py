@@ -532,10 +532,10 @@ def test_workload_full_size(name, oracle_mod):
     A, B, C0 = workloads.inputs(w)
     C = run_gpu(A, B, C0, w.alpha, w.beta)
     exact = w.dist == "int4"
-    flops_per_row = 2 * w.N * w.K
-    rows = None if w.M * flops_per_row <= 4e9 else sample_rows(w.M, max(8, int(2e9 // flops_per_row)))
-    r = check(A, B, C0, w.alpha, w.beta, C, oracle_mod, rows=rows, exact=exact, label=name)
-    print(f"{name}: max err/tol = {r:.3g} on {'all' if rows is None else len(rows)} rows")
+    # the whole of C: the largest (mlp_up, mlp_down, sweep8192, ~1 TFLOP each)
+    # take the multithreaded oracle about ten seconds on the GPU machine's host
+    r = check(A, B, C0, w.alpha, w.beta, C, oracle_mod, exact=exact, label=name)
+    print(f"{name}: max err/tol = {r:.3g} on all {w.M} rows", flush=True)
     assert np.all(np.isfinite(C))
 
 
@@ -567,6 +567,63 @@ def test_fp32_probe_bit_exact(oracle_mod):
     for variant in (sg.VARIANT_AUTO, sg.VARIANT_MFMA, sg.VARIANT_VALU):
         C = run_gpu(A, B, None, 1.0, 0.0, variant=variant)
         check(A, B, None, 1.0, 0.0, C, oracle_mod, exact=True, label=f"probe v{variant}")
+
+
+def probe_inputs(M, N, K, seed):
+    """The precision probe's draws at another shape: A = n * 2^-16 with
+    |n| <= 2^16 (17 significant bits), B in {-1, 0, 1}.  With K <= 256 every
+    partial sum is a multiple of 2^-16 below 2^8 in magnitude, exact in fp32
+    whatever the order, and inexact if either input were rounded to a format
+    with fewer significant bits (tf32, bf16, fp16)."""
+    assert K <= 256
+    return workloads.draw(M, N, K, "probe", seed, False)[:2]
+
+
+def test_fp32_probe_every_kernel(oracle_mod):
+    """The probe through every compiled fp32 kernel, bit for bit: each MFMA
+    tile (the transposed-A tiles on A stored K x M, the others also with B
+    stored N x K where they serve it), forced stream-K, each VALU tile, each
+    few-rows skinny tile (split over K and not) and each few-columns tile."""
+    M, N, K = 512, 512, 256
+    A, B = probe_inputs(M, N, K, 41)
+    ref = oracle_mod.sgemm(A, B)
+    At, Bt = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    for tile in tiles(sg.VARIANT_MFMA):
+        d = sg.tile_info(sg.VARIANT_MFMA, tile)
+        kw = dict(variant=sg.VARIANT_MFMA, tile=tile)
+        ta = bool(d["flags"] & sg.TILE_TRANS_A)
+        for tb in (False, True):
+            if tb and not d["flags"] & (sg.TILE_TRANS_B | sg.TILE_TRANS_A):
+                continue
+            C = run_gpu_op(At if ta else A, Bt if tb else B, None, 1.0, 0.0, ta, tb, **kw)
+            assert np.array_equal(C, ref), f"probe: MFMA tile {tile} ta={ta} tb={tb}"
+            if d["flags"] & sg.TILE_STREAMK:
+                # 8 tiles of 256 x 128 (or 4 of 256 x 256), 16 k-steps each,
+                # cut into 256 runs: every tile is split and fixed up
+                C = run_gpu_op(At if ta else A, Bt if tb else B, None, 1.0, 0.0, ta, tb,
+                               flags=sg.FLAG_STREAMK, **kw)
+                assert np.array_equal(C, ref), f"probe: stream-K tile {tile} ta={ta} tb={tb}"
+    for tile in tiles(sg.VARIANT_VALU):
+        C = run_gpu(A, B, None, 1.0, 0.0, variant=sg.VARIANT_VALU, tile=tile)
+        assert np.array_equal(C, ref), f"probe: VALU tile {tile}"
+    for tile in tiles(sg.VARIANT_SKINNY):
+        d = sg.tile_info(sg.VARIANT_SKINNY, tile)
+        if d["tm"] == 0:
+            Ar, Br = probe_inputs(16, 1000, 256, 42)
+            refr = oracle_mod.sgemm(Ar, Br)
+            for tb in (False, True):
+                for slices in (1, 0, 4):
+                    kw = dict(variant=sg.VARIANT_SKINNY, tile=tile, group_m=slices)
+                    C = run_gpu_op(Ar, np.ascontiguousarray(Br.T) if tb else Br, None, 1.0, 0.0,
+                                   False, tb, **kw)
+                    assert np.array_equal(C, refr), \
+                        f"probe: skinny tile {tile} tb={tb} slices={slices}"
+        else:
+            n = min(d["bn"], 16)
+            Ac, Bc = probe_inputs(777, n, 256, 43)
+            refc = oracle_mod.sgemm(Ac, Bc)
+            C = run_gpu(Ac, Bc, None, 1.0, 0.0, variant=sg.VARIANT_SKINNY, tile=tile)
+            assert np.array_equal(C, refc), f"probe: few-columns tile {tile} N={n}"
 
 
 def test_beta_zero_never_reads_c(oracle_mod):
