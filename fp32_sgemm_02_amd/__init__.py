@@ -20,7 +20,7 @@ __all__ = [
     "sgemm_mixed", "gemm", "gemm_batched", "gemm_mixed", "select", "tile_count", "tile_info", "status_string",
     "version", "workspace_release", "plan", "SgemmConfig", "TileDesc", "SgemmError", "LIB_PATH",
     "VARIANT_AUTO", "VARIANT_MFMA", "VARIANT_VALU", "VARIANT_SKINNY", "VARIANT_MFMA16",
-    "VARIANT_GENERIC16", "DTYPE_BF16", "DTYPE_F16", "FLAG_SCALAR_IO", "FLAG_UNTUNED", "FLAG_STREAMK",
+    "VARIANT_GENERIC16", "VARIANT_SMALL", "DTYPE_BF16", "DTYPE_F16", "FLAG_SCALAR_IO", "FLAG_UNTUNED", "FLAG_STREAMK",
     "TILE_WHOLE", "TILE_DIRECT", "TILE_TRANS_B", "TILE_TRANS_A", "TILE_STREAMK",
     "ACT_NONE", "ACT_RELU", "ACT_SILU", "ACT_GELU_ERF", "ACT_GELU_TANH",
 ]
@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp32sgemm.so")
 
 VARIANT_AUTO, VARIANT_MFMA, VARIANT_VALU, VARIANT_SKINNY = 0, 1, 2, 3
-VARIANT_MFMA16, VARIANT_GENERIC16 = 4, 5
+VARIANT_MFMA16, VARIANT_GENERIC16, VARIANT_SMALL = 4, 5, 6
 DTYPE_BF16, DTYPE_F16 = 1, 2
 FLAG_SCALAR_IO = 0x1
 FLAG_UNTUNED = 0x2

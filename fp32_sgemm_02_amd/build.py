@@ -28,7 +28,7 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "workspace.cpp", "scale.hip", "mfma_gemm.hip", "mfma_direct.hip", "mfma_direct_epi.hip",
            "mfma_direct_sk.hip",
            "mfma_direct_ta.hip", "mfma_direct_ta_epi.hip", "mfma_gemm16.hip", "valu_gemm.hip",
-           "skinny_gemm.hip"]
+           "skinny_gemm.hip", "small_gemm.hip"]
 PROBE_SOURCES = ["peak_probes.hip"]
 PROBE_LIB = os.path.join(HERE, "libfp32probes.so")
 

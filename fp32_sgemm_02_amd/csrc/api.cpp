@@ -17,7 +17,7 @@
 namespace sg {
 namespace {
 
-constexpr int kVersion = 400;   // 0.4.0
+constexpr int kVersion = 500;   // 0.5.0
 constexpr int kBadConfig = -13;
 constexpr int kBadTransA = -21;
 constexpr int kBadTransB = -22;
@@ -127,6 +127,7 @@ const TileEntry *family(int variant, int *count) {
     case SGEMM_VARIANT_MFMA: return mfma_family(count);
     case SGEMM_VARIANT_VALU: return valu_tiles(count);
     case SGEMM_VARIANT_SKINNY: return skinny_tiles(count);
+    case SGEMM_VARIANT_SMALL: return small_tiles(count);
     default: *count = 0; return nullptr;
     }
 }
@@ -349,6 +350,8 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
             !lookup_tuned(p.M, p.N, p.K, a)) {
             if (skinny_pick(p) >= 0)
                 a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
+            else if (small_pick(p) >= 0)
+                a = Tuned{SGEMM_VARIANT_SMALL, small_pick(p), 0};
             else
                 a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok, strips, &streamk), 0};
             if (a.tile < 0 && a.variant == SGEMM_VARIANT_MFMA) return kBadConfig;
@@ -364,6 +367,9 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     if (variant == SGEMM_VARIANT_SKINNY) {
         if (tile < 0) tile = skinny_pick(p);
         if (!skinny_fits(tile, p)) return kBadConfig;   // shape is not skinny
+    } else if (variant == SGEMM_VARIANT_SMALL) {
+        if (!small_fits(p)) return kBadConfig;
+        if (tile < 0) tile = small_choice(p);
     } else if (tile < 0) {
         tile = (variant == SGEMM_VARIANT_MFMA) ? default_mfma_tile(p, io_ok) : 0;
     }
@@ -372,8 +378,10 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
         if (explicit_tile || variant != SGEMM_VARIANT_MFMA || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // a tuned row naming a tile that is not compiled
     }
-    // (skinny tiles were checked by skinny_fits; they serve any transposition of B)
-    if (variant != SGEMM_VARIANT_SKINNY && !tile_applies(tiles[tile], pm, io_ok)) {
+    // (skinny and small tiles were checked by skinny_fits / small_fits; they
+    // serve any transposition of B)
+    if (variant != SGEMM_VARIANT_SKINNY && variant != SGEMM_VARIANT_SMALL &&
+        !tile_applies(tiles[tile], pm, io_ok)) {
         if (explicit_tile || trans) return kBadConfig;
         tile = general_mfma_tile(p.M, p.N);   // automatic choice that cannot run here
         if (strips) *strips = Strips{0, 0};
@@ -381,8 +389,8 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
     }
     if (streamk && (variant != SGEMM_VARIANT_MFMA || !tiles[tile].streamk)) return kBadConfig;
     // direct-load and skinny tiles pick 16-byte paths per operand themselves
-    const bool per_operand =
-        (tiles[tile].desc.flags & SGEMM_TILE_DIRECT) || variant == SGEMM_VARIANT_SKINNY;
+    const bool per_operand = (tiles[tile].desc.flags & SGEMM_TILE_DIRECT) ||
+                             variant == SGEMM_VARIANT_SKINNY || variant == SGEMM_VARIANT_SMALL;
     const bool vec = per_operand ? want_vec : io_ok;
     if (!(vec ? tiles[tile].vec : tiles[tile].scalar)) return kBadConfig;
     if (streamk && (!vec || !streamk_ok(p))) return kBadConfig;   // (automatic: never so)

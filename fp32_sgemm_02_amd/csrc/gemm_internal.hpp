@@ -148,6 +148,15 @@ size_t skinny_workspace_bytes(int tile, const Problem &p, int group_m);
 // K slices of a few-rows skinny launch (group_m as passed to its launcher).
 int skinny_slices(int tile, const Problem &p, int group_m);
 
+// Small-product family (small_gemm.hip): its tiles; whether it can run a
+// problem (A untransposed, 31-bit offsets); the tile automatic dispatch
+// gives a problem (-1: leave it to the tiled families); and its tile for a
+// problem it is asked to run without a tile.
+const TileEntry *small_tiles(int *count);
+bool small_fits(const Problem &p);
+int small_pick(const Problem &p);
+int small_choice(const Problem &p);
+
 // C = act(beta * C + bias) over p's batch (beta == 0: C is not read); with
 // no epilogue, C = beta * C.  The alpha == 0 / K == 0 case, and the bias and
 // activation pass after a kernel that does not apply them itself (beta = 1).

@@ -57,8 +57,9 @@ def candidates(sg, M, N, K, sweep_groups: bool):
     """(variant, tile, group_m, flags) to time.  The first is the automatic
     plan without the tuned table (the cost model, edge strips included); when
     it wins, the shape needs no table row.  Then every MFMA tile (and its
-    stream-K form where it has one), every VALU tile, and for skinny shapes
-    every skinny tile (the few-rows ones at each K-slice count)."""
+    stream-K form where it has one), every VALU tile, every small-product
+    tile, and for skinny shapes every skinny tile (the few-rows ones at each
+    K-slice count)."""
     out = [(sg.VARIANT_AUTO, -1, 0, sg.FLAG_UNTUNED)]
     for tile in range(sg.tile_count(sg.VARIANT_MFMA)):
         groups = GROUPS if sweep_groups else (0,)
@@ -68,6 +69,8 @@ def candidates(sg, M, N, K, sweep_groups: bool):
             out.append((sg.VARIANT_MFMA, tile, 0, sg.FLAG_STREAMK))
     for tile in range(sg.tile_count(sg.VARIANT_VALU)):
         out.append((sg.VARIANT_VALU, tile, 0, 0))
+    for tile in range(sg.tile_count(sg.VARIANT_SMALL)):
+        out.append((sg.VARIANT_SMALL, tile, 0, 0))
     if M <= 16 or N <= 16:
         for tile in range(sg.tile_count(sg.VARIANT_SKINNY)):
             rows_kind = sg.tile_info(sg.VARIANT_SKINNY, tile)["tm"] == 0

@@ -94,7 +94,10 @@ enum sgemm_variant {
     SGEMM_VARIANT_SKINNY = 3,  /* memory-bound shapes: M <= 16 or N <= 16 */
     SGEMM_VARIANT_MFMA16 = 4,  /* sgemm_mixed: 16-bit-input matrix-core tiles */
     SGEMM_VARIANT_GENERIC16 = 5, /* sgemm_mixed: the generic 16-bit-input kernel */
-    SGEMM_VARIANT_COUNT = 6
+    SGEMM_VARIANT_SMALL = 6,   /* small products: one wave per 16 x 16 or 16 x 64 block of C,
+                                  operands from memory into registers, optional k-groups;
+                                  A untransposed (either B) */
+    SGEMM_VARIANT_COUNT = 7
 };
 
 /* Input formats of sgemm_mixed. */
@@ -129,7 +132,8 @@ typedef struct sgemm_tile_desc {
     int bm, bn, bk;   /* workgroup tile of C (bm x bn) and K step (bk) */
     int wm, wn;       /* per-wave tile of C */
     int tm, tn;       /* per-lane micro-tile (VALU family; 0 for MFMA); skinny family:
-                         tm = kernel kind (0: few rows of C, 1: few columns) */
+                         tm = kernel kind (0: few rows of C, 1: few columns); small
+                         family: tm = k-groups (waves sharing one block of C over K) */
     int threads;      /* workgroup size */
     int lds_bytes;    /* LDS per workgroup */
     int stages;       /* LDS buffers in the K pipeline (0: no LDS staging) */

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tables():
-    assert sg.version() == 400
+    assert sg.version() == 500
     for v in (sg.VARIANT_MFMA, sg.VARIANT_VALU, sg.VARIANT_SKINNY):
         n = sg.tile_count(v)
         assert n > 0
@@ -228,11 +228,37 @@ def test_automatic_selection():
     assert sg.select(4096, 1, 4096).variant == sg.VARIANT_SKINNY
     assert sg.select(16, 14336, 4096).variant == sg.VARIANT_SKINNY
     # lda = 33 rules out 16-byte A rows: a general tile runs its 4-byte path,
-    # a direct-load or skinny tile picks the width per operand
+    # a direct-load, skinny or small-product tile picks the width per operand
     cfg = sg.select(777, 777, 33, 0x10000, 33)
     d = sg.tile_info(cfg.variant, cfg.tile)
-    assert cfg.flags & sg.FLAG_SCALAR_IO or d["flags"] & sg.TILE_DIRECT
+    assert (cfg.flags & sg.FLAG_SCALAR_IO or d["flags"] & sg.TILE_DIRECT or
+            cfg.variant == sg.VARIANT_SMALL)
     assert sg.select(256, 256, 256, 0x10000, 256, 0x20000, 256, 0x30000, 256).flags == 0
+
+
+def test_small_product_selection():
+    """Fewer than 256 tiles of 64 x 64 (over the batch), at most 1.5 GFLOP,
+    A untransposed: the small-product family, 16 x 64 blocks where B's rows
+    take 16-byte loads and such blocks are many, 16 x 16 blocks otherwise,
+    k-groups for long K; otherwise (or M / N <= 16) another family."""
+    a, b, c = 0x10000, 0x20000, 0x30000
+
+    def pick(M, N, K, **kw):
+        cfg = sg.select(M, N, K, a, K, b, N, c, N, **kw)
+        return cfg.variant, cfg.tile
+
+    assert pick(256, 256, 256) == (sg.VARIANT_SMALL, 0)    # few 16 x 64 blocks: 16 x 16
+    assert pick(384, 384, 384) == (sg.VARIANT_SMALL, 2)
+    assert pick(512, 512, 512) == (sg.VARIANT_SMALL, 2)
+    assert pick(777, 777, 33) == (sg.VARIANT_SMALL, 1)     # N % 4 != 0: 16 x 16 blocks
+    assert pick(256, 256, 4096) == (sg.VARIANT_SMALL, 5)   # long K: 8 k-groups
+    assert pick(512, 512, 2048) == (sg.VARIANT_SMALL, 2)
+    assert pick(64, 64, 64) == (sg.VARIANT_SMALL, 1)       # a few k-steps, few blocks
+    assert pick(1024, 1024, 1024)[0] == sg.VARIANT_MFMA     # 256 tiles of 64 x 64
+    assert pick(768, 768, 65536)[0] == sg.VARIANT_MFMA      # 77 GFLOP: stream-K
+    assert pick(16, 4096, 4096)[0] == sg.VARIANT_SKINNY
+    assert pick(256, 256, 256, trans_a=True)[0] == sg.VARIANT_MFMA
+    assert pick(384, 384, 384, trans_b=True) == (sg.VARIANT_SMALL, 2)
 
 
 def test_cblas_entry_point_validation():
@@ -267,8 +293,9 @@ def test_cblas_entry_point_validation():
 def test_op_plan_covers_transpositions():
     """The automatic plan of a transposed product names a tile that serves
     that transposition: the skinny family on skinny shapes (few rows: any
-    transposition; few columns: A untransposed), else an MFMA tile flagged for
-    it; edge strips only with A untransposed."""
+    transposition; few columns: A untransposed), the small-product family
+    (B either way, A untransposed) on products of few 64 x 64 tiles, else an
+    MFMA tile flagged for it; edge strips only with A untransposed."""
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
         for M, N, K in ((4096, 4096, 4096), (4097, 1000, 3001), (2049, 2048, 64), (37, 45, 5),
                         (1, 4096, 4096), (16, 14336, 4096), (4096, 1, 4096)):
@@ -277,6 +304,10 @@ def test_op_plan_covers_transpositions():
             lab = (ta, tb, M, N, K)
             if M <= 16 or (N <= 16 and not ta):
                 assert cfg.variant == sg.VARIANT_SKINNY, lab
+                continue
+            if cfg.variant == sg.VARIANT_SMALL:
+                assert not ta and (M // 64 + 1) * (N // 64 + 1) < 300, lab
+                assert sg.tile_info(sg.VARIANT_SMALL, cfg.tile)["flags"] & sg.TILE_TRANS_B, lab
                 continue
             assert cfg.variant == sg.VARIANT_MFMA, lab
             f = sg.tile_info(sg.VARIANT_MFMA, cfg.tile)["flags"]

@@ -583,7 +583,8 @@ def test_fp32_probe_every_kernel(oracle_mod):
     """The probe through every compiled fp32 kernel, bit for bit: each MFMA
     tile (the transposed-A tiles on A stored K x M, the others also with B
     stored N x K where they serve it), forced stream-K, each VALU tile, each
-    few-rows skinny tile (split over K and not) and each few-columns tile."""
+    few-rows skinny tile (split over K and not), each few-columns tile and
+    each small-product tile."""
     M, N, K = 512, 512, 256
     A, B = probe_inputs(M, N, K, 41)
     ref = oracle_mod.sgemm(A, B)
@@ -624,6 +625,11 @@ def test_fp32_probe_every_kernel(oracle_mod):
             refc = oracle_mod.sgemm(Ac, Bc)
             C = run_gpu(Ac, Bc, None, 1.0, 0.0, variant=sg.VARIANT_SKINNY, tile=tile)
             assert np.array_equal(C, refc), f"probe: few-columns tile {tile} N={n}"
+    for tile in tiles(sg.VARIANT_SMALL):
+        for tb in (False, True):
+            C = run_gpu_op(A, Bt if tb else B, None, 1.0, 0.0, False, tb,
+                           variant=sg.VARIANT_SMALL, tile=tile)
+            assert np.array_equal(C, ref), f"probe: small tile {tile} tb={tb}"
 
 
 def test_beta_zero_never_reads_c(oracle_mod):

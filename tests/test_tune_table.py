@@ -31,7 +31,7 @@ def test_shipped_table_parses_and_names_compiled_tiles():
     rows = tune.read_table()
     assert (4096, 4096, 4096) in rows
     for shape, r in rows.items():
-        assert r["variant"] in (1, 2, 3), shape
+        assert r["variant"] in (1, 2, 3, 6), shape
         assert 0 <= r["tile"] < sg.tile_count(r["variant"]), f"{shape}: tile {r['tile']} not compiled"
         # the tuned row is what automatic dispatch picks for aligned operands
         M, N, K = shape
