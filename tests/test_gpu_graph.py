@@ -73,3 +73,39 @@ def test_graph_replays_match_eager():
         # the program's own eager work between replays
         x = torch.randn(1000, device=DEV)
         float((x * x).sum())
+
+
+
+def test_graph_edge_strips(oracle_mod):
+    """A plan with edge strips (4097 x 1000 x 301: the last row by the skinny
+    family in a second launch) captured in a graph: every replay, with eager work between replays, reproduces the
+    eager result, which matches the oracle bit for bit (integer inputs)."""
+    M, N, K = 4097, 1000, 301
+    A, B, C0 = workloads.draw(M, N, K, "int4", 960, True)
+    dA, dB, dC0 = _dev(A), _dev(B), _dev(C0)
+    assert sg.plan(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC0.data_ptr(), N)[1] == 1
+    ref = oracle_mod.sgemm(A, B, C0.copy(), 0.5, -1.25)
+    C = dC0.clone()
+    sg.gemm(dA, dB, C, 0.5, -1.25)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), ref), "eager"
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        C.copy_(dC0)
+        sg.gemm(dA, dB, C, 0.5, -1.25)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        C.copy_(dC0)
+        sg.gemm(dA, dB, C, 0.5, -1.25)
+    for rep in range(3):
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), ref), f"replay {rep}"
+        x = torch.randn(1000, device=DEV)
+        float((x * x).sum())
+    del g
