@@ -345,8 +345,11 @@ constexpr int kMaxSplitStrips = kWorkspaceCounters;
 // grid within about one workgroup per CU (measured best over M = 1..16,
 // N = 256..14336, K = 3001..16384: HBM is saturated only while every CU
 // streams, and a second round of workgroups costs more than it balances),
-// with every wave still running two rounds of loads or more and the partial
-// sums (written and read once) under ~3 % of B's bytes.
+// with every wave still running two rounds of loads or more where that leaves
+// 128 workgroups or more (1 x 256 x 16384: 32 slices 8.7 us, 64 slices 10.6;
+// 1 x 512 x 8192: 16 slices 8.1 us, 32 slices 9.2), else one round at least
+// (the one-row edge strip of 4097 x 1000 x 3001: 11 slices 7.8 us, 5 slices
+// 9.2), and the partial sums (written and read once) under ~3 % of B's bytes.
 template <int Q, int WK, int U>
 int rows_slices(const Problem &p, int want) {
     using S = RowsShape<Q, WK, U>;
@@ -359,7 +362,8 @@ int rows_slices(const Problem &p, int want) {
         if (s > (chunks + WK - 1) / WK) s = (chunks + WK - 1) / WK;
     } else {
         s = 256 / strips;
-        const long long rounds = chunks / (2LL * WK * U);
+        const long long two = chunks / (2LL * WK * U), one = chunks / ((long long)WK * U);
+        const long long rounds = strips * two >= 128 ? two : one;
         if (s > rounds) s = rounds;
         const long long by_bytes = (long long)(0.015 * p.K / (p.M > 0 ? p.M : 1));
         if (s > by_bytes) s = by_bytes;

@@ -268,6 +268,44 @@ def rows_tiles():
             if sg.tile_info(sg.VARIANT_SKINNY, t)["tm"] == 0]
 
 
+def test_workspace_per_thread_default_stream(oracle_mod):
+    """Two host threads running split-K plans on the per-thread default stream
+    (hipStreamPerThread: one handle value, a different stream on each host
+    thread) at the same time, with different workspace sizes: each thread
+    keeps its own workspace, and every result matches the oracle bit for bit."""
+    import threading
+
+    per_thread = 2   # the handle value of hipStreamPerThread
+    cases = [(1, 4096, 4096, 31), (3, 2048, 8192, 32)]
+    data = []
+    for M, N, K, seed in cases:
+        assert sg.plan(M, N, K)[0].group_m > 1, f"{(M, N, K)} is no longer split"
+        A, B, _ = workloads.draw(M, N, K, "int4", seed, False)
+        data.append((dev(A), dev(B), torch.full((M, N), float("nan"), device=DEV),
+                     oracle_mod.sgemm(A, B)))
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            torch.cuda.set_device(0)
+            dA, dB, C, _ = data[i]
+            for _ in range(20):
+                sg.gemm(dA, dB, C, stream=per_thread)
+        except Exception as ex:   # reported by the main thread
+            errors.append(ex)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(data))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (M, N, K, _), (_, _, C, ref) in zip(cases, data):
+        assert np.array_equal(C.cpu().numpy(), ref), f"{(M, N, K)} per-thread stream"
+
+
 @pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
 @pytest.mark.parametrize("tile", range(6))
 def test_skinny_split_k(tile, ta, tb, oracle_mod):
