@@ -240,51 +240,18 @@ __device__ __forceinline__ float wave_sum(const floatx4 (&red)[WK][4 * Q][64], i
     return sum;
 }
 
-// Each wave walks its chunks of a strip segment in rounds of U with two
-// register sets: the loads of round r + 1 are issued before the MFMAs of
-// round r, so a round's memory latency overlaps the previous round's
-// arithmetic (chunks past the segment read as zero and touch no memory).
-//
-// Partial sums are written and read as device-coherent (agent-scope)
-// accesses, which bypass the per-XCD caches that are not coherent with each
-// other; every wave waits for its stores to complete before the workgroup
-// counts its arrival, so the workgroup that counts last finds every partial
-// sum in memory.  (A release fence would also write back each XCD's whole L2,
-// once per wave: measured to cost more than the split saves.)
-template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0>
-__global__ void __launch_bounds__(64 * WK) rows_kernel(Problem p, RowsGrid grid) {
-    static_assert(IN == 0 || (TB && !TA), "16-bit inputs: B transposed (word form)");
-    using S = RowsShape<Q, WK, U>;
-    __shared__ floatx4 red[WK][S::ACC][64];
-    __shared__ int last;
-    select_batch(p);
-    // the wave index is uniform over the wave: in a scalar register, so the
-    // buffer resources built from it are too
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int i = lane & 15, g = lane >> 4;
-    const int strip = blockIdx.x % grid.strips, slice = blockIdx.x / grid.strips;
-    const int n0 = strip * S::COLS, ncols = min(S::COLS, p.N - n0);
-    const int kb = slice * grid.kslice, ke = min(p.K, kb + grid.kslice);
-    const int c1 = (ke - kb + 15) / 16;   // chunks of the slice
-
-    floatx4 acc[S::ACC];
+// The end of a few-rows workgroup: the waves' sums meet in LDS (red), then
+// the workgroup stores its cells of C (one slice), or its partial sums, and
+// the last workgroup of the strip to arrive adds the slices in order.
+template <int Q, int WK>
+__device__ __forceinline__ void rows_finish(const Problem &p, const RowsGrid &grid,
+                                            floatx4 (&red)[WK][4 * Q][64], int &last,
+                                            const floatx4 (&acc)[4 * Q], int tid, int strip,
+                                            int slice, int n0, int ncols) {
+    using S = RowsShape<Q, WK, 1>;
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int a = 0; a < S::ACC; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // wave w takes the groups of U consecutive chunks w, w + WK, ...
-    const int groups = (c1 + U - 1) / U;
-    RowsRound<Q, U> r0, r1;
-    rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * wave, i, g, r0);
-    for (int j = wave; j < groups; j += 2 * WK) {
-        rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * (j + WK), i, g, r1);
-        pipeline_fence();
-        rows_mfma<Q, U, TB, IN>(r0, acc);
-        if (j + WK >= groups) break;
-        rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * (j + 2 * WK), i, g, r0);
-        pipeline_fence();
-        rows_mfma<Q, U, TB, IN>(r1, acc);
-    }
-#pragma unroll
-    for (int a = 0; a < S::ACC; ++a) red[wave][a][lane] = acc[a];
+    for (int a = 0; a < 4 * Q; ++a) red[wave][a][lane] = acc[a];
     __syncthreads();
     const int cells = p.M * S::COLS;
     if (grid.slices == 1) {
@@ -333,6 +300,153 @@ __global__ void __launch_bounds__(64 * WK) rows_kernel(Problem p, RowsGrid grid)
     }
     if (tid == 0)   // ready for the next launch on the stream
         __hip_atomic_store(grid.count + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Each wave walks its chunks of a strip segment in rounds of U with two
+// register sets: the loads of round r + 1 are issued before the MFMAs of
+// round r, so a round's memory latency overlaps the previous round's
+// arithmetic (chunks past the segment read as zero and touch no memory).
+//
+// Partial sums are written and read as device-coherent (agent-scope)
+// accesses, which bypass the per-XCD caches that are not coherent with each
+// other; every wave waits for its stores to complete before the workgroup
+// counts its arrival, so the workgroup that counts last finds every partial
+// sum in memory.  (A release fence would also write back each XCD's whole L2,
+// once per wave: measured to cost more than the split saves.)
+template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0>
+__global__ void __launch_bounds__(64 * WK) rows_kernel(Problem p, RowsGrid grid) {
+    static_assert(IN == 0 || (TB && !TA), "16-bit inputs: B transposed (word form)");
+    using S = RowsShape<Q, WK, U>;
+    __shared__ floatx4 red[WK][S::ACC][64];
+    __shared__ int last;
+    select_batch(p);
+    // the wave index is uniform over the wave: in a scalar register, so the
+    // buffer resources built from it are too
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int strip = blockIdx.x % grid.strips, slice = blockIdx.x / grid.strips;
+    const int n0 = strip * S::COLS, ncols = min(S::COLS, p.N - n0);
+    const int kb = slice * grid.kslice, ke = min(p.K, kb + grid.kslice);
+    const int c1 = (ke - kb + 15) / 16;   // chunks of the slice
+
+    floatx4 acc[S::ACC];
+#pragma unroll
+    for (int a = 0; a < S::ACC; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // wave w takes the groups of U consecutive chunks w, w + WK, ...
+    const int groups = (c1 + U - 1) / U;
+    RowsRound<Q, U> r0, r1;
+    rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * wave, i, g, r0);
+    for (int j = wave; j < groups; j += 2 * WK) {
+        rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * (j + WK), i, g, r1);
+        pipeline_fence();
+        rows_mfma<Q, U, TB, IN>(r0, acc);
+        if (j + WK >= groups) break;
+        rows_load<Q, WK, U, VA, VB, TA, TB>(p, ke, n0, ncols, kb + 16 * U * (j + 2 * WK), i, g, r0);
+        pipeline_fence();
+        rows_mfma<Q, U, TB, IN>(r1, acc);
+    }
+    rows_finish<Q, WK>(p, grid, red, last, acc, tid, strip, slice, n0, ncols);
+}
+
+// B stored transposed, staged through LDS (64 columns, four waves, rounds of
+// four 16-row k-chunks).  Loading B^T straight into the MFMA layout gives
+// each column's row of B^T to four lanes, 64 contiguous bytes per row and
+// load; here each wave copies its round (64 rows of B^T and the <= 16 rows of
+// A, 64 k each) into LDS buffers of its own with direct global-to-LDS loads in
+// which 16 lanes read 256 contiguous bytes of one row, then reads its MFMA
+// operands from LDS.  Row r of a B buffer holds the 16 four-float pieces of
+// its 64 k in slots piece ^ (r >> 2), row r of an A buffer in slots
+// piece ^ r, so that the 16 lanes of an operand read (B rows 4i + c, A rows
+// i, one piece each) hit 16 different slots: no bank conflicts.  Two buffers
+// per wave: round j + 1 is in flight while round j is consumed.  Every load
+// of the loop goes to LDS, so the only waits are the wave's own counts of
+// its loads (no barrier in the loop); a buffer is refilled only after the
+// MFMAs that used its previous contents, which waited for their LDS reads.
+constexpr int kStagedFloats = 64 * 64 + 16 * 64;   // one round: B^T, then A
+
+// Issue round kr .. kr + 63 of the slice ending at ke into `buf`.
+__device__ __forceinline__ void staged_issue(const Problem &p, float *buf, int n0, int ncols,
+                                             int kr, int ke, int lane) {
+    const int ldb = (int)p.ldb, lda = (int)p.lda, krem = ke - kr;
+    const int rsub = lane >> 4, slot = lane & 15;
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(p.B + (long long)n0 * p.ldb + kr, 4 * ((long long)(ncols - 1) * p.ldb + krem));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int r = 4 * q + rsub, k = 4 * (slot ^ q);
+        const int off = (r < ncols && k < krem) ? (r * ldb + k) * 4 : kOff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void *)(buf + 256 * q), 16, off, 0, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + kr, 4 * ((long long)(p.M - 1) * p.lda + krem));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 4 * q + rsub, k = 4 * (slot ^ r);
+        const int off = (r < p.M && k < krem) ? (r * lda + k) * 4 : kOff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void *)(buf + 64 * 64 + 256 * q), 16, off, 0, 0,
+            0);
+    }
+}
+
+// The MFMAs of the round in `buf`, once its loads have landed (the 20 loads
+// of the next round may still be in flight).
+__device__ __forceinline__ void staged_consume(const float *buf, int lane, floatx4 (&acc)[4]) {
+    __builtin_amdgcn_s_waitcnt((20 & 15) | ((20 >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    const int i = lane & 15, g = lane >> 4;
+    RowsRound<1, 4> r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        r.a[u] = *reinterpret_cast<const floatx4 *>(buf + 64 * 64 + i * 64 + 4 * ((4 * u + g) ^ i));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int row = 4 * i + c, slot = (4 * u + g) ^ i;
+            r.b[u][c][0] = *reinterpret_cast<const floatx4 *>(buf + row * 64 + 4 * slot);
+        }
+    }
+    rows_mfma<1, 4, true, 0>(r, acc);
+}
+
+template <int WK>
+__global__ void __launch_bounds__(64 * WK) rows_tb_staged_kernel(Problem p, RowsGrid grid) {
+    using S = RowsShape<1, WK, 4>;
+    // two buffers per wave, as separate arrays so that the compiler can tell a
+    // read of one from the direct loads into the other; the waves' sums (and
+    // the arrival flag) reuse the first array after the loop
+    __shared__ __attribute__((aligned(1024))) float stage0[WK][kStagedFloats];
+    __shared__ __attribute__((aligned(1024))) float stage1[WK][kStagedFloats];
+    static_assert(sizeof(floatx4) * WK * S::ACC * 64 + 16 <= sizeof(float) * WK * kStagedFloats,
+                  "the waves' sums fit the first buffer array");
+    select_batch(p);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int strip = blockIdx.x % grid.strips, slice = blockIdx.x / grid.strips;
+    const int n0 = strip * S::COLS, ncols = min(S::COLS, p.N - n0);
+    const int kb = slice * grid.kslice, ke = min(p.K, kb + grid.kslice);
+    const int c1 = (ke - kb + 15) / 16;
+
+    floatx4 acc[S::ACC];
+#pragma unroll
+    for (int a = 0; a < S::ACC; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float *buf0 = stage0[wave], *buf1 = stage1[wave];
+    const int groups = (c1 + 3) / 4;   // rounds of 64 k; wave w takes w, w + WK, ...
+    staged_issue(p, buf0, n0, ncols, kb + 64 * wave, ke, lane);
+    for (int j = wave; j < groups; j += 2 * WK) {
+        staged_issue(p, buf1, n0, ncols, kb + 64 * (j + WK), ke, lane);
+        pipeline_fence();
+        staged_consume(buf0, lane, acc);
+        if (j + WK >= groups) break;
+        staged_issue(p, buf0, n0, ncols, kb + 64 * (j + 2 * WK), ke, lane);
+        pipeline_fence();
+        staged_consume(buf1, lane, acc);
+    }
+    // every wave's last (zero-filling) loads have landed before the buffers
+    // are reused for the sums
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto &red = *reinterpret_cast<floatx4 (*)[WK][S::ACC][64]>(&stage0[0][0]);
+    int &last = *reinterpret_cast<int *>(&red[WK - 1][S::ACC - 1][63] + 1);
+    rows_finish<1, WK>(p, grid, red, last, acc, tid, strip, slice, n0, ncols);
 }
 
 // Counters of the workspace: one per strip, so a split launch has at most
@@ -395,14 +509,25 @@ size_t rows_workspace(const Problem &p, int group_m) {
     return slices == 1 ? 0 : (size_t)slices * p.M * p.N * 4;
 }
 
-template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0>
+// ST: the LDS-staged kernel for B stored transposed (Q = 1, WK = 4, U = 4,
+// 16-byte rows of A and B, fp32).
+template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0, bool ST = false>
 hipError_t launch_rows_as(const Problem &p, int want_slices, hipStream_t stream) {
     using S = RowsShape<Q, WK, U>;
+    static_assert(!ST || (Q == 1 && WK == 4 && U == 4 && VA && VB && TB && !TA && IN == 0),
+                  "staged kernel: 64 columns, 4 waves, A and B^T in 16-byte rows");
+    auto launch = [&](dim3 grid_dim, const RowsGrid &grid) {
+        if constexpr (ST)
+            hipLaunchKernelGGL((rows_tb_staged_kernel<WK>), grid_dim, dim3(S::NT), 0, stream, p,
+                               grid);
+        else
+            hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>), grid_dim, dim3(S::NT),
+                               0, stream, p, grid);
+    };
     RowsGrid grid{(p.N + S::COLS - 1) / S::COLS, 1, 0, nullptr, nullptr};
     grid.kslice = rows_kslice<Q, WK, U>(p, want_slices, &grid.slices);
     if (grid.slices == 1) {
-        hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>), dim3(grid.strips, p.batch),
-                           dim3(S::NT), 0, stream, p, grid);
+        launch(dim3(grid.strips, p.batch), grid);
         return hipGetLastError();
     }
     Workspace w;
@@ -410,8 +535,7 @@ hipError_t launch_rows_as(const Problem &p, int want_slices, hipStream_t stream)
     if (e != hipSuccess) return e;
     grid.part = static_cast<float *>(w.ptr);
     grid.count = w.counters;
-    hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>),
-                       dim3(grid.strips * grid.slices), dim3(S::NT), 0, stream, p, grid);
+    launch(dim3(grid.strips * grid.slices), grid);
     e = hipGetLastError();
     const hipError_t f = workspace_release(w, stream);
     return e != hipSuccess ? e : f;
@@ -419,6 +543,10 @@ hipError_t launch_rows_as(const Problem &p, int want_slices, hipStream_t stream)
 
 template <int Q, int WK, int U, bool TA, bool TB>
 hipError_t launch_rows_ab(const Problem &p, int groups, bool va, bool vb, hipStream_t stream) {
+    if constexpr (Q == 1 && WK == 4 && U == 4 && TB && !TA) {
+        // A and B^T in 16-byte rows: staged through LDS (256-byte row runs per load)
+        if (va && vb) return launch_rows_as<1, 4, 4, true, true, false, true, 0, true>(p, groups, stream);
+    }
     if (va && vb) return launch_rows_as<Q, WK, U, true, true, TA, TB>(p, groups, stream);
     if (va) return launch_rows_as<Q, WK, U, true, false, TA, TB>(p, groups, stream);
     if (vb) return launch_rows_as<Q, WK, U, false, true, TA, TB>(p, groups, stream);
@@ -714,14 +842,22 @@ bool skinny_fits(int tile, const Problem &p) {
 namespace {
 
 // Few-rows tile choice (measured with operands rotated past the Infinity
-// Cache, graph-replayed): 128-column strips of 8 waves where many rows of
-// A would otherwise be re-read per 64 columns of B (M > 4, wide N); 64-column
-// strips otherwise, 16 waves for narrow products (few strips, split deeply)
-// and 4 waves (several workgroups per CU) for the rest.  Few columns: the
+// Cache, graph-replayed): B stored transposed with 16-byte rows, the
+// LDS-staged 64-column tile; otherwise 128-column strips of 8 waves where
+// many rows of A would otherwise be re-read per 64 columns of B (M > 4, wide
+// N); 64-column strips otherwise, 16 waves for narrow products (few strips,
+// split deeply) and 4 waves (several workgroups per CU) for the rest.  Few columns: the
 // narrowest tile that holds N.
 int choose_skinny(const Problem &p) {
     const int M = p.M, N = p.N;
     if (M <= 16) {
+        // B stored N x K in 16-byte rows (and A too): the LDS-staged kernel
+        // (16 x 14336 x 4096: 49.6 us against 54.9 for the 64-column tile
+        // loading B^T straight into registers)
+        if (p.trans_b && !p.trans_a && p.K % 4 == 0 &&
+            rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
+            rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4))
+            return 4;
         if (!p.trans_b && M > 4 && N >= 8192) return 0;
         return N <= 2048 ? 3 : 2;
     }

@@ -14,7 +14,7 @@ import pytest
 
 import fp32_sgemm_02_amd as sg
 import workloads
-from parity import max_err_ratio, sample_rows
+from parity import epilogue_err_ratio, max_err_ratio, sample_rows
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -471,6 +471,53 @@ def test_skinny_tiles(tile, oracle_mod):
         Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 300 + i, True)
         C = run_gpu(Ai, Bi, Ci, 0.5, -1.25, **kw)
         check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=f"skinny t{tile} int")
+
+
+def staged_tile():
+    """The few-rows tile of 64 columns, 4 waves and 4 chunks per round: with B
+    stored transposed and 16-byte rows of A and B it runs the LDS-staged kernel."""
+    for t in tiles(sg.VARIANT_SKINNY):
+        d = sg.tile_info(sg.VARIANT_SKINNY, t)
+        if d["tm"] == 0 and d["bn"] == 64 and d["threads"] == 256 and d["bk"] == 64:
+            return t
+    return None
+
+
+@pytest.mark.parametrize("slices", [1, 0, 3, 8])
+def test_skinny_staged_transposed_b(slices, oracle_mod):
+    """Few rows with B stored N x K through the LDS-staged kernel: ragged
+    strips (N not a multiple of 64), K not a multiple of the 64-k round, one
+    to sixteen rows, split over K or not; integer inputs bit for bit,
+    uniform inputs within tolerance, bias + activation, and two calls alike."""
+    tile = staged_tile()
+    if tile is None:
+        pytest.skip("no 64-column 4-wave tile with 4 chunks per round")
+    for i, (M, N, K) in enumerate([(16, 4100, 336), (1, 1000, 3004), (7, 64, 4096),
+                                   (16, 2048, 4096), (3, 200, 68), (11, 130, 1028)]):
+        kw = dict(variant=sg.VARIANT_SKINNY, tile=tile, group_m=slices)
+        lab = f"staged t{tile} s{slices} {(M, N, K)}"
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 3100 + i, True)
+        Bt = np.ascontiguousarray(Bi.T)
+        C = run_gpu_op(Ai, Bt, Ci, 0.5, -1.25, False, True, **kw)
+        check_op(Ai, Bt, Ci, 0.5, -1.25, C, False, True, oracle_mod, exact=True, label=lab + " int")
+        C2 = run_gpu_op(Ai, Bt, Ci, 0.5, -1.25, False, True, **kw)
+        assert np.array_equal(C, C2), f"{lab}: two calls differ"
+        A, B, C0 = uniform(M, N, K, 3200 + i)
+        Bt = np.ascontiguousarray(B.T)
+        check_op(A, Bt, C0, 1.0, 0.0, run_gpu_op(A, Bt, None, 1.0, 0.0, False, True, **kw),
+                 False, True, oracle_mod, label=lab)
+    M, N, K = 9, 300, 512
+    A, B, C0 = uniform(M, N, K, 3300)
+    Bt = np.ascontiguousarray(B.T)
+    bias = np.random.default_rng(3301).uniform(-1, 1, N).astype(F32)
+    C = dev(C0)
+    sg.gemm(dev(A), dev(Bt), C, 1.0, 0.5, trans_b=True, bias=dev(bias), act=sg.ACT_SILU,
+            variant=sg.VARIANT_SKINNY, tile=tile, group_m=slices)
+    torch.cuda.synchronize()
+    ref = oracle_mod.sgemm(A, Bt, C0.copy(), 1.0, 0.5, trans_b=True, bias=bias, act=sg.ACT_SILU)
+    x = oracle_mod.sgemm(A, Bt, C0.copy(), 1.0, 0.5, trans_b=True, bias=bias, act=sg.ACT_NONE)
+    r = epilogue_err_ratio(C.cpu().numpy(), ref, x, K, 1.0, 0.5, A, Bt, C0, bias, sg.ACT_SILU)
+    assert r <= 1.0, f"staged epilogue: {r}"
 
 
 @pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
