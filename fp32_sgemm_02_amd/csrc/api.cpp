@@ -562,8 +562,8 @@ int pick_tile16(const Problem &pw) {
 // unknown dtype.  The matrix-core tiles serve A untransposed with B
 // transposed when K, lda, ldb are even and A, B 4-byte aligned (the operands
 // are then word matrices along k), and so does the few-rows skinny kernel
-// for M <= 8 (automatic choice only); everything else runs the generic
-// kernel.
+// for M <= 8, or M <= 16 with 16-byte rows of A and B (automatic choice
+// only); everything else runs the generic kernel.
 int run16(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha, const void *A,
           int lda, const void *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
           const sgemm_config *cfg) {
@@ -597,9 +597,14 @@ int run16(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
                static_cast<const float *>(B), ldb / 2, C, ldc};
     pw.trans_b = 1;
     if (variant == SGEMM_VARIANT_AUTO) {
-        // up to 8 rows in word form: the skinny kernel streams W once (at
-        // 16 rows the 64 x 64 k-group tile was measured faster)
-        if (mfma_ok && M <= 8) return to_status(launch_skinny16(dtype, pw, stream));
+        // few rows in word form: the skinny kernel streams W once; up to 8
+        // rows with any word layout, up to 16 where A and W rows take
+        // 16-byte loads (the LDS-staged kernel; with 4-byte loads the 64 x 64
+        // k-group tile was measured faster at 16 rows)
+        const bool staged = pw.K % 4 == 0 && rows_aligned(pw.A, pw.lda, 0, 1, 4) &&
+                            rows_aligned(pw.B, pw.ldb, 0, 1, 4);
+        if (mfma_ok && (M <= 8 || (M <= 16 && staged)))
+            return to_status(launch_skinny16(dtype, pw, stream));
         variant = (mfma_ok && pick_tile16(pw) >= 0) ? SGEMM_VARIANT_MFMA16
                                                     : SGEMM_VARIANT_GENERIC16;
     }

@@ -390,7 +390,9 @@ __device__ __forceinline__ void staged_issue(const Problem &p, float *buf, int n
 }
 
 // The MFMAs of the round in `buf`, once its loads have landed (the 20 loads
-// of the next round may still be in flight).
+// of the next round may still be in flight).  IN: input format as in
+// rows_mfma (16-bit inputs in word form: k counts 32-bit words).
+template <int IN>
 __device__ __forceinline__ void staged_consume(const float *buf, int lane, floatx4 (&acc)[4]) {
     __builtin_amdgcn_s_waitcnt((20 & 15) | ((20 >> 4) << 14) | (7 << 4) | (15 << 8));
     asm volatile("" ::: "memory");
@@ -405,10 +407,10 @@ __device__ __forceinline__ void staged_consume(const float *buf, int lane, float
             r.b[u][c][0] = *reinterpret_cast<const floatx4 *>(buf + row * 64 + 4 * slot);
         }
     }
-    rows_mfma<1, 4, true, 0>(r, acc);
+    rows_mfma<1, 4, true, IN>(r, acc);
 }
 
-template <int WK>
+template <int WK, int IN>
 __global__ void __launch_bounds__(64 * WK) rows_tb_staged_kernel(Problem p, RowsGrid grid) {
     using S = RowsShape<1, WK, 4>;
     // two buffers per wave, as separate arrays so that the compiler can tell a
@@ -434,11 +436,11 @@ __global__ void __launch_bounds__(64 * WK) rows_tb_staged_kernel(Problem p, Rows
     for (int j = wave; j < groups; j += 2 * WK) {
         staged_issue(p, buf1, n0, ncols, kb + 64 * (j + WK), ke, lane);
         pipeline_fence();
-        staged_consume(buf0, lane, acc);
+        staged_consume<IN>(buf0, lane, acc);
         if (j + WK >= groups) break;
         staged_issue(p, buf0, n0, ncols, kb + 64 * (j + 2 * WK), ke, lane);
         pipeline_fence();
-        staged_consume(buf1, lane, acc);
+        staged_consume<IN>(buf1, lane, acc);
     }
     // every wave's last (zero-filling) loads have landed before the buffers
     // are reused for the sums
@@ -510,16 +512,16 @@ size_t rows_workspace(const Problem &p, int group_m) {
 }
 
 // ST: the LDS-staged kernel for B stored transposed (Q = 1, WK = 4, U = 4,
-// 16-byte rows of A and B, fp32).
+// 16-byte rows of A and B).
 template <int Q, int WK, int U, bool VA, bool VB, bool TA, bool TB, int IN = 0, bool ST = false>
 hipError_t launch_rows_as(const Problem &p, int want_slices, hipStream_t stream) {
     using S = RowsShape<Q, WK, U>;
-    static_assert(!ST || (Q == 1 && WK == 4 && U == 4 && VA && VB && TB && !TA && IN == 0),
+    static_assert(!ST || (Q == 1 && WK == 4 && U == 4 && VA && VB && TB && !TA),
                   "staged kernel: 64 columns, 4 waves, A and B^T in 16-byte rows");
     auto launch = [&](dim3 grid_dim, const RowsGrid &grid) {
         if constexpr (ST)
-            hipLaunchKernelGGL((rows_tb_staged_kernel<WK>), grid_dim, dim3(S::NT), 0, stream, p,
-                               grid);
+            hipLaunchKernelGGL((rows_tb_staged_kernel<WK, IN>), grid_dim, dim3(S::NT), 0, stream,
+                               p, grid);
         else
             hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>), grid_dim, dim3(S::NT),
                                0, stream, p, grid);
@@ -768,7 +770,9 @@ template <int IN>
 hipError_t launch_rows16_as(const Problem &pw, hipStream_t stream) {
     const bool va = rows_aligned(pw.A, pw.lda, pw.stride_a, pw.batch, 4) && pw.K % 4 == 0;
     const bool vb = rows_aligned(pw.B, pw.ldb, pw.stride_b, pw.batch, 4) && pw.K % 4 == 0;
-    if (va && vb) return launch_rows_as<1, 8, 4, true, true, false, true, IN>(pw, 0, stream);
+    // 16-byte rows: the LDS-staged kernel (256-byte runs of each weight row
+    // per load, as for fp32)
+    if (va && vb) return launch_rows_as<1, 4, 4, true, true, false, true, IN, true>(pw, 0, stream);
     return launch_rows_as<1, 8, 4, false, false, false, true, IN>(pw, 0, stream);
 }
 

@@ -319,7 +319,10 @@ int sgemm_strided_batched_ex(int trans_a, int trans_b, int M, int N, int K, floa
  * GEMM Scrapbook".  Arguments after dtype as sgemm_op's.  The matrix-core
  * tiles (family SGEMM_VARIANT_MFMA16) serve trans_a = 0, trans_b = 1 (C = X
  * W^T with W stored N x K) when K, lda and ldb are even and A, B are 4-byte
- * aligned; every other case runs the generic kernel
+ * aligned; automatic dispatch runs such products of at most 8 rows (16
+ * where the rows of A and W take 16-byte loads) through the few-rows kernel
+ * of the skinny family in the same word form, streaming W once; every other
+ * case runs the generic kernel
  * (SGEMM_VARIANT_GENERIC16: 16-bit values decoded to fp32 in LDS, fp32
  * FMAs; correct for any layout, not tuned).  A and B need 2-byte alignment
  * (-5, -7).  Status codes as sgemm_op's, -30 for an unknown dtype, -13 when
