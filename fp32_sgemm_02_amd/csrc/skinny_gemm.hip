@@ -748,8 +748,12 @@ template <int Q, int WK, int U>
 constexpr TileEntry rows_entry() {
     using S = RowsShape<Q, WK, U>;
     // the launchers apply a problem's bias / activation themselves, so the
-    // 16-byte launcher is also the fused one
-    return TileEntry{{16, S::COLS, 16 * U, 16, S::COLS, 0, 0, S::NT, S::LDS_BYTES, 0, 0},
+    // 16-byte launcher is also the fused one; the LDS figure is the larger of
+    // the register kernel's and, for the tile that also runs the LDS-staged
+    // kernel (B stored transposed), that kernel's (all 160 KB)
+    constexpr bool staged = Q == 1 && WK == 4 && U == 4;
+    constexpr int lds = staged ? 2 * WK * kStagedFloats * 4 : S::LDS_BYTES;
+    return TileEntry{{16, S::COLS, 16 * U, 16, S::COLS, 0, 0, S::NT, lds, 0, 0},
                      &launch_rows<Q, WK, U, true>, &launch_rows<Q, WK, U, false>, 0,
                      &launch_rows<Q, WK, U, true>};
 }
