@@ -214,18 +214,26 @@ small_kernel(Problem p, int tiles_n, int cvec) {
     }
 
     // double-buffered rounds of U chunks.  Chunks past c1 read zeros without
-    // touching memory, so the loads are issued unconditionally: a load under
-    // a branch would make the compiler wait for every load in flight at the
-    // join, including the prefetch that should overlap the MFMAs.
+    // touching memory, so the loads inside the loop are issued
+    // unconditionally: a load under a branch would make the compiler wait for
+    // every load in flight at the join, including the prefetch that should
+    // overlap the MFMAs.  A share of at most one round (short K) takes its
+    // one round alone, without the loop's two rounds of prefetch past it; the
+    // branch is uniform and comes before any load is in flight.
     SmallRound<CB, U> r0, r1;
-    small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c0, kend, r0);
-    for (int c = c0; c < c1; c += 2 * U) {
-        small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c + U, kend, r1);
+    if (c1 - c0 <= U) {
+        small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c0, kend, r0);
         small_mma<CB, U, TB>(r0, acc);
-        pipeline_fence();
-        small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c + 2 * U, kend, r0);
-        if (c + U < c1) small_mma<CB, U, TB>(r1, acc);
-        pipeline_fence();
+    } else {
+        small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c0, kend, r0);
+        for (int c = c0; c < c1; c += 2 * U) {
+            small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c + U, kend, r1);
+            small_mma<CB, U, TB>(r0, acc);
+            pipeline_fence();
+            small_load<CB, U, TB, VA, VB>(p, ra, rb, row, col, g, c + 2 * U, kend, r0);
+            if (c + U < c1) small_mma<CB, U, TB>(r1, acc);
+            pipeline_fence();
+        }
     }
 
     // k-groups 1.. leave their sums in LDS; group 0 adds them in group order
@@ -366,15 +374,17 @@ int small_choice(const Problem &p) {
 }
 
 // Automatic dispatch: products with fewer than 256 tiles of 64 x 64 (the
-// smallest tiled-family workgroup tile) across the batch, A untransposed, and
-// at most 1.5 GFLOP.  Without reuse through LDS the family is bound by L2
-// bandwidth at a few tens of TFLOP/s, so larger products with few tiles (long
-// K) go to stream-K (768 x 768 x 65536: 0.64 ms there).
+// smallest tiled-family workgroup tile) across the batch -- or exactly 256 of
+// them with K <= 64 (1000 x 1000 x 64: 5.9 us against 7.6) -- A
+// untransposed, and at most 1.5 GFLOP.  Without reuse through LDS the family
+// is bound by L2 bandwidth at a few tens of TFLOP/s, so larger products with
+// few tiles (long K) go to stream-K (768 x 768 x 65536: 0.64 ms there).
 int small_pick(const Problem &p) {
     if (!small_fits(p)) return -1;
     const long long t64 = (long long)((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch;
     const double flops = 2.0 * p.M * p.N * (double)p.K * p.batch;
-    return (t64 < 256 && flops <= 1.5e9) ? small_choice(p) : -1;
+    const bool few = t64 < 256 || (t64 == 256 && p.K <= 64);
+    return (few && flops <= 1.5e9) ? small_choice(p) : -1;
 }
 
 }  // namespace sg

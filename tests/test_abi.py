@@ -255,6 +255,7 @@ def test_small_product_selection():
     assert pick(512, 512, 2048) == (sg.VARIANT_SMALL, 2)
     assert pick(64, 64, 64) == (sg.VARIANT_SMALL, 1)       # a few k-steps, few blocks
     assert pick(1024, 1024, 1024)[0] == sg.VARIANT_MFMA     # 256 tiles of 64 x 64
+    assert pick(1000, 1000, 64) == (sg.VARIANT_SMALL, 7)    # ... with K <= 64: no k-groups
     assert pick(768, 768, 65536)[0] == sg.VARIANT_MFMA      # 77 GFLOP: stream-K
     assert pick(16, 4096, 4096)[0] == sg.VARIANT_SKINNY
     assert pick(256, 256, 256, trans_a=True)[0] == sg.VARIANT_MFMA
