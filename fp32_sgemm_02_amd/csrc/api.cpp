@@ -168,13 +168,29 @@ int general_mfma_tile(int M, int N) {
 constexpr int kCUs = 256;
 constexpr double kPeakFlops = 157.3e12;   // fp32 MFMA, dense
 
+// A tile of one k-group whose waves own fewer than 64 x 128 outputs each,
+// running alone on its CU (at most one workgroup per CU: two waves per SIMD),
+// covers less of its loads' latency than at 4096^3, where its efficiency was
+// measured with several workgroups per CU.  Graph-replayed, the 8-wave
+// 128 x 128 tile of 32 x 64 wave tiles ran 3.4-6.5 % behind the k-group tiles
+// on products that give it exactly one round (4096 x 1000 x 3001, 4096 x
+// 1024 x 4096, 2048 x 2048 x 4096, 1024 x 4096 x 4096, 4096 x 1000 x 1000)
+// and ahead of them from two rounds on (4096 x 2048 x 4096, 2816^3).
+constexpr double kLoneWorkgroupPenalty = 1.05;
+
 // Estimated time of tile t on `batch` M x N outputs: rounds of workgroups
 // over the 256 CUs, each round costing one tile's work at the tile's measured
 // efficiency.  Rounding up to whole rounds is what makes a 4097-row product
 // with 256-row tiles cost as much as a 4352-row one.
 double tile_cost(const TileEntry &t, int M, int N, int batch = 1) {
-    const long long rounds = (tiles_for(t, M, N) * batch + kCUs - 1) / kCUs;
-    return (double)rounds * t.desc.bm * t.desc.bn / (t.eff_pct > 0 ? t.eff_pct : 50);
+    const long long n = tiles_for(t, M, N) * batch;
+    const long long rounds = (n + kCUs - 1) / kCUs;
+    double c = (double)rounds * t.desc.bm * t.desc.bn / (t.eff_pct > 0 ? t.eff_pct : 50);
+    const sgemm_tile_desc &d = t.desc;
+    if (n <= kCUs && d.wm > 0 && d.wn > 0 && d.wm * d.wn < 64 * 128 &&
+        d.threads / 64 == (d.bm / d.wm) * (d.bn / d.wn))   // one k-group
+        c *= kLoneWorkgroupPenalty;
+    return c;
 }
 
 // Edge strips.  When a tile leaves at most 16 rows (or columns) past its last

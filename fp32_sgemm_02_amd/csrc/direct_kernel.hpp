@@ -64,7 +64,15 @@ bool direct_applies(const Problem &p, int bm, int bn, int bk, bool edges);
 namespace {
 
 // AV, BV: floats per direct load of A and B (4: buffer_load_dwordx4, needs
-// 16-byte aligned rows; 1: buffer_load_dword, any 4-byte aligned layout).
+// 16-byte aligned rows; 1: buffer_load_dword, any 4-byte aligned layout;
+// 5: buffer_load_dwordx4 from rows that are only 4-byte aligned, with the
+// k-tail stage taken by dword loads -- k-contiguous operands only, i.e. A
+// untransposed and B transposed).  A 16-byte load needs no 16-byte alignment
+// on gfx9-family parts run by the ROCm driver (unaligned access mode; the
+// compiler emits such loads itself for 4-byte aligned 16-byte data).  What it
+// cannot do is stop at the K bound inside a chunk: on the last stage a chunk
+// may straddle K, and there each float is loaded alone so that those past K
+// read zeros.
 // KG: k-groups.  With KG > 1 the waves form KG groups that each own the same
 // BM x BN tile of C and take turns over the 16-wide k-chunks of a stage
 // (group g: chunks g*KC/KG ..); their partial sums meet in LDS at the end.
@@ -112,9 +120,10 @@ struct DirectShape {
     static constexpr int B_STAGE = BK * BN;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int LDS_BYTES = NBUF * STAGE * 4;
-    static constexpr int LA = A_STAGE / AV / 64 / NW;   // direct loads per wave per stage (A)
-    static constexpr int LB = B_STAGE / BV / 64 / NW;   // ... (B)
-    static constexpr int AVEC = AV, BVEC = BV;
+    static constexpr int AVEC = AV == 1 ? 1 : 4, BVEC = BV == 1 ? 1 : 4;   // floats per load
+    static constexpr bool A_SPLIT = AV == 5, B_SPLIT = BV == 5;   // dword loads on the k tail
+    static constexpr int LA = A_STAGE / AVEC / 64 / NW;   // direct loads per wave per stage (A)
+    static constexpr int LB = B_STAGE / BVEC / 64 / NW;   // ... (B)
     static constexpr int L = LA + LB;
     static constexpr int KC = BK / 16;                  // 16-wide k-chunks per stage
     static constexpr int KCW = KC / KG;                 // ... per wave
@@ -123,11 +132,16 @@ struct DirectShape {
     static_assert(KG >= 1 && KC % KG == 0, "k-groups split the chunks of a stage evenly");
     static_assert(RED_FLOATS <= NBUF * STAGE, "k-group partial sums fit the LDS ring");
     static_assert(WM % 16 == 0 && WN % 64 == 0, "wave tile: 16-row x 64-column units");
-    static_assert((AV == 4 || AV == 1) && (BV == 4 || BV == 1), "dword or dwordx4 loads");
-    static_assert(LA * 64 * NW * AV == A_STAGE && LB * 64 * NW * BV == B_STAGE,
+    static_assert((AV == 4 || AV == 1 || AV == 5) && (BV == 4 || BV == 1 || BV == 5),
+                  "dword or dwordx4 loads");
+    static_assert(!A_SPLIT || !TA, "split tail loads need k-contiguous A rows");
+    static_assert(!B_SPLIT || TB, "split tail loads need k-contiguous B rows");
+    static_assert(LA * 64 * NW * AVEC == A_STAGE && LB * 64 * NW * BVEC == B_STAGE,
                   "stage loads divide evenly over the waves");
     static_assert(NBUF >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring of 2+ stages");
-    static_assert(L * (NBUF - 1) <= 63, "outstanding loads fit the vmcnt counter");
+    // the k-tail stage of a split operand issues 4 dword loads per 16-byte load
+    static_assert(L * (NBUF - 1) + 3 * (A_SPLIT ? LA : 0) + 3 * (B_SPLIT ? LB : 0) <= 63,
+                  "outstanding loads fit the vmcnt counter");
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -150,6 +164,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 // without touching memory.  Rows past M and columns past N are fixed per
 // lane; the k bound is applied on the last stage only.
 constexpr int kOutOfRange = (int)0x80000000u;
+
+// Row r and k (within the stage) of float w of a k-contiguous tile image (A
+// untransposed, B transposed): rows of BK floats whose 16-byte chunks sit in
+// swizzled slots.
+template <class S>
+__device__ __forceinline__ void kimage_pos(int w, int &r, int &k) {
+    constexpr int BK = S::KC * 16;
+    r = w / BK;
+    const int kk = w % BK;
+    k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
+}
+
+// Column of the tile held in LDS row r of a transposed-B image: row 64q +
+// 16c + i holds column 64q + 4i + c, so that the 16-row block c of a
+// 64-column group is columns 4i + c.
+__device__ __forceinline__ int tb_column(int r) {
+    return (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3);
+}
 
 template <class S>
 struct DirectLanes {
@@ -174,8 +206,8 @@ __device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int m0,
             d.a_k[j] = r;
             d.a_off[j] = (GUARD && m0 + m >= p.M) ? kOutOfRange : (r * (int)p.lda + m) * 4;
         } else {
-            const int r = w / BK, kk = w % BK;
-            const int k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
+            int r, k;
+            kimage_pos<S>(w, r, k);
             d.a_k[j] = k;
             d.a_off[j] = (GUARD && m0 + r >= p.M) ? kOutOfRange : (r * (int)p.lda + k) * 4;
         }
@@ -184,12 +216,10 @@ __device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int m0,
     for (int j = 0; j < S::LB; ++j) {
         const int w = (wave * S::LB + j) * 64 * S::BVEC + S::BVEC * lane;
         if constexpr (S::TRANS_B) {
-            // BN rows of BK floats, swizzled like A; LDS row 64q + 16c + i
-            // holds column n = 64q + 4i + c of the tile, so that the 16-row
-            // block c of a 64-column group is columns 4i + c
-            const int r = w / BK, kk = w % BK;
-            const int k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
-            const int n = (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3);
+            // BN rows of BK floats, swizzled like A, rows permuted (tb_column)
+            int r, k;
+            kimage_pos<S>(w, r, k);
+            const int n = tb_column(r);
             d.b_k[j] = k;
             d.b_off[j] = (GUARD && n0 + n >= p.N) ? kOutOfRange : (n * (int)p.ldb + k) * 4;
         } else {
@@ -222,18 +252,54 @@ __device__ __forceinline__ void issue_stage(const Problem &p, int m0, int n0, in
                          (int)(BK * p.ldb * 4), 0x00020000);
     const int krem = p.K - t * BK;   // k below this stays inside the matrix
     const bool tail = GUARD && krem < BK;
+    static_assert(GUARD || !(S::A_SPLIT || S::B_SPLIT), "split tail loads are guarded");
 #pragma unroll
     for (int q = 0; q < S::L; ++q) {
         if (q < lo || q >= hi) continue;
         if (q < S::LA) {
-            lds_void *dst = (lds_void *)(buf + (wave * S::LA + q) * 64 * S::AVEC);
+            float *dst = buf + (wave * S::LA + q) * 64 * S::AVEC;
+            if constexpr (S::A_SPLIT) {
+                if (tail) {
+                    // the 256 floats of this load as four dword loads (lane l
+                    // of load e fills float 64e + l), each checked against K
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        int r, k;
+                        kimage_pos<S>((wave * S::LA + q) * 256 + 64 * e + (threadIdx.x & 63), r,
+                                      k);
+                        const int off = (k >= krem || m0 + r >= p.M) ? kOutOfRange
+                                                                     : (r * (int)p.lda + k) * 4;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(dst + 64 * e),
+                                                                 4, off, 0, 0, 0);
+                    }
+                    continue;
+                }
+            }
             const int off = (tail && d.a_k[q] >= krem) ? kOutOfRange : d.a_off[q];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 4 * S::AVEC, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)dst, 4 * S::AVEC, off, 0, 0,
+                                                     0);
         } else {
             const int j = q - S::LA;
-            lds_void *dst = (lds_void *)(buf + S::A_STAGE + (wave * S::LB + j) * 64 * S::BVEC);
+            float *dst = buf + S::A_STAGE + (wave * S::LB + j) * 64 * S::BVEC;
+            if constexpr (S::B_SPLIT) {
+                if (tail) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        int r, k;
+                        kimage_pos<S>((wave * S::LB + j) * 256 + 64 * e + (threadIdx.x & 63), r,
+                                      k);
+                        const int n = tb_column(r);
+                        const int off = (k >= krem || n0 + n >= p.N) ? kOutOfRange
+                                                                     : (n * (int)p.ldb + k) * 4;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(dst + 64 * e),
+                                                                 4, off, 0, 0, 0);
+                    }
+                    continue;
+                }
+            }
             const int off = (tail && d.b_k[j] >= krem) ? kOutOfRange : d.b_off[j];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 4 * S::BVEC, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)dst, 4 * S::BVEC, off, 0, 0,
+                                                     0);
         }
     }
 }
@@ -708,9 +774,12 @@ hipError_t launch_one(const Problem &p, int group_m, bool cvec, hipStream_t stre
 // tiles compiled with EDGES) a guarded instance with dwordx4 loads for each
 // operand whose rows allow them (16-byte aligned rows, and the length along
 // the row -- K, or N for untransposed B -- a multiple of 4, so that a 16-byte
-// chunk is entirely inside or outside the matrix).  Transposed B is served by
-// the EDGES tiles only.  VEC = false (4-byte I/O asked for) uses dword loads
-// and scalar stores.
+// chunk is entirely inside or outside the matrix).  A k-contiguous operand
+// (A untransposed, B transposed) whose rows do not allow them takes dwordx4
+// loads from its 4-byte aligned rows with the k-tail stage split into dword
+// loads (load width 5); the others take dword loads.  Transposed B is served
+// by the EDGES tiles only.  VEC = false (4-byte I/O asked for) uses dword
+// loads and scalar stores.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, bool TB, bool TA, bool EDGES,
           bool VEC>
 hipError_t launch_for(const Problem &p, int group_m, hipStream_t stream) {
@@ -726,16 +795,21 @@ hipError_t launch_for(const Problem &p, int group_m, hipStream_t stream) {
                                                                                 stream);
     }
     if constexpr (EDGES) {
+        constexpr int AS = TA ? 1 : 5, BS = TB ? 5 : 1;   // widths for rows without 16-byte loads
+        if (!VEC)
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 1, 1, true>(p, group_m, cv,
+                                                                               stream);
         if (av && bv)
             return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 4, 4, true>(p, group_m, cv,
                                                                                stream);
         if (av)
-            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 4, 1, true>(p, group_m, cv,
-                                                                               stream);
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 4, BS, true>(p, group_m, cv,
+                                                                                stream);
         if (bv)
-            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 1, 4, true>(p, group_m, cv,
-                                                                               stream);
-        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, 1, 1, true>(p, group_m, cv, stream);
+            return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AS, 4, true>(p, group_m, cv,
+                                                                                stream);
+        return launch_one<BM, BN, BK, WM, WN, NBUF, KG, TB, TA, AS, BS, true>(p, group_m, cv,
+                                                                             stream);
     }
     return hipErrorInvalidValue;
 }
@@ -785,8 +859,9 @@ hipError_t launch_direct_epi(const Problem &p, int group_m, hipStream_t stream) 
 
 // The launcher for 16-bit inputs (IN = 1 or 2).  `pw` is the problem in
 // 32-bit words along k (K, lda, ldb halved; A untransposed, B transposed, so
-// each word holds two adjacent k values); it takes dwordx4 loads of an
-// operand whose word rows allow them, as launch_for does.
+// each word holds two adjacent k values); it takes dwordx4 loads when both
+// operands' word rows allow them, and otherwise split-tail loads (width 5,
+// as launch_for) from the 4-byte aligned word rows.
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int KG, int IN>
 hipError_t launch_direct16(const Problem &pw, int group_m, hipStream_t stream) {
     if (pw.trans_a || !pw.trans_b) return hipErrorInvalidValue;
@@ -797,7 +872,8 @@ hipError_t launch_direct16(const Problem &pw, int group_m, hipStream_t stream) {
     if (av && bv)
         return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, false, 4, 4, true, false, IN>(
             pw, group_m, cv, stream);
-    return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, false, 1, 1, true, false, IN>(
+    // otherwise dwordx4 loads from 4-byte aligned word rows, dword loads on the k tail
+    return launch_one<BM, BN, BK, WM, WN, NBUF, KG, true, false, 5, 5, true, false, IN>(
         pw, group_m, cv, stream);
 }
 
