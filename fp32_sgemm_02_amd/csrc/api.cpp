@@ -48,7 +48,6 @@ int colmajor_status(int st) {
 }
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // 16-byte vector I/O needs every row start of A, B and C (of every batch
 // entry) on a 16-byte boundary ("The GEMM Scrapbook", vectorisation chapter:

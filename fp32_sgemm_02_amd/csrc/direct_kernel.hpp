@@ -194,7 +194,6 @@ struct DirectLanes {
 template <class S, bool GUARD>
 __device__ __forceinline__ DirectLanes<S> direct_lanes(const Problem &p, int m0, int n0, int wave,
                                                        int lane) {
-    constexpr int BK = S::KC * 16;
     DirectLanes<S> d;
 #pragma unroll
     for (int j = 0; j < S::LA; ++j) {

@@ -138,7 +138,7 @@ hipError_t workspace_acquire(size_t bytes, hipStream_t stream, const Problem &p,
         if (e != hipSuccess) return e;
         e = clear_counters(base, stream);
         if (e != hipSuccess) {
-            hipFreeAsync(base, stream);
+            (void)hipFreeAsync(base, stream);   // the launch error is the one reported
             return e;
         }
         c.ptr = base;
