@@ -405,7 +405,7 @@ const TileEntry *mfma_tiles(int *count) {
         mfma_entry<256, 128, 16, 128, 64, 3, 1>(75),    // 3: 4 waves, 128 accumulators per lane
         mfma_entry<128, 128, 16, 64, 64, 3, 2>(81),     // 4: 2 waves per SIMD
         mfma_entry<128, 128, 32, 64, 64, 2, 2>(82),     // 5
-        mfma_entry<128, 64, 32, 64, 64, 2, 1>(75),      // 6: 2 waves, too many registers for 2 per SIMD
+        mfma_entry<128, 64, 32, 64, 64, 2, 1>(75),      // 6: 2 waves (1 per SIMD: registers)
         mfma_entry<64, 64, 32, 32, 64, 2, 2>(75),       // 7: small problems
     };
     *count = sizeof(tiles) / sizeof(tiles[0]);

@@ -725,6 +725,87 @@ hipError_t launch_cols_bm(const Problem &p, bool va, hipStream_t stream) {
               : launch_cols_as<NB, R, W, U, false, BM>(p, stream);
 }
 
+// One column of C (N = 1) with A in 16-byte rows and the column of B a
+// contiguous, 16-byte aligned vector x (B a tight K x 1 block, or its one row
+// when stored transposed).  Wave w takes rows w, w + waves, ... in turn and
+// streams them as one sequence of rounds of U chunks (1 KB of a row each),
+// the next round's loads (of this row or the next) in flight while a round
+// is multiplied, so the load pipeline does not drain between rows; one
+// resource spans all of A (M * lda below 2^29 floats).  The C values that
+// beta needs are read at the start, one per lane (a wave has at most 64
+// rows), and reach lane 0 by a shuffle.
+constexpr int kCol1Blocks = 512;
+
+template <int U>
+__global__ void __launch_bounds__(256) col1_kernel(Problem p) {
+    select_batch(p);
+    const int lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = gridDim.x * 4;
+    if (wid >= p.M) return;                       // whole wave leaves together; no barrier below
+    const int lda = (int)p.lda, K = p.K;
+    const int chunks = (K + 255) / 256, rpr = (chunks + U - 1) / U;   // rounds per row
+    const int rows = (p.M - 1 - wid) / nw + 1, rounds = rows * rpr;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, 4 * ((long long)(p.M - 1) * p.lda + K));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.B, 4LL * K);
+    // C of this wave's row `lane` (beta != 0 only)
+    const float cold = (p.beta != 0.f && lane < rows) ? p.C[(long long)(wid + lane * nw) * p.ldc]
+                                                      : 0.f;
+    auto issue = [&](int j, floatx4 (&a)[U], floatx4 (&x)[U]) {
+        const bool ok = j < rounds;
+        const int row = wid + (j / rpr) * nw, c0 = (j % rpr) * U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (c0 + u) * 256 + 4 * lane;
+            const bool in = ok && k < K;
+            a[u] = ld4<true>(ra, in ? (row * lda + k) * 4 : kOff);
+            x[u] = ld4<false>(rx, in ? k * 4 : kOff);
+        }
+    };
+    float acc = 0.f;
+    auto consume = [&](int j, const floatx4 (&a)[U], const floatx4 (&x)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(a[u][e], x[u][e], acc);
+        if (j % rpr == rpr - 1) {
+            // butterfly reduction over the 64 lanes (fixed order)
+            float v = acc;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            const int r = j / rpr;
+            const float c = __shfl(cold, r, 64);
+            if (lane == 0) {
+                float out = p.alpha * v;
+                if (p.beta != 0.f) out = fmaf(p.beta, c, out);
+                if (p.has_epilogue()) out = activate(p.act, p.bias ? out + p.bias[0] : out);
+                p.C[(long long)(wid + r * nw) * p.ldc] = out;
+            }
+            acc = 0.f;
+        }
+    };
+    floatx4 a0[U], x0[U], a1[U], x1[U];
+    issue(0, a0, x0);
+    for (int j = 0; j < rounds; j += 2) {
+        issue(j + 1, a1, x1);
+        pipeline_fence();
+        consume(j, a0, x0);
+        if (j + 1 >= rounds) break;
+        issue(j + 2, a0, x0);
+        pipeline_fence();
+        consume(j + 1, a1, x1);
+    }
+}
+
+// Whether col1_kernel serves these operands (see there).
+bool col1_applies(const Problem &p) {
+    const bool x_vec = p.trans_b ? rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4)
+                                 : p.ldb == 1 && rows_aligned(p.B, 4, p.stride_b, p.batch, 4);
+    return p.N == 1 && !p.trans_a && p.K % 4 == 0 && x_vec &&
+           rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
+           (long long)p.M * p.lda < (1LL << 29) && p.M <= 64LL * 4 * kCol1Blocks;
+}
+
 // VEC: 16-byte loads of A where its rows allow them, and of B where it is one
 // tight K x NB block or stored transposed with aligned rows (decided per
 // operand; K a multiple of 4); otherwise 4-byte loads.  A stored transposed is
@@ -732,6 +813,13 @@ hipError_t launch_cols_bm(const Problem &p, bool va, hipStream_t stream) {
 template <int NB, int R, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
     if (p.trans_a) return hipErrorInvalidValue;
+    if constexpr (NB == 1 && VEC) {
+        if (col1_applies(p)) {
+            const int blocks = min((p.M + 3) / 4, kCol1Blocks);
+            hipLaunchKernelGGL(col1_kernel<4>, dim3(blocks, p.batch), dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     const bool k4 = p.K % 4 == 0;
     const bool va = VEC && k4 && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
     const bool vb = VEC && k4 && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4);

@@ -449,7 +449,10 @@ def test_cblas_orders(order, ta, tb, oracle_mod):
 
 SKINNY_CASES = {
     0: [(1, 1000, 3001), (16, 4100, 333), (7, 77, 4097), (3, 5, 9)],
-    1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9)],
+    1: [(1000, 1, 3001), (513, 3, 1000), (77, 16, 4097), (5, 2, 9),
+        # one column, K a multiple of 4: the row-streaming kernel (two or
+        # three rows per wave at 5000 rows)
+        (1000, 1, 3000), (5000, 1, 1024), (3, 1, 4)],
 }
 
 
@@ -471,6 +474,46 @@ def test_skinny_tiles(tile, oracle_mod):
         Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 300 + i, True)
         C = run_gpu(Ai, Bi, Ci, 0.5, -1.25, **kw)
         check(Ai, Bi, Ci, 0.5, -1.25, C, oracle_mod, exact=True, label=f"skinny t{tile} int")
+
+
+def test_one_column_stream(oracle_mod):
+    """One column of C with A in 16-byte rows and a contiguous column of B:
+    the row-streaming kernel (rows handed to the waves in turn), through
+    automatic dispatch.  Integer inputs bit for bit: more rows than waves,
+    beta reading C, B stored as a column and as a row (transposed), padded
+    16-byte rows of A, a batch, and bias + ReLU; a padded row length that is
+    not a multiple of 4 takes the general few-columns kernel."""
+    rng = np.random.default_rng(77)
+    for (M, K) in ((9000, 512), (4096, 4096), (7, 4), (2049, 1000)):
+        A, B, C0 = workloads.draw(M, 1, K, "int4", M + K, True)
+        lab = f"one column {(M, K)}"
+        C = run_gpu(A, B, C0, 0.5, -1.25)
+        check(A, B, C0, 0.5, -1.25, C, oracle_mod, exact=True, label=lab)
+        Bt = np.ascontiguousarray(B.T)
+        C = run_gpu_op(A, Bt, C0, 0.5, -1.25, False, True)
+        check_op(A, Bt, C0, 0.5, -1.25, C, False, True, oracle_mod, exact=True, label=lab + " B^T")
+        for pad in (4, 1):
+            Ap = torch.full((M, K + pad), float("nan"), device=DEV)
+            Ap[:, :K] = dev(A)
+            Cd = dev(C0)
+            sg.gemm(Ap[:, :K], dev(B), Cd, 0.5, -1.25)
+            torch.cuda.synchronize()
+            check(A, B, C0, 0.5, -1.25, Cd.cpu().numpy(), oracle_mod, exact=True,
+                  label=f"{lab} lda={K + pad}")
+    bat, M, K = 3, 3000, 256
+    A = rng.integers(-4, 5, (bat, M, K)).astype(F32)
+    B = rng.integers(-4, 5, (bat, K, 1)).astype(F32)
+    ref = oracle_mod.sgemm_batched(A, B)
+    C = sg.gemm_batched(dev(A), dev(B))
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), ref), "one column, batched"
+    A, B, C0 = workloads.draw(5000, 1, 512, "int4", 78, True)
+    bias = np.array([3.0], dtype=F32)
+    ref = oracle_mod.sgemm(A, B, C0.copy(), 1.0, 0.5, bias=bias, act=sg.ACT_RELU)
+    C = dev(C0)
+    sg.gemm(dev(A), dev(B), C, 1.0, 0.5, bias=dev(bias), act=sg.ACT_RELU)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), ref), "one column, bias + ReLU"
 
 
 def staged_tile():
