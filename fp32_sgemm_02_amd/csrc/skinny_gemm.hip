@@ -559,8 +559,36 @@ hipError_t launch_rows_ab(const Problem &p, int groups, bool va, bool vb, hipStr
 // rows 16-byte aligned and the stored row length a multiple of 4); otherwise
 // 4-byte loads throughout.  group_m, when positive, asks for that many K
 // slices.
+bool col1_applies(const Problem &p);
+hipError_t launch_col1(const Problem &p, hipStream_t stream);
+
+// One row of C with B stored transposed (x W^T, W N x K) is, transposed, one
+// column: C^T = W x^T, W's rows as the rows of A and x as the column, C's row
+// as a column with unit row stride.  Run that way (the one-column kernel)
+// when the library picks the K split, there is no bias (a bias per column of
+// C would be one per row there) and the operands allow it.
+Problem one_row_as_column(const Problem &p) {
+    Problem q = p;
+    q.M = p.N;
+    q.N = 1;
+    q.A = p.B;
+    q.lda = p.ldb;
+    q.stride_a = p.stride_b;
+    q.B = p.A;
+    q.ldb = p.lda;
+    q.stride_b = p.stride_a;
+    q.ldc = 1;
+    return q;
+}
+
 template <int Q, int WK, int U, bool VEC>
 hipError_t launch_rows(const Problem &p, int group_m, hipStream_t stream) {
+    if constexpr (VEC) {
+        if (group_m <= 0 && p.M == 1 && p.trans_b && !p.trans_a && !p.bias) {
+            const Problem q = one_row_as_column(p);
+            if (col1_applies(q)) return launch_col1(q, stream);
+        }
+    }
     const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
                     p.K % 4 == 0;
     const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) &&
@@ -806,6 +834,12 @@ bool col1_applies(const Problem &p) {
            (long long)p.M * p.lda < (1LL << 29) && p.M <= 64LL * 4 * kCol1Blocks;
 }
 
+hipError_t launch_col1(const Problem &p, hipStream_t stream) {
+    const int blocks = min((p.M + 3) / 4, kCol1Blocks);
+    hipLaunchKernelGGL(col1_kernel<4>, dim3(blocks, p.batch), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 // VEC: 16-byte loads of A where its rows allow them, and of B where it is one
 // tight K x NB block or stored transposed with aligned rows (decided per
 // operand; K a multiple of 4); otherwise 4-byte loads.  A stored transposed is
@@ -814,11 +848,7 @@ template <int NB, int R, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
     if (p.trans_a) return hipErrorInvalidValue;
     if constexpr (NB == 1 && VEC) {
-        if (col1_applies(p)) {
-            const int blocks = min((p.M + 3) / 4, kCol1Blocks);
-            hipLaunchKernelGGL(col1_kernel<4>, dim3(blocks, p.batch), dim3(256), 0, stream, p);
-            return hipGetLastError();
-        }
+        if (col1_applies(p)) return launch_col1(p, stream);
     }
     const bool k4 = p.K % 4 == 0;
     const bool va = VEC && k4 && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);

@@ -482,7 +482,8 @@ def test_one_column_stream(oracle_mod):
     automatic dispatch.  Integer inputs bit for bit: more rows than waves,
     beta reading C, B stored as a column and as a row (transposed), padded
     16-byte rows of A, a batch, and bias + ReLU; a padded row length that is
-    not a multiple of 4 takes the general few-columns kernel."""
+    not a multiple of 4 takes the general few-columns kernel.  Also one row
+    of C with W stored N x K, which runs as that column problem transposed."""
     rng = np.random.default_rng(77)
     for (M, K) in ((9000, 512), (4096, 4096), (7, 4), (2049, 1000)):
         A, B, C0 = workloads.draw(M, 1, K, "int4", M + K, True)
@@ -507,6 +508,26 @@ def test_one_column_stream(oracle_mod):
     C = sg.gemm_batched(dev(A), dev(B))
     torch.cuda.synchronize()
     assert np.array_equal(C.cpu().numpy(), ref), "one column, batched"
+    # one row with B stored transposed (x W^T): run as the column W x^T when
+    # there is no bias; with a bias, or a K split asked for, the few-rows path
+    for (N, K) in ((14336, 4096), (1000, 3000), (257, 8)):
+        A, B, C0 = workloads.draw(1, N, K, "int4", N + K, True)
+        Bt = np.ascontiguousarray(B.T)
+        lab = f"one row x W^T {(N, K)}"
+        C = run_gpu_op(A, Bt, C0, 0.5, -1.25, False, True)
+        check_op(A, Bt, C0, 0.5, -1.25, C, False, True, oracle_mod, exact=True, label=lab)
+        for kw in (dict(act=sg.ACT_RELU), dict(bias=np.full(N, 2.0, F32), act=sg.ACT_RELU)):
+            ref = oracle_mod.sgemm(A, Bt, C0.copy(), 1.0, 0.5, trans_b=True, **kw)
+            C = dev(C0)
+            b = kw.get("bias")
+            sg.gemm(dev(A), dev(Bt), C, 1.0, 0.5, trans_b=True, act=kw["act"],
+                    bias=None if b is None else dev(b))
+            torch.cuda.synchronize()
+            assert np.array_equal(C.cpu().numpy(), ref), f"{lab} {sorted(kw)}"
+        C = run_gpu_op(A, Bt, C0, 0.5, -1.25, False, True, variant=sg.VARIANT_SKINNY,
+                       tile=staged_tile(), group_m=2)
+        check_op(A, Bt, C0, 0.5, -1.25, C, False, True, oracle_mod, exact=True,
+                 label=lab + " split asked for")
     A, B, C0 = workloads.draw(5000, 1, 512, "int4", 78, True)
     bias = np.array([3.0], dtype=F32)
     ref = oracle_mod.sgemm(A, B, C0.copy(), 1.0, 0.5, bias=bias, act=sg.ACT_RELU)
