@@ -560,6 +560,7 @@ hipError_t launch_rows_ab(const Problem &p, int groups, bool va, bool vb, hipStr
 // 4-byte loads throughout.  group_m, when positive, asks for that many K
 // slices.
 bool col1_applies(const Problem &p);
+template <int IN>
 hipError_t launch_col1(const Problem &p, hipStream_t stream);
 
 // One row of C with B stored transposed (x W^T, W N x K) is, transposed, one
@@ -586,7 +587,7 @@ hipError_t launch_rows(const Problem &p, int group_m, hipStream_t stream) {
     if constexpr (VEC) {
         if (group_m <= 0 && p.M == 1 && p.trans_b && !p.trans_a && !p.bias) {
             const Problem q = one_row_as_column(p);
-            if (col1_applies(q)) return launch_col1(q, stream);
+            if (col1_applies(q)) return launch_col1<0>(q, stream);
         }
     }
     const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
@@ -761,10 +762,41 @@ hipError_t launch_cols_bm(const Problem &p, bool va, hipStream_t stream) {
 // is multiplied, so the load pipeline does not drain between rows; one
 // resource spans all of A (M * lda below 2^29 floats).  The C values that
 // beta needs are read at the start, one per lane (a wave has at most 64
-// rows), and reach lane 0 by a shuffle.
+// rows), and reach lane 0 by a shuffle.  With 16-bit inputs (IN = 1, 2) the
+// problem is in word form (K, lda, ldb count 32-bit words of two k values).
 constexpr int kCol1Blocks = 512;
 
-template <int U>
+// acc + the dot product of four words of a row of A and of x: four floats
+// (IN = 0), or eight 16-bit values in word form (IN = 1 bfloat16, 2 float16;
+// the low half of a word holds the even k), each product exact in fp32.
+template <int IN>
+__device__ __forceinline__ float col1_dot(const floatx4 &a, const floatx4 &x, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (IN == 0) {
+            acc = fmaf(a[e], x[e], acc);
+        } else {
+            const unsigned wa = __float_as_uint(a[e]), wx = __float_as_uint(x[e]);
+            float al, ah, xl, xh;
+            if constexpr (IN == 1) {
+                al = __uint_as_float(wa << 16);
+                ah = __uint_as_float(wa & 0xffff0000u);
+                xl = __uint_as_float(wx << 16);
+                xh = __uint_as_float(wx & 0xffff0000u);
+            } else {
+                al = (float)__builtin_bit_cast(_Float16, (unsigned short)(wa & 0xffffu));
+                ah = (float)__builtin_bit_cast(_Float16, (unsigned short)(wa >> 16));
+                xl = (float)__builtin_bit_cast(_Float16, (unsigned short)(wx & 0xffffu));
+                xh = (float)__builtin_bit_cast(_Float16, (unsigned short)(wx >> 16));
+            }
+            acc = fmaf(al, xl, acc);
+            acc = fmaf(ah, xh, acc);
+        }
+    }
+    return acc;
+}
+
+template <int U, int IN>
 __global__ void __launch_bounds__(256) col1_kernel(Problem p) {
     select_batch(p);
     const int lane = threadIdx.x & 63;
@@ -793,9 +825,7 @@ __global__ void __launch_bounds__(256) col1_kernel(Problem p) {
     float acc = 0.f;
     auto consume = [&](int j, const floatx4 (&a)[U], const floatx4 (&x)[U]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = fmaf(a[u][e], x[u][e], acc);
+        for (int u = 0; u < U; ++u) acc = col1_dot<IN>(a[u], x[u], acc);
         if (j % rpr == rpr - 1) {
             // butterfly reduction over the 64 lanes (fixed order)
             float v = acc;
@@ -834,9 +864,10 @@ bool col1_applies(const Problem &p) {
            (long long)p.M * p.lda < (1LL << 29) && p.M <= 64LL * 4 * kCol1Blocks;
 }
 
+template <int IN>
 hipError_t launch_col1(const Problem &p, hipStream_t stream) {
     const int blocks = min((p.M + 3) / 4, kCol1Blocks);
-    hipLaunchKernelGGL(col1_kernel<4>, dim3(blocks, p.batch), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((col1_kernel<4, IN>), dim3(blocks, p.batch), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -848,7 +879,7 @@ template <int NB, int R, int W, int U, bool VEC>
 hipError_t launch_cols(const Problem &p, int, hipStream_t stream) {
     if (p.trans_a) return hipErrorInvalidValue;
     if constexpr (NB == 1 && VEC) {
-        if (col1_applies(p)) return launch_col1(p, stream);
+        if (col1_applies(p)) return launch_col1<0>(p, stream);
     }
     const bool k4 = p.K % 4 == 0;
     const bool va = VEC && k4 && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4);
@@ -902,6 +933,13 @@ hipError_t launch_rows16_as(const Problem &pw, hipStream_t stream) {
 
 hipError_t launch_skinny16(int dtype, const Problem &pw, hipStream_t stream) {
     if (pw.M > 16 || pw.trans_a || !pw.trans_b) return hipErrorInvalidValue;
+    if (pw.M == 1 && !pw.bias) {
+        // one row: the transposed one-column product, in word form
+        const Problem q = one_row_as_column(pw);
+        if (col1_applies(q))
+            return dtype == SGEMM_DTYPE_BF16 ? launch_col1<1>(q, stream)
+                                             : launch_col1<2>(q, stream);
+    }
     return dtype == SGEMM_DTYPE_BF16 ? launch_rows16_as<1>(pw, stream)
                                      : launch_rows16_as<2>(pw, stream);
 }

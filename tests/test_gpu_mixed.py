@@ -112,10 +112,12 @@ def test_mixed_automatic_every_layout(ta, tb, dtype, tname, oracle_mod):
 def test_mixed_few_rows(dtype, tname, oracle_mod):
     """Decode-like shapes (M <= 16) with W stored N x K: the few-rows skinny
     kernel in word form (M <= 8), 16-byte and 4-byte loads, and the k-group
-    tiles above that."""
+    tiles above that; one row runs as the transposed one-column product
+    (W's rows streamed, more rows than waves at 9000) where the word rows
+    take 16-byte loads."""
     rng = np.random.default_rng(40 + dtype)
     for M, N, K in ((1, 5000, 4096), (8, 300, 64), (5, 4100, 66), (3, 17, 2), (16, 14336, 512),
-                    (9, 300, 64)):
+                    (9, 300, 64), (1, 14336, 4096), (1, 9000, 1024), (1, 300, 24), (1, 77, 6)):
         lab = f"{tname} few rows {(M, N, K)}"
         run_check(rng, dtype, tname, M, N, K, False, True, False, oracle_mod, lab)
         run_check(rng, dtype, tname, M, N, K, False, True, True, oracle_mod, lab + " int")
