@@ -363,10 +363,13 @@ int resolve(const Problem &p, const sgemm_config *cfg, Choice &out, Strips *stri
         Tuned a;
         if (trans || (flags & SGEMM_FLAG_UNTUNED) || p.batch > 1 ||
             !lookup_tuned(p.M, p.N, p.K, a)) {
-            if (skinny_pick(p) >= 0)
+            const int small = small_pick(p);
+            if (small >= 0 && small_tiny_batch(p))
+                a = Tuned{SGEMM_VARIANT_SMALL, small, 0};
+            else if (skinny_pick(p) >= 0)
                 a = Tuned{SGEMM_VARIANT_SKINNY, -1, 0};
-            else if (small_pick(p) >= 0)
-                a = Tuned{SGEMM_VARIANT_SMALL, small_pick(p), 0};
+            else if (small >= 0)
+                a = Tuned{SGEMM_VARIANT_SMALL, small, 0};
             else
                 a = Tuned{SGEMM_VARIANT_MFMA, default_mfma_tile(p, io_ok, strips, &streamk), 0};
             if (a.tile < 0 && a.variant == SGEMM_VARIANT_MFMA) return kBadConfig;

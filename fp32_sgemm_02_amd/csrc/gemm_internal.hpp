@@ -155,6 +155,7 @@ int skinny_slices(int tile, const Problem &p, int group_m);
 const TileEntry *small_tiles(int *count);
 bool small_fits(const Problem &p);
 int small_pick(const Problem &p);
+bool small_tiny_batch(const Problem &p);   // a batch of tiny products (small family first)
 int small_choice(const Problem &p);
 
 // C = act(beta * C + bias) over p's batch (beta == 0: C is not read); with

@@ -379,12 +379,23 @@ int small_choice(const Problem &p) {
 // untransposed, and at most 1.5 GFLOP.  Without reuse through LDS the family
 // is bound by L2 bandwidth at a few tens of TFLOP/s, so larger products with
 // few tiles (long K) go to stream-K (768 x 768 x 65536: 0.64 ms there).
+//
+// Batches of tiny products (each at most 64 x 64 and half that in area, K <=
+// 512) take the family whatever their count: a tiled-family workgroup would
+// leave most of its tile idle, and the few-rows kernel is built for long
+// rows of B.  Graph-replayed: 4096 x 32^3 18.3 us against 22.7 (the 64 x 64
+// k-group tile), 2048 x 16 x 64 x 128 with B^T 19.3 against 31.8 (few rows);
+// 1024 x 64^3 stays on the tiled family (9.2 us against 13.8).
+bool small_tiny_batch(const Problem &p) {
+    return p.batch > 1 && p.M <= 64 && p.N <= 64 && (long long)p.M * p.N <= 2048 && p.K <= 512;
+}
+
 int small_pick(const Problem &p) {
     if (!small_fits(p)) return -1;
     const long long t64 = (long long)((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch;
     const double flops = 2.0 * p.M * p.N * (double)p.K * p.batch;
     const bool few = t64 < 256 || (t64 == 256 && p.K <= 64);
-    return (few && flops <= 1.5e9) ? small_choice(p) : -1;
+    return ((few || small_tiny_batch(p)) && flops <= 1.5e9) ? small_choice(p) : -1;
 }
 
 }  // namespace sg

@@ -63,10 +63,12 @@ def check(A, B, C0, alpha, beta, C, ref, exact, label):
 @pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
 def test_batched_shapes(ta, tb, oracle_mod):
     """Stacks of ragged and tile-sized products, every transposition,
-    alpha/beta and beta = 0 over NaN, integers bit-exact."""
+    alpha/beta and beta = 0 over NaN, integers bit-exact; batches of tiny
+    products (the small-product family takes them, A untransposed)."""
     rng = np.random.default_rng(int(ta) * 2 + int(tb))
     for batch, (M, N, K) in ((3, (300, 257, 129)), (7, (64, 64, 64)), (5, (128, 96, 33)),
-                             (2, (1000, 300, 77)), (1, (37, 45, 5)), (16, (128, 128, 64))):
+                             (2, (1000, 300, 77)), (1, (37, 45, 5)), (16, (128, 128, 64)),
+                             (300, (32, 32, 32)), (64, (16, 64, 128)), (40, (5, 33, 17))):
         for integer in (False, True):
             A, B, C0, As, Bs = stacks(rng, batch, M, N, K, ta, tb, integer)
             lab = f"batch {batch} {(M, N, K)} ta={ta} tb={tb} int={integer}"
