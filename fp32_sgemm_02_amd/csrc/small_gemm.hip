@@ -361,9 +361,17 @@ bool small_fits(const Problem &p) {
 // 3.99 us against 4.64), else over 16 x 64 blocks.
 int small_choice(const Problem &p) {
     const long long nc = (p.K + 15) / 16;
-    const bool wide = p.N >= 64 && (p.trans_b ? p.K % 4 == 0 : p.N % 4 == 0);
+    const bool rows16 = p.trans_b ? p.K % 4 == 0 : p.N % 4 == 0;   // B rows in 16-byte loads
+    const bool wide = p.N >= 64 && rows16;
     const long long b16 = (long long)((p.M + 15) / 16) * ((p.N + 15) / 16) * p.batch;
     const long long b64 = (long long)((p.M + 15) / 16) * ((p.N + 63) / 64) * p.batch;
+    // very long K on a thin product (M or N at most 64) with more than a few
+    // blocks: 16 x 64 blocks of eight k-groups while they are at most one per
+    // CU (64 x 4096 x 4096 25.7 us, four k-groups 27.9; 4096 x 48 x 8192
+    // 46.0, 16 x 16 blocks 89.8), else 32 x 64 workgroups of two k-groups (32
+    // x 14336 x 4096 49.2 us against 67.5)
+    if (rows16 && nc >= 256 && b64 > 64 && (p.M <= 64 || p.N <= 64))
+        return b64 <= 256 ? 6 : 3;
     if (!wide) {
         if (nc >= 32 && b16 <= 512) return nc >= 64 && b16 <= 256 ? 5 : 0;
         return 1;
@@ -378,7 +386,13 @@ int small_choice(const Problem &p) {
 // them with K <= 64 (1000 x 1000 x 64: 5.9 us against 7.6) -- A
 // untransposed, and at most 1.5 GFLOP.  Without reuse through LDS the family
 // is bound by L2 bandwidth at a few tens of TFLOP/s, so larger products with
-// few tiles (long K) go to stream-K (768 x 768 x 65536: 0.64 ms there).
+// few tiles (long K) go to stream-K (768 x 768 x 65536: 0.64 ms there) --
+// except thin ones (M or N at most 64) whose C covers less than 160 tiles of
+// 64 x 64 in area: they leave most CUs, or most rows or columns of the tiled
+// families' tiles and of stream-K's 256-row tiles, idle.  64 x 4096 x 4096
+// 25.7 us here against 72.8 for the best tiled plan, 33 x 2048 x 8192 42.1
+// against 90.2, 32 x 14336 x 4096 49.2 against 80.9; 64 x 14336 x 4096 (224
+// full tiles) stays tiled (76.7 us against 85.3).
 //
 // Batches of tiny products (each at most 64 x 64 and half that in area, K <=
 // 512) take the family whatever their count: a tiled-family workgroup would
@@ -395,7 +409,10 @@ int small_pick(const Problem &p) {
     const long long t64 = (long long)((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch;
     const double flops = 2.0 * p.M * p.N * (double)p.K * p.batch;
     const bool few = t64 < 256 || (t64 == 256 && p.K <= 64);
-    return ((few || small_tiny_batch(p)) && flops <= 1.5e9) ? small_choice(p) : -1;
+    const bool thin = (p.M <= 64 || p.N <= 64) && (long long)p.M * p.N < 160LL * 64 * 64;
+    return ((few && (flops <= 1.5e9 || thin)) || (small_tiny_batch(p) && flops <= 1.5e9))
+               ? small_choice(p)
+               : -1;
 }
 
 }  // namespace sg
