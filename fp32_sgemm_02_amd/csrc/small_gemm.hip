@@ -387,12 +387,13 @@ int small_choice(const Problem &p) {
 // untransposed, and at most 1.5 GFLOP.  Without reuse through LDS the family
 // is bound by L2 bandwidth at a few tens of TFLOP/s, so larger products with
 // few tiles (long K) go to stream-K (768 x 768 x 65536: 0.64 ms there) --
-// except thin ones (M or N at most 64) whose C covers less than 160 tiles of
-// 64 x 64 in area: they leave most CUs, or most rows or columns of the tiled
-// families' tiles and of stream-K's 256-row tiles, idle.  64 x 4096 x 4096
-// 25.7 us here against 72.8 for the best tiled plan, 33 x 2048 x 8192 42.1
-// against 90.2, 32 x 14336 x 4096 49.2 against 80.9; 64 x 14336 x 4096 (224
-// full tiles) stays tiled (76.7 us against 85.3).
+// except narrow ones (M or N at most 200) whose C covers less than 200
+// tiles of 64 x 64 in area: they leave most CUs, or most rows or columns of
+// the tiled families' tiles and of stream-K's 256-row tiles, idle.  64 x
+// 4096 x 4096 25.7 us here against 72.8 for the best tiled plan, 33 x 2048 x
+// 8192 42.1 against 90.2, 32 x 14336 x 4096 49.2 against 80.9, 3000 x 100
+// x 3000 36.6 against 60.9, 192 x 4096 x 4096 66.5 against 75.3; 64 x 14336
+// x 4096 (224 full tiles) stays tiled (76.7 us against 85.3).
 //
 // Batches of tiny products (each at most 64 x 64 and half that in area, K <=
 // 512) take the family whatever their count: a tiled-family workgroup would
@@ -409,8 +410,8 @@ int small_pick(const Problem &p) {
     const long long t64 = (long long)((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch;
     const double flops = 2.0 * p.M * p.N * (double)p.K * p.batch;
     const bool few = t64 < 256 || (t64 == 256 && p.K <= 64);
-    const bool thin = (p.M <= 64 || p.N <= 64) && (long long)p.M * p.N < 160LL * 64 * 64;
-    return ((few && (flops <= 1.5e9 || thin)) || (small_tiny_batch(p) && flops <= 1.5e9))
+    const bool narrow = (p.M <= 200 || p.N <= 200) && (long long)p.M * p.N < 200LL * 64 * 64;
+    return ((few && (flops <= 1.5e9 || narrow)) || (small_tiny_batch(p) && flops <= 1.5e9))
                ? small_choice(p)
                : -1;
 }

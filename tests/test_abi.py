@@ -280,12 +280,13 @@ def test_small_product_selection():
     assert pick(1024, 1024, 1024)[0] == sg.VARIANT_MFMA     # 256 tiles of 64 x 64
     assert pick(1000, 1000, 64) == (sg.VARIANT_SMALL, 7)    # ... with K <= 64: no k-groups
     assert pick(768, 768, 65536)[0] == sg.VARIANT_MFMA      # 77 GFLOP: stream-K
-    # thin products with long K: the family whatever their flops, while C
-    # covers less than 160 tiles of 64 x 64 in area
+    # narrow products (M or N <= 200) with long K: the family whatever their
+    # flops, while C covers less than 200 tiles of 64 x 64 in area
     assert pick(64, 4096, 4096) == (sg.VARIANT_SMALL, 6)
     assert pick(4096, 48, 8192) == (sg.VARIANT_SMALL, 6)
     assert pick(32, 14336, 4096) == (sg.VARIANT_SMALL, 3)
     assert pick(64, 14336, 4096)[0] == sg.VARIANT_MFMA
+    assert pick(3000, 100, 3000) == (sg.VARIANT_SMALL, 2)
     assert pick(16, 4096, 4096)[0] == sg.VARIANT_SKINNY
     assert pick(256, 256, 256, trans_a=True)[0] == sg.VARIANT_MFMA
     assert pick(384, 384, 384, trans_b=True) == (sg.VARIANT_SMALL, 2)
