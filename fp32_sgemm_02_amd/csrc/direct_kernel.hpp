@@ -15,7 +15,7 @@
 //   * the LDS image is unpadded: lane l of a load lands at byte 16*l of its
 //     1 KB block.  Bank conflicts on the A-fragment reads are avoided by an
 //     XOR swizzle instead of padding: the 16-byte chunk c of A-tile row r is
-//     stored in slot c ^ ((r >> 1) & (BK/4 - 1)), a pattern measured
+//     stored in slot c ^ ((r >> 1) & (BK/4 - 1)) (kswz below), a pattern measured
 //     conflict-free for the 16-row x 4-chunk reads of a wave ("The GEMM
 //     Scrapbook", warptiling chapter: arrange accesses so the lanes hit
 //     distinct banks);
@@ -154,7 +154,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Direct loads of one stage.  The A tile is BM rows of CPR_A 16-byte chunks
 // stored row-major; the chunk in slot `slot` of row r holds logical chunk
-// slot ^ swz(r), swz(r) = (r >> 1) & (CPR_A - 1).  Load j of a wave fills the
+// slot ^ swz(r) (kswz below).  Load j of a wave fills the
 // next 64 * AV floats of the tile image (lane l writes floats AV*l .. +AV-1 of
 // them), so each lane loads whatever global element(s) belong there.  The B
 // slice (BK x BN, row-major, unswizzled) is filled the same way.
@@ -165,15 +165,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // lane; the k bound is applied on the last stage only.
 constexpr int kOutOfRange = (int)0x80000000u;
 
-// Row r and k (within the stage) of float w of a k-contiguous tile image (A
-// untransposed, B transposed): rows of BK floats whose 16-byte chunks sit in
-// swizzled slots.
+// The swizzle of a k-contiguous tile image (A untransposed, B transposed):
+// the 16-byte chunk c of row r sits in slot c ^ kswz(r).  It depends on the
+// row within its 16-row block only (the fragment reads of an MFMA block take
+// rows 16b + i, i = lane % 16, one logical chunk), and gives those 16 rows
+// distinct banks: rows of 64 or 128 bytes (BK = 16, 32) share a 256-byte
+// bank line four or two at a time, so the rows pair up as r >> 1.
+template <class S>
+__device__ __forceinline__ int kswz(int r) {
+    static_assert(S::CPR_A == 4 || S::CPR_A == 8, "rows of 64 or 128 bytes");
+    return (r >> 1) & (S::CPR_A - 1);
+}
+
+// Row r and k (within the stage) of float w of a k-contiguous tile image:
+// rows of BK floats whose 16-byte chunks sit in swizzled slots (kswz).
 template <class S>
 __device__ __forceinline__ void kimage_pos(int w, int &r, int &k) {
     constexpr int BK = S::KC * 16;
     r = w / BK;
     const int kk = w % BK;
-    k = 4 * ((kk / 4) ^ ((r >> 1) & (S::CPR_A - 1))) + kk % 4;
+    k = 4 * ((kk / 4) ^ kswz<S>(r)) + kk % 4;
 }
 
 // Column of the tile held in LDS row r of a transposed-B image: row 64q +
@@ -326,7 +337,7 @@ __device__ __forceinline__ void read_a(const float *buf, int kc, int rb, int lan
         a = *reinterpret_cast<const floatx4 *>(buf + (16 * kc + 4 * g + rb % 4) * BMT +
                                                wr * S::RB * 16 + (rb / 4) * 64 + 4 * i);
     } else {
-        const int slot = (4 * kc + g) ^ ((i >> 1) & (S::CPR_A - 1));
+        const int slot = (4 * kc + g) ^ kswz<S>(i);
         a = *reinterpret_cast<const floatx4 *>(
             buf + (wr * S::RB * 16 + rb * 16 + i) * (S::CPR_A * 4) + 4 * slot);
     }
@@ -344,7 +355,7 @@ __device__ __forceinline__ void read_b_part(const float *buf, int kc, int part, 
                                             BFrag<S> &b) {
     const int i = lane & 15, g = lane >> 4;
     if constexpr (S::TRANS_B) {
-        const int slot = (4 * kc + g) ^ ((i >> 1) & (S::CPR_A - 1));
+        const int slot = (4 * kc + g) ^ kswz<S>(i);
 #pragma unroll
         for (int q = 0; q < S::CG; ++q) {
             const int cb = part * S::CG + q;

@@ -504,10 +504,21 @@ def test_one_column_stream(oracle_mod):
     bat, M, K = 3, 3000, 256
     A = rng.integers(-4, 5, (bat, M, K)).astype(F32)
     B = rng.integers(-4, 5, (bat, K, 1)).astype(F32)
-    ref = oracle_mod.sgemm_batched(A, B)
-    C = sg.gemm_batched(dev(A), dev(B))
+    C0 = rng.integers(-4, 5, (bat, M, 1)).astype(F32)
+    ref = oracle_mod.sgemm_batched(A, B, C0.copy(), 0.5, -1.25)
+    C = dev(C0)
+    sg.gemm_batched(dev(A), dev(B), C, 0.5, -1.25)
     torch.cuda.synchronize()
     assert np.array_equal(C.cpu().numpy(), ref), "one column, batched"
+    # a batch of single rows times W^T (one W per entry): the transposed form
+    W = rng.integers(-4, 5, (bat, 700, K)).astype(F32)
+    X = rng.integers(-4, 5, (bat, 1, K)).astype(F32)
+    C0 = rng.integers(-4, 5, (bat, 1, 700)).astype(F32)
+    ref = oracle_mod.sgemm_batched(X, W, C0.copy(), 0.5, -1.25, trans_b=True)
+    C = dev(C0)
+    sg.gemm_batched(dev(X), dev(W), C, 0.5, -1.25, trans_b=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), ref), "one row x W^T, batched"
     # one row with B stored transposed (x W^T): run as the column W x^T when
     # there is no bias; with a bias, or a K split asked for, the few-rows path
     for (N, K) in ((14336, 4096), (1000, 3000), (257, 8)):
