@@ -78,10 +78,12 @@ __device__ __forceinline__ void store_cell(const Problem &p, float *dst, int col
 }
 
 // ---------------------------------------------------------------- kind 0 ----
-// The split of a few-rows launch: workgroup w owns strip w % strips and K
-// slice w / strips, rows [slice * kslice, min(K, (slice + 1) * kslice)).
+// The split of a few-rows launch: workgroup w owns strip w % strips (columns
+// [strip * width, min(N, (strip + 1) * width))) and K slice w / strips, rows
+// [slice * kslice, min(K, (slice + 1) * kslice)).
 struct RowsGrid {
-    int strips;        // column strips of 64*Q
+    int strips;        // column strips
+    int width;         // columns per strip: a multiple of 4, at most 64*Q
     int slices;        // K slices (1: no split, no workspace)
     int kslice;        // rows of K per slice, a multiple of 16
     float *part;       // slices x M x N partial sums (row-major, leading dimension N)
@@ -325,7 +327,7 @@ __global__ void __launch_bounds__(64 * WK) rows_kernel(Problem p, RowsGrid grid)
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, g = lane >> 4;
     const int strip = blockIdx.x % grid.strips, slice = blockIdx.x / grid.strips;
-    const int n0 = strip * S::COLS, ncols = min(S::COLS, p.N - n0);
+    const int n0 = strip * grid.width, ncols = min(grid.width, p.N - n0);
     const int kb = slice * grid.kslice, ke = min(p.K, kb + grid.kslice);
     const int c1 = (ke - kb + 15) / 16;   // chunks of the slice
 
@@ -423,7 +425,7 @@ __global__ void __launch_bounds__(64 * WK) rows_tb_staged_kernel(Problem p, Rows
     select_batch(p);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int strip = blockIdx.x % grid.strips, slice = blockIdx.x / grid.strips;
-    const int n0 = strip * S::COLS, ncols = min(S::COLS, p.N - n0);
+    const int n0 = strip * grid.width, ncols = min(grid.width, p.N - n0);
     const int kb = slice * grid.kslice, ke = min(p.K, kb + grid.kslice);
     const int c1 = (ke - kb + 15) / 16;
 
@@ -497,6 +499,32 @@ int rows_kslice(const Problem &p, int want, int *slices) {
     return *slices == 1 ? 16 * ((p.K + 15) / 16) : kslice;
 }
 
+// Columns per strip of a few-rows launch with `slices` K slices.  Each CU
+// streams at most ~25 GB/s, so a launch whose workgroups are fewer than the
+// CUs, each reading a large share of B, ends when the busiest CU does:
+// 16 x 14336 x 4096 with B stored N x K in 64-row strips is 224 workgroups
+// of 1 MB for 256 CUs.  With B stored transposed and large (32 MB or more)
+// the strips are narrowed so that strips x slices comes as close to the CU
+// count as a width that is a multiple of 4 allows (56 rows: 256 workgroups
+// of 0.92 MB; graph-replayed 53.3 -> 48.7 us, 16 x 11008 x 4096 42.2 ->
+// 38.7 us); lanes past a strip's width load nothing.  A strip of untransposed
+// B is a run of each of its rows, and a width that is not a multiple of 32
+// floats splits 128-byte lines between strips that both fetch them: narrowed
+// that way 16 x 14336 x 4096 ran 44 -> 54 us, so those strips keep the
+// tile's width.
+constexpr int kRowsCUs = 256;
+template <int Q, int WK, int U>
+int rows_width(const Problem &p, int slices) {
+    using S = RowsShape<Q, WK, U>;
+    const long long strips = (p.N + S::COLS - 1) / S::COLS;
+    if (!p.trans_b || p.batch != 1 || strips * slices >= kRowsCUs ||
+        4LL * p.K * p.N < (32LL << 20))
+        return S::COLS;
+    const long long want = kRowsCUs / slices;   // strips
+    const long long w = 4 * ((p.N + 4 * want - 1) / (4 * want));
+    return w < S::COLS ? (int)w : S::COLS;
+}
+
 template <int Q, int WK, int U>
 int rows_slice_count(const Problem &p, int group_m) {
     int slices = 1;
@@ -526,8 +554,10 @@ hipError_t launch_rows_as(const Problem &p, int want_slices, hipStream_t stream)
             hipLaunchKernelGGL((rows_kernel<Q, WK, U, VA, VB, TA, TB, IN>), grid_dim, dim3(S::NT),
                                0, stream, p, grid);
     };
-    RowsGrid grid{(p.N + S::COLS - 1) / S::COLS, 1, 0, nullptr, nullptr};
+    RowsGrid grid{0, S::COLS, 1, 0, nullptr, nullptr};
     grid.kslice = rows_kslice<Q, WK, U>(p, want_slices, &grid.slices);
+    grid.width = rows_width<Q, WK, U>(p, grid.slices);
+    grid.strips = (p.N + grid.width - 1) / grid.width;
     if (grid.slices == 1) {
         launch(dim3(grid.strips, p.batch), grid);
         return hipGetLastError();

@@ -595,6 +595,45 @@ def test_skinny_staged_transposed_b(slices, oracle_mod):
     assert r <= 1.0, f"staged epilogue: {r}"
 
 
+def test_skinny_balanced_strips(oracle_mod):
+    """Few-rows products with B stored N x K, large (32 MB or more), whose
+    natural strips times K slices fall short of the 256 CUs run narrower
+    strips (a multiple of 4 rows of B^T, not the tile's 64) so that every CU
+    streams.  Through the LDS-staged kernel: 16 x 9001 x 4096 as 251 strips
+    of 36 rows (the last one row), in fp32 and bfloat16; 8 x 6000 x 8192 as
+    125 strips of 48 rows and 2 K slices; one row with a bias (not the
+    one-column route) as 256 strips of 56 rows.  With K = 4097 (4-byte
+    loads, the register kernel) 6 x 9000 x 4097 as 250 strips of 36 rows.
+    Integer inputs, beta reading C: the whole of C bit for bit."""
+    for i, (M, N, K) in enumerate([(16, 9001, 4096), (8, 6000, 8192), (6, 9000, 4097)]):
+        Ai, Bi, Ci = workloads.draw(M, N, K, "int4", 3400 + i, True)
+        Bt = np.ascontiguousarray(Bi.T)
+        C = run_gpu_op(Ai, Bt, Ci, 0.5, -1.25, False, True)
+        check_op(Ai, Bt, Ci, 0.5, -1.25, C, False, True, oracle_mod, exact=True,
+                 label=f"balanced strips {(M, N, K)}")
+    rng = np.random.default_rng(3410)
+    M, N, K = 1, 14336, 4096
+    x = rng.integers(-4, 5, (M, K)).astype(F32)
+    w = rng.integers(-4, 5, (N, K)).astype(F32)
+    C0 = rng.integers(-4, 5, (M, N)).astype(F32)
+    bias = rng.integers(-8, 9, N).astype(F32)
+    C = dev(C0)
+    sg.gemm(dev(x), dev(w), C, 0.5, -1.25, trans_b=True, bias=dev(bias), act=sg.ACT_RELU)
+    torch.cuda.synchronize()
+    ref = oracle_mod.sgemm(x, w, C0.copy(), 0.5, -1.25, trans_b=True, bias=bias, act=sg.ACT_RELU)
+    assert np.array_equal(C.cpu().numpy(), ref), "balanced strips, one row with bias"
+    M, N, K = 16, 9001, 4096
+    x = rng.integers(-4, 5, (M, K)).astype(F32)
+    w = rng.integers(-4, 5, (N, K)).astype(F32)
+    C0 = rng.integers(-4, 5, (M, N)).astype(F32)
+    C = dev(C0)
+    sg.gemm_mixed(dev(x).to(torch.bfloat16), dev(w).to(torch.bfloat16), C, 0.5, -1.25,
+                  trans_b=True)
+    torch.cuda.synchronize()
+    ref = oracle_mod.sgemm(x, w, C0.copy(), 0.5, -1.25, trans_b=True)
+    assert np.array_equal(C.cpu().numpy(), ref), "balanced strips, bfloat16 x W^T"
+
+
 @pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
 @pytest.mark.parametrize("tile", range(16))
 def test_skinny_tiles_transposed(tile, ta, tb, oracle_mod):
