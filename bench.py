@@ -699,7 +699,9 @@ def read_counter_csv(path: str) -> dict:
 
 def record_traffic(args):
     """The HBM traffic record of the kernel this command times: the dominant
-    kernel (largest summed duration, probes excluded) of two counter runs,
+    library kernel (largest summed duration; probes, and torch's kernels that
+    prepare operands such as the transposed copies of --op, excluded) of two
+    counter runs,
     scaled by the copy calibration, keyed by the kernel's name and the hash
     of its source files, so that bench.py reports it only while the source is
     unchanged."""
@@ -713,7 +715,7 @@ def record_traffic(args):
     tile = args.tile if args.tile >= 0 else chosen.tile
     desc = sg.tile_info(variant, tile) if tile >= 0 else {}
     fetch, write = (read_counter_csv(f) for f in args.record_traffic)
-    names = [n for n in fetch if "probe_" not in n]
+    names = [n for n in fetch if "probe_" not in n and "sg::" in n]
     main = max(names, key=lambda n: fetch[n][2])
     f_kib, w_kib = fetch[main][1], write[main][1]
     rec = {"kernel": main, "workload": w.name, "source_hash": kernel_source_hash(variant, desc),
