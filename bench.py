@@ -477,6 +477,8 @@ def sweep(args):
             print(json.dumps(row), flush=True)
         if name in TRANSPOSED_SWEEP:
             rows.extend(sweep_transposed(torch, sg, time_graph, w, sets[0]))
+        if name in WEIGHT_NT_SWEEP:
+            rows.append(sweep_weight_nt(torch, sg, time_graph, w, sets))
         if name in EPILOGUE_SWEEP:
             rows.extend(sweep_epilogue(torch, sg, time_graph, w, sets))
         del sets
@@ -513,6 +515,30 @@ def sweep_transposed(torch, sg, time_graph, w, operands):
         out.append(row)
         del As, Bs
     return out
+
+
+WEIGHT_NT_SWEEP = ("row_1x4096x4096", "mlp_decode16")
+
+
+def sweep_weight_nt(torch, sg, time_graph, w, sets):
+    """A memory-bound workload with B stored N x K (a linear layer's weight,
+    C = A W^T: decode), rotated over the same operand copies, through the
+    entry point that allocates nothing; graph-replay device time per call."""
+    ops = [(A, B.t().contiguous(), C) for A, B, C in sets]
+    call_i = lambda i: sg.gemm(*ops[i % len(ops)], w.alpha, w.beta, trans_b=True, noalloc=True)
+    med = statistics.median(time_graph(torch, call_i, max(len(ops), 20))) / 1e3
+    A, Bt, C = ops[0]
+    cfg = sg.select(w.M, w.N, w.K, A.data_ptr(), A.stride(0), Bt.data_ptr(), Bt.stride(0),
+                    C.data_ptr(), C.stride(0), trans_b=True)
+    gbs = w.min_bytes / med / 1e9
+    row = {"workload": f"{w.name}_NT", "M": w.M, "N": w.N, "K": w.K, "op": "NT",
+           "variant": cfg.variant, "tile": cfg.tile, "group_m": cfg.group_m,
+           "kernel_ms_median": round(med * 1e3, 4), "gflops": round(w.flops / med / 1e9, 1),
+           "gbs": round(gbs, 1), "bound": "hbm",
+           "pct_roofline": round(100 * gbs / PEAK_HBM_GBS, 2), "operand_copies": len(ops)}
+    print(json.dumps(row), flush=True)
+    del ops
+    return row
 
 
 EPILOGUE_SWEEP = ("mlp_up", "mlp_decode16")
