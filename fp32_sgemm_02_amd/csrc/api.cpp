@@ -753,9 +753,12 @@ int sgemm_op_plan(int trans_a, int trans_b, int M, int N, int K, const float *A,
     if (st != 0) return st;
     out->variant = ch.variant;
     out->tile = ch.tile;
-    // a few-rows skinny plan reports the K slices it splits into
+    // a few-rows skinny plan reports the K slices it splits into (none when
+    // its one row runs as the one-column product)
     out->group_m = (ch.variant == SGEMM_VARIANT_SKINNY && sg::skinny_kind(ch.tile) == 0)
-                       ? sg::skinny_slices(ch.tile, p, ch.group_m)
+                       ? (sg::skinny_one_row_column(p, ch.group_m, ch.vec)
+                              ? 1
+                              : sg::skinny_slices(ch.tile, p, ch.group_m))
                        : ch.group_m;
     out->flags = (ch.vec ? 0 : SGEMM_FLAG_SCALAR_IO) | (ch.streamk ? SGEMM_FLAG_STREAMK : 0);
     if (edge_rows) *edge_rows = sp.rows;

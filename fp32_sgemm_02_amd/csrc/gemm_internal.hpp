@@ -147,6 +147,10 @@ bool skinny_fits(int tile, const Problem &p);
 size_t skinny_workspace_bytes(int tile, const Problem &p, int group_m);
 // K slices of a few-rows skinny launch (group_m as passed to its launcher).
 int skinny_slices(int tile, const Problem &p, int group_m);
+// Whether the few-rows launcher runs p (one row, B stored transposed, no
+// bias; group_m as passed to it, vec: 16-byte I/O) as the one-column product,
+// which splits nothing.
+bool skinny_one_row_column(const Problem &p, int group_m, bool vec);
 
 // Small-product family (small_gemm.hip): its tiles; whether it can run a
 // problem (A untransposed, 31-bit offsets); the tile automatic dispatch

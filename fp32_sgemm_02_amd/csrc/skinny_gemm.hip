@@ -612,14 +612,17 @@ Problem one_row_as_column(const Problem &p) {
     return q;
 }
 
+// Whether a few-rows launch runs p as that column problem: one row, B
+// stored transposed, no bias, the library's K split (group_m <= 0), 16-byte
+// I/O (vec) and operands the one-column kernel takes.
+bool takes_one_column(const Problem &p, int group_m, bool vec) {
+    return vec && group_m <= 0 && p.M == 1 && p.trans_b && !p.trans_a && !p.bias &&
+           col1_applies(one_row_as_column(p));
+}
+
 template <int Q, int WK, int U, bool VEC>
 hipError_t launch_rows(const Problem &p, int group_m, hipStream_t stream) {
-    if constexpr (VEC) {
-        if (group_m <= 0 && p.M == 1 && p.trans_b && !p.trans_a && !p.bias) {
-            const Problem q = one_row_as_column(p);
-            if (col1_applies(q)) return launch_col1<0>(q, stream);
-        }
-    }
+    if (takes_one_column(p, group_m, VEC)) return launch_col1<0>(one_row_as_column(p), stream);
     const bool va = VEC && !p.trans_a && rows_aligned(p.A, p.lda, p.stride_a, p.batch, 4) &&
                     p.K % 4 == 0;
     const bool vb = VEC && rows_aligned(p.B, p.ldb, p.stride_b, p.batch, 4) &&
@@ -998,6 +1001,12 @@ int skinny_slices(int tile, const Problem &p, int group_m) {
 #undef SG_ROWS_SL
     constexpr int n = sizeof(fns) / sizeof(fns[0]);
     return (tile >= 0 && tile < n) ? fns[tile](p, group_m) : 1;
+}
+
+// Whether the few-rows launcher runs p (its library-chosen K split asked for
+// with group_m <= 0) as the one-column product, which splits nothing.
+bool skinny_one_row_column(const Problem &p, int group_m, bool vec) {
+    return takes_one_column(p, group_m, vec);
 }
 
 // Workspace bytes of a few-rows launch of `tile` with `group_m` asked-for

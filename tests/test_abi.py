@@ -357,6 +357,23 @@ def test_op_plan_covers_transpositions():
                              None, None) == -22
 
 
+def test_one_row_with_b_transposed_plans_no_split():
+    """One row of C with B stored transposed (x W^T) and no bias runs as the
+    one-column product (C^T = W x^T), which splits nothing: its plan reports
+    one K slice, where the same row with B untransposed is split over K.  When
+    the one-column kernel cannot take it (x not 16-byte aligned), the few-rows
+    kernel runs it and the plan reports that kernel's slices."""
+    nt, _, _ = sg.plan(1, 4096, 4096, 0x10000, None, 0x20000, None, 0x30000, None, trans_b=True)
+    nn, _, _ = sg.plan(1, 4096, 4096, 0x10000, None, 0x20000, None, 0x30000, None)
+    assert nt.variant == nn.variant == sg.VARIANT_SKINNY
+    assert nt.group_m == 1, nt.group_m
+    assert nn.group_m > 1, nn.group_m
+    # x 4 bytes past a 16-byte boundary: the few-rows kernel and its split
+    rows, _, _ = sg.plan(1, 4096, 4096, 0x10004, None, 0x20000, None, 0x30000, None,
+                         trans_b=True)
+    assert rows.variant == sg.VARIANT_SKINNY and rows.group_m > 1, (rows.tile, rows.group_m)
+
+
 def test_epilogue_entry_point_validation():
     """sgemm_epilogue: act codes, bias alignment, and the quick returns that
     no longer apply when an epilogue is asked for are checked on the host."""
