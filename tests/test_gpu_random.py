@@ -7,10 +7,10 @@ Inputs are mostly integers in [-4, 4] and alpha, beta small dyadic
 rationals, so every product and sum is exact in fp32 and the whole of C must
 match the oracle bit for bit whatever kernel, tile, split or summation order
 the library picks; a third of the single products take uniform [-1, 1]
-inputs held to the fp32 tolerance.  With beta = 0, C starts as NaN (C is never read).  The shape
-draws mix tiny problems, skinny ones (M or N up to 16, long K), mid-size
-ragged ones and a few that span many tiles, so that every kernel family and
-its edge paths are reached.
+inputs held to the fp32 tolerance.  With beta = 0, C starts as NaN (C is
+never read).  The shape draws mix tiny problems, skinny ones (M or N up to
+16, long K), mid-size ragged ones and a few that span many tiles, so that
+every kernel family and its edge paths are reached.
 """
 from __future__ import annotations
 
@@ -40,7 +40,8 @@ def draw_shape(rng):
     if kind == 0:   # tiny
         return tuple(int(v) for v in rng.integers(1, 40, 3))
     if kind == 1:   # few rows or few columns, long K
-        small, wide, k = int(rng.integers(1, 17)), int(rng.integers(1, 3000)), int(rng.integers(1, 6000))
+        small, wide = int(rng.integers(1, 17)), int(rng.integers(1, 3000))
+        k = int(rng.integers(1, 6000))
         return (small, wide, k) if rng.integers(0, 2) else (wide, small, k)
     if kind == 2:   # mid-size, ragged
         return tuple(int(v) for v in rng.integers(40, 700, 3))
@@ -123,7 +124,8 @@ def test_random_batches(block, oracle_mod):
         Bs = np.ascontiguousarray(B.transpose(0, 2, 1)) if tb else B
         dB = torch.from_numpy(Bs[0] if shared else Bs).to(DEV)
         dC = torch.from_numpy(C0).to(DEV)
-        label = f"batch block {block} case {case}: {bat} x {(M, N, K)} ta={ta} tb={tb} shared={shared}"
+        label = (f"batch block {block} case {case}: {bat} x {(M, N, K)} ta={ta} tb={tb} "
+                 f"shared={shared}")
         print(label, flush=True)
         sg.gemm_batched(torch.from_numpy(As).to(DEV), dB, dC, alpha, beta, trans_a=ta, trans_b=tb)
         torch.cuda.synchronize()
@@ -154,8 +156,9 @@ def test_random_16bit(tname, oracle_mod):
         dC = torch.from_numpy(C0 if beta != 0.0 else np.full((M, N), np.nan, dtype=F32)).to(DEV)
         label = f"{tname} case {case}: {(M, N, K)} ta={ta} tb={tb} alpha={alpha} beta={beta}"
         print(label, flush=True)
-        sg.gemm_mixed(torch.from_numpy(As).to(DEV).to(dtype), torch.from_numpy(Bs).to(DEV).to(dtype),
-                      dC, alpha, beta, trans_a=ta, trans_b=tb)
+        dA = torch.from_numpy(As).to(DEV).to(dtype)
+        dB = torch.from_numpy(Bs).to(DEV).to(dtype)
+        sg.gemm_mixed(dA, dB, dC, alpha, beta, trans_a=ta, trans_b=tb)
         torch.cuda.synchronize()
         ref = oracle_mod.sgemm(As, Bs, C0.copy(), alpha, beta, trans_a=ta, trans_b=tb)
         assert np.array_equal(dC.cpu().numpy(), ref), label
