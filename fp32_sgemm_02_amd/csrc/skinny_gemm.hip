@@ -499,9 +499,10 @@ int rows_kslice(const Problem &p, int want, int *slices) {
     return *slices == 1 ? 16 * ((p.K + 15) / 16) : kslice;
 }
 
-// Columns per strip of a few-rows launch with `slices` K slices.  Each CU
-// streams at most ~25 GB/s, so a launch whose workgroups are fewer than the
-// CUs, each reading a large share of B, ends when the busiest CU does:
+// Columns per strip of a few-rows launch with `slices` K slices.  A
+// workgroup of these kernels streams about 20-25 GB/s (one per CU), so a
+// launch whose workgroups are fewer than the CUs, each reading a large share
+// of B, leaves CUs idle and ends when the slowest workgroup does:
 // 16 x 14336 x 4096 with B stored N x K in 64-row strips is 224 workgroups
 // of 1 MB for 256 CUs.  With B stored transposed and large (32 MB or more)
 // the strips are narrowed so that strips x slices comes as close to the CU
